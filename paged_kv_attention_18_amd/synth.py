@@ -1,0 +1,225 @@
+"""Seeded synthetic inputs for the paged-attention forward pass.
+
+This module draws lengths, block tables and query/key/value values.  It holds
+none of the attention arithmetic, so the oracle and the HIP path can both be
+fed from it.
+
+Recipe (one seed per workload):
+  * numpy ``Generator(PCG64(seed))`` draws, in this order, the context lengths
+    (and query lengths), then one permutation of the physical block ids;
+  * query, key cache and value cache are float32 N(0, 1) from
+    ``torch.Generator`` seeded with ``seed * 16 + {1, 2, 3}`` on the target
+    device, drawn in chunks and rounded to fp16/bf16 (round to nearest even);
+  * every sequence takes the next ceil(kv / block_size) ids of the permutation,
+    so no physical block is shared; unused table entries hold block 0, a valid
+    id as the pages require of every entry;
+  * blocks that no sequence references (the slack) keep their random values.
+
+The five named workloads follow the shapes, dtypes, length mixes and mask
+modes of the operator's documented use: decode (one query token per sequence),
+GQA decode, long skewed decode, parallel decoding / splitfuse with the causal
+mask aligned at prefix = kvSeqLen - qSeqLen, and single-KV-head decode with
+576/512 key/value head sizes.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Callable, Optional
+
+import numpy as np
+import torch
+
+DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    head_num: int
+    kv_head_num: int
+    head_size_k: int
+    head_size_v: int
+    block_size: int
+    dtype: str                 # "f16" | "bf16"
+    mask: str                  # "none" | "causal"
+    scale: float
+    lengths: Callable          # rng -> (context_lens int32[B], q_seq_lens int32[B] or None)
+    num_blocks: Optional[int] = None   # fixed pool size; None -> used blocks + slack
+    slack: float = 0.10
+    seed: int = 0
+
+
+def _tiny_lengths(rng):
+    return rng.integers(1, 129, size=4).astype(np.int32), None
+
+
+def _gqa_lengths(rng):
+    return rng.integers(512, 4097, size=64).astype(np.int32), None
+
+
+def _skewed_lengths(rng):
+    u = rng.uniform(math.log(256.0), math.log(32768.0), size=256)
+    kv = np.clip(np.floor(np.exp(u)), 256, 32768).astype(np.int32)
+    kv[rng.choice(256, size=4, replace=False)] = 32768   # "a few sequences at 32768"
+    return kv, None
+
+
+def _splitfuse_lengths(rng):
+    qlen = rng.choice(np.array([4, 8, 16], dtype=np.int32), size=32)
+    qlen[rng.choice(32, size=16, replace=False)] = 512      # prefill chunks for half the batch
+    hist = rng.integers(0, 8193, size=32).astype(np.int32)
+    return (qlen + hist).astype(np.int32), qlen.astype(np.int32)
+
+
+def _mla_lengths(rng):
+    return rng.integers(1024, 16385, size=128).astype(np.int32), None
+
+
+WORKLOADS = {
+    1: Workload("tiny_decode", 4, 4, 4, 64, 64, 16, "f16", "none", 1.0 / 8.0,
+                _tiny_lengths, num_blocks=64, seed=1001),
+    2: Workload("gqa_decode", 64, 32, 8, 128, 128, 128, "bf16", "none", 1.0 / math.sqrt(128),
+                _gqa_lengths, seed=1002),
+    3: Workload("skewed_long_decode", 256, 64, 8, 128, 128, 128, "f16", "none",
+                1.0 / math.sqrt(128), _skewed_lengths, seed=1003),
+    4: Workload("splitfuse_causal", 32, 32, 8, 128, 128, 128, "f16", "causal",
+                1.0 / math.sqrt(128), _splitfuse_lengths, seed=1004),
+    5: Workload("mla_decode", 128, 64, 1, 576, 512, 128, "bf16", "none", 1.0 / math.sqrt(576),
+                _mla_lengths, seed=1005),
+}
+
+
+def by_name(name: str) -> Workload:
+    for w in WORKLOADS.values():
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def fixed_lengths(context_lens, q_seq_lens=None):
+    """A ``lengths`` callable that ignores the generator (for hand-made cases)."""
+    kv = np.asarray(context_lens, dtype=np.int32)
+    ql = None if q_seq_lens is None else np.asarray(q_seq_lens, dtype=np.int32)
+    return lambda rng: (kv.copy(), None if ql is None else ql.copy())
+
+
+@dataclasses.dataclass
+class Problem:
+    """One generated input set.  Tensors live on ``device``; lengths and
+    tables are also kept as host numpy arrays."""
+    workload: Workload
+    context_lens: torch.Tensor       # int32 [B]
+    q_seq_lens: Optional[torch.Tensor]  # int32 [B] or None (one query token each)
+    block_tables: torch.Tensor       # int32 [B, max_num_blocks_per_seq]
+    query: torch.Tensor              # [T, H, Dk]
+    key_cache: torch.Tensor          # [num_blocks, block_size, Hkv, Dk]
+    value_cache: torch.Tensor        # [num_blocks, block_size, Hkv, Dv]
+    context_lens_np: np.ndarray
+    q_seq_lens_np: Optional[np.ndarray]
+    block_tables_np: np.ndarray
+    num_blocks: int
+    max_num_blocks_per_seq: int
+
+    @property
+    def batch(self) -> int:
+        return int(self.context_lens_np.shape[0])
+
+    @property
+    def num_q_tokens(self) -> int:
+        return int(self.query.shape[0])
+
+    @property
+    def max_q_seq_len(self) -> int:
+        if self.q_seq_lens_np is None:
+            return 1
+        return int(self.q_seq_lens_np.max()) if self.batch else 0
+
+    def kv_tokens(self) -> int:
+        return int(self.context_lens_np.astype(np.int64).sum())
+
+
+def _normal(shape, dtype, seed, device, chunk_elems=1 << 26):
+    """float32 N(0,1) from a seeded torch generator, rounded to ``dtype``."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    n = flat.numel()
+    for s in range(0, n, chunk_elems):
+        e = min(n, s + chunk_elems)
+        flat[s:e] = torch.randn(e - s, generator=gen, device=device, dtype=torch.float32).to(dtype)
+    return out
+
+
+def make_block_tables(context_lens, block_size, rng, num_blocks=None, slack=0.10, max_blocks=None):
+    """Distinct physical blocks per sequence, drawn from one permutation."""
+    need = (context_lens.astype(np.int64) + block_size - 1) // block_size
+    used = int(need.sum())
+    if num_blocks is None:
+        num_blocks = max(1, int(math.ceil(used * (1.0 + slack))))
+    if used > num_blocks:
+        raise ValueError(f"{used} blocks needed, pool has {num_blocks}")
+    mb = int(need.max()) if need.size else 0
+    if max_blocks is not None:
+        mb = max(mb, int(max_blocks))
+    mb = max(mb, 1)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    tables = np.zeros((context_lens.shape[0], mb), dtype=np.int32)
+    k = 0
+    for b, n in enumerate(need):
+        tables[b, :n] = perm[k:k + n]
+        k += n
+    return tables, num_blocks
+
+
+def generate(w: Workload, device="cpu", seed: Optional[int] = None, values=True,
+             max_blocks=None) -> Problem:
+    """Draw one problem for workload ``w`` (see the module docstring)."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kv, ql = w.lengths(rng)
+    kv = np.asarray(kv, dtype=np.int32)
+    tables, nb = make_block_tables(kv, w.block_size, rng, w.num_blocks, w.slack, max_blocks)
+    T = int(kv.shape[0]) if ql is None else int(np.asarray(ql, dtype=np.int64).sum())
+    dt = DTYPES[w.dtype]
+    qshape = (T, w.head_num, w.head_size_k)
+    kshape = (nb, w.block_size, w.kv_head_num, w.head_size_k)
+    vshape = (nb, w.block_size, w.kv_head_num, w.head_size_v)
+    if values:
+        q = _normal(qshape, dt, seed * 16 + 1, device)
+        kc = _normal(kshape, dt, seed * 16 + 2, device)
+        vc = _normal(vshape, dt, seed * 16 + 3, device)
+    else:
+        q = torch.zeros(qshape, dtype=dt, device=device)
+        kc = torch.zeros(kshape, dtype=dt, device=device)
+        vc = torch.zeros(vshape, dtype=dt, device=device)
+    return Problem(
+        workload=w,
+        context_lens=torch.from_numpy(kv.copy()).to(device),
+        q_seq_lens=None if ql is None else torch.from_numpy(np.asarray(ql, np.int32).copy()).to(device),
+        block_tables=torch.from_numpy(tables.copy()).to(device),
+        query=q, key_cache=kc, value_cache=vc,
+        context_lens_np=kv, q_seq_lens_np=None if ql is None else np.asarray(ql, np.int32),
+        block_tables_np=tables, num_blocks=nb, max_num_blocks_per_seq=int(tables.shape[1]),
+    )
+
+
+def custom(batch_lens, head_num, kv_head_num, head_size_k, head_size_v, block_size,
+           dtype="f16", mask="none", scale=None, q_seq_lens=None, num_blocks=None,
+           slack=0.25, seed=7, name="custom", device="cpu", max_blocks=None) -> Problem:
+    """A small hand-shaped problem (tests)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_size_k)
+    w = Workload(name, len(batch_lens), head_num, kv_head_num, head_size_k, head_size_v,
+                 block_size, dtype, mask, float(scale), fixed_lengths(batch_lens, q_seq_lens),
+                 num_blocks=num_blocks, slack=slack, seed=seed)
+    return generate(w, device=device, max_blocks=max_blocks)
+
+
+def kv_bytes(p: Problem) -> int:
+    """Key+value bytes the method must read: each visible (sequence, KV head,
+    token) row once, K and V head sizes at 2 bytes per element."""
+    w = p.workload
+    return p.kv_tokens() * w.kv_head_num * (w.head_size_k + w.head_size_v) * 2

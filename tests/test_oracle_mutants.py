@@ -1,0 +1,66 @@
+"""Plants plausible mistakes in the oracle's C source and checks that each one
+makes at least one pin fail (so the pins would have caught it).  CPU only; the
+mutants are compiled into a temporary directory and never touch the oracle
+that the other tests use."""
+import os
+
+import pytest
+
+import pins
+from oracle import pa_ref
+
+# (name, exact snippet in pa_ref.c, mistaken replacement)
+MUTANTS = [
+    ("gqa_modulo", "const int g = h / group;", "const int g = h % Hkv;"),
+    ("slot_shift", "int slot = j % bs;\n        const int64_t krow",
+     "int slot = (j + 1) % bs;\n        const int64_t krow"),
+    ("causal_off_by_one", "if (P->mask == REF_MASK_CAUSAL && prefix + i + 1 < n)\n        n = prefix + i + 1;",
+     "if (P->mask == REF_MASK_CAUSAL && prefix + i < n)\n        n = prefix + i;"),
+    ("causal_always", "if (P->mask == REF_MASK_CAUSAL && prefix + i + 1 < n)",
+     "if (prefix + i + 1 < n)"),
+    ("prefix_plus_one", "const int prefix = kv - qlen > 0 ? kv - qlen : 0;",
+     "const int prefix = kv - qlen + 1 > 0 ? kv - qlen + 1 : 0;"),
+    ("no_scale", "z[j] = P->scale * dot;", "z[j] = dot;"),
+    ("lse_no_log", "*lse = zmax + log(wsum);", "*lse = zmax + wsum;"),
+    ("kv_layout_bhsd", "const int64_t krow = (((int64_t)phys * bs + slot) * Hkv + g) * Dk;",
+     "const int64_t krow = (((int64_t)phys * Hkv + g) * bs + slot) * Dk;"),
+    ("v_layout_bhsd", "const int64_t vrow = (((int64_t)phys * bs + slot) * Hkv + g) * Dv;",
+     "const int64_t vrow = (((int64_t)phys * Hkv + g) * bs + slot) * Dv;"),
+    ("mean_not_softmax", "o[e] /= wsum;", "o[e] /= (double)n;"),
+    ("row_offset_dropped", "const int64_t t = P->row_start[b] + i;", "const int64_t t = i;"),
+    ("q_head_is_kv_head", "const uint16_t *q = P->query + (t * H + h) * (int64_t)Dk;",
+     "const uint16_t *q = P->query + (t * H + g) * (int64_t)Dk;"),
+    ("f16_exponent_bias", "v = ldexp((double)(1024 + frac), expo - 25);",
+     "v = ldexp((double)(1024 + frac), expo - 24);"),
+    ("f16_subnormal_scale", "v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
+    ("bf16_shift", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = ((uint32_t)b << 16) | 0x8000u;"),
+    ("table_row_stride",
+     "int32_t phys = P->block_tables[(int64_t)b * P->max_num_blocks_per_seq + j / bs];\n        if (phys < 0",
+     "int32_t phys = P->block_tables[(int64_t)b * (P->max_num_blocks_per_seq - 1) + j / bs];\n        if (phys < 0"),
+    ("v_uses_first_token", "o[e] += z[j] * elem(P->value_cache, vrow + e, P->dtype);",
+     "o[e] += z[j] * elem(P->value_cache, vrow - (int64_t)slot * Hkv * Dv + e, P->dtype);"),
+    ("exp_without_shift_in_lse", "*lse = zmax + log(wsum);", "*lse = log(wsum);"),
+]
+
+
+def test_mutant_snippets_are_unique():
+    src = open(pa_ref.SRC).read()
+    for name, old, new in MUTANTS:
+        assert src.count(old) == 1, name
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(pa_ref.SRC).read()
+    assert src.count(old) == 1
+    path = tmp_path / f"mut_{name}.c"
+    path.write_text(src.replace(old, new))
+    lib_path = pa_ref.build(str(path), str(tmp_path / f"libmut_{name}.so"))
+    lib = pa_ref.load(lib_path)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passes every pin"
