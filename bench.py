@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of the paged-attention forward pass on one MI355X.
+
+One step is one full forward pass (plan + attention + merge) over one batch of
+the named synthetic workload (default: GQA decode, batch 64, 32 query / 8 KV
+heads, head size 128, block size 128, context lengths uniform in
+[512, 4096], bf16).  Inputs are resident in HBM before timing starts; the
+timed steps rotate over several copies of the KV cache so no step finds the
+previous step's KV bytes in the caches.
+
+Prints one JSON line: tokens/s (query tokens per second), the attention
+kernel's achieved HBM bandwidth on the KV bytes the method must read (each
+visible (sequence, KV head, token) row of K and V once) against the 8 TB/s
+peak, and the oracle's own throughput on the host cores for context.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode tokens/s + achieved HBM GB/s (KV bytes read) vs peak, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+CPU_SHARE = 16          # host threads a one-GPU machine grants
+
+
+def kernel_sources_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_attention_18_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources") != kernel_sources_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(p, target_s, threads):
+    """The oracle on a bounded sample of the same workload (whole sequences,
+    all heads), timed on the host cores."""
+    import numpy as np
+    import torch
+
+    from oracle import pa_ref
+
+    w = p.workload
+    kv = p.context_lens_np.astype(np.int64)
+    ql = np.ones(p.batch, np.int64) if p.q_seq_lens_np is None else p.q_seq_lens_np.astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(ql)])
+    # oracle work per sequence ~ rows x visible tokens x (Dk + Dv)
+    cost = ql * kv * w.head_num * (w.head_size_k + w.head_size_v)
+    order = np.random.default_rng(0).permutation(p.batch)
+
+    def sub_problem(seqs):
+        bs = w.block_size
+        blocks, tables = [], []
+        for b in seqs:
+            n = int((kv[b] + bs - 1) // bs)
+            tables.append(list(range(len(blocks), len(blocks) + n)))
+            blocks.extend(p.block_tables_np[b, :n].tolist())
+        mb = max(1, max(len(t) for t in tables))
+        bt = np.zeros((len(seqs), mb), np.int32)
+        for i, t in enumerate(tables):
+            bt[i, :len(t)] = t
+        idx = torch.tensor(blocks, dtype=torch.long, device=p.key_cache.device)
+        qidx = torch.cat([torch.arange(int(cu[b]), int(cu[b + 1])) for b in seqs]).to(p.query.device)
+        return pa_ref.Inputs(p.query[qidx], p.key_cache[idx], p.value_cache[idx], bt, kv[seqs],
+                             None if p.q_seq_lens_np is None else ql[seqs], w.head_num, w.kv_head_num,
+                             w.dtype, w.mask, w.scale)
+
+    # calibrate the oracle's rate on the cheapest sequence
+    b0 = int(np.argmin(cost))
+    inp0 = sub_problem([b0])
+    t = time.perf_counter()
+    pa_ref.forward(inp0, threads=1)
+    rate = cost[b0] / max(1e-6, time.perf_counter() - t)           # work units / s / thread
+    budget = target_s * rate * threads
+    seqs, acc = [], 0.0
+    for b in order:
+        if acc + cost[b] > budget and seqs:
+            continue
+        seqs.append(int(b))
+        acc += cost[b]
+    seqs.sort()
+    inp = sub_problem(seqs)
+    t = time.perf_counter()
+    pa_ref.forward(inp, threads=threads)
+    dt = time.perf_counter() - t
+    tokens = int(ql[seqs].sum())
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(seqs)} of {p.batch} sequences ({tokens} query tokens, all {w.head_num} heads, "
+                      f"{int(kv[seqs].sum())} KV tokens), fp64, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa_decode",
+                    help="tiny_decode | gqa_decode | skewed_long_decode | splitfuse_causal | mla_decode")
+    ap.add_argument("--copies", type=int, default=0, help="KV cache copies to rotate over (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size, in seconds")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention has no cross-GPU path here)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_kv_attention_18_amd import binding, synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return
+
+    w = synth.WORKLOADS[int(args.workload)] if args.workload.isdigit() else synth.by_name(args.workload)
+    p = synth.generate(w, device=dev)
+    cache_bytes = (p.key_cache.numel() + p.value_cache.numel()) * p.key_cache.element_size()
+    copies = args.copies or max(3, math.ceil((1.5 * (1 << 30)) / cache_bytes))
+    kcs = [p.key_cache] + [p.key_cache.clone() for _ in range(copies - 1)]
+    vcs = [p.value_cache] + [p.value_cache.clone() for _ in range(copies - 1)]
+    att = binding.for_problem(p)
+    desc = att.describe()
+    out = torch.empty(p.num_q_tokens, w.head_num, w.head_size_v, dtype=p.query.dtype, device=dev)
+    ql_max = max(1, p.max_q_seq_len)
+
+    def step(k):
+        att.forward(p.query, kcs[k % copies], vcs[k % copies], p.block_tables, p.context_lens,
+                    p.q_seq_lens, max_q_seq_len=ql_max, out=out)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    if att.device_error() != 0:
+        raise RuntimeError("device error flag set during warm-up")
+
+    binding.pa_set_timing(att.handle, 1)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step(k)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    kms, passes = binding.pa_read_timing(att.handle)
+    binding.pa_set_timing(att.handle, 0)
+    assert passes == args.steps
+
+    ms_per_step = total_ms / args.steps
+    tokens = p.num_q_tokens
+    kv_bytes = synth.kv_bytes(p)
+    attn_ms = kms[1] / passes
+    achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+    kernel = "decode_kernel" if desc["path"] == "valu" else "tile_kernel"
+    traffic = measured_traffic(w.name, kernel)
+
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": p.batch, "head_num": w.head_num, "kv_head_num": w.kv_head_num,
+            "head_size_k": w.head_size_k, "head_size_v": w.head_size_v, "block_size": w.block_size,
+            "mask": w.mask, "query_tokens": tokens, "kv_tokens": p.kv_tokens(), "kv_bytes": kv_bytes,
+            "seed": w.seed, "kv_cache_copies": copies, "path": desc["path"],
+            "partitions": desc["partitions"], "parallelism": "none (1 GPU)",
+        },
+        "pass_hbm_gbps": kv_bytes / (ms_per_step * 1e-3) / 1e9,
+        "kernels_ms": {"plan": kms[0] / passes, "attention": attn_ms, "merge": kms[2] / passes},
+        "roofline": {
+            "kernel": kernel,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        threads = min(CPU_SHARE, len(os.sched_getaffinity(0)))
+        result["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds, threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-attention forward library.
+ *
+ * The operation (Ascend ATB "PagedAttentionOperation", Constraints; the pages
+ * give the operator's tensors and constraints, the formula is the usual
+ * attention): for every sequence b, query token i of b and query head h,
+ *
+ *     out[t0+i][h] = softmax_j( scale * q[t0+i][h] . K_j + mask(i, j) ) . V_j
+ *
+ * over the KV tokens j < context_lens[b] of sequence b, where
+ *   - token j sits in physical block block_tables[b][j / block_size], slot
+ *     j % block_size; every table entry is in [0, num_blocks) and each row
+ *     holds at least ceil(context_lens[b] / block_size) ids (Constraints);
+ *   - query head h reads KV head h / (head_num / kv_head_num) (GQA requires
+ *     head_num % kv_head_num == 0, Constraints);
+ *   - scale is one scalar (scaleType TOR, Constraints, mask type 5 list);
+ *   - PA_MASK_NONE: every row sees all context_lens[b] tokens (maskType
+ *     UNDEFINED, Constraints); PA_MASK_CAUSAL: parallel decoding / splitfuse
+ *     (mask type 5), context_lens[b] counts history plus the current query
+ *     tokens, prefix = max(0, context_lens[b] - q_seq_lens[b]), and row i
+ *     sees tokens j <= prefix + i (the causal mask with its upper triangle,
+ *     diagonal excluded, invisible; Constraints, mask type 5 list).  Masked
+ *     tokens get weight exactly 0;
+ *   - query and output rows are packed (TND): sequence b's rows start at
+ *     t0 = q_seq_lens[0] + ... + q_seq_lens[b-1] (the cu_seqlens_q prefix-sum
+ *     convention of the SparseAttnSharedkvMetadata README, parameter table);
+ *   - key and value head sizes may differ, each in (0, 576]
+ *     (Constraints: head sizes; block_size <= 128 when either exceeds 256).
+ *
+ * Accumulation is fp32; out has the query's dtype (round to nearest even);
+ * the optional lse output is fp32, natural log: lse = max_j z_j + ln sum_j
+ * exp(z_j - max_j z_j) with z_j = scale * q . K_j.  A row with no visible
+ * token gets out = 0 and lse = -inf.
+ *
+ * Ownership: every tensor argument of pa_forward is a device pointer owned by
+ * the caller.  The handle owns its workspace (work plan, split partials, an
+ * error word), allocated once by pa_create and freed by pa_destroy.
+ * pa_forward allocates nothing, does not synchronise, and enqueues all of its
+ * work on the given stream, so it may be captured in a HIP graph.  One handle
+ * must not be used by two streams at once (the workspace is shared).
+ *
+ * Errors: functions return a pa_status synchronously.  Argument and shape
+ * errors are reported before any device work is queued.  Problems that can
+ * only be seen in device data (a block id outside [0, num_blocks), a table
+ * too short for context_lens, q_seq_lens > context_lens in causal mode,
+ * q_seq_lens that do not sum to num_q_tokens, negative lengths) never cause an
+ * out-of-bounds access: the kernels clamp them and set a device error word
+ * that pa_get_device_error reads back.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,   /* NULL pointer, bad size, shape outside the documented limits */
+    PA_ERR_UNSUPPORTED = 2,   /* valid by the operator's rules but not built here (see pa_create) */
+    PA_ERR_HIP = 3,           /* a HIP runtime call failed */
+    PA_ERR_OOM = 4            /* workspace allocation failed */
+} pa_status;
+
+typedef enum { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
+
+typedef enum {
+    PA_MASK_NONE = 0,    /* maskType UNDEFINED: all context_lens[b] tokens visible */
+    PA_MASK_CAUSAL = 1   /* mask type 5 (parallel decoding / splitfuse), prefix-aligned */
+} pa_mask;
+
+/* pa_config.flags */
+enum {
+    PA_FLAG_FORCE_VALU = 1u << 0,  /* testing: take the VALU decode path whenever it can run */
+    PA_FLAG_FORCE_MFMA = 1u << 1,  /* testing: take the MFMA tile path always */
+    PA_FLAG_NO_SPLIT = 1u << 2     /* testing: one workgroup per (sequence, KV head, row tile); no merge */
+};
+
+/* Device error word bits (pa_get_device_error). */
+enum {
+    PA_DEVERR_BLOCK_ID = 1u << 0,     /* a block id outside [0, num_blocks): read as zeros */
+    PA_DEVERR_TABLE_SHORT = 1u << 1,  /* ceil(context_lens / block_size) > max_num_blocks_per_seq: clamped */
+    PA_DEVERR_QLEN = 1u << 2,         /* q_seq_lens < 0, > max_q_seq_len, or > context_lens (causal): clamped */
+    PA_DEVERR_TOKENS = 1u << 3,       /* sum of q_seq_lens != num_q_tokens: rows past the end not written */
+    PA_DEVERR_CTX = 1u << 4           /* context_lens < 0: treated as 0 */
+};
+
+typedef struct {
+    int32_t head_num;                /* query heads H */
+    int32_t kv_head_num;             /* KV heads Hkv; H % Hkv == 0 */
+    int32_t head_size_k;             /* key / query head size Dk, 0 < Dk <= 576 */
+    int32_t head_size_v;             /* value / output head size Dv, 0 < Dv <= 576 */
+    int32_t block_size;              /* tokens per KV block; % 16 == 0; <= 256, <= 128 in causal
+                                        mode or when Dk or Dv > 256 */
+    int64_t num_blocks;              /* physical blocks in each cache */
+    int32_t max_batch;               /* largest batch pa_forward will be given */
+    int32_t max_num_blocks_per_seq;  /* block_tables row length (its stride, in int32) */
+    int32_t max_q_seq_len;           /* largest q_seq_lens[b] pa_forward will be given (1 for decode) */
+    pa_dtype dtype;                  /* query, caches and output */
+    float scale;                     /* the TOR scale, e.g. 1/sqrt(Dk) */
+    pa_mask mask;
+    uint32_t flags;                  /* PA_FLAG_* */
+    int32_t num_partitions;          /* workgroups of the attention launch; 0 = chosen from the CU count */
+} pa_config;
+
+typedef struct pa_handle pa_handle;
+
+/*
+ * Validates cfg, selects the kernels, and allocates the workspace on the
+ * current HIP device.  Rules checked before any HIP call (PA_ERR_INVALID_ARG):
+ * H, Hkv > 0 and H % Hkv == 0; 0 < Dk, Dv <= 576; block_size > 0,
+ * block_size % 16 == 0, block_size <= 256, and block_size <= 128 in causal
+ * mode or when Dk or Dv > 256; num_blocks > 0; max_batch > 0;
+ * max_num_blocks_per_seq > 0; max_q_seq_len > 0; dtype and mask in range;
+ * scale finite; num_partitions >= 0.  PA_ERR_UNSUPPORTED: a (Dk, Dv) pair this
+ * build has no kernels for (64/64, 128/128, 256/256, 576/512 are built), or a
+ * device that is not gfx950.  On success *out receives the handle.
+ */
+pa_status pa_create(const pa_config *cfg, pa_handle **out);
+
+/*
+ * One forward pass, enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream).  All tensors are device pointers, row-major, contiguous:
+ *   query        [num_q_tokens, H, Dk]  dtype   (TND, rows of sequence b contiguous)
+ *   key_cache    [num_blocks, block_size, Hkv, Dk]  dtype
+ *   value_cache  [num_blocks, block_size, Hkv, Dv]  dtype
+ *   block_tables [batch, max_num_blocks_per_seq]  int32
+ *   context_lens [batch]  int32   (kvSeqLen: history + current query tokens)
+ *   q_seq_lens   [batch]  int32, or NULL for one query token per sequence
+ *   out          [num_q_tokens, H, Dv]  dtype   (written)
+ *   lse          [num_q_tokens, H]  float32, or NULL   (written)
+ * batch in [0, max_batch]; max_q_seq_len in [1, cfg.max_q_seq_len] bounds
+ * q_seq_lens (1 when q_seq_lens is NULL); num_q_tokens >= 0 equals the sum of
+ * q_seq_lens (batch when NULL).  Returns PA_ERR_INVALID_ARG for a NULL
+ * handle or tensor (q_seq_lens and lse excepted), a NULL q_seq_lens with
+ * num_q_tokens != batch, or sizes out of range; PA_ERR_HIP if a launch fails.
+ */
+pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache,
+                     const void *value_cache, const int32_t *block_tables,
+                     const int32_t *context_lens, const int32_t *q_seq_lens, int32_t batch,
+                     int32_t num_q_tokens, int32_t max_q_seq_len, void *out, float *lse,
+                     void *stream);
+
+/* Frees the workspace and the handle (synchronises the device first).  NULL is a no-op. */
+pa_status pa_destroy(pa_handle *h);
+
+/* A static English description of a status code. */
+const char *pa_status_string(pa_status s);
+
+/*
+ * Reads the device error word (PA_DEVERR_* bits accumulated since the last
+ * clear) into *code, then clears it if `clear` is non-zero.  Synchronises the
+ * device.
+ */
+pa_status pa_get_device_error(pa_handle *h, uint32_t *code, int32_t clear);
+
+/*
+ * Per-kernel timing for measurement.  While enabled, pa_forward records HIP
+ * events on its stream around each of its kernels (plan, attention, merge).
+ * pa_read_timing synchronises, adds up the elapsed times of all recorded
+ * passes since the last read into ms[3] (plan, attention, merge) and the
+ * number of passes into *count, and resets the totals.  At most 1024 passes
+ * are kept between reads; later ones are not timed.
+ */
+pa_status pa_set_timing(pa_handle *h, int32_t enable);
+pa_status pa_read_timing(pa_handle *h, double ms[3], int32_t *count);
+
+/*
+ * What pa_create chose, for logging and tests: *path is 0 for the VALU decode
+ * kernel, 1 for the MFMA tile kernel (for a call with max_q_seq_len =
+ * cfg.max_q_seq_len); *rows_per_tile and *tokens_per_chunk describe its work
+ * unit; *partitions is the attention grid size.
+ */
+pa_status pa_describe(const pa_handle *h, int32_t max_q_seq_len, int32_t *path,
+                      int32_t *rows_per_tile, int32_t *tokens_per_chunk, int32_t *partitions);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

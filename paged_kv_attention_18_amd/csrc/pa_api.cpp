@@ -1,0 +1,388 @@
+// pa_api.cpp -- host side of the C ABI declared in include/pa.h: argument
+// checks, kernel selection, workspace, launches and timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kMaxTimedPasses = 1024;
+
+struct Variant {
+    int path;        // 0 = VALU decode, 1 = MFMA tile
+    int rows_pad;    // VALU: padded rows per unit
+    int row_blocks;  // MFMA: 16-row blocks per wave
+    int rows_per_tile;
+    int chunk;
+    int partitions;  // balanced-mode grid
+};
+
+int next_pow2(int x)
+{
+    int p = 1;
+    while (p < x)
+        p <<= 1;
+    return p;
+}
+
+bool valid_dtype(int d) { return d == PA_F16 || d == PA_BF16; }
+bool valid_mask(int m) { return m == PA_MASK_NONE || m == PA_MASK_CAUSAL; }
+
+}  // namespace
+
+struct pa_handle {
+    pa_config cfg;
+    int device = 0;
+    int num_cus = 256;
+    void *ws_base = nullptr;
+    size_t ws_bytes = 0;
+    pa::Workspace ws{};
+    int max_partitions = 0;
+    size_t max_partial_floats = 0;
+    // timing
+    bool timing = false;
+    std::vector<hipEvent_t> events;   // 4 per pass
+    int timed = 0;
+
+    Variant choose(int max_q) const
+    {
+        Variant v{};
+        const int G = cfg.head_num / cfg.kv_head_num;
+        const int rows = max_q * G;
+        const bool dec_ok = pa::decode_supported(cfg.head_size_k, cfg.head_size_v);
+        bool valu = dec_ok && rows < 16;
+        if (cfg.flags & PA_FLAG_FORCE_VALU)
+            valu = dec_ok && rows <= 16;
+        if (cfg.flags & PA_FLAG_FORCE_MFMA)
+            valu = false;
+        if (valu) {
+            v.path = 0;
+            v.rows_pad = next_pow2(rows < 1 ? 1 : rows);
+            v.rows_per_tile = v.rows_pad;
+            v.chunk = pa::kDecodeChunk;
+            v.partitions = num_cus * pa::decode_wgs_per_cu(cfg.dtype, cfg.head_size_k, cfg.head_size_v, v.rows_pad);
+        } else {
+            v.path = 1;
+            const int r1 = pa::tile_rows(cfg.head_size_k, cfg.head_size_v, 1);
+            v.row_blocks = (rows > r1 && pa::tile_supported(cfg.head_size_k, cfg.head_size_v, 2)) ? 2 : 1;
+            v.rows_per_tile = pa::tile_rows(cfg.head_size_k, cfg.head_size_v, v.row_blocks);
+            v.chunk = pa::tile_chunk(cfg.head_size_k, cfg.head_size_v);
+            v.partitions = num_cus * pa::tile_wgs_per_cu(cfg.dtype, cfg.head_size_k, cfg.head_size_v, v.row_blocks);
+        }
+        if (cfg.num_partitions > 0)
+            v.partitions = cfg.num_partitions;
+        return v;
+    }
+};
+
+extern "C" {
+
+const char *pa_status_string(pa_status s)
+{
+    switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_OOM: return "out of device memory";
+    }
+    return "unknown status";
+}
+
+static pa_status check_config(const pa_config *c)
+{
+    if (!c)
+        return PA_ERR_INVALID_ARG;
+    if (c->head_num <= 0 || c->kv_head_num <= 0 || c->head_num % c->kv_head_num != 0)
+        return PA_ERR_INVALID_ARG;
+    if (c->head_size_k <= 0 || c->head_size_k > 576 || c->head_size_v <= 0 || c->head_size_v > 576)
+        return PA_ERR_INVALID_ARG;
+    if (c->block_size <= 0 || c->block_size % 16 != 0 || c->block_size > 256)
+        return PA_ERR_INVALID_ARG;
+    if ((c->mask == PA_MASK_CAUSAL || c->head_size_k > 256 || c->head_size_v > 256) && c->block_size > 128)
+        return PA_ERR_INVALID_ARG;
+    if (c->num_blocks <= 0 || c->max_batch <= 0 || c->max_num_blocks_per_seq <= 0 || c->max_q_seq_len <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (!valid_dtype(c->dtype) || !valid_mask(c->mask) || !std::isfinite(c->scale) || c->num_partitions < 0)
+        return PA_ERR_INVALID_ARG;
+    if ((c->flags & PA_FLAG_FORCE_VALU) && (c->flags & PA_FLAG_FORCE_MFMA))
+        return PA_ERR_INVALID_ARG;
+    if (c->flags & ~(uint32_t)(PA_FLAG_FORCE_VALU | PA_FLAG_FORCE_MFMA | PA_FLAG_NO_SPLIT))
+        return PA_ERR_INVALID_ARG;
+    // Item indices are int32 on the device: bound the largest possible count.
+    const int G = c->head_num / c->kv_head_num;
+    const double tiles = std::ceil((double)c->max_q_seq_len * G / 16.0);
+    const double chunks = std::ceil((double)c->max_num_blocks_per_seq * c->block_size / 32.0) + 1.0;
+    if ((double)c->max_batch * c->kv_head_num * tiles * chunks > 2.0e9)
+        return PA_ERR_INVALID_ARG;
+    if ((double)c->max_num_blocks_per_seq * c->block_size > 2.0e9)
+        return PA_ERR_INVALID_ARG;
+    // Shapes with kernels in this build.
+    const bool dec = pa::decode_supported(c->head_size_k, c->head_size_v);
+    const bool til = pa::tile_supported(c->head_size_k, c->head_size_v, 1);
+    if (!dec && !til)
+        return PA_ERR_UNSUPPORTED;
+    if ((c->flags & PA_FLAG_FORCE_VALU) && !dec)
+        return PA_ERR_UNSUPPORTED;
+    if ((c->flags & PA_FLAG_FORCE_MFMA) && !til)
+        return PA_ERR_UNSUPPORTED;
+    if (!til && (int64_t)c->max_q_seq_len * G > 16)
+        return PA_ERR_UNSUPPORTED;   // only the VALU kernel exists for this shape
+    return PA_OK;
+}
+
+pa_status pa_create(const pa_config *cfg, pa_handle **out)
+{
+    if (!out)
+        return PA_ERR_INVALID_ARG;
+    *out = nullptr;
+    pa_status st = check_config(cfg);
+    if (st != PA_OK)
+        return st;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return PA_ERR_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return PA_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return PA_ERR_UNSUPPORTED;
+
+    pa_handle *h = new (std::nothrow) pa_handle;
+    if (!h)
+        return PA_ERR_OOM;
+    h->cfg = *cfg;
+    h->device = dev;
+    h->num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+
+    // Largest grid and partial slot over every call this handle may see.
+    size_t max_floats = 0;
+    int max_p = 8;
+    // The variant depends on max_q * G only through thresholds at or below 65
+    // rows, so the calls with max_q <= 65 and max_q = cfg->max_q_seq_len
+    // cover every case.
+    const int qmax = cfg->max_q_seq_len;
+    std::vector<int> qs;
+    for (int q = 1; q <= qmax && q <= 65; ++q)
+        qs.push_back(q);
+    if (qmax > 65)
+        qs.push_back(qmax);
+    for (int q : qs) {
+        const Variant v = h->choose(q);
+        const size_t f = (size_t)v.rows_per_tile * (cfg->head_size_v + 2);
+        if (f > max_floats)
+            max_floats = f;
+        if (v.partitions > max_p)
+            max_p = v.partitions;
+    }
+    h->max_partitions = max_p;
+    h->max_partial_floats = max_floats;
+
+    const int B = cfg->max_batch;
+    auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    size_t off = 0;
+    const size_t o_hdr = off; off = align(off + 4 * sizeof(int32_t));
+    const size_t o_cuq = off; off = align(off + (B + 1) * sizeof(int32_t));
+    const size_t o_wsb = off; off = align(off + (B + 1) * sizeof(int32_t));
+    const size_t o_ipg = off; off = align(off + B * sizeof(int32_t));
+    const size_t o_ql = off; off = align(off + B * sizeof(int32_t));
+    const size_t o_kv = off; off = align(off + B * sizeof(int32_t));
+    const size_t o_wgb = off; off = align(off + max_p * sizeof(int32_t));
+    const size_t o_err = off; off = align(off + sizeof(uint32_t));
+    const size_t o_part = off; off = align(off + 2 * (size_t)max_p * max_floats * sizeof(float));
+    h->ws_bytes = off;
+    if (hipMalloc(&h->ws_base, h->ws_bytes) != hipSuccess) {
+        delete h;
+        return PA_ERR_OOM;
+    }
+    if (hipMemset(h->ws_base, 0, h->ws_bytes) != hipSuccess) {
+        (void)hipFree(h->ws_base);
+        delete h;
+        return PA_ERR_HIP;
+    }
+    char *base = (char *)h->ws_base;
+    h->ws.hdr = (int32_t *)(base + o_hdr);
+    h->ws.cu_q = (int32_t *)(base + o_cuq);
+    h->ws.wsb = (int32_t *)(base + o_wsb);
+    h->ws.ipg = (int32_t *)(base + o_ipg);
+    h->ws.qlen = (int32_t *)(base + o_ql);
+    h->ws.kvlen = (int32_t *)(base + o_kv);
+    h->ws.wg_b = (int32_t *)(base + o_wgb);
+    h->ws.err = (uint32_t *)(base + o_err);
+    h->ws.partials = (float *)(base + o_part);
+    *out = h;
+    return PA_OK;
+}
+
+pa_status pa_destroy(pa_handle *h)
+{
+    if (!h)
+        return PA_OK;
+    pa_status st = PA_OK;
+    if (hipDeviceSynchronize() != hipSuccess)
+        st = PA_ERR_HIP;
+    for (hipEvent_t e : h->events)
+        (void)hipEventDestroy(e);
+    if (h->ws_base && hipFree(h->ws_base) != hipSuccess)
+        st = PA_ERR_HIP;
+    delete h;
+    return st;
+}
+
+pa_status pa_describe(const pa_handle *h, int32_t max_q_seq_len, int32_t *path, int32_t *rows_per_tile,
+                      int32_t *tokens_per_chunk, int32_t *partitions)
+{
+    if (!h || max_q_seq_len < 1 || max_q_seq_len > h->cfg.max_q_seq_len)
+        return PA_ERR_INVALID_ARG;
+    const Variant v = h->choose(max_q_seq_len);
+    if (path)
+        *path = v.path;
+    if (rows_per_tile)
+        *rows_per_tile = v.rows_per_tile;
+    if (tokens_per_chunk)
+        *tokens_per_chunk = v.chunk;
+    if (partitions)
+        *partitions = v.partitions;
+    return PA_OK;
+}
+
+pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, const void *value_cache,
+                     const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_seq_lens,
+                     int32_t batch, int32_t num_q_tokens, int32_t max_q_seq_len, void *out, float *lse,
+                     void *stream)
+{
+    if (!h || !query || !key_cache || !value_cache || !block_tables || !context_lens || !out)
+        return PA_ERR_INVALID_ARG;
+    const pa_config &c = h->cfg;
+    if (batch < 0 || batch > c.max_batch || num_q_tokens < 0)
+        return PA_ERR_INVALID_ARG;
+    if (!q_seq_lens) {
+        if (num_q_tokens != batch || max_q_seq_len != 1)
+            return PA_ERR_INVALID_ARG;
+    }
+    if (max_q_seq_len < 1 || max_q_seq_len > c.max_q_seq_len)
+        return PA_ERR_INVALID_ARG;
+    if (batch == 0 || num_q_tokens == 0)
+        return PA_OK;
+    hipStream_t s = (hipStream_t)stream;
+    const Variant v = h->choose(max_q_seq_len);
+    const int G = c.head_num / c.kv_head_num;
+
+    pa::Params p{};
+    p.query = query;
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.q_seq_lens = q_seq_lens;
+    p.out = out;
+    p.lse = lse;
+    p.num_blocks = c.num_blocks;
+    p.batch = batch;
+    p.num_q_tokens = num_q_tokens;
+    p.head_num = c.head_num;
+    p.kv_head_num = c.kv_head_num;
+    p.group = G;
+    p.head_size_k = c.head_size_k;
+    p.head_size_v = c.head_size_v;
+    p.block_size = c.block_size;
+    p.bs_shift = (c.block_size & (c.block_size - 1)) == 0 ? __builtin_ctz(c.block_size) : -1;
+    p.max_blocks = c.max_num_blocks_per_seq;
+    p.max_q = max_q_seq_len;
+    p.causal = c.mask == PA_MASK_CAUSAL;
+    p.scale_log2 = c.scale * 1.4426950408889634f;
+    p.rows_per_tile = v.rows_per_tile;
+    p.chunk = v.chunk;
+    p.max_tiles = (max_q_seq_len * G + v.rows_per_tile - 1) / v.rows_per_tile;
+    p.no_split = (c.flags & PA_FLAG_NO_SPLIT) ? 1 : 0;
+    p.partitions = p.no_split ? batch * c.kv_head_num * p.max_tiles
+                              : (v.partitions < h->max_partitions ? v.partitions : h->max_partitions);
+    p.partial_stride = v.rows_per_tile * (c.head_size_v + 2);
+    p.ws = h->ws;
+
+    const bool timed = h->timing && h->timed < kMaxTimedPasses;
+    hipEvent_t *ev = timed ? &h->events[4 * h->timed] : nullptr;
+    if (timed && hipEventRecord(ev[0], s) != hipSuccess)
+        return PA_ERR_HIP;
+    if (pa::launch_plan(p, s) != hipSuccess)
+        return PA_ERR_HIP;
+    if (timed && hipEventRecord(ev[1], s) != hipSuccess)
+        return PA_ERR_HIP;
+    hipError_t e = v.path == 0 ? pa::launch_decode(p, c.dtype, v.rows_pad, s)
+                               : pa::launch_tile(p, c.dtype, v.row_blocks, s);
+    if (e != hipSuccess)
+        return PA_ERR_HIP;
+    if (timed && hipEventRecord(ev[2], s) != hipSuccess)
+        return PA_ERR_HIP;
+    if (pa::launch_merge(p, c.dtype, s) != hipSuccess)
+        return PA_ERR_HIP;
+    if (timed) {
+        if (hipEventRecord(ev[3], s) != hipSuccess)
+            return PA_ERR_HIP;
+        ++h->timed;
+    }
+    return PA_OK;
+}
+
+pa_status pa_get_device_error(pa_handle *h, uint32_t *code, int32_t clear)
+{
+    if (!h || !code)
+        return PA_ERR_INVALID_ARG;
+    if (hipDeviceSynchronize() != hipSuccess)
+        return PA_ERR_HIP;
+    if (hipMemcpy(code, h->ws.err, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+        return PA_ERR_HIP;
+    if (clear && hipMemset(h->ws.err, 0, sizeof(uint32_t)) != hipSuccess)
+        return PA_ERR_HIP;
+    if (clear && hipDeviceSynchronize() != hipSuccess)
+        return PA_ERR_HIP;
+    return PA_OK;
+}
+
+pa_status pa_set_timing(pa_handle *h, int32_t enable)
+{
+    if (!h)
+        return PA_ERR_INVALID_ARG;
+    if (enable && h->events.empty()) {
+        h->events.resize(4 * kMaxTimedPasses);
+        for (auto &e : h->events)
+            if (hipEventCreate(&e) != hipSuccess)
+                return PA_ERR_HIP;
+    }
+    h->timing = enable != 0;
+    h->timed = 0;
+    return PA_OK;
+}
+
+pa_status pa_read_timing(pa_handle *h, double ms[3], int32_t *count)
+{
+    if (!h || !ms || !count)
+        return PA_ERR_INVALID_ARG;
+    ms[0] = ms[1] = ms[2] = 0.0;
+    *count = h->timed;
+    if (h->timed > 0) {
+        if (hipEventSynchronize(h->events[4 * h->timed - 1]) != hipSuccess)
+            return PA_ERR_HIP;
+        for (int k = 0; k < h->timed; ++k) {
+            for (int j = 0; j < 3; ++j) {
+                float t = 0.f;
+                if (hipEventElapsedTime(&t, h->events[4 * k + j], h->events[4 * k + j + 1]) != hipSuccess)
+                    return PA_ERR_HIP;
+                ms[j] += t;
+            }
+        }
+    }
+    h->timed = 0;
+    return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,357 @@
+// pa_internal.h -- launch parameters, workspace layout and shared device code
+// of the paged-attention library (gfx950).  Internal: not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// Work decomposition (shared by the plan, attention and merge kernels).
+//
+//  unit  = (sequence b, KV head g, row tile qt).  A row is one (query token i,
+//          query head h of group g); the rows of (b, g) are ordered i-major,
+//          r = i * G + (h - g * G), and cut into tiles of R rows.
+//  item  = (unit, chunk c): the KV tokens [c * CT, (c + 1) * CT) of the unit,
+//          CT tokens per chunk.  A unit has nch = max(1, ceil(nvis / CT))
+//          items, nvis being the KV tokens its rows can see.
+//  Items are numbered b-major, then g, then qt, then c.  The attention grid
+//  of P workgroups takes contiguous ranges of `per` items each (balanced
+//  mode), or one unit per workgroup (no-split mode, per = 0).  A unit whose
+//  items are spread over several workgroups leaves fp32 partials (acc, m, l)
+//  that the merge kernel combines; slot 0 of workgroup w holds the partial of
+//  its first unit, slot 1 that of its last.
+
+struct Workspace {
+    int32_t *hdr;        // [4]: W (total items), per, P, unused
+    int32_t *cu_q;       // [max_batch + 1]: first packed query row of each sequence
+    int32_t *wsb;        // [max_batch + 1]: first item of each sequence
+    int32_t *ipg;        // [max_batch]: items of each (b, g) (equal for all g of b)
+    int32_t *qlen;       // [max_batch]: sanitised q_seq_lens
+    int32_t *kvlen;      // [max_batch]: sanitised context_lens
+    int32_t *wg_b;       // [P]: sequence holding the first item of each workgroup
+    float *partials;     // [2 * P][R * (DV + 2)]
+    uint32_t *err;       // device error word
+};
+
+struct Params {
+    const void *query;
+    const void *key_cache;
+    const void *value_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    const int32_t *q_seq_lens;   // may be null: one query token per sequence
+    void *out;
+    float *lse;                  // may be null
+    int64_t num_blocks;
+    int32_t batch, num_q_tokens, head_num, kv_head_num, group;
+    int32_t head_size_k, head_size_v;
+    int32_t block_size, bs_shift;      // bs_shift = log2(block_size) or -1
+    int32_t max_blocks;                // block_tables row length
+    int32_t max_q;                     // bound on q_seq_lens for this call
+    int32_t causal;
+    float scale_log2;                  // scale * log2(e)
+    int32_t rows_per_tile;             // R
+    int32_t chunk;                     // CT
+    int32_t partitions;                // P
+    int32_t no_split;
+    int32_t max_tiles;                 // ceil(max_q * G / R)
+    int32_t partial_stride;            // floats per partial slot = R * (DV + 2)
+    Workspace ws;
+};
+
+// Launchers (defined in the .hip files).
+hipError_t launch_plan(const Params &p, hipStream_t s);
+hipError_t launch_merge(const Params &p, int dtype, hipStream_t s);
+// Returns hipErrorInvalidValue when no kernel exists for the shape.
+hipError_t launch_decode(const Params &p, int dtype, int rows_pad, hipStream_t s);
+hipError_t launch_tile(const Params &p, int dtype, int row_blocks, hipStream_t s);
+// Shapes and occupancy used by the host to pick kernels and size the grid.
+bool decode_supported(int dk, int dv);
+bool tile_supported(int dk, int dv, int row_blocks);
+int decode_wgs_per_cu(int dtype, int dk, int dv, int rows_pad);   // resident workgroups per CU
+int tile_wgs_per_cu(int dtype, int dk, int dv, int row_blocks);
+int tile_chunk(int dk, int dv);
+int tile_rows(int dk, int dv, int row_blocks);
+
+constexpr int kDecodeChunk = 64;     // CT of the VALU decode kernel
+constexpr int kThreads = 256;        // threads per attention workgroup
+constexpr int kBtWindow = 256;       // block-table entries staged in LDS at a time
+
+#ifdef __HIPCC__
+// ------------------------------------------------------------ device side
+
+// Visible KV tokens of rows [r0, r1] of (b, g): a row (i, hh) sees tokens
+// j < kv, and in causal mode only j <= prefix + i.
+__device__ __forceinline__ int tile_nvis(int kv, int qlen, int G, int r1, int causal)
+{
+    if (!causal)
+        return kv;
+    const int prefix = kv - qlen > 0 ? kv - qlen : 0;
+    const int lim = prefix + r1 / G + 1;
+    return lim < kv ? lim : kv;
+}
+
+__device__ __forceinline__ int unit_chunks(int kv, int qlen, int G, int R, int CT, int qt, int causal)
+{
+    const int rows = qlen * G;
+    int r1 = (qt + 1) * R;
+    r1 = (r1 < rows ? r1 : rows) - 1;
+    const int n = tile_nvis(kv, qlen, G, r1, causal);
+    const int c = (n + CT - 1) / CT;
+    return c > 1 ? c : 1;
+}
+
+__device__ __forceinline__ void set_error(uint32_t *err, uint32_t bit)
+{
+    atomicOr(err, bit);
+}
+
+// fp32 -> fp16 / bf16 bit patterns, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
+{
+    _Float16 h = (_Float16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <int DT>
+__device__ __forceinline__ uint16_t to_bits(float f)
+{
+    if constexpr (DT == 0)
+        return f32_to_f16_bits(f);
+    else
+        return f32_to_bf16_bits(f);
+}
+
+// Low / high 16-bit element of a packed pair, widened to fp32.
+template <int DT>
+__device__ __forceinline__ float lo_f32(uint32_t w)
+{
+    if constexpr (DT == 0)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    else
+        return __builtin_bit_cast(float, w << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float hi_f32(uint32_t w)
+{
+    if constexpr (DT == 0)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    else
+        return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+__device__ __forceinline__ int div_bs(int j, int bs, int shift)
+{
+    return shift >= 0 ? (j >> shift) : (j / bs);
+}
+
+__device__ __forceinline__ int mod_bs(int j, int bs, int shift)
+{
+    return shift >= 0 ? (j & (bs - 1)) : (j % bs);
+}
+
+// Cross-lane moves.  pair_swap<D>: the value of the partner lane in the
+// other half of this lane's aligned group of 2D lanes.  For D < 16 the
+// partner is the mirror image (DPP row_mirror / row_half_mirror / quad_perm),
+// for D >= 16 it is lane ^ D.
+template <int D>
+__device__ __forceinline__ float pair_swap(float v)
+{
+    const int x = __builtin_bit_cast(int, v);
+    int r;
+    if constexpr (D == 8)
+        r = __builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false);   // row_mirror
+    else if constexpr (D == 4)
+        r = __builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false);   // row_half_mirror
+    else if constexpr (D == 2)
+        r = __builtin_amdgcn_mov_dpp(x, 0x4e, 0xf, 0xf, false);    // quad_perm 2,3,0,1
+    else if constexpr (D == 1)
+        r = __builtin_amdgcn_mov_dpp(x, 0xb1, 0xf, 0xf, false);    // quad_perm 1,0,3,2
+    else
+        r = __shfl_xor(x, D);
+    return __builtin_bit_cast(float, r);
+}
+
+// Transposing reduction.  On entry every lane of an aligned group of W lanes
+// holds NV partial sums v[0..NV) of the same NV quantities.  On exit lane l
+// holds complete sums: if NV >= W, v[0..NV/W) are quantities
+// (NV/W) * (l % W) + k; otherwise v[0] is quantity (l % W) / (W / NV).
+template <int NV, int W, int N>
+__device__ __forceinline__ void treduce(float (&v)[N], int lane)
+{
+    if constexpr (W > 1) {
+        constexpr int D = W / 2;
+        const bool upper = (lane & D) != 0;
+        if constexpr (NV >= 2) {
+#pragma unroll
+            for (int k = 0; k < NV / 2; ++k) {
+                const float keep = upper ? v[k + NV / 2] : v[k];
+                const float send = upper ? v[k] : v[k + NV / 2];
+                v[k] = keep + pair_swap<D>(send);
+            }
+            treduce<NV / 2, D>(v, lane);
+        } else {
+            v[0] += pair_swap<D>(v[0]);
+            treduce<1, D>(v, lane);
+        }
+    }
+}
+
+// Max over an aligned group of W lanes (every lane gets the result).
+template <int W>
+__device__ __forceinline__ float group_max(float v)
+{
+    if constexpr (W >= 64)
+        v = fmaxf(v, pair_swap<32>(v));
+    if constexpr (W >= 32)
+        v = fmaxf(v, pair_swap<16>(v));
+    if constexpr (W >= 16)
+        v = fmaxf(v, pair_swap<8>(v));
+    if constexpr (W >= 8)
+        v = fmaxf(v, pair_swap<4>(v));
+    if constexpr (W >= 4)
+        v = fmaxf(v, pair_swap<2>(v));
+    if constexpr (W >= 2)
+        v = fmaxf(v, pair_swap<1>(v));
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_sum(float v)
+{
+    if constexpr (W >= 64)
+        v += pair_swap<32>(v);
+    if constexpr (W >= 32)
+        v += pair_swap<16>(v);
+    if constexpr (W >= 16)
+        v += pair_swap<8>(v);
+    if constexpr (W >= 8)
+        v += pair_swap<4>(v);
+    if constexpr (W >= 4)
+        v += pair_swap<2>(v);
+    if constexpr (W >= 2)
+        v += pair_swap<1>(v);
+    return v;
+}
+
+// Workgroup index with consecutive logical indices on the same XCD: the
+// dispatcher deals workgroups round-robin over the 8 XCDs.
+__device__ __forceinline__ int xcd_logical_index(int bid, int nwg)
+{
+    if (nwg % 8 != 0)
+        return bid;
+    return (bid % 8) * (nwg / 8) + bid / 8;
+}
+
+// The cursor a workgroup walks its item range with.
+struct Cursor {
+    int b, g, qt, c;     // current unit and chunk
+    int nch;             // chunks of the current unit
+    int ntile;           // row tiles of sequence b
+    int item;            // global index of (unit, c)
+};
+
+__device__ __forceinline__ int seq_tiles(const Params &p, int qlen)
+{
+    return (qlen * p.group + p.rows_per_tile - 1) / p.rows_per_tile;
+}
+
+// Position the cursor at item `item`, which lies in sequence b.
+__device__ __forceinline__ void cursor_seek(const Params &p, Cursor &cu, int b, int item)
+{
+    const int kv = p.ws.kvlen[b];
+    const int ql = p.ws.qlen[b];
+    const int ipg = p.ws.ipg[b];
+    int local = item - p.ws.wsb[b];
+    cu.b = b;
+    cu.g = local / ipg;
+    local -= cu.g * ipg;
+    cu.ntile = seq_tiles(p, ql);
+    int qt = 0;
+    int n = unit_chunks(kv, ql, p.group, p.rows_per_tile, p.chunk, 0, p.causal);
+    while (local >= n) {
+        local -= n;
+        ++qt;
+        n = unit_chunks(kv, ql, p.group, p.rows_per_tile, p.chunk, qt, p.causal);
+    }
+    cu.qt = qt;
+    cu.c = local;
+    cu.nch = n;
+    cu.item = item;
+}
+
+// Move to the first chunk of the next unit (skipping sequences without
+// rows); the caller has already advanced cu.item past the current unit.
+__device__ __forceinline__ void cursor_next_unit(const Params &p, Cursor &cu)
+{
+    cu.c = 0;
+    if (++cu.qt >= cu.ntile) {
+        cu.qt = 0;
+        if (++cu.g >= p.kv_head_num) {
+            cu.g = 0;
+            do {
+                ++cu.b;
+            } while (cu.b < p.batch && p.ws.ipg[cu.b] == 0);
+            if (cu.b >= p.batch)
+                return;
+            cu.ntile = seq_tiles(p, p.ws.qlen[cu.b]);
+        }
+    }
+    cu.nch = unit_chunks(p.ws.kvlen[cu.b], p.ws.qlen[cu.b], p.group, p.rows_per_tile, p.chunk,
+                         cu.qt, p.causal);
+}
+
+// The item range of logical workgroup w; returns false if it has none.
+__device__ __forceinline__ bool wg_range(const Params &p, int w, Cursor &cu, int &end)
+{
+    const int W = p.ws.hdr[0];
+    const int per = p.ws.hdr[1];
+    if (per > 0) {
+        const int s = w * per;
+        if (s >= W)
+            return false;
+        end = s + per < W ? s + per : W;
+        cursor_seek(p, cu, p.ws.wg_b[w], s);
+        return true;
+    }
+    // no-split: workgroup w is unit (b, g, qt) with qt < max_tiles
+    const int per_b = p.kv_head_num * p.max_tiles;
+    const int b = w / per_b;
+    if (b >= p.batch)
+        return false;
+    const int g = (w % per_b) / p.max_tiles;
+    const int qt = w % p.max_tiles;
+    const int ql = p.ws.qlen[b];
+    if (qt >= seq_tiles(p, ql))
+        return false;
+    const int kv = p.ws.kvlen[b];
+    int start = p.ws.wsb[b] + g * p.ws.ipg[b];
+    for (int t = 0; t < qt; ++t)
+        start += unit_chunks(kv, ql, p.group, p.rows_per_tile, p.chunk, t, p.causal);
+    cu.b = b;
+    cu.g = g;
+    cu.qt = qt;
+    cu.c = 0;
+    cu.ntile = seq_tiles(p, ql);
+    cu.nch = unit_chunks(kv, ql, p.group, p.rows_per_tile, p.chunk, qt, p.causal);
+    cu.item = start;
+    end = start + cu.nch;
+    return true;
+}
+
+#endif  // __HIPCC__
+
+}  // namespace pa

@@ -1,0 +1,217 @@
+// pa_plan.hip -- the device-side work planner and the log-sum-exp merge.
+//
+// The planner plays the role of the task-list generator that the
+// SparseAttnSharedkvMetadata README describes (function section: a list of
+// start/end points -- batch, head, Q block, K block -- for every core,
+// consumed by the attention operator, and reduction tasks for split rows).
+// Here it runs on the GPU in one workgroup, reads only the lengths, and
+// gives every attention workgroup an equal number of KV chunks; the result
+// depends on the lengths alone, so outputs are deterministic.
+//
+// The merge combines the fp32 partials of rows whose KV range was split over
+// several workgroups: with per-part running max m_p (log2 domain), sum l_p
+// and unnormalised output acc_p,
+//     M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  o = sum_p 2^(m_p - M) acc_p / L,
+// which is the softmax over the union of the parts exactly (the "FlashDecode
+// reduction" tasks of the same README's metadata output).
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
+{
+    __shared__ int s_q[kPlanThreads];
+    __shared__ int s_w[kPlanThreads];
+    __shared__ int s_carry_q, s_carry_w;
+    __shared__ uint32_t s_err;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        s_carry_q = 0;
+        s_carry_w = 0;
+        s_err = 0;
+    }
+    __syncthreads();
+    const int G = p.group;
+    const int R = p.rows_per_tile;
+    const int64_t cap64 = (int64_t)p.max_blocks * p.block_size;
+    const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
+    for (int base = 0; base < p.batch; base += kPlanThreads) {
+        const int b = base + tid;
+        int ql = 0, items = 0;
+        uint32_t err = 0;
+        if (b < p.batch) {
+            int kv = p.context_lens[b];
+            ql = p.q_seq_lens ? p.q_seq_lens[b] : 1;
+            if (kv < 0) {
+                err |= PA_DEVERR_CTX;
+                kv = 0;
+            }
+            if (kv > cap) {
+                err |= PA_DEVERR_TABLE_SHORT;
+                kv = cap;
+            }
+            if (ql < 0) {
+                err |= PA_DEVERR_QLEN;
+                ql = 0;
+            }
+            if (ql > p.max_q) {
+                err |= PA_DEVERR_QLEN;
+                ql = p.max_q;
+            }
+            if (p.causal && ql > kv)
+                err |= PA_DEVERR_QLEN;
+            const int ntile = (ql * G + R - 1) / R;
+            int ipg = 0;
+            for (int qt = 0; qt < ntile; ++qt)
+                ipg += unit_chunks(kv, ql, G, R, p.chunk, qt, p.causal);
+            items = ipg * p.kv_head_num;
+            p.ws.qlen[b] = ql;
+            p.ws.kvlen[b] = kv;
+            p.ws.ipg[b] = ipg;
+        }
+        if (err)
+            atomicOr(&s_err, err);
+        // inclusive scans of ql and items over this chunk of sequences
+        s_q[tid] = ql;
+        s_w[tid] = items;
+        __syncthreads();
+        for (int d = 1; d < kPlanThreads; d <<= 1) {
+            const int aq = tid >= d ? s_q[tid - d] : 0;
+            const int aw = tid >= d ? s_w[tid - d] : 0;
+            __syncthreads();
+            s_q[tid] += aq;
+            s_w[tid] += aw;
+            __syncthreads();
+        }
+        if (b < p.batch) {
+            p.ws.cu_q[b] = s_carry_q + s_q[tid] - ql;
+            p.ws.wsb[b] = s_carry_w + s_w[tid] - items;
+        }
+        __syncthreads();
+        if (tid == kPlanThreads - 1) {
+            s_carry_q += s_q[tid];
+            s_carry_w += s_w[tid];
+        }
+        __syncthreads();
+    }
+    const int W = s_carry_w;
+    const int per = p.no_split ? 0 : (W + p.partitions - 1) / p.partitions;
+    if (tid == 0) {
+        p.ws.cu_q[p.batch] = s_carry_q;
+        p.ws.wsb[p.batch] = W;
+        p.ws.hdr[0] = W;
+        p.ws.hdr[1] = per > 0 ? per : (p.no_split ? 0 : 1);
+        p.ws.hdr[2] = p.partitions;
+        p.ws.hdr[3] = 0;
+        if (s_carry_q != p.num_q_tokens)
+            s_err |= PA_DEVERR_TOKENS;
+    }
+    __syncthreads();
+    __threadfence_block();
+    if (!p.no_split) {
+        const int pe = per > 0 ? per : 1;
+        for (int w = tid; w < p.partitions; w += kPlanThreads) {
+            const int s = w * pe;
+            int bsel = 0;
+            if (s < W) {
+                int lo = 0, hi = p.batch - 1;   // the last b with wsb[b] <= s
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (p.ws.wsb[mid] <= s)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                bsel = lo;
+            }
+            p.ws.wg_b[w] = bsel;
+        }
+    }
+    if (tid == 0 && s_err)
+        set_error(p.ws.err, s_err);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void merge_kernel(Params p)
+{
+    const int per = p.ws.hdr[1];
+    if (per <= 0)
+        return;
+    const int u = blockIdx.x;
+    const int per_b = p.kv_head_num * p.max_tiles;
+    const int b = u / per_b;
+    if (b >= p.batch)
+        return;
+    const int g = (u % per_b) / p.max_tiles;
+    const int qt = u % p.max_tiles;
+    const int ql = p.ws.qlen[b];
+    const int G = p.group;
+    const int R = p.rows_per_tile;
+    if (qt * R >= ql * G)
+        return;
+    const int kv = p.ws.kvlen[b];
+    int us = p.ws.wsb[b] + g * p.ws.ipg[b];
+    for (int t = 0; t < qt; ++t)
+        us += unit_chunks(kv, ql, G, R, p.chunk, t, p.causal);
+    const int ue = us + unit_chunks(kv, ql, G, R, p.chunk, qt, p.causal);
+    const int first = us / per;
+    const int last = (ue - 1) / per;
+    if (first == last)
+        return;
+    const int DV = p.head_size_v;
+    int rows = ql * G - qt * R;
+    rows = rows < R ? rows : R;
+    const int t0 = p.ws.cu_q[b];
+    uint16_t *out = (uint16_t *)p.out;
+    for (int idx = threadIdx.x; idx < rows * DV; idx += kThreads) {
+        const int r = idx / DV;
+        const int e = idx - r * DV;
+        float M = -INFINITY;
+        for (int w = first; w <= last; ++w) {
+            const float *part = p.ws.partials + (size_t)(2 * w + (w * per >= us ? 0 : 1)) * p.partial_stride;
+            M = fmaxf(M, part[R * DV + r]);
+        }
+        float L = 0.f, acc = 0.f;
+        for (int w = first; w <= last; ++w) {
+            const float *part = p.ws.partials + (size_t)(2 * w + (w * per >= us ? 0 : 1)) * p.partial_stride;
+            const float m = part[R * DV + r];
+            const float f = m == -INFINITY ? 0.f : exp2f(m - M);
+            L += f * part[R * DV + R + r];
+            acc += f * part[r * DV + e];
+        }
+        const int rg = qt * R + r;
+        const int t = t0 + rg / G;
+        const int h = g * G + rg % G;
+        if (t >= p.num_q_tokens)
+            continue;
+        out[((size_t)t * p.head_num + h) * DV + e] = to_bits<DT>(L > 0.f ? acc / L : 0.f);
+        if (e == 0 && p.lse)
+            p.lse[(size_t)t * p.head_num + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const Params &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const Params &p, int dtype, hipStream_t s)
+{
+    const int grid = p.batch * p.kv_head_num * p.max_tiles;
+    if (grid <= 0 || p.no_split)
+        return hipSuccess;
+    if (dtype == 0)
+        hipLaunchKernelGGL(merge_kernel<0>, dim3(grid), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL(merge_kernel<1>, dim3(grid), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,319 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
+
+Small problems are compared element by element; they span several chunks,
+several row tiles and ragged tails.  The five named workloads are compared at
+full size on sampled rows, with the launch configuration the benchmark uses.
+Probes check gathering, masking and poison handling bit for bit."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import pa_ref
+from paged_kv_attention_18_amd import binding, synth
+
+from gpu_util import (assert_close, assert_lse_close, log, oracle_full, run_hip, sample_rows,
+                      to_device)
+
+pytestmark = pytest.mark.gpu
+
+F = binding
+
+
+def check_full(p_cpu, flags=0, num_partitions=0, what=""):
+    ref_o, ref_l = oracle_full(p_cpu)
+    p = to_device(p_cpu)
+    o, l, att = run_hip(p, flags=flags, num_partitions=num_partitions)
+    e = assert_close(o, ref_o, p_cpu.workload.dtype, what)
+    assert_lse_close(l, ref_l, what)
+    assert att.device_error() == 0
+    return e
+
+
+# ------------------------------------------------------------------ decode
+DECODE_CASES = [
+    # (lens, H, Hkv, D, bs, dtype)
+    ([1, 17, 64, 33, 100, 300], 4, 4, 64, 16, "f16"),       # G = 1, tiny tails
+    ([700, 129, 2050, 5], 32, 8, 128, 128, "bf16"),         # G = 4
+    ([1000, 64, 65, 3000], 16, 2, 128, 64, "f16"),          # G = 8
+    ([513, 2, 1500], 8, 8, 256, 32, "bf16"),                # Dk = 256
+    ([90, 400], 12, 1, 64, 48, "f16"),                      # G = 12 (16-row pad), bs not a power of 2
+    ([257, 31], 2, 1, 128, 16, "bf16"),                     # G = 2
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"G{c[1]//c[2]}_D{c[3]}_bs{c[4]}_{c[5]}")
+def test_decode_valu_parity(case):
+    lens, H, Hkv, D, bs, dt = case
+    log(f"decode {case}")
+    p = synth.custom(lens, H, Hkv, D, D, bs, dt, seed=sum(lens) % 1000)
+    check_full(p, what=f"decode {case}")
+
+
+@pytest.mark.parametrize("case", DECODE_CASES[:3], ids=["G1", "G4", "G8"])
+def test_decode_no_split_and_forced_mfma_agree(case):
+    lens, H, Hkv, D, bs, dt = case
+    log(f"modes {case}")
+    p = synth.custom(lens, H, Hkv, D, D, bs, dt, seed=3)
+    check_full(p, flags=F.PA_FLAG_NO_SPLIT, what="no-split")
+    check_full(p, flags=F.PA_FLAG_FORCE_MFMA, what="mfma")
+    check_full(p, num_partitions=7, what="7 partitions")
+
+
+# ------------------------------------------------------------ causal / MFMA
+CAUSAL_CASES = [
+    # (kv, qlen, H, Hkv, D, bs, dtype)
+    ([300, 37, 520, 16], [40, 5, 300, 16], 8, 2, 128, 128, "f16"),
+    ([1100, 90], [130, 90], 8, 8, 64, 32, "bf16"),
+    ([700, 260], [64, 20], 4, 1, 256, 64, "f16"),
+    ([150, 40, 1], [4, 8, 1], 32, 8, 128, 128, "f16"),      # splitfuse decode half (16-32 rows)
+]
+
+
+@pytest.mark.parametrize("case", CAUSAL_CASES, ids=lambda c: f"H{c[2]}_{c[3]}_D{c[4]}_{c[6]}")
+def test_causal_mfma_parity(case):
+    kv, ql, H, Hkv, D, bs, dt = case
+    log(f"causal {case}")
+    p = synth.custom(kv, H, Hkv, D, D, bs, dt, "causal", q_seq_lens=ql, seed=11)
+    check_full(p, what=f"causal {case}")
+    check_full(p, flags=F.PA_FLAG_NO_SPLIT, what="causal no-split")
+
+
+def test_causal_small_rows_valu():
+    # qlen * G < 16 in causal mode takes the VALU kernel
+    log("causal valu")
+    p = synth.custom([50, 9, 200], 8, 4, 128, 128, 16, "bf16", "causal", q_seq_lens=[7, 3, 5], seed=12)
+    check_full(p, what="causal valu")
+    check_full(p, flags=F.PA_FLAG_FORCE_MFMA, what="causal forced mfma")
+
+
+def test_no_mask_multi_token():
+    log("no-mask multi token")
+    p = synth.custom([80, 300], 8, 2, 64, 64, 16, "f16", "none", q_seq_lens=[3, 9], seed=13)
+    check_full(p, what="none multi")
+
+
+def test_mla_shape_small():
+    log("mla small")
+    p = synth.custom([1500, 77, 640, 33], 64, 1, 576, 512, 128, "bf16", scale=1 / 24, seed=14)
+    check_full(p, what="mla")
+    check_full(p, flags=F.PA_FLAG_NO_SPLIT, what="mla no-split")
+
+
+def test_mla_shape_f16_causal_small():
+    log("mla causal")
+    p = synth.custom([300, 70], 16, 1, 576, 512, 64, "f16", "causal", q_seq_lens=[5, 2], seed=15)
+    check_full(p, what="mla causal")
+
+
+# ------------------------------------------------------------------ probes
+def test_one_hot_gather_bit_exact():
+    """K zero except the row of logical token t*, q one-hot: out is V[t*] bit for bit."""
+    log("one-hot")
+    for D, bs, dt, H, Hkv in ((128, 128, "bf16", 8, 2), (64, 16, "f16", 4, 4), (576, 128, "bf16", 16, 1)):
+        Dv = 512 if D == 576 else D
+        p = synth.custom([700, 129, 40], H, Hkv, D, Dv, bs, dt, seed=21)
+        rng = np.random.default_rng(1)
+        p.key_cache.zero_()
+        p.query.zero_()
+        p.query[:, :, 0] = 64.0
+        stars = []
+        for b in range(p.batch):
+            n = int(p.context_lens_np[b])
+            t = int(rng.choice([0, n - 1, min(bs, n - 1), int(rng.integers(0, n))]))
+            stars.append(t)
+            blk = int(p.block_tables_np[b, t // bs])
+            p.key_cache[blk, t % bs, :, 0] = 64.0
+        for flags in (0, F.PA_FLAG_NO_SPLIT):
+            o, _, _ = run_hip(to_device(p), flags=flags)
+            for b, t in enumerate(stars):
+                blk = int(p.block_tables_np[b, t // bs])
+                for h in range(H):
+                    want = p.value_cache[blk, t % bs, h // (H // Hkv)].to(torch.float64).numpy()
+                    assert np.array_equal(o[b, h], want), (D, b, h, t)
+
+
+def test_lse_counts_visible_tokens():
+    """q = 0: every logit is 0, lse = ln(#visible) exactly recoverable per row."""
+    log("lse count")
+    for mask, ql in (("none", None), ("causal", [5, 40, 1, 17])):
+        kv = [5, 300, 1, 1000]
+        p = synth.custom(kv, 8, 2, 128, 128, 16 if mask == "none" else 64, "f16", mask, q_seq_lens=ql, seed=22)
+        p.query.zero_()
+        _, l, _ = run_hip(to_device(p))
+        t0 = 0
+        qls = ql or [1] * len(kv)
+        for b, (n, q) in enumerate(zip(kv, qls)):
+            prefix = max(0, n - q)
+            for i in range(q):
+                vis = n if mask == "none" else min(n, prefix + i + 1)
+                got = np.exp(l[t0 + i])
+                assert np.all(np.rint(got) == vis), (mask, b, i, got[:2], vis)
+            t0 += q
+
+
+def test_poison_tails_and_slack():
+    """NaN in tail slots, unreferenced blocks and padding table entries leaves
+    the output bit-identical and finite."""
+    log("poison")
+    for D, dt, mask, ql in ((128, "bf16", "none", None), (128, "f16", "causal", [20, 3]), (576, "bf16", "none", None)):
+        Dv = 512 if D == 576 else D
+        H, Hkv = (16, 1) if D == 576 else (8, 2)
+        p = synth.custom([70, 200], H, Hkv, D, Dv, 64, dt, mask, q_seq_lens=ql, seed=23, max_blocks=8)
+        clean, _, _ = run_hip(to_device(p))
+        bs = 64
+        used = set()
+        for b in range(p.batch):
+            n = int(p.context_lens_np[b])
+            nb = (n + bs - 1) // bs
+            used.update(p.block_tables_np[b, :nb].tolist())
+            last = int(p.block_tables_np[b, nb - 1])
+            if n % bs:
+                p.key_cache[last, n % bs:] = float("nan")
+                p.value_cache[last, n % bs:] = float("nan")
+            p.block_tables_np[b, nb:] = -1            # never read
+        for blk in range(p.num_blocks):
+            if blk not in used:
+                p.key_cache[blk] = float("nan")
+                p.value_cache[blk] = float("nan")
+        dirty, _, att = run_hip(to_device(p))
+        assert np.array_equal(clean, dirty), (D, mask)
+
+
+def test_masked_positions_have_zero_weight():
+    """Changing K/V at token j changes no causal row that cannot see j."""
+    log("mask weight")
+    p = synth.custom([300], 8, 2, 128, 128, 64, "f16", "causal", q_seq_lens=[40], seed=24)
+    base, _, _ = run_hip(to_device(p))
+    prefix = 260
+    j = prefix + 20            # visible from row i >= 20
+    blk = int(p.block_tables_np[0, j // 64])
+    p.key_cache[blk, j % 64] = 3.0
+    p.value_cache[blk, j % 64] = -7.0
+    pert, _, _ = run_hip(to_device(p))
+    assert np.array_equal(base[:20], pert[:20])
+    assert not np.array_equal(base[20:], pert[20:])
+
+
+def test_block_permutation_bit_exact():
+    log("permutation")
+    for case in (DECODE_CASES[1], DECODE_CASES[2]):
+        lens, H, Hkv, D, bs, dt = case
+        p = synth.custom(lens, H, Hkv, D, D, bs, dt, seed=25)
+        o1, l1, _ = run_hip(to_device(p))
+        perm = np.random.default_rng(4).permutation(p.num_blocks)
+        inv = torch.from_numpy(np.argsort(perm).astype(np.int64))
+        p2 = synth.Problem(**{**p.__dict__})
+        p2.key_cache = p.key_cache[inv].clone()
+        p2.value_cache = p.value_cache[inv].clone()
+        p2.block_tables_np = perm[p.block_tables_np].astype(np.int32)
+        o2, l2, _ = run_hip(to_device(p2))
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_deterministic_runs():
+    log("determinism")
+    p = to_device(synth.custom([3000, 100, 2049], 32, 8, 128, 128, 128, "bf16", seed=26))
+    att = binding.for_problem(p)
+    a = binding.run_problem(att, p).clone()
+    b = binding.run_problem(att, p).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_bad_block_id_is_flagged_not_read():
+    log("bad block id")
+    p = synth.custom([100, 50], 4, 2, 64, 64, 16, "f16", seed=27)
+    p.block_tables_np[0, 2] = p.num_blocks + 5
+    p.block_tables_np[1, 0] = -3
+    g = to_device(p)
+    att = binding.for_problem(g)
+    binding.run_problem(att, g)
+    torch.cuda.synchronize()
+    assert att.device_error() & F.PA_DEVERR_BLOCK_ID
+    assert att.device_error() == 0          # cleared by the previous read
+
+
+def test_bad_lengths_are_clamped_and_flagged():
+    log("bad lengths")
+    p = synth.custom([100, 50], 4, 2, 64, 64, 16, "f16", seed=28)
+    g = to_device(p)
+    g.context_lens = torch.tensor([100, 10_000], dtype=torch.int32, device="cuda")   # table too short
+    att = binding.for_problem(g)
+    binding.run_problem(att, g)
+    torch.cuda.synchronize()
+    assert att.device_error() & F.PA_DEVERR_TABLE_SHORT
+
+
+def test_empty_context_outputs_zero():
+    log("empty context")
+    p = synth.custom([0, 33], 4, 2, 64, 64, 16, "f16", seed=29)
+    o, l, _ = run_hip(to_device(p))
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+    ref_o, ref_l = oracle_full(p)
+    assert_close(o[1:], ref_o[1:], "f16")
+
+
+def test_describe_paths():
+    p = to_device(synth.custom([10], 32, 8, 128, 128, 128, "bf16", seed=30))
+    assert binding.for_problem(p).describe()["path"] == "valu"
+    p = to_device(synth.custom([10], 64, 1, 576, 512, 128, "bf16", seed=30))
+    assert binding.for_problem(p).describe()["path"] == "mfma"
+
+
+# ----------------------------------------------------- the named workloads
+def full_size_sampled(n, rows, seed=0):
+    w = synth.WORKLOADS[n]
+    log(f"workload {w.name}: generating on the GPU")
+    p = synth.generate(w, device="cuda")
+    o, l, att = run_hip(p)
+    assert att.device_error() == 0
+    log(f"workload {w.name}: oracle on {rows} rows ({att.describe()})")
+    toks, heads = sample_rows(p, rows, seed)
+    inp = pa_ref.Inputs.from_problem(p)
+    ro, rl = pa_ref.rows(inp, toks, heads)
+    e = assert_close(o[toks, heads], ro, w.dtype, w.name)
+    assert_lse_close(l[toks, heads], rl, w.name)
+    # properties that hold at any size: finite everywhere, |o| <= max |V|
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    vmax = float(p.value_cache.abs().max())
+    assert np.abs(o).max() <= vmax * (1 + 1e-2)
+    log(f"workload {w.name}: max err {e:.2e}")
+    return p, o, l
+
+
+def test_workload_tiny_decode_full():
+    w = synth.WORKLOADS[1]
+    p = synth.generate(w)
+    check_full(p, what=w.name)
+
+
+def test_workload_gqa_decode_sampled():
+    full_size_sampled(2, 256)
+
+
+def test_workload_skewed_long_decode_sampled():
+    p, o, l = full_size_sampled(3, 128, seed=1)
+    # the longest sequences (32768 tokens) are sampled explicitly
+    long_b = np.flatnonzero(p.context_lens_np == 32768)[:2]
+    inp = pa_ref.Inputs.from_problem(p)
+    toks = np.repeat(long_b, 2).astype(np.int32)
+    heads = np.array([0, 63] * len(long_b), np.int32)
+    ro, rl = pa_ref.rows(inp, toks, heads)
+    assert_close(o[toks, heads], ro, "f16", "skewed long rows")
+
+
+def test_workload_splitfuse_causal_sampled():
+    p, o, l = full_size_sampled(4, 192, seed=2)
+    # rows at chunk starts and ends of the prefill sequences
+    cu = np.concatenate([[0], np.cumsum(p.q_seq_lens_np)])
+    big = np.flatnonzero(p.q_seq_lens_np == 512)[:3]
+    toks = np.concatenate([[cu[b], cu[b] + 1, cu[b + 1] - 1] for b in big]).astype(np.int32)
+    heads = (np.arange(len(toks)) * 7 % 32).astype(np.int32)
+    ro, rl = pa_ref.rows(pa_ref.Inputs.from_problem(p), toks, heads)
+    assert_close(o[toks, heads], ro, "f16", "splitfuse chunk edges")
+
+
+def test_workload_mla_decode_sampled():
+    full_size_sampled(5, 128, seed=3)
