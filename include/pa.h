@@ -73,9 +73,10 @@ typedef enum {
 
 /* pa_config.flags */
 enum {
-    PA_FLAG_FORCE_VALU = 1u << 0,  /* testing: take the VALU decode path whenever it can run */
+    PA_FLAG_FORCE_VALU = 1u << 0,  /* testing: require the VALU decode path (at most 8 rows per unit,
+                                      i.e. max_q_seq_len * head_num / kv_head_num <= 8) */
     PA_FLAG_FORCE_MFMA = 1u << 1,  /* testing: take the MFMA tile path always */
-    PA_FLAG_NO_SPLIT = 1u << 2     /* testing: one workgroup per (sequence, KV head, row tile); no merge */
+    PA_FLAG_NO_SPLIT = 1u << 2     /* testing: one worker per (sequence, KV head, row tile); no merge */
 };
 
 /* Device error word bits (pa_get_device_error). */

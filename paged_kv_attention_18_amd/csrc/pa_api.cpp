@@ -22,7 +22,7 @@ struct Variant {
     int row_blocks;  // MFMA: 16-row blocks per wave
     int rows_per_tile;
     int chunk;
-    int partitions;  // balanced-mode grid
+    int partitions;  // balanced-mode workers (waves for the VALU kernel, workgroups for MFMA)
 };
 
 int next_pow2(int x)
@@ -58,24 +58,23 @@ struct pa_handle {
         const int G = cfg.head_num / cfg.kv_head_num;
         const int rows = max_q * G;
         const bool dec_ok = pa::decode_supported(cfg.head_size_k, cfg.head_size_v);
-        bool valu = dec_ok && rows < 16;
-        if (cfg.flags & PA_FLAG_FORCE_VALU)
-            valu = dec_ok && rows <= 16;
+        // VALU for thin units (the VALU kernel is built for at most 8 rows)
+        bool valu = dec_ok && rows <= 8;
         if (cfg.flags & PA_FLAG_FORCE_MFMA)
             valu = false;
         if (valu) {
             v.path = 0;
             v.rows_pad = next_pow2(rows < 1 ? 1 : rows);
             v.rows_per_tile = v.rows_pad;
-            v.chunk = pa::kDecodeChunk;
-            v.partitions = num_cus * pa::decode_wgs_per_cu(cfg.dtype, cfg.head_size_k, cfg.head_size_v, v.rows_pad);
+            v.chunk = pa::decode_chunk(cfg.head_size_k, v.rows_pad);
+            v.partitions = num_cus * pa::decode_workers_per_cu(cfg.dtype, cfg.head_size_k, cfg.head_size_v, v.rows_pad);
         } else {
             v.path = 1;
             const int r1 = pa::tile_rows(cfg.head_size_k, cfg.head_size_v, 1);
             v.row_blocks = (rows > r1 && pa::tile_supported(cfg.head_size_k, cfg.head_size_v, 2)) ? 2 : 1;
             v.rows_per_tile = pa::tile_rows(cfg.head_size_k, cfg.head_size_v, v.row_blocks);
             v.chunk = pa::tile_chunk(cfg.head_size_k, cfg.head_size_v);
-            v.partitions = num_cus * pa::tile_wgs_per_cu(cfg.dtype, cfg.head_size_k, cfg.head_size_v, v.row_blocks);
+            v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, cfg.head_size_k, cfg.head_size_v, v.row_blocks);
         }
         if (cfg.num_partitions > 0)
             v.partitions = cfg.num_partitions;
@@ -134,8 +133,10 @@ static pa_status check_config(const pa_config *c)
         return PA_ERR_UNSUPPORTED;
     if ((c->flags & PA_FLAG_FORCE_MFMA) && !til)
         return PA_ERR_UNSUPPORTED;
-    if (!til && (int64_t)c->max_q_seq_len * G > 16)
+    if (!til && (int64_t)c->max_q_seq_len * G > 8)
         return PA_ERR_UNSUPPORTED;   // only the VALU kernel exists for this shape
+    if ((c->flags & PA_FLAG_FORCE_VALU) && (int64_t)c->max_q_seq_len * G > 8)
+        return PA_ERR_UNSUPPORTED;   // the VALU kernel takes at most 8 rows per unit
     return PA_OK;
 }
 
@@ -176,6 +177,8 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
         qs.push_back(q);
     if (qmax > 65)
         qs.push_back(qmax);
+    int max_tiles = 1;
+    const int G = cfg->head_num / cfg->kv_head_num;
     for (int q : qs) {
         const Variant v = h->choose(q);
         const size_t f = (size_t)v.rows_per_tile * (cfg->head_size_v + 2);
@@ -183,7 +186,11 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
             max_floats = f;
         if (v.partitions > max_p)
             max_p = v.partitions;
+        const int tiles = (int)(((int64_t)q * G + v.rows_per_tile - 1) / v.rows_per_tile);
+        if (tiles > max_tiles)
+            max_tiles = tiles;
     }
+    (void)max_tiles;
     h->max_partitions = max_p;
     h->max_partial_floats = max_floats;
 

@@ -71,17 +71,21 @@ hipError_t launch_tile(const Params &p, int dtype, int row_blocks, hipStream_t s
 // Shapes and occupancy used by the host to pick kernels and size the grid.
 bool decode_supported(int dk, int dv);
 bool tile_supported(int dk, int dv, int row_blocks);
-int decode_wgs_per_cu(int dtype, int dk, int dv, int rows_pad);   // resident workgroups per CU
-int tile_wgs_per_cu(int dtype, int dk, int dv, int row_blocks);
+int tile_workers_per_cu(int dtype, int dk, int dv, int row_blocks);   // resident workgroups per CU
 int tile_chunk(int dk, int dv);
 int tile_rows(int dk, int dv, int row_blocks);
+int decode_chunk(int dk, int rows_pad);
+int decode_workers_per_cu(int dtype, int dk, int dv, int rows_pad);   // resident waves per CU
 
-constexpr int kDecodeChunk = 64;     // CT of the VALU decode kernel
 constexpr int kThreads = 256;        // threads per attention workgroup
 constexpr int kBtWindow = 256;       // block-table entries staged in LDS at a time
 
 #ifdef __HIPCC__
 // ------------------------------------------------------------ device side
+
+// 128-bit register data as a native vector (HIP's uint4 is a struct, and a
+// select between two structs is lowered through memory).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Visible KV tokens of rows [r0, r1] of (b, g): a row (i, hh) sees tokens
 // j < kv, and in causal mode only j <= prefix + i.

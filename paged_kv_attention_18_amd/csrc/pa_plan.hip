@@ -135,13 +135,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         set_error(p.ws.err, s_err);
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void merge_kernel(Params p)
+// Rows per merge workgroup: enough to give every thread ~4 outputs.
+__host__ __device__ inline int merge_rows_per_wg(int dv)
 {
+    const int r = (4 * kThreads) / dv;
+    return r < 1 ? 1 : (r > 64 ? 64 : r);
+}
+
+// One workgroup per (unit, group of rows).  Worker w's partial of a unit is
+// in slot 0 if the unit started at or before w's range, else in slot 1.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_groups)
+{
+    __shared__ float s_m[64], s_inv[64];
     const int per = p.ws.hdr[1];
     if (per <= 0)
         return;
-    const int u = blockIdx.x;
+    const int u = blockIdx.x / row_groups;
+    const int rgp = blockIdx.x % row_groups;
     const int per_b = p.kv_head_num * p.max_tiles;
     const int b = u / per_b;
     if (b >= p.batch)
@@ -151,8 +162,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p)
     const int ql = p.ws.qlen[b];
     const int G = p.group;
     const int R = p.rows_per_tile;
-    if (qt * R >= ql * G)
+    const int DV = p.head_size_v;
+    int rows = ql * G - qt * R;
+    rows = rows < R ? rows : R;
+    const int RPW = merge_rows_per_wg(DV);
+    const int r0 = rgp * RPW;
+    if (r0 >= rows)
         return;
+    const int nr = rows - r0 < RPW ? rows - r0 : RPW;
     const int kv = p.ws.kvlen[b];
     int us = p.ws.wsb[b] + g * p.ws.ipg[b];
     for (int t = 0; t < qt; ++t)
@@ -162,35 +179,48 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p)
     const int last = (ue - 1) / per;
     if (first == last)
         return;
-    const int DV = p.head_size_v;
-    int rows = ql * G - qt * R;
-    rows = rows < R ? rows : R;
-    const int t0 = p.ws.cu_q[b];
-    uint16_t *out = (uint16_t *)p.out;
-    for (int idx = threadIdx.x; idx < rows * DV; idx += kThreads) {
-        const int r = idx / DV;
-        const int e = idx - r * DV;
+    auto part_of = [&](int w) -> const float * {
+        return p.ws.partials + (size_t)(2 * w + (w * per >= us ? 0 : 1)) * p.partial_stride;
+    };
+    // row statistics: M = max_p m_p, L = sum_p l_p 2^(m_p - M)
+    if (threadIdx.x < nr) {
+        const int r = r0 + threadIdx.x;
         float M = -INFINITY;
+        for (int w = first; w <= last; ++w)
+            M = fmaxf(M, part_of(w)[R * DV + r]);
+        float L = 0.f;
         for (int w = first; w <= last; ++w) {
-            const float *part = p.ws.partials + (size_t)(2 * w + (w * per >= us ? 0 : 1)) * p.partial_stride;
-            M = fmaxf(M, part[R * DV + r]);
+            const float *pt = part_of(w);
+            const float m = pt[R * DV + r];
+            L += m == -INFINITY ? 0.f : pt[R * DV + R + r] * exp2f(m - M);
         }
-        float L = 0.f, acc = 0.f;
+        s_m[threadIdx.x] = M;
+        s_inv[threadIdx.x] = L > 0.f ? 1.f / L : 0.f;
+        const int rg = qt * R + r;
+        const int t = p.ws.cu_q[b] + rg / G;
+        if (p.lse && t < p.num_q_tokens)
+            p.lse[(size_t)t * p.head_num + g * G + rg % G] =
+                L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+    }
+    __syncthreads();
+    uint16_t *out = (uint16_t *)p.out;
+    const int t0 = p.ws.cu_q[b];
+    for (int idx = threadIdx.x; idx < nr * DV; idx += kThreads) {
+        const int rr = idx / DV;
+        const int e = idx - rr * DV;
+        const int r = r0 + rr;
+        const float M = s_m[rr];
+        float acc = 0.f;
         for (int w = first; w <= last; ++w) {
-            const float *part = p.ws.partials + (size_t)(2 * w + (w * per >= us ? 0 : 1)) * p.partial_stride;
-            const float m = part[R * DV + r];
-            const float f = m == -INFINITY ? 0.f : exp2f(m - M);
-            L += f * part[R * DV + R + r];
-            acc += f * part[r * DV + e];
+            const float *pt = part_of(w);
+            const float m = pt[R * DV + r];
+            if (m != -INFINITY)
+                acc += exp2f(m - M) * pt[r * DV + e];
         }
         const int rg = qt * R + r;
         const int t = t0 + rg / G;
-        const int h = g * G + rg % G;
-        if (t >= p.num_q_tokens)
-            continue;
-        out[((size_t)t * p.head_num + h) * DV + e] = to_bits<DT>(L > 0.f ? acc / L : 0.f);
-        if (e == 0 && p.lse)
-            p.lse[(size_t)t * p.head_num + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+        if (t < p.num_q_tokens)
+            out[((size_t)t * p.head_num + g * G + rg % G) * DV + e] = to_bits<DT>(acc * s_inv[rr]);
     }
 }
 
@@ -204,13 +234,17 @@ hipError_t launch_plan(const Params &p, hipStream_t s)
 
 hipError_t launch_merge(const Params &p, int dtype, hipStream_t s)
 {
-    const int grid = p.batch * p.kv_head_num * p.max_tiles;
+    const int row_groups = (p.rows_per_tile + merge_rows_per_wg(p.head_size_v) - 1) /
+                           merge_rows_per_wg(p.head_size_v);
+    const long long grid = (long long)p.batch * p.kv_head_num * p.max_tiles * row_groups;
     if (grid <= 0 || p.no_split)
         return hipSuccess;
+    if (grid > 0x7fffffff)
+        return hipErrorInvalidValue;
     if (dtype == 0)
-        hipLaunchKernelGGL(merge_kernel<0>, dim3(grid), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(merge_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, row_groups);
     else
-        hipLaunchKernelGGL(merge_kernel<1>, dim3(grid), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(merge_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, row_groups);
     return hipGetLastError();
 }
 

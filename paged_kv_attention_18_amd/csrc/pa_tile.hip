@@ -43,7 +43,7 @@ struct Mfma;
 template <>
 struct Mfma<0> {
     typedef _Float16 v8 __attribute__((ext_vector_type(8)));
-    static __device__ __forceinline__ f32x4 run(uint4 a, uint4 b, f32x4 c)
+    static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c)
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c,
                                                       0, 0, 0);
@@ -53,7 +53,7 @@ struct Mfma<0> {
 template <>
 struct Mfma<1> {
     typedef __bf16 v8 __attribute__((ext_vector_type(8)));
-    static __device__ __forceinline__ f32x4 run(uint4 a, uint4 b, f32x4 c)
+    static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c)
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c,
                                                        0, 0, 0);
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
         const int64_t row_stride_v = (int64_t)Hkv * DV;
 
         // Q^T operand and the visible limit of this lane's rows
-        uint4 qb[MB][KS];
+        u32x4 qb[MB][KS];
         int lim[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
             const uint16_t *src = qg + ((size_t)t * H + g * G + rg % G) * DK + 8 * lg;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                qb[mb][ks] = ok ? *(const uint4 *)(src + 32 * ks) : make_uint4(0, 0, 0, 0);
+                qb[mb][ks] = ok ? *(const u32x4 *)(src + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
         }
 
         f32x4 oacc[MB][ND];
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
                 for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                     for (int n = 0; n < NTT; ++n) {
-                        const uint4 a = *(const uint4 *)(kb + (16 * n + lr) * KP + 32 * ks + 8 * lg);
+                        const u32x4 a = *(const u32x4 *)(kb + (16 * n + lr) * KP + 32 * ks + 8 * lg);
 #pragma unroll
                         for (int mb = 0; mb < MB; ++mb)
                             sacc[mb][n] = Mfma<DT>::run(a, qb[mb][ks], sacc[mb][n]);
@@ -368,12 +368,12 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
                 // --------------------------------------------- O += P V
 #pragma unroll
                 for (int kk = 0; kk < PVK; ++kk) {
-                    uint4 pa[MB];
+                    u32x4 pa[MB];
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
                         const f32x4 s0 = sacc[mb][2 * kk], s1 = sacc[mb][2 * kk + 1];
-                        pa[mb] = make_uint4(pack2<DT>(s0[0], s0[1]), pack2<DT>(s0[2], s0[3]),
-                                            pack2<DT>(s1[0], s1[1]), pack2<DT>(s1[2], s1[3]));
+                        pa[mb] = u32x4{pack2<DT>(s0[0], s0[1]), pack2<DT>(s0[2], s0[3]),
+                                       pack2<DT>(s1[0], s1[1]), pack2<DT>(s1[2], s1[3])};
                     }
 #pragma unroll
                     for (int nd = 0; nd < ND; ++nd) {
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
                         const uint16_t *vrow = vb + col * VTP;
                         const uint2 v0 = *(const uint2 *)(vrow + 4 * vt_group<KT>(8 * kk + lg, col));
                         const uint2 v1 = *(const uint2 *)(vrow + 4 * vt_group<KT>(8 * kk + 4 + lg, col));
-                        const uint4 bv = make_uint4(v0.x, v0.y, v1.x, v1.y);
+                        const u32x4 bv = {v0.x, v0.y, v1.x, v1.y};
 #pragma unroll
                         for (int mb = 0; mb < MB; ++mb)
                             oacc[mb][nd] = Mfma<DT>::run(pa[mb], bv, oacc[mb][nd]);
@@ -514,7 +514,7 @@ int tile_rows(int dk, int dv, int row_blocks)
     return 16 * row_blocks * (nw / cs);
 }
 
-int tile_wgs_per_cu(int dtype, int dk, int dv, int row_blocks)
+int tile_workers_per_cu(int dtype, int dk, int dv, int row_blocks)
 {
     int threads = 0;
     const void *k = tile_kernel_ptr(dtype, dk, dv, row_blocks, &threads);
