@@ -204,6 +204,7 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
     const size_t o_ql = off; off = align(off + B * sizeof(int32_t));
     const size_t o_kv = off; off = align(off + B * sizeof(int32_t));
     const size_t o_wgb = off; off = align(off + max_p * sizeof(int32_t));
+    const size_t o_spl = off; off = align(off + (size_t)max_p * 8 * sizeof(int32_t));
     const size_t o_err = off; off = align(off + sizeof(uint32_t));
     const size_t o_part = off; off = align(off + 2 * (size_t)max_p * max_floats * sizeof(float));
     h->ws_bytes = off;
@@ -224,6 +225,7 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
     h->ws.qlen = (int32_t *)(base + o_ql);
     h->ws.kvlen = (int32_t *)(base + o_kv);
     h->ws.wg_b = (int32_t *)(base + o_wgb);
+    h->ws.splits = (int32_t *)(base + o_spl);
     h->ws.err = (uint32_t *)(base + o_err);
     h->ws.partials = (float *)(base + o_part);
     *out = h;

@@ -31,7 +31,8 @@ struct Workspace {
     int32_t *ipg;        // [max_batch]: items of each (b, g) (equal for all g of b)
     int32_t *qlen;       // [max_batch]: sanitised q_seq_lens
     int32_t *kvlen;      // [max_batch]: sanitised context_lens
-    int32_t *wg_b;       // [P]: sequence holding the first item of each workgroup
+    int32_t *wg_b;       // [P]: sequence holding the first item of each worker
+    int32_t *splits;     // [P][8]: split units (b, g, qt, first item, end item; b < 0: none)
     float *partials;     // [2 * P][R * (DV + 2)]
     uint32_t *err;       // device error word
 };

@@ -114,21 +114,52 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
     __threadfence_block();
     if (!p.no_split) {
         const int pe = per > 0 ? per : 1;
-        for (int w = tid; w < p.partitions; w += kPlanThreads) {
-            const int s = w * pe;
-            int bsel = 0;
-            if (s < W) {
-                int lo = 0, hi = p.batch - 1;   // the last b with wsb[b] <= s
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (p.ws.wsb[mid] <= s)
-                        lo = mid;
-                    else
-                        hi = mid - 1;
-                }
-                bsel = lo;
+        // Worker w starts at item w * pe: sequence b owns the workers whose
+        // start lies in [wsb[b], wsb[b+1]).
+        for (int base = 0; base < p.batch; base += kPlanThreads) {
+            const int b = base + tid;
+            if (b < p.batch) {
+                const int lo = p.ws.wsb[b], hi = p.ws.wsb[b + 1];
+                if (hi > lo)
+                    for (int w = (lo + pe - 1) / pe; w * pe < hi && w < p.partitions; ++w)
+                        p.ws.wg_b[w] = b;
             }
-            p.ws.wg_b[w] = bsel;
+        }
+        __syncthreads();
+        __threadfence_block();
+        // A unit is split when a worker boundary falls strictly inside it;
+        // it is listed once, at its first inner boundary w (entry w - 1).
+        for (int w = 1 + tid; w < p.partitions; w += kPlanThreads) {
+            int32_t *d = p.ws.splits + (size_t)(w - 1) * 8;
+            const int s = w * pe;
+            int b = -1, g = 0, qt = 0, us = 0, ue = 0;
+            if (s < W) {
+                const int bb = p.ws.wg_b[w];
+                const int kv = p.ws.kvlen[bb], ql = p.ws.qlen[bb], ipg = p.ws.ipg[bb];
+                int local = s - p.ws.wsb[bb];
+                const int gg = local / ipg;
+                local -= gg * ipg;
+                int u0 = p.ws.wsb[bb] + gg * ipg;
+                int t = 0, n = unit_chunks(kv, ql, G, R, p.chunk, 0, p.causal);
+                while (local >= n) {
+                    local -= n;
+                    u0 += n;
+                    ++t;
+                    n = unit_chunks(kv, ql, G, R, p.chunk, t, p.causal);
+                }
+                if (s > u0 && s - pe <= u0) {
+                    b = bb;
+                    g = gg;
+                    qt = t;
+                    us = u0;
+                    ue = u0 + n;
+                }
+            }
+            d[0] = b;
+            d[1] = g;
+            d[2] = qt;
+            d[3] = us;
+            d[4] = ue;
         }
     }
     if (tid == 0 && s_err)
@@ -142,43 +173,31 @@ __host__ __device__ inline int merge_rows_per_wg(int dv)
     return r < 1 ? 1 : (r > 64 ? 64 : r);
 }
 
-// One workgroup per (unit, group of rows).  Worker w's partial of a unit is
-// in slot 0 if the unit started at or before w's range, else in slot 1.
+// One workgroup per (split unit, group of rows).  Worker w's partial of a
+// unit is in slot 0 if the unit started at or before w's range, else in slot 1.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_groups)
 {
     __shared__ float s_m[64], s_inv[64];
     const int per = p.ws.hdr[1];
-    if (per <= 0)
+    const int32_t *d = p.ws.splits + (size_t)(blockIdx.x / row_groups) * 8;
+    const int b = d[0];
+    if (b < 0 || per <= 0)
         return;
-    const int u = blockIdx.x / row_groups;
+    const int g = d[1], qt = d[2], us = d[3], ue = d[4];
     const int rgp = blockIdx.x % row_groups;
-    const int per_b = p.kv_head_num * p.max_tiles;
-    const int b = u / per_b;
-    if (b >= p.batch)
-        return;
-    const int g = (u % per_b) / p.max_tiles;
-    const int qt = u % p.max_tiles;
-    const int ql = p.ws.qlen[b];
     const int G = p.group;
     const int R = p.rows_per_tile;
     const int DV = p.head_size_v;
-    int rows = ql * G - qt * R;
+    int rows = p.ws.qlen[b] * G - qt * R;
     rows = rows < R ? rows : R;
     const int RPW = merge_rows_per_wg(DV);
     const int r0 = rgp * RPW;
     if (r0 >= rows)
         return;
     const int nr = rows - r0 < RPW ? rows - r0 : RPW;
-    const int kv = p.ws.kvlen[b];
-    int us = p.ws.wsb[b] + g * p.ws.ipg[b];
-    for (int t = 0; t < qt; ++t)
-        us += unit_chunks(kv, ql, G, R, p.chunk, t, p.causal);
-    const int ue = us + unit_chunks(kv, ql, G, R, p.chunk, qt, p.causal);
     const int first = us / per;
     const int last = (ue - 1) / per;
-    if (first == last)
-        return;
     auto part_of = [&](int w) -> const float * {
         return p.ws.partials + (size_t)(2 * w + (w * per >= us ? 0 : 1)) * p.partial_stride;
     };
@@ -236,7 +255,7 @@ hipError_t launch_merge(const Params &p, int dtype, hipStream_t s)
 {
     const int row_groups = (p.rows_per_tile + merge_rows_per_wg(p.head_size_v) - 1) /
                            merge_rows_per_wg(p.head_size_v);
-    const long long grid = (long long)p.batch * p.kv_head_num * p.max_tiles * row_groups;
+    const long long grid = (long long)(p.partitions - 1) * row_groups;
     if (grid <= 0 || p.no_split)
         return hipSuccess;
     if (grid > 0x7fffffff)
