@@ -206,6 +206,8 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
     const size_t o_wgb = off; off = align(off + max_p * sizeof(int32_t));
     const size_t o_spl = off; off = align(off + (size_t)max_p * 8 * sizeof(int32_t));
     const size_t o_err = off; off = align(off + sizeof(uint32_t));
+    const size_t zero_bytes = 16 * (size_t)cfg->kv_head_num * (size_t)(cfg->head_size_k > cfg->head_size_v ? cfg->head_size_k : cfg->head_size_v) * 2;
+    const size_t o_zero = off; off = align(off + zero_bytes);
     const size_t o_part = off; off = align(off + 2 * (size_t)max_p * max_floats * sizeof(float));
     h->ws_bytes = off;
     if (hipMalloc(&h->ws_base, h->ws_bytes) != hipSuccess) {
@@ -227,6 +229,7 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
     h->ws.wg_b = (int32_t *)(base + o_wgb);
     h->ws.splits = (int32_t *)(base + o_spl);
     h->ws.err = (uint32_t *)(base + o_err);
+    h->ws.zeros = base + o_zero;
     h->ws.partials = (float *)(base + o_part);
     *out = h;
     return PA_OK;

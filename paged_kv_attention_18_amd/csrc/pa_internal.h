@@ -34,6 +34,7 @@ struct Workspace {
     int32_t *wg_b;       // [P]: sequence holding the first item of each worker
     int32_t *splits;     // [P][8]: split units (b, g, qt, first item, end item; b < 0: none)
     float *partials;     // [2 * P][R * (DV + 2)]
+    const void *zeros;   // 16 token rows of zeros (K or V), read in place of a bad block
     uint32_t *err;       // device error word
 };
 

@@ -11,24 +11,32 @@
 // share its rows and split the Dv output columns (CS = 2 halves the output
 // accumulator per wave for Dv = 512).  Per KT-token chunk:
 //
-//   stage  K rows are copied to LDS as they are ([token][Dk], padded pitch);
-//          V rows are transposed in registers (4 tokens x 8 columns at a
-//          time) and stored as [column][token] with an XOR swizzle of the
-//          4-token groups, so both the stores and the MFMA operand reads are
-//          free of bank conflicts.  Loads run one chunk ahead (double buffer).
+//   stage  K and V rows are copied from the paged cache straight into LDS
+//          with global_load_lds_dwordx4 (no registers, no ALU work), one chunk
+//          ahead, into two LDS buffers.  Each lane picks the global 16-byte
+//          piece that lands at its LDS slot, which realises an XOR swizzle of
+//          the pieces within a row (K: piece ^ (row & 7); V: piece ^ 2(row & 3)),
+//          so the operand reads below are free of bank conflicts.  Tokens that
+//          are not visible, or whose block id is out of range, are loaded from
+//          a zero page: masked V rows are zeros, never multiplied away.
 //   S^T    = K . Q^T with v_mfma_f32_16x16x32_{f16,bf16}: K is the A operand
-//          (16 tokens x 32 dims per lane group), Q^T the B operand, held in
-//          registers for the whole unit.  The accumulator gives every lane
-//          one query row and 4 + 4 tokens, which is exactly the A-operand
-//          layout P needs for the next product, so P never leaves registers.
+//          (ds_read_b128), Q^T the B operand, held in registers for the whole
+//          unit.  The accumulator gives every lane one query row and 4 + 4
+//          tokens, which is exactly the A-operand layout P needs for the next
+//          product, so P never leaves registers.
 //   mask   select -inf where j >= kv or (causal) j > prefix + i; chunks that
 //          lie wholly inside every row's visible range skip the test, and
 //          chunks wholly outside are never planned.
-//   PV     O += P . V with the same instruction; V^T read from LDS.
+//   PV     O += P . V with the same instruction; the V operand is read from
+//          the row-major tile with ds_read_b64_tr_b16 (a transposing LDS read:
+//          within each 16-lane group, lane i receives element i % 4 of the
+//          8-byte chunks addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and
+//          12 + i / 4), two reads per operand.
 //
-// Row statistics (running max and sum, log2 domain) stay per wave; at the end
-// of a unit's range O is normalised into the output, or written as an fp32
-// partial for the merge kernel.
+// One barrier per chunk; the LDS loads of the next chunk are in flight while
+// the current one is computed.  Row statistics (running max and sum, log2
+// domain) stay per wave; at the end of a unit's range O is normalised into
+// the output, or written as an fp32 partial for the merge kernel.
 #include "pa_internal.h"
 
 namespace pa {
@@ -60,56 +68,61 @@ struct Mfma<1> {
     }
 };
 
-// Position of 4-token group q in LDS column `col` of the transposed V tile.
-template <int KT>
-__device__ __forceinline__ int vt_group(int q, int col)
-{
-    if constexpr (KT == 32)
-        return q ^ ((((col >> 4) * 5) ^ (col >> 5)) & 7);
-    else
-        return q ^ ((col ^ (col >> 2)) & 15);
-}
-
-template <int KT>
-constexpr int vt_pitch()
-{
-    return KT == 32 ? 36 : 64;
-}
-
+// Two 16-bit values packed as (lo, hi), round to nearest even.
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi)
 {
-    return (uint32_t)to_bits<DT>(lo) | ((uint32_t)to_bits<DT>(hi) << 16);
+    if constexpr (DT == 0) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        const b2 v = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+// Read-only for the whole launch: loads through this address space with a
+// uniform address become scalar loads (s_load), which do not share the vector
+// memory counter with the LDS loads in flight.
+typedef __attribute__((address_space(4))) const int32_t c_i32;
+
+__device__ __forceinline__ int sload(const int32_t *ptr, size_t i)
+{
+    return ((const c_i32 *)ptr)[i];
 }
 
 template <int DT, int DK, int DV, int MB, int KT, int NW, int CS>
 __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
 {
-    constexpr int NT = 64 * NW;
     constexpr int RGS = NW / CS;                  // row groups
     constexpr int R = 16 * MB * RGS;              // rows per tile
-    constexpr int KP = DK + 8;
-    constexpr int VTP = vt_pitch<KT>();
+    constexpr int RBK = 2 * DK, RBV = 2 * DV;     // LDS row bytes
     constexpr int KS = DK / 32;
     constexpr int NTT = KT / 16;
     constexpr int ND = DV / 16 / CS;              // output column tiles per wave
     constexpr int PVK = KT / 32;
-    constexpr int NKP_T = KT * DK / 8;            // 128-bit K pieces per chunk
-    constexpr int NKP = (NKP_T + NT - 1) / NT;
-    constexpr int NVP_T = (KT / 4) * (DV / 8);    // 4-token x 8-column V pieces per chunk
-    constexpr int NVP = (NVP_T + NT - 1) / NT;
-    constexpr int KBUF = KT * KP;
-    constexpr int VBUF = DV * VTP;
+    constexpr int IPGK = RBK / 64;                // 1 KiB LDS-load instructions per 16-token group (K)
+    constexpr int IPGV = RBV / 64;
+    constexpr int MK = (IPGK + NW - 1) / NW;      // ... per wave per group (upper bound)
+    constexpr int MV = (IPGV + NW - 1) / NW;
     static_assert(DK % 32 == 0 && DV % 64 == 0 && (KT == 32 || KT == 64), "shape");
-    static_assert(NW % CS == 0 && (DV / 16) % CS == 0, "split");
+    static_assert(NW % CS == 0 && ND % 4 == 0, "split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2 * KBUF];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[2 * VBUF];
-    __shared__ int32_t sBT[kBtWindow];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK0[KT * RBK];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK1[KT * RBK];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV0[KT * RBV];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV1[KT * RBV];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rgi = wave / CS;          // row group
     const int csl = wave % CS;          // column slice
     const int col0 = csl * (DV / CS);
@@ -123,37 +136,69 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
         return;
 
     const uint16_t *__restrict__ qg = (const uint16_t *)p.query;
-    const uint16_t *__restrict__ kg = (const uint16_t *)p.key_cache;
-    const uint16_t *__restrict__ vg = (const uint16_t *)p.value_cache;
+    const char *__restrict__ kg = (const char *)p.key_cache;
+    const char *__restrict__ vg = (const char *)p.value_cache;
+    const char *__restrict__ zg = (const char *)p.ws.zeros;
     uint16_t *__restrict__ og = (uint16_t *)p.out;
     const int G = p.group;
     const int H = p.head_num;
-    const int Hkv = p.kv_head_num;
     const int bs = p.block_size;
     const int bsh = p.bs_shift;
+    const uint32_t rsk = (uint32_t)p.kv_head_num * RBK;   // bytes per token row of the cache
+    const uint32_t rsv = (uint32_t)p.kv_head_num * RBV;
+    const uint32_t nb32 = p.num_blocks < 0x7fffffff ? (uint32_t)p.num_blocks : 0x7fffffffu;
     uint32_t err = 0;
     bool first_seg = true;
+
+    // Per-lane byte offset, inside a 16-token group of the cache, of the piece
+    // that load instruction wave + NW m of the group moves; the piece is the
+    // one whose LDS slot holds the swizzled layout.
+    uint32_t voK[MK], voV[MV];
+#pragma unroll
+    for (int m = 0; m < MK; ++m) {
+        const int x = (wave + NW * m) * 1024 + 16 * lane;
+        const int row = x / RBK;
+        voK[m] = row * rsk + 16 * (((x % RBK) >> 4) ^ (row & 7));
+    }
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+        const int x = (wave + NW * m) * 1024 + 16 * lane;
+        const int row = x / RBV;
+        voV[m] = row * rsv + 16 * (((x % RBV) >> 4) ^ (2 * (row & 3)));
+    }
+    // LDS read offsets.  K (A operand): row 16 n + lr, piece 4 ks + lg, which
+    // the swizzle moves by +-64 bytes depending on bit 2 of the row.
+    const int kq = 16 * (lg ^ (lr & 3));
+    const int kb2 = 64 * ((lr >> 2) & 1);
+    const int koE = lr * RBK + kq + kb2, koO = lr * RBK + kq - kb2;
+    // V (B operand, transposing read): row 4 lg + lr / 4 (+ 32 kk, + 16),
+    // columns col0 + 16 nd + 4 (lr % 4) .. + 3.
+    int vo[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        vo[m] = (4 * lg + (lr >> 2)) * RBV + 32 * (m ^ (lr >> 2)) + 16 * ((lr & 3) >> 1) + 8 * (lr & 1) + 2 * col0;
 
     while (true) {
         const int b = cu.b, g = cu.g, qt = cu.qt;
         const int c0 = cu.c;
         const int c1 = cu.nch < c0 + (end - cu.item) ? cu.nch : c0 + (end - cu.item);
         const bool whole = (c0 == 0 && c1 == cu.nch);
-        const int kv = p.ws.kvlen[b];
-        const int ql = p.ws.qlen[b];
+        const int kv = sload(p.ws.kvlen, b);
+        const int ql = sload(p.ws.qlen, b);
         const int rows = ql * G;
         int rows_tile = rows - qt * R;
         rows_tile = rows_tile < R ? rows_tile : R;
-        const int t0 = p.ws.cu_q[b];
+        const int t0 = sload(p.ws.cu_q, b);
         const int prefix = kv - ql > 0 ? kv - ql : 0;
         const int nvis = tile_nvis(kv, ql, G, qt * R + rows_tile - 1, p.causal);
-        const int nblk = nvis > 0 ? div_bs(nvis - 1, bs, bsh) + 1 : 0;
+        const int nblk = nvis > 0 ? div_bs(nvis - 1, bs, bsh) + 1 : 1;
         // the fewest visible tokens of any row of the tile (masking threshold)
         const int min_lim = p.causal ? tile_nvis(kv, ql, G, qt * R, 1) : kv;
         const int wr0 = rgi * 16 * MB;
         const bool wave_active = wr0 < rows_tile;
-        const int64_t row_stride_k = (int64_t)Hkv * DK;
-        const int64_t row_stride_v = (int64_t)Hkv * DV;
+        const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks;
+        const char *kgh = kg + (size_t)g * RBK;
+        const char *vgh = vg + (size_t)g * RBV;
 
         // Q^T operand and the visible limit of this lane's rows
         u32x4 qb[MB][KS];
@@ -184,213 +229,170 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
             lsum[mb] = 0.f;
         }
 
-        int win0 = div_bs(c0 * KT, bs, bsh);
-        auto load_window = [&](int first_blk) {
-            __syncthreads();
-            for (int k = tid; k < kBtWindow; k += NT) {
-                const int blk = first_blk + k;
-                sBT[k] = blk < nblk ? p.block_tables[(size_t)b * p.max_blocks + blk] : 0;
+        // Block id of each 16-token group of a chunk (clamped table index;
+        // range-checked when used).
+        int bid[NTT];
+        auto fetch_bids = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+            for (int q = 0; q < NTT; ++q) {
+                const int blk = div_bs(c * KT + 16 * q, bs, bsh);
+                bid[q] = sload(bt, blk < nblk ? blk : nblk - 1);
             }
-            __syncthreads();
         };
-        load_window(win0);
+        // Issue the LDS loads of chunk c.  Groups wholly past the visible
+        // range are not loaded; their stale LDS rows are masked in compute.
+        auto issue = [&](int c, lds_u8 *kb, lds_u8 *vb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int q = 0; q < NTT; ++q) {
+                const int j0 = c * KT + 16 * q;
+                if (j0 >= nvis)
+                    break;
+                const bool inb = (unsigned)bid[q] < nb32;
+                err |= inb ? 0u : (uint32_t)PA_DEVERR_BLOCK_ID;
+                const size_t trow = (size_t)bid[q] * bs + mod_bs(j0, bs, bsh);
+                const char *kbase = inb ? kgh + trow * rsk : zg;
+                const char *vbase = inb ? vgh + trow * rsv : zg;
+#pragma unroll
+                for (int m = 0; m < MK; ++m)
+                    if (wave + NW * m < IPGK)
+                        __builtin_amdgcn_global_load_lds((const void *)(kbase + voK[m]),
+                                                         (lds_void *)(kb + (q * IPGK + wave + NW * m) * 1024), 16, 0, 0);
+#pragma unroll
+                for (int m = 0; m < MV; ++m)
+                    if (wave + NW * m < IPGV)
+                        __builtin_amdgcn_global_load_lds((const void *)(vbase + voV[m]),
+                                                         (lds_void *)(vb + (q * IPGV + wave + NW * m) * 1024), 16, 0, 0);
+            }
+        };
 
-        uint4 kreg[NKP];
-        uint4 vreg[NVP][4];
-        auto row_offset = [&](int j, int64_t stride, int d, bool &ok) -> size_t {
-            const int phys = sBT[div_bs(j, bs, bsh) - win0];
-            ok = (unsigned)phys < (unsigned long long)p.num_blocks;
-            return ((size_t)phys * bs + mod_bs(j, bs, bsh)) * stride + (size_t)g * d;
-        };
-        auto issue = [&](int c) {
-            const int jb = c * KT;
-#pragma unroll
-            for (int k = 0; k < NKP; ++k) {
-                const int piece = tid + NT * k;
-                const int row = piece / (DK / 8);
-                const int col = (piece % (DK / 8)) * 8;
-                const int j = jb + row;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (piece < NKP_T && j < nvis) {
-                    bool ok;
-                    const size_t off = row_offset(j, row_stride_k, DK, ok);
-                    if (ok)
-                        v = *(const uint4 *)(kg + off + col);
-                    else
-                        err |= PA_DEVERR_BLOCK_ID;
-                }
-                kreg[k] = v;
-            }
-#pragma unroll
-            for (int k = 0; k < NVP; ++k) {
-                const int piece = tid + NT * k;
-                const int x = piece & 63, y = piece >> 6;
-                const int col8 = (x & 7) + 8 * (y % (DV / 64));
-                const int tg = (x >> 3) + 8 * (y / (DV / 64));
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int j = jb + 4 * tg + q;
-                    uint4 v = make_uint4(0, 0, 0, 0);
-                    if (piece < NVP_T && j < nvis) {
-                        bool ok;
-                        const size_t off = row_offset(j, row_stride_v, DV, ok);
-                        if (ok)
-                            v = *(const uint4 *)(vg + off + col8 * 8);
-                    }
-                    vreg[k][q] = v;
-                }
-            }
-        };
-        auto store = [&](int buf) {
-#pragma unroll
-            for (int k = 0; k < NKP; ++k) {
-                const int piece = tid + NT * k;
-                if (piece < NKP_T) {
-                    const int row = piece / (DK / 8);
-                    const int col = (piece % (DK / 8)) * 8;
-                    *(uint4 *)(sK + buf * KBUF + row * KP + col) = kreg[k];
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < NVP; ++k) {
-                const int piece = tid + NT * k;
-                if (piece < NVP_T) {
-                    const int x = piece & 63, y = piece >> 6;
-                    const int col8 = (x & 7) + 8 * (y % (DV / 64));
-                    const int tg = (x >> 3) + 8 * (y / (DV / 64));
-                    const uint32_t w0[4] = {vreg[k][0].x, vreg[k][0].y, vreg[k][0].z, vreg[k][0].w};
-                    const uint32_t w1[4] = {vreg[k][1].x, vreg[k][1].y, vreg[k][1].z, vreg[k][1].w};
-                    const uint32_t w2[4] = {vreg[k][2].x, vreg[k][2].y, vreg[k][2].z, vreg[k][2].w};
-                    const uint32_t w3[4] = {vreg[k][3].x, vreg[k][3].y, vreg[k][3].z, vreg[k][3].w};
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int colA = col8 * 8 + 2 * m, colB = colA + 1;
-                        const uint2 lo = make_uint2(__builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u),
-                                                    __builtin_amdgcn_perm(w3[m], w2[m], 0x05040100u));
-                        const uint2 hi = make_uint2(__builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u),
-                                                    __builtin_amdgcn_perm(w3[m], w2[m], 0x07060302u));
-                        *(uint2 *)(sVt + buf * VBUF + colA * VTP + 4 * vt_group<KT>(tg, colA)) = lo;
-                        *(uint2 *)(sVt + buf * VBUF + colB * VTP + 4 * vt_group<KT>(tg, colB)) = hi;
-                    }
-                }
-            }
-        };
-        auto ensure_window = [&](int c) {
-            const int jb = c * KT;
-            int jl = jb + KT - 1;
-            jl = jl < nvis - 1 ? jl : nvis - 1;
-            if (jl < jb)
+        // one chunk from (kb, vb): S^T, mask, online softmax, PV
+        auto compute = [&](const lds_u8 *kb, const lds_u8 *vb, int c) __attribute__((always_inline)) {
+            if (!wave_active)
                 return;
-            if (div_bs(jl, bs, bsh) >= win0 + kBtWindow) {
-                win0 = div_bs(jb, bs, bsh);
-                load_window(win0);
+            const int jb = c * KT;
+            f32x4 sacc[MB][NTT];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int n = 0; n < NTT; ++n)
+                    sacc[mb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int n = 0; n < NTT; ++n) {
+                    const u32x4 a = *(const lds_u32x4 *)(kb + ((ks & 1) ? koO : koE) + 16 * n * RBK + 64 * ks);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        sacc[mb][n] = Mfma<DT>::run(a, qb[mb][ks], sacc[mb][n]);
+                }
             }
-        };
-
-        issue(c0);
-        store(0);
-        __syncthreads();
-
-        for (int c = c0; c < c1; ++c) {
-            const int buf = (c - c0) & 1;
-            const bool has_next = c + 1 < c1;
-            if (has_next) {
-                ensure_window(c + 1);
-                issue(c + 1);
-            }
-            if (wave_active) {
-                const uint16_t *kb = sK + buf * KBUF;
-                const uint16_t *vb = sVt + buf * VBUF;
-                const int jb = c * KT;
-                // ---------------------------------------- S^T = K . Q^T
-                f32x4 sacc[MB][NTT];
+            const bool need_mask = jb + KT > min_lim;
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < MB; ++mb) {
+                float mx = -INFINITY;
 #pragma unroll
-                    for (int n = 0; n < NTT; ++n)
-                        sacc[mb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int n = 0; n < NTT; ++n) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                    for (int n = 0; n < NTT; ++n) {
-                        const u32x4 a = *(const u32x4 *)(kb + (16 * n + lr) * KP + 32 * ks + 8 * lg);
-#pragma unroll
-                        for (int mb = 0; mb < MB; ++mb)
-                            sacc[mb][n] = Mfma<DT>::run(a, qb[mb][ks], sacc[mb][n]);
+                    for (int r = 0; r < 4; ++r) {
+                        float v = sacc[mb][n][r] * p.scale_log2;
+                        if (need_mask) {
+                            const int j = jb + 16 * n + 4 * lg + r;
+                            v = j < lim[mb] ? v : -INFINITY;
+                        }
+                        sacc[mb][n][r] = v;
+                        mx = fmaxf(mx, v);
                     }
                 }
-                // ------------------------------------- mask, softmax
-                const bool need_mask = jb + KT > min_lim;
+                mx = fmaxf(mx, pair_swap<16>(mx));
+                mx = fmaxf(mx, pair_swap<32>(mx));
+                const float m_new = fmaxf(m_run[mb], mx);
+                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[mb] - m_new);
+                float ps = 0.f;
+#pragma unroll
+                for (int n = 0; n < NTT; ++n) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float v = sacc[mb][n][r];
+                        const float pv = v == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v - m_new);
+                        sacc[mb][n][r] = pv;
+                        ps += pv;
+                    }
+                }
+                lsum[mb] = lsum[mb] * alpha + ps;
+                m_run[mb] = m_new;
+                // O rows 4 lg + r take the factor of the lane holding that row
+                if (__any(alpha != 1.f)) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float ar = __shfl(alpha, 4 * lg + r);
+#pragma unroll
+                        for (int nd = 0; nd < ND; ++nd)
+                            oacc[mb][nd][r] *= ar;
+                    }
+                }
+            }
+            // V rows of tokens at or past nvis may be stale or unwritten
+            // cache slots: zero their operand halves (P is 0 there).
+            const bool tail = jb + KT > nvis;
+#pragma unroll
+            for (int kk = 0; kk < PVK; ++kk) {
+                u32x4 pa[MB];
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
-                    float mx = -INFINITY;
-#pragma unroll
-                    for (int n = 0; n < NTT; ++n) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            float s = sacc[mb][n][r] * p.scale_log2;
-                            if (need_mask) {
-                                const int j = jb + 16 * n + 4 * lg + r;
-                                s = j < lim[mb] ? s : -INFINITY;
-                            }
-                            sacc[mb][n][r] = s;
-                            mx = fmaxf(mx, s);
-                        }
-                    }
-                    mx = fmaxf(mx, pair_swap<16>(mx));
-                    mx = fmaxf(mx, pair_swap<32>(mx));
-                    const float m_new = fmaxf(m_run[mb], mx);
-                    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run[mb] - m_new);
-                    float ps = 0.f;
-#pragma unroll
-                    for (int n = 0; n < NTT; ++n) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float s = sacc[mb][n][r];
-                            const float pv = s == -INFINITY ? 0.f : exp2f(s - m_new);
-                            sacc[mb][n][r] = pv;
-                            ps += pv;
-                        }
-                    }
-                    lsum[mb] = lsum[mb] * alpha + ps;
-                    m_run[mb] = m_new;
-                    // O rows 4 lg + r take the factor of the lane holding that row
-                    if (__ballot(alpha != 1.f) != 0) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float ar = __shfl(alpha, 4 * lg + r);
-#pragma unroll
-                            for (int nd = 0; nd < ND; ++nd)
-                                oacc[mb][nd][r] *= ar;
-                        }
-                    }
+                    const f32x4 s0 = sacc[mb][2 * kk], s1 = sacc[mb][2 * kk + 1];
+                    pa[mb] = u32x4{pack2<DT>(s0[0], s0[1]), pack2<DT>(s0[2], s0[3]),
+                                   pack2<DT>(s1[0], s1[1]), pack2<DT>(s1[2], s1[3])};
                 }
-                // --------------------------------------------- O += P V
+                u32x4 vm = {~0u, ~0u, ~0u, ~0u};
+                if (tail) {
+                    const int tb = jb + 32 * kk + 4 * lg;
 #pragma unroll
-                for (int kk = 0; kk < PVK; ++kk) {
-                    u32x4 pa[MB];
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        const f32x4 s0 = sacc[mb][2 * kk], s1 = sacc[mb][2 * kk + 1];
-                        pa[mb] = u32x4{pack2<DT>(s0[0], s0[1]), pack2<DT>(s0[2], s0[3]),
-                                       pack2<DT>(s1[0], s1[1]), pack2<DT>(s1[2], s1[3])};
-                    }
+                        for (int e = 0; e < 2; ++e)
+                            vm[2 * h + e] = (tb + 16 * h + 2 * e < nvis ? 0xffffu : 0u) |
+                                            (tb + 16 * h + 2 * e + 1 < nvis ? 0xffff0000u : 0u);
+                }
 #pragma unroll
-                    for (int nd = 0; nd < ND; ++nd) {
-                        const int col = col0 + 16 * nd + lr;
-                        const uint16_t *vrow = vb + col * VTP;
-                        const uint2 v0 = *(const uint2 *)(vrow + 4 * vt_group<KT>(8 * kk + lg, col));
-                        const uint2 v1 = *(const uint2 *)(vrow + 4 * vt_group<KT>(8 * kk + 4 + lg, col));
-                        const u32x4 bv = {v0.x, v0.y, v1.x, v1.y};
+                for (int nd = 0; nd < ND; ++nd) {
+                    const int off = 32 * kk * RBV + 32 * (nd & ~3);
+                    const v4i16 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off));
+                    const v4i16 b1 =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off + 16 * RBV));
+                    const uint2 lo = __builtin_bit_cast(uint2, b0), hi = __builtin_bit_cast(uint2, b1);
+                    u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
+                    if (tail)
+                        bv &= vm;
 #pragma unroll
-                        for (int mb = 0; mb < MB; ++mb)
-                            oacc[mb][nd] = Mfma<DT>::run(pa[mb], bv, oacc[mb][nd]);
-                    }
+                    for (int mb = 0; mb < MB; ++mb)
+                        oacc[mb][nd] = Mfma<DT>::run(pa[mb], bv, oacc[mb][nd]);
                 }
             }
-            if (has_next)
-                store(buf ^ 1);
-            __syncthreads();
+        };
+
+        // all waves are done reading both buffers (previous segment)
+        __syncthreads();
+        fetch_bids(c0);
+        issue(c0, (lds_u8 *)sK0, (lds_u8 *)sV0);
+        if (c0 + 1 < c1)
+            fetch_bids(c0 + 1);
+        for (int c = c0; c < c1; c += 2) {
+            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of chunk c are in LDS
+            __builtin_amdgcn_s_barrier();         // ... and every other wave's
+            if (c + 1 < c1)
+                issue(c + 1, (lds_u8 *)sK1, (lds_u8 *)sV1);
+            compute((const lds_u8 *)sK0, (const lds_u8 *)sV0, c);
+            if (c + 1 >= c1)
+                break;
+            if (c + 2 < c1)
+                fetch_bids(c + 2);   // scalar loads land while this wave waits below
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+            __builtin_amdgcn_s_barrier();
+            if (c + 2 < c1)
+                issue(c + 2, (lds_u8 *)sK0, (lds_u8 *)sV0);
+            compute((const lds_u8 *)sK1, (const lds_u8 *)sV1, c + 1);
+            if (c + 3 < c1)
+                fetch_bids(c + 3);
         }
 
         // -------------------------------------------------------- finalise
@@ -434,7 +436,6 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
                 }
             }
         }
-        __syncthreads();
 
         first_seg = false;
         cu.item += c1 - c0;
