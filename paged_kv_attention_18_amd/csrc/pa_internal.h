@@ -191,6 +191,45 @@ __device__ __forceinline__ float pair_swap(float v)
     return __builtin_bit_cast(float, r);
 }
 
+// For D = 16 or 32: {this lane's v, lane (l ^ D)'s v}, in an order that
+// depends on the lane (gfx950 v_permlane16_swap / v_permlane32_swap, no LDS
+// round trip).  Enough for symmetric combinations such as max and sum.
+template <int D>
+__device__ __forceinline__ float xor_max(float v)
+{
+    const unsigned x = __builtin_bit_cast(unsigned, v);
+    unsigned a, b;
+    if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        a = r[0];
+        b = r[1];
+    } else {
+        static_assert(D == 32, "D");
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        a = r[0];
+        b = r[1];
+    }
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
+template <int D>
+__device__ __forceinline__ float xor_sum(float v)
+{
+    const unsigned x = __builtin_bit_cast(unsigned, v);
+    unsigned a, b;
+    if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        a = r[0];
+        b = r[1];
+    } else {
+        static_assert(D == 32, "D");
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        a = r[0];
+        b = r[1];
+    }
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
 // Transposing reduction.  On entry every lane of an aligned group of W lanes
 // holds NV partial sums v[0..NV) of the same NV quantities.  On exit lane l
 // holds complete sums: if NV >= W, v[0..NV/W) are quantities

@@ -99,7 +99,7 @@ __device__ __forceinline__ int sload(const int32_t *ptr, size_t i)
 }
 
 template <int DT, int DK, int DV, int MB, int KT, int NW, int CS>
-__global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
+__global__ __launch_bounds__(64 * NW, (DK <= 128 && DV <= 128) ? 2 : 1) void tile_kernel(Params p)
 {
     constexpr int RGS = NW / CS;                  // row groups
     constexpr int R = 16 * MB * RGS;              // rows per tile
@@ -147,6 +147,14 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
     const uint32_t rsk = (uint32_t)p.kv_head_num * RBK;   // bytes per token row of the cache
     const uint32_t rsv = (uint32_t)p.kv_head_num * RBV;
     const uint32_t nb32 = p.num_blocks < 0x7fffffff ? (uint32_t)p.num_blocks : 0x7fffffffu;
+    // Scores are kept raw (q . k) and scaled on the way into exp2 by
+    // sc = |scale| log2(e); a negative scale is folded into Q.
+    const bool neg_scale = p.scale_log2 < 0.f;
+    const float sc = fmaxf(fabsf(p.scale_log2), 1e-30f);   // scale 0: every visible token weighs 1
+    // The running max used as exp2 reference is only moved when a row's
+    // max grows by more than 2^8 (P stays below 256, exact in the
+    // 16-bit operand types); a moved reference rescales O and the sum.
+    const float grow_raw = 8.f / sc;
     uint32_t err = 0;
     bool first_seg = true;
 
@@ -212,8 +220,11 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
             lim[mb] = p.causal ? (prefix + rg / G + 1 < kv ? prefix + rg / G + 1 : kv) : kv;
             const uint16_t *src = qg + ((size_t)t * H + g * G + rg % G) * DK + 8 * lg;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) {
                 qb[mb][ks] = ok ? *(const u32x4 *)(src + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+                if (neg_scale)   // exact: softmax(c s) = softmax(|c| (-s)) with -s = (-q) . k
+                    qb[mb][ks] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+            }
         }
 
         f32x4 oacc[MB][ND];
@@ -294,34 +305,21 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
                 for (int n = 0; n < NTT; ++n) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float v = sacc[mb][n][r] * p.scale_log2;
                         if (need_mask) {
                             const int j = jb + 16 * n + 4 * lg + r;
-                            v = j < lim[mb] ? v : -INFINITY;
+                            sacc[mb][n][r] = j < lim[mb] ? sacc[mb][n][r] : -INFINITY;
                         }
-                        sacc[mb][n][r] = v;
-                        mx = fmaxf(mx, v);
+                        mx = fmaxf(mx, sacc[mb][n][r]);
                     }
                 }
-                mx = fmaxf(mx, pair_swap<16>(mx));
-                mx = fmaxf(mx, pair_swap<32>(mx));
-                const float m_new = fmaxf(m_run[mb], mx);
-                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[mb] - m_new);
-                float ps = 0.f;
-#pragma unroll
-                for (int n = 0; n < NTT; ++n) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float v = sacc[mb][n][r];
-                        const float pv = v == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v - m_new);
-                        sacc[mb][n][r] = pv;
-                        ps += pv;
-                    }
-                }
-                lsum[mb] = lsum[mb] * alpha + ps;
-                m_run[mb] = m_new;
-                // O rows 4 lg + r take the factor of the lane holding that row
-                if (__any(alpha != 1.f)) {
+                mx = xor_max<16>(mx);
+                mx = xor_max<32>(mx);
+                if (__any(mx > m_run[mb] + grow_raw)) {
+                    const float m_new = fmaxf(m_run[mb], mx);
+                    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run[mb] - m_new) * sc);
+                    lsum[mb] *= alpha;
+                    m_run[mb] = m_new;
+                    // O rows 4 lg + r take the factor of the lane holding that row
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float ar = __shfl(alpha, 4 * lg + r);
@@ -330,6 +328,18 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
                             oacc[mb][nd][r] *= ar;
                     }
                 }
+                const float mref = m_run[mb] == -INFINITY ? 0.f : m_run[mb] * sc;
+                float ps = 0.f;
+#pragma unroll
+                for (int n = 0; n < NTT; ++n) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][n][r], sc, -mref));
+                        sacc[mb][n][r] = pv;
+                        ps += pv;
+                    }
+                }
+                lsum[mb] += ps;
             }
             // V rows of tokens at or past nvis may be stale or unwritten
             // cache slots: zero their operand halves (P is 0 there).
@@ -401,12 +411,12 @@ __global__ __launch_bounds__(64 * NW) void tile_kernel(Params p)
             float *part = p.ws.partials + (size_t)(2 * w + slot) * p.partial_stride;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-                float L = lsum[mb] + pair_swap<16>(lsum[mb]);
-                L += pair_swap<32>(L);
+                const float L = xor_sum<32>(xor_sum<16>(lsum[mb]));
+                const float Ms = m_run[mb] * sc;   // log2 domain
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float Lr = __shfl(L, 4 * lg + r);
-                    const float Mr = __shfl(m_run[mb], 4 * lg + r);
+                    const float Mr = __shfl(Ms, 4 * lg + r);
                     const int row_t = wr0 + 16 * mb + 4 * lg + r;
                     if (row_t >= rows_tile)
                         continue;

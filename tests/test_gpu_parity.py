@@ -68,6 +68,7 @@ CAUSAL_CASES = [
     ([1100, 90], [130, 90], 8, 8, 64, 32, "bf16"),
     ([700, 260], [64, 20], 4, 1, 256, 64, "f16"),
     ([150, 40, 1], [4, 8, 1], 32, 8, 128, 128, "f16"),      # splitfuse decode half (16-32 rows)
+    ([200, 97], [20, 33], 8, 2, 128, 48, "bf16"),           # block size not a power of 2
 ]
 
 
@@ -78,6 +79,17 @@ def test_causal_mfma_parity(case):
     p = synth.custom(kv, H, Hkv, D, D, bs, dt, "causal", q_seq_lens=ql, seed=11)
     check_full(p, what=f"causal {case}")
     check_full(p, flags=F.PA_FLAG_NO_SPLIT, what="causal no-split")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 2.5], ids=["negative", "zero", "large"])
+def test_scale_sign_and_degenerate_values(scale):
+    # The MFMA path folds the sign of the scale into Q; scale 0 weighs every
+    # visible token equally.
+    log(f"scale {scale}")
+    p = synth.custom([300, 45], 8, 2, 128, 128, 64, "f16", "causal", q_seq_lens=[40, 45], scale=scale, seed=16)
+    check_full(p, what=f"mfma scale {scale}")
+    p = synth.custom([300, 45, 1000], 8, 2, 128, 128, 64, "bf16", scale=scale, seed=17)
+    check_full(p, what=f"valu scale {scale}")
 
 
 def test_causal_small_rows_valu():
