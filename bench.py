@@ -124,6 +124,10 @@ def main():
     ap.add_argument("--workload", default="gqa_decode",
                     help="tiny_decode | gqa_decode | skewed_long_decode | splitfuse_causal | mla_decode")
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies to rotate over (0 = auto)")
+    ap.add_argument("--flags", type=int, default=0, help="pa_config.flags (PA_FLAG_* bits; 0 = automatic)")
+    ap.add_argument("--partitions", type=int, default=0, help="pa_config.num_partitions (0 = automatic)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the forward pass from HIP graphs (one per KV copy) for the throughput figure")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size, in seconds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -160,7 +164,7 @@ def main():
     copies = args.copies or max(3, math.ceil((1.5 * (1 << 30)) / cache_bytes))
     kcs = [p.key_cache] + [p.key_cache.clone() for _ in range(copies - 1)]
     vcs = [p.value_cache] + [p.value_cache.clone() for _ in range(copies - 1)]
-    att = binding.for_problem(p)
+    att = binding.for_problem(p, flags=args.flags, num_partitions=args.partitions)
     desc = att.describe()
     out = torch.empty(p.num_q_tokens, w.head_num, w.head_size_v, dtype=p.query.dtype, device=dev)
     ql_max = max(1, p.max_q_seq_len)
@@ -175,16 +179,43 @@ def main():
     if att.device_error() != 0:
         raise RuntimeError("device error flag set during warm-up")
 
-    binding.pa_set_timing(att.handle, 1)
     stream = torch.cuda.current_stream()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for k in range(args.steps):
-        step(k)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+    run = step
+    if args.graph:
+        # one captured forward pass per KV copy, replayed in the same rotation
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for k in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(k)
+                graphs.append(g)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        run = lambda k: graphs[k % copies].replay()
+        for k in range(args.warmup):
+            run(k)
+        torch.cuda.synchronize()
+
+    def timed(n):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(n):
+            run(k)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop)
+
+    # (1) whole-pass throughput, no per-kernel events in the stream
+    total_ms = timed(args.steps)
+    # (2) the same steps again with HIP events around each kernel of the pass
+    #     (eager launches: events are recorded on the stream the kernels use)
+    binding.pa_set_timing(att.handle, 1)
+    run = step
+    timed_ms = timed(args.steps)
     kms, passes = binding.pa_read_timing(att.handle)
     binding.pa_set_timing(att.handle, 0)
     assert passes == args.steps
@@ -215,9 +246,11 @@ def main():
             "head_size_k": w.head_size_k, "head_size_v": w.head_size_v, "block_size": w.block_size,
             "mask": w.mask, "query_tokens": tokens, "kv_tokens": p.kv_tokens(), "kv_bytes": kv_bytes,
             "seed": w.seed, "kv_cache_copies": copies, "path": desc["path"],
-            "partitions": desc["partitions"], "parallelism": "none (1 GPU)",
+            "partitions": desc["partitions"], "flags": args.flags, "parallelism": "none (1 GPU)",
         },
         "pass_hbm_gbps": kv_bytes / (ms_per_step * 1e-3) / 1e9,
+        "launch": "hip graph replay" if args.graph else "eager",
+        "ms_per_step_with_kernel_events": timed_ms / args.steps,
         "kernels_ms": {"plan": kms[0] / passes, "attention": attn_ms, "merge": kms[2] / passes},
         "roofline": {
             "kernel": kernel,

@@ -19,7 +19,7 @@ constexpr int kMaxTimedPasses = 1024;
 struct Variant {
     int path;        // 0 = VALU decode, 1 = MFMA tile
     int rows_pad;    // VALU: padded rows per unit
-    int row_blocks;  // MFMA: 16-row blocks per wave
+    int tile_variant;  // MFMA: kernel variant (pa::tile_supported)
     int rows_per_tile;
     int chunk;
     int partitions;  // balanced-mode workers (waves for the VALU kernel, workgroups for MFMA)
@@ -70,11 +70,14 @@ struct pa_handle {
             v.partitions = num_cus * pa::decode_workers_per_cu(cfg.dtype, cfg.head_size_k, cfg.head_size_v, v.rows_pad);
         } else {
             v.path = 1;
-            const int r1 = pa::tile_rows(cfg.head_size_k, cfg.head_size_v, 1);
-            v.row_blocks = (rows > r1 && pa::tile_supported(cfg.head_size_k, cfg.head_size_v, 2)) ? 2 : 1;
-            v.rows_per_tile = pa::tile_rows(cfg.head_size_k, cfg.head_size_v, v.row_blocks);
-            v.chunk = pa::tile_chunk(cfg.head_size_k, cfg.head_size_v);
-            v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, cfg.head_size_k, cfg.head_size_v, v.row_blocks);
+            const int dk = cfg.head_size_k, dv = cfg.head_size_v;
+            int var = 0;
+            if (rows > 16 && pa::tile_supported(dk, dv, 1))
+                var = (rows > pa::tile_rows(dk, dv, 1) && pa::tile_supported(dk, dv, 2)) ? 2 : 1;
+            v.tile_variant = var;
+            v.rows_per_tile = pa::tile_rows(dk, dv, var);
+            v.chunk = pa::tile_chunk(dk, dv, var);
+            v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var);
         }
         if (cfg.num_partitions > 0)
             v.partitions = cfg.num_partitions;
@@ -119,14 +122,14 @@ static pa_status check_config(const pa_config *c)
     // Item indices are int32 on the device: bound the largest possible count.
     const int G = c->head_num / c->kv_head_num;
     const double tiles = std::ceil((double)c->max_q_seq_len * G / 16.0);
-    const double chunks = std::ceil((double)c->max_num_blocks_per_seq * c->block_size / 32.0) + 1.0;
+    const double chunks = std::ceil((double)c->max_num_blocks_per_seq * c->block_size / 16.0) + 1.0;
     if ((double)c->max_batch * c->kv_head_num * tiles * chunks > 2.0e9)
         return PA_ERR_INVALID_ARG;
     if ((double)c->max_num_blocks_per_seq * c->block_size > 2.0e9)
         return PA_ERR_INVALID_ARG;
     // Shapes with kernels in this build.
     const bool dec = pa::decode_supported(c->head_size_k, c->head_size_v);
-    const bool til = pa::tile_supported(c->head_size_k, c->head_size_v, 1);
+    const bool til = pa::tile_supported(c->head_size_k, c->head_size_v, 0);
     if (!dec && !til)
         return PA_ERR_UNSUPPORTED;
     if ((c->flags & PA_FLAG_FORCE_VALU) && !dec)
@@ -330,7 +333,7 @@ pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, con
     if (timed && hipEventRecord(ev[1], s) != hipSuccess)
         return PA_ERR_HIP;
     hipError_t e = v.path == 0 ? pa::launch_decode(p, c.dtype, v.rows_pad, s)
-                               : pa::launch_tile(p, c.dtype, v.row_blocks, s);
+                               : pa::launch_tile(p, c.dtype, v.tile_variant, s);
     if (e != hipSuccess)
         return PA_ERR_HIP;
     if (timed && hipEventRecord(ev[2], s) != hipSuccess)

@@ -69,13 +69,15 @@ hipError_t launch_plan(const Params &p, hipStream_t s);
 hipError_t launch_merge(const Params &p, int dtype, hipStream_t s);
 // Returns hipErrorInvalidValue when no kernel exists for the shape.
 hipError_t launch_decode(const Params &p, int dtype, int rows_pad, hipStream_t s);
-hipError_t launch_tile(const Params &p, int dtype, int row_blocks, hipStream_t s);
+hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s);
 // Shapes and occupancy used by the host to pick kernels and size the grid.
 bool decode_supported(int dk, int dv);
-bool tile_supported(int dk, int dv, int row_blocks);
-int tile_workers_per_cu(int dtype, int dk, int dv, int row_blocks);   // resident workgroups per CU
-int tile_chunk(int dk, int dv);
-int tile_rows(int dk, int dv, int row_blocks);
+// MFMA tile kernel variants: 0 for units of at most 16 rows, 1 for up to
+// tile_rows(.., 1) rows, 2 above; tile_supported says which exist.
+bool tile_supported(int dk, int dv, int variant);
+int tile_workers_per_cu(int dtype, int dk, int dv, int variant);   // resident workgroups per CU
+int tile_chunk(int dk, int dv, int variant);
+int tile_rows(int dk, int dv, int variant);
 int decode_chunk(int dk, int rows_pad);
 int decode_workers_per_cu(int dtype, int dk, int dv, int rows_pad);   // resident waves per CU
 

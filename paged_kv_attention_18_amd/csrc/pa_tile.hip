@@ -39,6 +39,8 @@
 // the output, or written as an fp32 partial for the merge kernel.
 #include "pa_internal.h"
 
+#include <type_traits>
+
 namespace pa {
 
 namespace {
@@ -98,8 +100,79 @@ __device__ __forceinline__ int sload(const int32_t *ptr, size_t i)
     return ((const c_i32 *)ptr)[i];
 }
 
-template <int DT, int DK, int DV, int MB, int KT, int NW, int CS>
-__global__ __launch_bounds__(64 * NW, (DK <= 128 && DV <= 128) ? 2 : 1) void tile_kernel(Params p)
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at dst + 16 l (global_load_lds_dwordx4, LDS base in M0).  Issued from
+// inline assembly so that the compiler does not add waits of its own for
+// these stores; the kernel waits for them explicitly (vmcnt + barrier)
+// before it reads the LDS they fill.
+__device__ __forceinline__ void lds_load16(const void *src, lds_u8 *dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+}
+
+template <int DT>
+struct Mfma16;   // 16 x 16 x 16 products (PV over 16-token chunks)
+
+template <>
+struct Mfma16<0> {
+    typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+    static __device__ __forceinline__ f32x4 run(uint2 a, uint2 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4, a), __builtin_bit_cast(v4, b), c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mfma16<1> {
+    static __device__ __forceinline__ f32x4 run(uint2 a, uint2 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, a), __builtin_bit_cast(v4i16, b), c,
+                                                         0, 0, 0);
+    }
+};
+
+// s_waitcnt with vmcnt(n) only (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most LW * min(ahead, A) vector memory instructions of this
+// wave are outstanding.
+template <int LW, int A>
+__device__ __forceinline__ void wait_ahead(int ahead)
+{
+    if constexpr (A == 0) {
+        wait_vm<0>();
+    } else {
+        if (ahead >= A)
+            wait_vm<LW * A>();
+        else
+            wait_ahead<LW, A - 1>(ahead);
+    }
+}
+
+// Workgroups per CU the register budget is cut for: as many as fit in LDS
+// (at most 4; at most 2 with two 16-row blocks per wave, 1 at head sizes
+// above 128).
+template <int DK, int DV, int MB, int KT, int S>
+constexpr int tile_min_wgs()
+{
+    constexpr int lds = S * KT * 2 * (DK + DV) + 2048;
+    constexpr int fit = (160 * 1024) / lds;
+    constexpr int cap = MB == 2 ? ((DK > 128 || DV > 128) ? 1 : 2) : 4;
+    return fit < 1 ? 1 : (fit > cap ? cap : fit);
+}
+
+// DT: 0 f16 / 1 bf16.  MB: 16-row blocks per wave.  KT: tokens per chunk
+// (16, 32 or 64).  NW: waves.  CS: waves sharing a row group (column split).
+// S: LDS stages (chunks c + 1 .. c + S - 1 are in flight while c is
+// computed).
+template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S>
+__global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S>())) void tile_kernel(Params p)
 {
     constexpr int RGS = NW / CS;                  // row groups
     constexpr int R = 16 * MB * RGS;              // rows per tile
@@ -107,18 +180,26 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 && DV <= 128) ? 2 : 1) void til
     constexpr int KS = DK / 32;
     constexpr int NTT = KT / 16;
     constexpr int ND = DV / 16 / CS;              // output column tiles per wave
-    constexpr int PVK = KT / 32;
     constexpr int IPGK = RBK / 64;                // 1 KiB LDS-load instructions per 16-token group (K)
     constexpr int IPGV = RBV / 64;
-    constexpr int MK = (IPGK + NW - 1) / NW;      // ... per wave per group (upper bound)
+    constexpr int MK = (IPGK + NW - 1) / NW;      // ... per wave per group
     constexpr int MV = (IPGV + NW - 1) / NW;
-    static_assert(DK % 32 == 0 && DV % 64 == 0 && (KT == 32 || KT == 64), "shape");
-    static_assert(NW % CS == 0 && ND % 4 == 0, "split");
+    constexpr int LW = NTT * (MK + MV);           // load instructions per wave per chunk, all waves alike
+    constexpr bool PAD = MK * NW != IPGK || MV * NW != IPGV;
+    static_assert(DK % 32 == 0 && DV % 64 == 0 && (KT == 16 || KT == 32 || KT == 64), "shape");
+    static_assert(NW % CS == 0 && ND % 4 == 0 && S >= 2 && S <= 4, "split");
+    static_assert(LW * (S - 2) < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(1024))) uint8_t sK0[KT * RBK];
-    __shared__ __attribute__((aligned(1024))) uint8_t sK1[KT * RBK];
     __shared__ __attribute__((aligned(1024))) uint8_t sV0[KT * RBV];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK1[KT * RBK];
     __shared__ __attribute__((aligned(1024))) uint8_t sV1[KT * RBV];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK2[S > 2 ? KT * RBK : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV2[S > 2 ? KT * RBV : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK3[S > 3 ? KT * RBK : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV3[S > 3 ? KT * RBV : 16];
+    // destination of the padding loads that keep every wave's count at LW
+    __shared__ __attribute__((aligned(1024))) uint8_t sJunk[PAD ? 1024 : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -166,20 +247,20 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 && DV <= 128) ? 2 : 1) void til
     for (int m = 0; m < MK; ++m) {
         const int x = (wave + NW * m) * 1024 + 16 * lane;
         const int row = x / RBK;
-        voK[m] = row * rsk + 16 * (((x % RBK) >> 4) ^ (row & 7));
+        voK[m] = (wave + NW * m) < IPGK ? row * rsk + 16 * (((x % RBK) >> 4) ^ (row & 7)) : 16 * lane;
     }
 #pragma unroll
     for (int m = 0; m < MV; ++m) {
         const int x = (wave + NW * m) * 1024 + 16 * lane;
         const int row = x / RBV;
-        voV[m] = row * rsv + 16 * (((x % RBV) >> 4) ^ (2 * (row & 3)));
+        voV[m] = (wave + NW * m) < IPGV ? row * rsv + 16 * (((x % RBV) >> 4) ^ (2 * (row & 3))) : 16 * lane;
     }
     // LDS read offsets.  K (A operand): row 16 n + lr, piece 4 ks + lg, which
     // the swizzle moves by +-64 bytes depending on bit 2 of the row.
     const int kq = 16 * (lg ^ (lr & 3));
     const int kb2 = 64 * ((lr >> 2) & 1);
     const int koE = lr * RBK + kq + kb2, koO = lr * RBK + kq - kb2;
-    // V (B operand, transposing read): row 4 lg + lr / 4 (+ 32 kk, + 16),
+    // V (B operand, transposing read): row 4 lg + lr / 4 (+ 16 n),
     // columns col0 + 16 nd + 4 (lr % 4) .. + 3.
     int vo[4];
 #pragma unroll
@@ -250,29 +331,33 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 && DV <= 128) ? 2 : 1) void til
                 bid[q] = sload(bt, blk < nblk ? blk : nblk - 1);
             }
         };
-        // Issue the LDS loads of chunk c.  Groups wholly past the visible
-        // range are not loaded; their stale LDS rows are masked in compute.
+        // Issue the LDS loads of chunk c: exactly LW instructions per wave.
+        // Groups wholly past the visible range read the zero page; their
+        // rows are masked in compute anyway.
         auto issue = [&](int c, lds_u8 *kb, lds_u8 *vb) __attribute__((always_inline)) {
 #pragma unroll
             for (int q = 0; q < NTT; ++q) {
                 const int j0 = c * KT + 16 * q;
-                if (j0 >= nvis)
-                    break;
+                const bool vis = j0 < nvis;
                 const bool inb = (unsigned)bid[q] < nb32;
-                err |= inb ? 0u : (uint32_t)PA_DEVERR_BLOCK_ID;
+                err |= (vis && !inb) ? (uint32_t)PA_DEVERR_BLOCK_ID : 0u;
                 const size_t trow = (size_t)bid[q] * bs + mod_bs(j0, bs, bsh);
-                const char *kbase = inb ? kgh + trow * rsk : zg;
-                const char *vbase = inb ? vgh + trow * rsv : zg;
+                const char *kbase = (vis && inb) ? kgh + trow * rsk : zg;
+                const char *vbase = (vis && inb) ? vgh + trow * rsv : zg;
 #pragma unroll
-                for (int m = 0; m < MK; ++m)
-                    if (wave + NW * m < IPGK)
-                        __builtin_amdgcn_global_load_lds((const void *)(kbase + voK[m]),
-                                                         (lds_void *)(kb + (q * IPGK + wave + NW * m) * 1024), 16, 0, 0);
+                for (int m = 0; m < MK; ++m) {
+                    const int i = wave + NW * m;
+                    lds_u8 *dst = (!PAD || i < IPGK) ? kb + (q * IPGK + i) * 1024 : (lds_u8 *)sJunk;
+                    const char *src = (!PAD || i < IPGK) ? kbase : zg;
+                    lds_load16(src + voK[m], dst);
+                }
 #pragma unroll
-                for (int m = 0; m < MV; ++m)
-                    if (wave + NW * m < IPGV)
-                        __builtin_amdgcn_global_load_lds((const void *)(vbase + voV[m]),
-                                                         (lds_void *)(vb + (q * IPGV + wave + NW * m) * 1024), 16, 0, 0);
+                for (int m = 0; m < MV; ++m) {
+                    const int i = wave + NW * m;
+                    lds_u8 *dst = (!PAD || i < IPGV) ? vb + (q * IPGV + i) * 1024 : (lds_u8 *)sJunk;
+                    const char *src = (!PAD || i < IPGV) ? vbase : zg;
+                    lds_load16(src + voV[m], dst);
+                }
             }
         };
 
@@ -344,65 +429,138 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 && DV <= 128) ? 2 : 1) void til
             // V rows of tokens at or past nvis may be stale or unwritten
             // cache slots: zero their operand halves (P is 0 there).
             const bool tail = jb + KT > nvis;
+            if constexpr (KT == 16) {
+                uint2 pa[MB];
 #pragma unroll
-            for (int kk = 0; kk < PVK; ++kk) {
-                u32x4 pa[MB];
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    const f32x4 s0 = sacc[mb][2 * kk], s1 = sacc[mb][2 * kk + 1];
-                    pa[mb] = u32x4{pack2<DT>(s0[0], s0[1]), pack2<DT>(s0[2], s0[3]),
-                                   pack2<DT>(s1[0], s1[1]), pack2<DT>(s1[2], s1[3])};
-                }
-                u32x4 vm = {~0u, ~0u, ~0u, ~0u};
+                for (int mb = 0; mb < MB; ++mb)
+                    pa[mb] = uint2{pack2<DT>(sacc[mb][0][0], sacc[mb][0][1]), pack2<DT>(sacc[mb][0][2], sacc[mb][0][3])};
+                uint2 vm = {~0u, ~0u};
                 if (tail) {
-                    const int tb = jb + 32 * kk + 4 * lg;
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-#pragma unroll
-                        for (int e = 0; e < 2; ++e)
-                            vm[2 * h + e] = (tb + 16 * h + 2 * e < nvis ? 0xffffu : 0u) |
-                                            (tb + 16 * h + 2 * e + 1 < nvis ? 0xffff0000u : 0u);
+                    const int tb = jb + 4 * lg;
+                    vm.x = (tb < nvis ? 0xffffu : 0u) | (tb + 1 < nvis ? 0xffff0000u : 0u);
+                    vm.y = (tb + 2 < nvis ? 0xffffu : 0u) | (tb + 3 < nvis ? 0xffff0000u : 0u);
                 }
 #pragma unroll
                 for (int nd = 0; nd < ND; ++nd) {
-                    const int off = 32 * kk * RBV + 32 * (nd & ~3);
-                    const v4i16 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off));
-                    const v4i16 b1 =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off + 16 * RBV));
-                    const uint2 lo = __builtin_bit_cast(uint2, b0), hi = __builtin_bit_cast(uint2, b1);
-                    u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
-                    if (tail)
-                        bv &= vm;
+                    const v4i16 b0 =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + 32 * (nd & ~3)));
+                    uint2 bv = __builtin_bit_cast(uint2, b0);
+                    if (tail) {
+                        bv.x &= vm.x;
+                        bv.y &= vm.y;
+                    }
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb)
-                        oacc[mb][nd] = Mfma<DT>::run(pa[mb], bv, oacc[mb][nd]);
+                        oacc[mb][nd] = Mfma16<DT>::run(pa[mb], bv, oacc[mb][nd]);
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < KT / 32; ++kk) {
+                    u32x4 pa[MB];
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const f32x4 s0 = sacc[mb][2 * kk], s1 = sacc[mb][2 * kk + 1];
+                        pa[mb] = u32x4{pack2<DT>(s0[0], s0[1]), pack2<DT>(s0[2], s0[3]),
+                                       pack2<DT>(s1[0], s1[1]), pack2<DT>(s1[2], s1[3])};
+                    }
+                    u32x4 vm = {~0u, ~0u, ~0u, ~0u};
+                    if (tail) {
+                        const int tb = jb + 32 * kk + 4 * lg;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int e = 0; e < 2; ++e)
+                                vm[2 * h + e] = (tb + 16 * h + 2 * e < nvis ? 0xffffu : 0u) |
+                                                (tb + 16 * h + 2 * e + 1 < nvis ? 0xffff0000u : 0u);
+                    }
+#pragma unroll
+                    for (int nd = 0; nd < ND; ++nd) {
+                        const int off = 32 * kk * RBV + 32 * (nd & ~3);
+                        const v4i16 b0 =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off));
+                        const v4i16 b1 =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off + 16 * RBV));
+                        const uint2 lo = __builtin_bit_cast(uint2, b0), hi = __builtin_bit_cast(uint2, b1);
+                        u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
+                        if (tail)
+                            bv &= vm;
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            oacc[mb][nd] = Mfma<DT>::run(pa[mb], bv, oacc[mb][nd]);
+                    }
                 }
             }
         };
 
-        // all waves are done reading both buffers (previous segment)
+        auto kbuf = [&](auto st) __attribute__((always_inline)) -> lds_u8 * {
+            if constexpr (decltype(st)::value == 0)
+                return (lds_u8 *)sK0;
+            else if constexpr (decltype(st)::value == 1)
+                return (lds_u8 *)sK1;
+            else if constexpr (decltype(st)::value == 2)
+                return (lds_u8 *)sK2;
+            else
+                return (lds_u8 *)sK3;
+        };
+        auto vbuf = [&](auto st) __attribute__((always_inline)) -> lds_u8 * {
+            if constexpr (decltype(st)::value == 0)
+                return (lds_u8 *)sV0;
+            else if constexpr (decltype(st)::value == 1)
+                return (lds_u8 *)sV1;
+            else if constexpr (decltype(st)::value == 2)
+                return (lds_u8 *)sV2;
+            else
+                return (lds_u8 *)sV3;
+        };
+        // one pipeline step: chunk c sits in stage st
+        auto step = [&](auto st, int c) __attribute__((always_inline)) {
+            constexpr int ST = decltype(st)::value;
+            constexpr int NX = (ST + S - 1) % S;   // stage of chunk c + S - 1
+            wait_ahead<LW, S - 2>(c1 - 1 - c);     // this wave's loads of chunk c are in LDS
+            __builtin_amdgcn_s_barrier();          // ... and every wave's; stage NX is free
+            if (c + S - 1 < c1)
+                issue(c + S - 1, kbuf(std::integral_constant<int, NX>{}), vbuf(std::integral_constant<int, NX>{}));
+            compute(kbuf(st), vbuf(st), c);
+            if (c + S < c1)
+                fetch_bids(c + S);                 // scalar loads land during the next wait
+        };
+
+        // Q in registers before the LDS loads start: the vector memory
+        // counter then covers only those loads.  All waves are done reading
+        // every stage (previous segment).
+        wait_vm<0>();
         __syncthreads();
         fetch_bids(c0);
         issue(c0, (lds_u8 *)sK0, (lds_u8 *)sV0);
-        if (c0 + 1 < c1)
-            fetch_bids(c0 + 1);
-        for (int c = c0; c < c1; c += 2) {
-            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of chunk c are in LDS
-            __builtin_amdgcn_s_barrier();         // ... and every other wave's
-            if (c + 1 < c1)
-                issue(c + 1, (lds_u8 *)sK1, (lds_u8 *)sV1);
-            compute((const lds_u8 *)sK0, (const lds_u8 *)sV0, c);
+        if constexpr (S > 2) {
+            if (c0 + 1 < c1) {
+                fetch_bids(c0 + 1);
+                issue(c0 + 1, (lds_u8 *)sK1, (lds_u8 *)sV1);
+            }
+        }
+        if constexpr (S > 3) {
+            if (c0 + 2 < c1) {
+                fetch_bids(c0 + 2);
+                issue(c0 + 2, (lds_u8 *)sK2, (lds_u8 *)sV2);
+            }
+        }
+        if (c0 + S - 1 < c1)
+            fetch_bids(c0 + S - 1);
+        for (int c = c0; c < c1; c += S) {
+            step(std::integral_constant<int, 0>{}, c);
             if (c + 1 >= c1)
                 break;
-            if (c + 2 < c1)
-                fetch_bids(c + 2);   // scalar loads land while this wave waits below
-            __builtin_amdgcn_s_waitcnt(0x0f70);
-            __builtin_amdgcn_s_barrier();
-            if (c + 2 < c1)
-                issue(c + 2, (lds_u8 *)sK0, (lds_u8 *)sV0);
-            compute((const lds_u8 *)sK1, (const lds_u8 *)sV1, c + 1);
-            if (c + 3 < c1)
-                fetch_bids(c + 3);
+            step(std::integral_constant<int, 1>{}, c + 1);
+            if constexpr (S > 2) {
+                if (c + 2 >= c1)
+                    break;
+                step(std::integral_constant<int, 2>{}, c + 2);
+            }
+            if constexpr (S > 3) {
+                if (c + 3 >= c1)
+                    break;
+                step(std::integral_constant<int, 3>{}, c + 3);
+            }
         }
 
         // -------------------------------------------------------- finalise
@@ -459,90 +617,99 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 && DV <= 128) ? 2 : 1) void til
         set_error(p.ws.err, err);
 }
 
-// Kernel variants: (Dk, Dv) -> chunk KT, waves NW, column split CS.
-template <int DK, int DV>
-struct TileCfg {
-    static constexpr int KT = (DK <= 128 && DV <= 128) ? 64 : 32;
-    static constexpr int NW = DV > 256 ? 8 : 4;
-    static constexpr int CS = DV > 256 ? 2 : 1;
-    static constexpr int MB2 = DV > 256 ? 1 : 2;   // the larger row block count built
+// Variants per (Dk, Dv).  0: units of at most 16 rows (decode), memory-bound:
+// one wave per workgroup (no waiting on other waves), short chunks, three
+// stages.  1: up to 64 rows.  2: more rows, two 16-row
+// blocks per wave.  Dk = 576 has variant 0 only (64 rows per tile).
+struct TileShape {
+    int mb, kt, nw, cs, s;
 };
 
-template <int DT, int DK, int DV>
-const void *kernel_for(int mb)
+template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S>
+const void *pick(TileShape *t)
 {
-    using C = TileCfg<DK, DV>;
-    if (mb == 1)
-        return (const void *)&tile_kernel<DT, DK, DV, 1, C::KT, C::NW, C::CS>;
-    if (mb == 2 && C::MB2 == 2)
-        return (const void *)&tile_kernel<DT, DK, DV, C::MB2, C::KT, C::NW, C::CS>;
-    return nullptr;
+    *t = TileShape{MB, KT, NW, CS, S};
+    return (const void *)&tile_kernel<DT, DK, DV, MB, KT, NW, CS, S>;
+}
+
+template <int DT, int DK, int DV>
+const void *kernel_for(int variant, TileShape *t)
+{
+    if constexpr (DK > 256) {
+        return variant == 0 ? pick<DT, DK, DV, 1, 16, 8, 2, 4>(t) : nullptr;
+    } else {
+        constexpr int KT = DK <= 128 ? 64 : 32;
+        if (variant == 0) {   // one wave per workgroup, several workgroups per CU
+            if constexpr (DK <= 128)
+                return pick<DT, DK, DV, 1, 32, 1, 1, 3>(t);
+            else
+                return pick<DT, DK, DV, 1, 16, 1, 1, 3>(t);
+        }
+        if (variant == 1)
+            return pick<DT, DK, DV, 1, KT, 4, 1, 2>(t);
+        if (variant == 2)
+            return pick<DT, DK, DV, 2, KT, 4, 1, 2>(t);
+        return nullptr;
+    }
 }
 
 template <int DT>
-const void *kernel_dt(int dk, int dv, int mb, int *threads)
+const void *kernel_dt(int dk, int dv, int variant, TileShape *t)
 {
-    if (dk == 64 && dv == 64) {
-        *threads = 64 * TileCfg<64, 64>::NW;
-        return kernel_for<DT, 64, 64>(mb);
-    }
-    if (dk == 128 && dv == 128) {
-        *threads = 64 * TileCfg<128, 128>::NW;
-        return kernel_for<DT, 128, 128>(mb);
-    }
-    if (dk == 256 && dv == 256) {
-        *threads = 64 * TileCfg<256, 256>::NW;
-        return kernel_for<DT, 256, 256>(mb);
-    }
-    if (dk == 576 && dv == 512) {
-        *threads = 64 * TileCfg<576, 512>::NW;
-        return kernel_for<DT, 576, 512>(mb);
-    }
+    if (dk == 64 && dv == 64)
+        return kernel_for<DT, 64, 64>(variant, t);
+    if (dk == 128 && dv == 128)
+        return kernel_for<DT, 128, 128>(variant, t);
+    if (dk == 256 && dv == 256)
+        return kernel_for<DT, 256, 256>(variant, t);
+    if (dk == 576 && dv == 512)
+        return kernel_for<DT, 576, 512>(variant, t);
     return nullptr;
 }
 
-const void *tile_kernel_ptr(int dtype, int dk, int dv, int mb, int *threads)
+const void *tile_kernel_ptr(int dtype, int dk, int dv, int variant, TileShape *t)
 {
-    return dtype == 0 ? kernel_dt<0>(dk, dv, mb, threads) : kernel_dt<1>(dk, dv, mb, threads);
+    return dtype == 0 ? kernel_dt<0>(dk, dv, variant, t) : kernel_dt<1>(dk, dv, variant, t);
 }
 
 }  // namespace
 
-int tile_chunk(int dk, int dv)
+bool tile_supported(int dk, int dv, int variant)
 {
-    return (dk <= 128 && dv <= 128) ? 64 : 32;
+    TileShape t;
+    return tile_kernel_ptr(0, dk, dv, variant, &t) != nullptr;
 }
 
-bool tile_supported(int dk, int dv, int row_blocks)
+int tile_chunk(int dk, int dv, int variant)
 {
-    int threads = 0;
-    return tile_kernel_ptr(0, dk, dv, row_blocks, &threads) != nullptr;
+    TileShape t;
+    return tile_kernel_ptr(0, dk, dv, variant, &t) ? t.kt : 0;
 }
 
-int tile_rows(int dk, int dv, int row_blocks)
+int tile_rows(int dk, int dv, int variant)
 {
-    const int nw = dv > 256 ? 8 : 4, cs = dv > 256 ? 2 : 1;
-    return 16 * row_blocks * (nw / cs);
+    TileShape t;
+    return tile_kernel_ptr(0, dk, dv, variant, &t) ? 16 * t.mb * (t.nw / t.cs) : 0;
 }
 
-int tile_workers_per_cu(int dtype, int dk, int dv, int row_blocks)
+int tile_workers_per_cu(int dtype, int dk, int dv, int variant)
 {
-    int threads = 0;
-    const void *k = tile_kernel_ptr(dtype, dk, dv, row_blocks, &threads);
+    TileShape t;
+    const void *k = tile_kernel_ptr(dtype, dk, dv, variant, &t);
     int n = 0;
-    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, threads, 0) != hipSuccess || n < 1)
+    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * t.nw, 0) != hipSuccess || n < 1)
         return 1;
     return n;
 }
 
-hipError_t launch_tile(const Params &p, int dtype, int row_blocks, hipStream_t s)
+hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s)
 {
-    int threads = 0;
-    const void *k = tile_kernel_ptr(dtype, p.head_size_k, p.head_size_v, row_blocks, &threads);
+    TileShape t;
+    const void *k = tile_kernel_ptr(dtype, p.head_size_k, p.head_size_v, variant, &t);
     if (!k)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&p};
-    return hipLaunchKernel(k, dim3(p.partitions), dim3(threads), args, 0, s);
+    return hipLaunchKernel(k, dim3(p.partitions), dim3(64 * t.nw), args, 0, s);
 }
 
 }  // namespace pa
