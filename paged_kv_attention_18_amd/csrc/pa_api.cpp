@@ -15,6 +15,12 @@
 namespace {
 
 constexpr int kMaxTimedPasses = 1024;
+// Pieces of the item range per worker in balanced mode.  With more pieces
+// than workers, workers that finish early take the remaining pieces, which
+// evens out end times; it pays where a chunk is long (many rows on the
+// matrix cores) and costs a pipeline start per piece, which thin
+// (memory-bound) units cannot hide, so they keep one piece per worker.
+constexpr int kMaxPiecesPerWorker = 2;
 
 struct Variant {
     int path;        // 0 = VALU decode, 1 = MFMA tile
@@ -23,6 +29,7 @@ struct Variant {
     int rows_per_tile;
     int chunk;
     int partitions;  // balanced-mode workers (waves for the VALU kernel, workgroups for MFMA)
+    int pieces_per_worker;
 };
 
 int next_pow2(int x)
@@ -31,6 +38,13 @@ int next_pow2(int x)
     while (p < x)
         p <<= 1;
     return p;
+}
+
+// Floats per partial slot: R x Dv outputs, then R maxima and R sums, rounded
+// up to a multiple of 4 so every slot starts 16-byte aligned.
+size_t partial_floats(int rows, int dv)
+{
+    return ((size_t)rows * (dv + 2) + 3) & ~(size_t)3;
 }
 
 bool valid_dtype(int d) { return d == PA_F16 || d == PA_BF16; }
@@ -58,16 +72,22 @@ struct pa_handle {
         const int G = cfg.head_num / cfg.kv_head_num;
         const int rows = max_q * G;
         const bool dec_ok = pa::decode_supported(cfg.head_size_k, cfg.head_size_v);
-        // VALU for thin units (the VALU kernel is built for at most 8 rows)
-        bool valu = dec_ok && rows <= 8;
+        // VALU for the thinnest units.  From 5 rows on the matrix-core
+        // kernel with one padded 16-row block streams faster: at 8 rows
+        // (Dk = Dv = 128) the VALU kernel holds half the KV bytes in flight
+        // per wave that it holds at 4 rows.
+        bool valu = dec_ok && rows <= 4;
         if (cfg.flags & PA_FLAG_FORCE_MFMA)
             valu = false;
+        if ((cfg.flags & PA_FLAG_FORCE_VALU) && dec_ok && rows <= 8)
+            valu = true;
         if (valu) {
             v.path = 0;
             v.rows_pad = next_pow2(rows < 1 ? 1 : rows);
             v.rows_per_tile = v.rows_pad;
             v.chunk = pa::decode_chunk(cfg.head_size_k, v.rows_pad);
             v.partitions = num_cus * pa::decode_workers_per_cu(cfg.dtype, cfg.head_size_k, cfg.head_size_v, v.rows_pad);
+            v.pieces_per_worker = 1;
         } else {
             v.path = 1;
             const int dk = cfg.head_size_k, dv = cfg.head_size_v;
@@ -78,6 +98,7 @@ struct pa_handle {
             v.rows_per_tile = pa::tile_rows(dk, dv, var);
             v.chunk = pa::tile_chunk(dk, dv, var);
             v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var);
+            v.pieces_per_worker = var == 0 ? 1 : kMaxPiecesPerWorker;
         }
         if (cfg.num_partitions > 0)
             v.partitions = cfg.num_partitions;
@@ -184,7 +205,7 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
     const int G = cfg->head_num / cfg->kv_head_num;
     for (int q : qs) {
         const Variant v = h->choose(q);
-        const size_t f = (size_t)v.rows_per_tile * (cfg->head_size_v + 2);
+        const size_t f = partial_floats(v.rows_per_tile, cfg->head_size_v);
         if (f > max_floats)
             max_floats = f;
         if (v.partitions > max_p)
@@ -206,12 +227,13 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
     const size_t o_ipg = off; off = align(off + B * sizeof(int32_t));
     const size_t o_ql = off; off = align(off + B * sizeof(int32_t));
     const size_t o_kv = off; off = align(off + B * sizeof(int32_t));
-    const size_t o_wgb = off; off = align(off + max_p * sizeof(int32_t));
-    const size_t o_spl = off; off = align(off + (size_t)max_p * 8 * sizeof(int32_t));
+    const size_t max_pieces = (size_t)max_p * kMaxPiecesPerWorker;
+    const size_t o_wgb = off; off = align(off + max_pieces * sizeof(int32_t));
+    const size_t o_spl = off; off = align(off + max_pieces * 8 * sizeof(int32_t));
     const size_t o_err = off; off = align(off + sizeof(uint32_t));
     const size_t zero_bytes = 16 * (size_t)cfg->kv_head_num * (size_t)(cfg->head_size_k > cfg->head_size_v ? cfg->head_size_k : cfg->head_size_v) * 2;
     const size_t o_zero = off; off = align(off + zero_bytes);
-    const size_t o_part = off; off = align(off + 2 * (size_t)max_p * max_floats * sizeof(float));
+    const size_t o_part = off; off = align(off + 2 * max_pieces * max_floats * sizeof(float));
     h->ws_bytes = off;
     if (hipMalloc(&h->ws_base, h->ws_bytes) != hipSuccess) {
         delete h;
@@ -321,7 +343,8 @@ pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, con
     p.no_split = (c.flags & PA_FLAG_NO_SPLIT) ? 1 : 0;
     p.partitions = p.no_split ? batch * c.kv_head_num * p.max_tiles
                               : (v.partitions < h->max_partitions ? v.partitions : h->max_partitions);
-    p.partial_stride = v.rows_per_tile * (c.head_size_v + 2);
+    p.pieces = p.no_split ? 0 : p.partitions * v.pieces_per_worker;
+    p.partial_stride = (int32_t)partial_floats(v.rows_per_tile, c.head_size_v);
     p.ws = h->ws;
 
     const bool timed = h->timing && h->timed < kMaxTimedPasses;

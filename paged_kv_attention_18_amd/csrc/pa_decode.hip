@@ -147,10 +147,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
     const int lane = threadIdx.x & 63;
     const int kq = lane % L;
     const int grp = lane / L;
-    const int worker = xcd_logical_index(blockIdx.x, gridDim.x) * (kThreads / 64) + (threadIdx.x >> 6);
+    const int wave = threadIdx.x >> 6;
+    int piece = xcd_logical_index(blockIdx.x, gridDim.x) * (kThreads / 64) + wave;
     Cursor cu;
     int end;
-    if (!wg_range(p, worker, cu, end))
+    if (piece >= p.partitions || !wg_range(p, piece, cu, end))
         return;
 
     const uint16_t *__restrict__ qg = (const uint16_t *)p.query;
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
             }
         } else {
             const int slot = first_seg ? 0 : 1;
-            float *part = p.ws.partials + (size_t)(2 * worker + slot) * p.partial_stride;
+            float *part = p.ws.partials + (size_t)(2 * piece + slot) * p.partial_stride;
 #pragma unroll
             for (int k = 0; k < PER; ++k) {
                 const int q = PER * grp + k;
@@ -452,11 +453,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
 
         first_seg = false;
         cu.item += c1 - c0;
-        if (cu.item >= end)
-            break;
-        cursor_next_unit(p, cu);
-        if (cu.b >= p.batch)
-            break;
+        bool more = cu.item < end;
+        if (more) {
+            cursor_next_unit(p, cu);
+            more = cu.b < p.batch;
+        }
+        if (!more) {
+            // this piece is done: take the next one, if any
+            if (p.no_split || p.pieces <= p.partitions)
+                break;
+            int nxt = 0;
+            if (lane == 0)
+                nxt = grab_piece(p);
+            piece = __shfl(nxt, 0);
+            if (!wg_range(p, piece, cu, end))
+                break;
+            first_seg = true;
+        }
     }
     if (err)
         set_error(p.ws.err, err);

@@ -17,23 +17,27 @@ namespace pa {
 //  item  = (unit, chunk c): the KV tokens [c * CT, (c + 1) * CT) of the unit,
 //          CT tokens per chunk.  A unit has nch = max(1, ceil(nvis / CT))
 //          items, nvis being the KV tokens its rows can see.
-//  Items are numbered b-major, then g, then qt, then c.  The attention grid
-//  of P workgroups takes contiguous ranges of `per` items each (balanced
-//  mode), or one unit per workgroup (no-split mode, per = 0).  A unit whose
-//  items are spread over several workgroups leaves fp32 partials (acc, m, l)
-//  that the merge kernel combines; slot 0 of workgroup w holds the partial of
-//  its first unit, slot 1 that of its last.
+//  Items are numbered b-major, then g, then qt, then c.  In balanced mode the
+//  items are cut into N pieces of `per` consecutive items; the grid of P
+//  persistent workers (workgroups of the MFMA kernel, waves of the VALU
+//  kernel) takes piece w first, then further pieces from a shared counter
+//  (pieces P, P + 1, ...) until none is left, so the workers finish
+//  together even when they stream at different rates.  In no-split mode
+//  (per = 0) every workgroup is one unit.  A unit whose items lie in more
+//  than one piece is split: each of its pieces leaves an fp32 partial
+//  (acc, m, l) in its slot (2k if the unit is the first of piece k, 2k + 1
+//  if it is the last), and the merge kernel combines them.
 
 struct Workspace {
-    int32_t *hdr;        // [4]: W (total items), per, P, unused
+    int32_t *hdr;        // [4]: W (total items), per, N (pieces), next piece counter
     int32_t *cu_q;       // [max_batch + 1]: first packed query row of each sequence
     int32_t *wsb;        // [max_batch + 1]: first item of each sequence
     int32_t *ipg;        // [max_batch]: items of each (b, g) (equal for all g of b)
     int32_t *qlen;       // [max_batch]: sanitised q_seq_lens
     int32_t *kvlen;      // [max_batch]: sanitised context_lens
-    int32_t *wg_b;       // [P]: sequence holding the first item of each worker
-    int32_t *splits;     // [P][8]: split units (b, g, qt, first item, end item; b < 0: none)
-    float *partials;     // [2 * P][R * (DV + 2)]
+    int32_t *wg_b;       // [N]: sequence holding the first item of each piece
+    int32_t *splits;     // [N][8]: split units (b, g, qt, first item, end item; b < 0: none)
+    float *partials;     // [2 * N][R * (DV + 2)]
     const void *zeros;   // 16 token rows of zeros (K or V), read in place of a bad block
     uint32_t *err;       // device error word
 };
@@ -57,7 +61,8 @@ struct Params {
     float scale_log2;                  // scale * log2(e)
     int32_t rows_per_tile;             // R
     int32_t chunk;                     // CT
-    int32_t partitions;                // P
+    int32_t partitions;                // P: workers in the grid (no-split mode: units)
+    int32_t pieces;                    // N: pieces of the item range (balanced mode)
     int32_t no_split;
     int32_t max_tiles;                 // ceil(max_q * G / R)
     int32_t partial_stride;            // floats per partial slot = R * (DV + 2)
@@ -361,14 +366,15 @@ __device__ __forceinline__ void cursor_next_unit(const Params &p, Cursor &cu)
                          cu.qt, p.causal);
 }
 
-// The item range of logical workgroup w; returns false if it has none.
+// The item range of piece w (balanced mode) or of the unit of workgroup w
+// (no-split mode); returns false if it has none.
 __device__ __forceinline__ bool wg_range(const Params &p, int w, Cursor &cu, int &end)
 {
     const int W = p.ws.hdr[0];
     const int per = p.ws.hdr[1];
     if (per > 0) {
         const int s = w * per;
-        if (s >= W)
+        if (w >= p.pieces || s >= W)
             return false;
         end = s + per < W ? s + per : W;
         cursor_seek(p, cu, p.ws.wg_b[w], s);
@@ -397,6 +403,14 @@ __device__ __forceinline__ bool wg_range(const Params &p, int w, Cursor &cu, int
     cu.item = start;
     end = start + cu.nch;
     return true;
+}
+
+// Next piece for a worker that finished its current one (one lane calls).
+// The counter is updated at system scope, so workgroups on every XCD see one
+// sequence of values.
+__device__ __forceinline__ int grab_piece(const Params &p)
+{
+    return p.partitions + __hip_atomic_fetch_add(p.ws.hdr + 3, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 #endif  // __HIPCC__

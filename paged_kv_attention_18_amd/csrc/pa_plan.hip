@@ -1,16 +1,20 @@
-// pa_plan.hip -- the device-side work planner and the log-sum-exp merge.
+// pa_plan.hip -- the device-side work planner.
 //
 // The planner plays the role of the task-list generator that the
 // SparseAttnSharedkvMetadata README describes (function section: a list of
 // start/end points -- batch, head, Q block, K block -- for every core,
 // consumed by the attention operator, and reduction tasks for split rows).
-// Here it runs on the GPU in one workgroup, reads only the lengths, and
-// gives every attention workgroup an equal number of KV chunks; the result
-// depends on the lengths alone, so outputs are deterministic.
+// Here it runs on the GPU in one workgroup and reads only the lengths: it
+// sanitises them, numbers the (sequence, KV head, row tile, KV chunk) items,
+// cuts them into N equal pieces, lists the units that a piece boundary cuts
+// (the reduction tasks) and resets the counter the attention kernels use to
+// hand out pieces.  The pieces depend on the lengths alone, so the partial
+// sums that make up an output row, and the order they are merged in, do not
+// depend on which workgroup ran which piece.
 //
 // The merge combines the fp32 partials of rows whose KV range was split over
-// several workgroups: with per-part running max m_p (log2 domain), sum l_p
-// and unnormalised output acc_p,
+// several pieces: with per-part running max m_p (log2 domain), sum l_p and
+// unnormalised output acc_p,
 //     M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  o = sum_p 2^(m_p - M) acc_p / L,
 // which is the softmax over the union of the parts exactly (the "FlashDecode
 // reduction" tasks of the same README's metadata output).
@@ -99,42 +103,40 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         __syncthreads();
     }
     const int W = s_carry_w;
-    const int per = p.no_split ? 0 : (W + p.partitions - 1) / p.partitions;
+    const int per = p.no_split ? 0 : (W + p.pieces - 1) / p.pieces;
     if (tid == 0) {
         p.ws.cu_q[p.batch] = s_carry_q;
         p.ws.wsb[p.batch] = W;
         p.ws.hdr[0] = W;
         p.ws.hdr[1] = per > 0 ? per : (p.no_split ? 0 : 1);
-        p.ws.hdr[2] = p.partitions;
+        p.ws.hdr[2] = p.no_split ? 0 : p.pieces;
         p.ws.hdr[3] = 0;
         if (s_carry_q != p.num_q_tokens)
             s_err |= PA_DEVERR_TOKENS;
     }
-    __syncthreads();
-    __threadfence_block();
     if (!p.no_split) {
         const int pe = per > 0 ? per : 1;
-        // Worker w starts at item w * pe: sequence b owns the workers whose
+        // Piece k starts at item k * pe: sequence b owns the pieces whose
         // start lies in [wsb[b], wsb[b+1]).
+        __syncthreads();
         for (int base = 0; base < p.batch; base += kPlanThreads) {
             const int b = base + tid;
             if (b < p.batch) {
                 const int lo = p.ws.wsb[b], hi = p.ws.wsb[b + 1];
                 if (hi > lo)
-                    for (int w = (lo + pe - 1) / pe; w * pe < hi && w < p.partitions; ++w)
-                        p.ws.wg_b[w] = b;
+                    for (int k = (lo + pe - 1) / pe; k * pe < hi && k < p.pieces; ++k)
+                        p.ws.wg_b[k] = b;
             }
         }
         __syncthreads();
-        __threadfence_block();
-        // A unit is split when a worker boundary falls strictly inside it;
-        // it is listed once, at its first inner boundary w (entry w - 1).
-        for (int w = 1 + tid; w < p.partitions; w += kPlanThreads) {
-            int32_t *d = p.ws.splits + (size_t)(w - 1) * 8;
-            const int s = w * pe;
+        // A unit is split when a piece boundary falls strictly inside it; it
+        // is listed once, at its first inner boundary k (entry k - 1).
+        for (int k = 1 + tid; k < p.pieces; k += kPlanThreads) {
+            int32_t *d = p.ws.splits + (size_t)(k - 1) * 8;
+            const int s = k * pe;
             int b = -1, g = 0, qt = 0, us = 0, ue = 0;
             if (s < W) {
-                const int bb = p.ws.wg_b[w];
+                const int bb = p.ws.wg_b[k];
                 const int kv = p.ws.kvlen[bb], ql = p.ws.qlen[bb], ipg = p.ws.ipg[bb];
                 int local = s - p.ws.wsb[bb];
                 const int gg = local / ipg;
@@ -173,11 +175,14 @@ __host__ __device__ inline int merge_rows_per_wg(int dv)
     return r < 1 ? 1 : (r > 64 ? 64 : r);
 }
 
-// One workgroup per (split unit, group of rows).  Worker w's partial of a
-// unit is in slot 0 if the unit started at or before w's range, else in slot 1.
+// One workgroup per (split unit, group of rows).  Piece k's partial of a
+// unit is in slot 0 if the unit started at or before the piece, else in slot 1.
+// The loads of up to KB parts are issued together before any is used, so
+// each batch of parts costs one memory round trip.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_groups)
 {
+    constexpr int KB = 4;
     __shared__ float s_m[64], s_inv[64];
     const int per = p.ws.hdr[1];
     const int32_t *d = p.ws.splits + (size_t)(blockIdx.x / row_groups) * 8;
@@ -198,20 +203,34 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_group
     const int nr = rows - r0 < RPW ? rows - r0 : RPW;
     const int first = us / per;
     const int last = (ue - 1) / per;
-    auto part_of = [&](int w) -> const float * {
-        return p.ws.partials + (size_t)(2 * w + (w * per >= us ? 0 : 1)) * p.partial_stride;
+    auto part_of = [&](int k) -> const float * {
+        k = k < last ? k : last;
+        return p.ws.partials + (size_t)(2 * k + (k * per >= us ? 0 : 1)) * p.partial_stride;
     };
-    // row statistics: M = max_p m_p, L = sum_p l_p 2^(m_p - M)
+    // row statistics: M = max_p m_p, L = sum_p l_p 2^(m_p - M), by an online
+    // combination over the parts
     if (threadIdx.x < nr) {
         const int r = r0 + threadIdx.x;
-        float M = -INFINITY;
-        for (int w = first; w <= last; ++w)
-            M = fmaxf(M, part_of(w)[R * DV + r]);
-        float L = 0.f;
-        for (int w = first; w <= last; ++w) {
-            const float *pt = part_of(w);
-            const float m = pt[R * DV + r];
-            L += m == -INFINITY ? 0.f : pt[R * DV + R + r] * exp2f(m - M);
+        float M = -INFINITY, L = 0.f;
+        for (int k0 = first; k0 <= last; k0 += KB) {
+            float mk[KB], lk[KB];
+#pragma unroll
+            for (int i = 0; i < KB; ++i) {
+                const float *pt = part_of(k0 + i);
+                mk[i] = pt[R * DV + r];
+                lk[i] = pt[R * DV + R + r];
+            }
+#pragma unroll
+            for (int i = 0; i < KB; ++i) {
+                if (k0 + i > last || mk[i] == -INFINITY)
+                    continue;
+                if (mk[i] > M) {
+                    L = L * exp2f(M - mk[i]) + lk[i];
+                    M = mk[i];
+                } else {
+                    L += lk[i] * exp2f(mk[i] - M);
+                }
+            }
         }
         s_m[threadIdx.x] = M;
         s_inv[threadIdx.x] = L > 0.f ? 1.f / L : 0.f;
@@ -222,24 +241,41 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_group
                 L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
     }
     __syncthreads();
+    // four consecutive outputs per thread and step (DV is a multiple of 4)
     uint16_t *out = (uint16_t *)p.out;
     const int t0 = p.ws.cu_q[b];
-    for (int idx = threadIdx.x; idx < nr * DV; idx += kThreads) {
+    for (int idx = 4 * threadIdx.x; idx < nr * DV; idx += 4 * kThreads) {
         const int rr = idx / DV;
         const int e = idx - rr * DV;
         const int r = r0 + rr;
         const float M = s_m[rr];
-        float acc = 0.f;
-        for (int w = first; w <= last; ++w) {
-            const float *pt = part_of(w);
-            const float m = pt[R * DV + r];
-            if (m != -INFINITY)
-                acc += exp2f(m - M) * pt[r * DV + e];
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = first; k0 <= last; k0 += KB) {
+            float mk[KB];
+            float4 a[KB];
+#pragma unroll
+            for (int i = 0; i < KB; ++i) {
+                const float *pt = part_of(k0 + i);
+                mk[i] = pt[R * DV + r];
+                a[i] = *(const float4 *)(pt + r * DV + e);
+            }
+#pragma unroll
+            for (int i = 0; i < KB; ++i) {
+                const float w = (k0 + i > last || mk[i] == -INFINITY) ? 0.f : exp2f(mk[i] - M);
+                acc[0] += w * a[i].x;
+                acc[1] += w * a[i].y;
+                acc[2] += w * a[i].z;
+                acc[3] += w * a[i].w;
+            }
         }
         const int rg = qt * R + r;
         const int t = t0 + rg / G;
-        if (t < p.num_q_tokens)
-            out[((size_t)t * p.head_num + g * G + rg % G) * DV + e] = to_bits<DT>(acc * s_inv[rr]);
+        if (t < p.num_q_tokens) {
+            const float inv = s_inv[rr];
+            const uint32_t w0 = (uint32_t)to_bits<DT>(acc[0] * inv) | ((uint32_t)to_bits<DT>(acc[1] * inv) << 16);
+            const uint32_t w1 = (uint32_t)to_bits<DT>(acc[2] * inv) | ((uint32_t)to_bits<DT>(acc[3] * inv) << 16);
+            *(uint2 *)(out + ((size_t)t * p.head_num + g * G + rg % G) * DV + e) = uint2{w0, w1};
+        }
     }
 }
 
@@ -255,7 +291,7 @@ hipError_t launch_merge(const Params &p, int dtype, hipStream_t s)
 {
     const int row_groups = (p.rows_per_tile + merge_rows_per_wg(p.head_size_v) - 1) /
                            merge_rows_per_wg(p.head_size_v);
-    const long long grid = (long long)(p.partitions - 1) * row_groups;
+    const long long grid = (long long)(p.pieces - 1) * row_groups;
     if (grid <= 0 || p.no_split)
         return hipSuccess;
     if (grid > 0x7fffffff)

@@ -210,11 +210,12 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S>())) void 
     const int lr = lane & 15;
     const int lg = lane >> 4;
 
-    const int w = xcd_logical_index(blockIdx.x, gridDim.x);
+    int piece = xcd_logical_index(blockIdx.x, gridDim.x);
     Cursor cu;
     int end;
-    if (!wg_range(p, w, cu, end))
+    if (piece >= p.partitions || !wg_range(p, piece, cu, end))
         return;
+    __shared__ int s_piece;
 
     const uint16_t *__restrict__ qg = (const uint16_t *)p.query;
     const char *__restrict__ kg = (const char *)p.key_cache;
@@ -566,7 +567,7 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S>())) void 
         // -------------------------------------------------------- finalise
         if (wave_active) {
             const int slot = first_seg ? 0 : 1;
-            float *part = p.ws.partials + (size_t)(2 * w + slot) * p.partial_stride;
+            float *part = p.ws.partials + (size_t)(2 * piece + slot) * p.partial_stride;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const float L = xor_sum<32>(xor_sum<16>(lsum[mb]));
@@ -607,11 +608,23 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S>())) void 
 
         first_seg = false;
         cu.item += c1 - c0;
-        if (cu.item >= end)
-            break;
-        cursor_next_unit(p, cu);
-        if (cu.b >= p.batch)
-            break;
+        bool more = cu.item < end;
+        if (more) {
+            cursor_next_unit(p, cu);
+            more = cu.b < p.batch;
+        }
+        if (!more) {
+            // this piece is done: take the next one, if any
+            if (p.no_split || p.pieces <= p.partitions)
+                break;
+            if (threadIdx.x == 0)
+                s_piece = grab_piece(p);
+            __syncthreads();
+            piece = s_piece;
+            if (!wg_range(p, piece, cu, end))
+                break;
+            first_seg = true;
+        }
     }
     if (err)
         set_error(p.ws.err, err);

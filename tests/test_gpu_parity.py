@@ -49,6 +49,8 @@ def test_decode_valu_parity(case):
     log(f"decode {case}")
     p = synth.custom(lens, H, Hkv, D, D, bs, dt, seed=sum(lens) % 1000)
     check_full(p, what=f"decode {case}")
+    if H // Hkv <= 8:   # the VALU kernel also for 5..8 rows (default there: MFMA)
+        check_full(p, flags=F.PA_FLAG_FORCE_VALU, what=f"decode valu {case}")
 
 
 @pytest.mark.parametrize("case", DECODE_CASES[:3], ids=["G1", "G4", "G8"])
@@ -90,6 +92,26 @@ def test_scale_sign_and_degenerate_values(scale):
     check_full(p, what=f"mfma scale {scale}")
     p = synth.custom([300, 45, 1000], 8, 2, 128, 128, 64, "bf16", scale=scale, seed=17)
     check_full(p, what=f"valu scale {scale}")
+
+
+@pytest.mark.parametrize("flags", [0, F.PA_FLAG_FORCE_MFMA], ids=["valu", "mfma"])
+def test_split_units_merged_across_calls(flags):
+    # Many small pieces: every unit is split over several parts, written by
+    # workgroups that may sit on different XCDs and merged by the last one.
+    # One handle alternates between two problems of the same shape, so a
+    # merge that read a stale part of the previous call would show.
+    log(f"split merge {flags}")
+    pa = synth.custom([2000, 1500, 3000, 700], 8, 2, 128, 128, 64, "bf16", seed=40)
+    pb = synth.custom([2000, 1500, 3000, 700], 8, 2, 128, 128, 64, "bf16", seed=41)
+    refs = [oracle_full(pa), oracle_full(pb)]
+    gs = [to_device(pa), to_device(pb)]
+    att = binding.for_problem(gs[0], flags=flags, num_partitions=97)
+    for rep in range(3):
+        for k in (0, 1):
+            o, l, _ = run_hip(gs[k], att=att)
+            assert_close(o, refs[k][0], "bf16", f"rep {rep} problem {k}")
+            assert_lse_close(l, refs[k][1], f"rep {rep} problem {k}")
+    assert att.device_error() == 0
 
 
 def test_causal_small_rows_valu():
