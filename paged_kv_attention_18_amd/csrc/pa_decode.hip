@@ -1,9 +1,10 @@
 // pa_decode.hip -- split-KV paged-attention decode on the vector ALUs (gfx950).
 //
-// For units of at most 8 rows (rows = query tokens x query heads of one GQA
-// group), where the contraction is too thin for the matrix cores.  (Units of
-// 9 to 15 rows would need more than 16 x rows fp32 accumulators per lane in
-// this layout; they take the MFMA kernel with one padded 16-row block.)
+// For units of at most 4 rows (rows = query tokens x query heads of one GQA
+// group) by default, where the contraction is too thin for the matrix cores;
+// built for up to 8.  (From 5 rows on the MFMA kernel with one padded 16-row
+// block streams faster: this kernel keeps its chunks in registers, and the
+// accumulators of more rows leave room for fewer bytes in flight.)
 //
 // Every wave is an independent worker: the planner hands it a contiguous
 // range of (sequence, KV head, chunk) items and it streams them with its own
@@ -32,8 +33,8 @@
 //
 // At the end of a unit's range the wave sums its lanes' accumulators
 // (transposing reduction over the token groups) and writes either the
-// normalised output (whole unit) or an fp32 partial (acc, m, l).  The last
-// worker to finish a split unit merges its partials (log-sum-exp) in place.
+// normalised output (whole unit) or an fp32 partial (acc, m, l) for the
+// merge kernel.
 #include "pa_internal.h"
 
 namespace pa {

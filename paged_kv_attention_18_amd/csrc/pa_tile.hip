@@ -1,10 +1,10 @@
 // pa_tile.hip -- paged attention on the matrix cores (gfx950 MFMA).
 //
-// For units with 16 or more rows: parallel decoding / splitfuse chunks with
-// the prefix-aligned causal mask (Ascend ATB PagedAttentionOperation,
-// Constraints, mask type 5 list) and decode with a wide GQA group (e.g. 64
-// query heads on one KV head with 576/512 key/value head sizes, which the
-// same Constraints allow at block_size <= 128).
+// For units of 5 rows or more: parallel decoding / splitfuse chunks with the
+// prefix-aligned causal mask (Ascend ATB PagedAttentionOperation,
+// Constraints, mask type 5 list), decode with GQA groups of 8 or more, and a
+// wide GQA group on one KV head with 576/512 key/value head sizes (which the
+// same Constraints allow at block_size <= 128).  Rows are padded to 16.
 //
 // A workgroup of NW waves owns a tile of rows of one (sequence, KV head).  The
 // waves form NW / CS row groups of 16 * MB rows; the CS waves of a row group
@@ -12,13 +12,14 @@
 // accumulator per wave for Dv = 512).  Per KT-token chunk:
 //
 //   stage  K and V rows are copied from the paged cache straight into LDS
-//          with global_load_lds_dwordx4 (no registers, no ALU work), one chunk
-//          ahead, into two LDS buffers.  Each lane picks the global 16-byte
-//          piece that lands at its LDS slot, which realises an XOR swizzle of
-//          the pieces within a row (K: piece ^ (row & 7); V: piece ^ 2(row & 3)),
-//          so the operand reads below are free of bank conflicts.  Tokens that
-//          are not visible, or whose block id is out of range, are loaded from
-//          a zero page: masked V rows are zeros, never multiplied away.
+//          with global_load_lds_dwordx4 (no registers, no ALU work) into a
+//          ring of S stages, S - 1 chunks ahead of the one computed.  Each
+//          lane picks the global 16-byte piece that lands at its LDS slot,
+//          which realises an XOR swizzle of the pieces within a row (K:
+//          piece ^ (row & 7); V: piece ^ 2(row & 3)), so the operand reads
+//          below are free of bank conflicts.  A block id out of range reads
+//          a zero page (and is flagged); rows past the visible range are
+//          masked (P = 0, and their V operand halves are zeroed).
 //   S^T    = K . Q^T with v_mfma_f32_16x16x32_{f16,bf16}: K is the A operand
 //          (ds_read_b128), Q^T the B operand, held in registers for the whole
 //          unit.  The accumulator gives every lane one query row and 4 + 4
@@ -27,16 +28,17 @@
 //   mask   select -inf where j >= kv or (causal) j > prefix + i; chunks that
 //          lie wholly inside every row's visible range skip the test, and
 //          chunks wholly outside are never planned.
-//   PV     O += P . V with the same instruction; the V operand is read from
-//          the row-major tile with ds_read_b64_tr_b16 (a transposing LDS read:
-//          within each 16-lane group, lane i receives element i % 4 of the
-//          8-byte chunks addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and
-//          12 + i / 4), two reads per operand.
+//   PV     O += P . V with the same instruction (16x16x16 for 16-token
+//          chunks); the V operand is read from the row-major tile with
+//          ds_read_b64_tr_b16 (a transposing LDS read: within each 16-lane
+//          group, lane i receives element i % 4 of the 8-byte chunks
+//          addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4).
 //
-// One barrier per chunk; the LDS loads of the next chunk are in flight while
-// the current one is computed.  Row statistics (running max and sum, log2
-// domain) stay per wave; at the end of a unit's range O is normalised into
-// the output, or written as an fp32 partial for the merge kernel.
+// Every wave issues the same number of LDS loads per chunk, so the wait for
+// chunk c is an exact vmcnt count, followed by one barrier.  Row statistics
+// (running max and sum, log2 domain) stay per wave; at the end of a unit's
+// range O is normalised into the output, or written as an fp32 partial for
+// the merge kernel.
 #include "pa_internal.h"
 
 #include <type_traits>
