@@ -18,8 +18,9 @@ constexpr int kMaxTimedPasses = 1024;
 // Pieces of the item range per worker in balanced mode.  With more pieces
 // than workers, workers that finish early take the remaining pieces, which
 // evens out end times; it pays where a chunk is long (many rows on the
-// matrix cores) and costs a pipeline start per piece, which thin
-// (memory-bound) units cannot hide, so they keep one piece per worker.
+// matrix cores).  The decode kernels keep one piece per worker: taking a
+// piece means waiting for an atomic's return, and that wait drains their
+// load pipelines (one in-order vector memory counter per wave).
 constexpr int kMaxPiecesPerWorker = 2;
 
 struct Variant {
@@ -72,15 +73,12 @@ struct pa_handle {
         const int G = cfg.head_num / cfg.kv_head_num;
         const int rows = max_q * G;
         const bool dec_ok = pa::decode_supported(cfg.head_size_k, cfg.head_size_v);
-        // VALU for the thinnest units.  From 5 rows on the matrix-core
-        // kernel with one padded 16-row block streams faster: at 8 rows
-        // (Dk = Dv = 128) the VALU kernel holds half the KV bytes in flight
-        // per wave that it holds at 4 rows.
-        bool valu = dec_ok && rows <= 4;
-        if (cfg.flags & PA_FLAG_FORCE_MFMA)
-            valu = false;
-        if ((cfg.flags & PA_FLAG_FORCE_VALU) && dec_ok && rows <= 8)
-            valu = true;
+        // The matrix-core kernels by default, also for thin decode units
+        // (one padded 16-row block): the streaming kernel keeps a ring of
+        // KV chunks in flight through LDS across units, which the VALU
+        // kernel (chunks held in registers) cannot match in bytes in flight.
+        // The VALU kernel stays available for up to 8 rows.
+        const bool valu = (cfg.flags & PA_FLAG_FORCE_VALU) && dec_ok && rows <= 8;
         if (valu) {
             v.path = 0;
             v.rows_pad = next_pow2(rows < 1 ? 1 : rows);

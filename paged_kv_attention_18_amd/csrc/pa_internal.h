@@ -309,6 +309,20 @@ __device__ __forceinline__ int xcd_logical_index(int bid, int nwg)
 }
 
 // The cursor a workgroup walks its item range with.
+// Loads of plan data and block tables at wave-uniform addresses, as scalar
+// loads: the data is read-only for the whole launch (address space 4), and
+// scalar loads do not share the vector memory counter with KV loads in
+// flight, so waiting for them never waits for those.
+typedef __attribute__((address_space(4))) const int32_t c_i32;
+
+__device__ __forceinline__ int sload(const int32_t *ptr, size_t i)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)(ptr + i);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return *(const c_i32 *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 struct Cursor {
     int b, g, qt, c;     // current unit and chunk
     int nch;             // chunks of the current unit
@@ -324,10 +338,10 @@ __device__ __forceinline__ int seq_tiles(const Params &p, int qlen)
 // Position the cursor at item `item`, which lies in sequence b.
 __device__ __forceinline__ void cursor_seek(const Params &p, Cursor &cu, int b, int item)
 {
-    const int kv = p.ws.kvlen[b];
-    const int ql = p.ws.qlen[b];
-    const int ipg = p.ws.ipg[b];
-    int local = item - p.ws.wsb[b];
+    const int kv = sload(p.ws.kvlen, b);
+    const int ql = sload(p.ws.qlen, b);
+    const int ipg = sload(p.ws.ipg, b);
+    int local = item - sload(p.ws.wsb, b);
     cu.b = b;
     cu.g = local / ipg;
     local -= cu.g * ipg;
@@ -356,13 +370,13 @@ __device__ __forceinline__ void cursor_next_unit(const Params &p, Cursor &cu)
             cu.g = 0;
             do {
                 ++cu.b;
-            } while (cu.b < p.batch && p.ws.ipg[cu.b] == 0);
+            } while (cu.b < p.batch && sload(p.ws.ipg, cu.b) == 0);
             if (cu.b >= p.batch)
                 return;
-            cu.ntile = seq_tiles(p, p.ws.qlen[cu.b]);
+            cu.ntile = seq_tiles(p, sload(p.ws.qlen, cu.b));
         }
     }
-    cu.nch = unit_chunks(p.ws.kvlen[cu.b], p.ws.qlen[cu.b], p.group, p.rows_per_tile, p.chunk,
+    cu.nch = unit_chunks(sload(p.ws.kvlen, cu.b), sload(p.ws.qlen, cu.b), p.group, p.rows_per_tile, p.chunk,
                          cu.qt, p.causal);
 }
 
@@ -370,14 +384,14 @@ __device__ __forceinline__ void cursor_next_unit(const Params &p, Cursor &cu)
 // (no-split mode); returns false if it has none.
 __device__ __forceinline__ bool wg_range(const Params &p, int w, Cursor &cu, int &end)
 {
-    const int W = p.ws.hdr[0];
-    const int per = p.ws.hdr[1];
+    const int W = sload(p.ws.hdr, 0);
+    const int per = sload(p.ws.hdr, 1);
     if (per > 0) {
         const int s = w * per;
         if (w >= p.pieces || s >= W)
             return false;
         end = s + per < W ? s + per : W;
-        cursor_seek(p, cu, p.ws.wg_b[w], s);
+        cursor_seek(p, cu, sload(p.ws.wg_b, w), s);
         return true;
     }
     // no-split: workgroup w is unit (b, g, qt) with qt < max_tiles
@@ -387,11 +401,11 @@ __device__ __forceinline__ bool wg_range(const Params &p, int w, Cursor &cu, int
         return false;
     const int g = (w % per_b) / p.max_tiles;
     const int qt = w % p.max_tiles;
-    const int ql = p.ws.qlen[b];
+    const int ql = sload(p.ws.qlen, b);
     if (qt >= seq_tiles(p, ql))
         return false;
-    const int kv = p.ws.kvlen[b];
-    int start = p.ws.wsb[b] + g * p.ws.ipg[b];
+    const int kv = sload(p.ws.kvlen, b);
+    int start = sload(p.ws.wsb, b) + g * sload(p.ws.ipg, b);
     for (int t = 0; t < qt; ++t)
         start += unit_chunks(kv, ql, p.group, p.rows_per_tile, p.chunk, t, p.causal);
     cu.b = b;

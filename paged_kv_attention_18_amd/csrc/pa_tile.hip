@@ -92,16 +92,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-// Read-only for the whole launch: loads through this address space with a
-// uniform address become scalar loads (s_load), which do not share the vector
-// memory counter with the LDS loads in flight.
-typedef __attribute__((address_space(4))) const int32_t c_i32;
-
-__device__ __forceinline__ int sload(const int32_t *ptr, size_t i)
-{
-    return ((const c_i32 *)ptr)[i];
-}
-
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes
 // land at dst + 16 l (global_load_lds_dwordx4, LDS base in M0).  Issued from
 // inline assembly so that the compiler does not add waits of its own for
@@ -632,18 +622,392 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S>())) void 
         set_error(p.ws.err, err);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming kernel for units of at most 16 rows (decode).  One wave is a
+// worker with its own S-stage LDS ring, and the ring does not drain between
+// units or pieces: the wave issues chunk k + S - 1 of its stream (whatever
+// unit or piece it belongs to) while it computes chunk k.  The first chunk
+// of every segment also carries the segment's 16 x Dk Q tile into its stage,
+// and each stage carries the chunk's segment parameters in a small LDS
+// record, so the compute side never waits for a lookup.  A worker keeps
+// one piece: taking further pieces from a shared counter needs the atomic's
+// return, and waiting for it is a wait on every load of the in-order vector
+// memory counter, which drains the ring.
+template <int DT, int DK, int DV, int KT, int S>
+__global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
+{
+    constexpr int RBK = 2 * DK, RBV = 2 * DV;     // LDS row bytes
+    constexpr int KS = DK / 32;
+    constexpr int NTT = KT / 16;
+    constexpr int ND = DV / 16;
+    constexpr int IPGK = RBK / 64;                // 1 KiB loads per 16 rows of K (and of the Q tile)
+    constexpr int IPGV = RBV / 64;
+    constexpr int LW = NTT * (IPGK + IPGV);       // loads per chunk (plus IPGK for a Q tile)
+    constexpr int STK = KT * RBK, STV = KT * RBV, STQ = 16 * RBK;
+    constexpr int MW = 12;                        // ints per stage record
+    static_assert(DK <= 256 && DV <= 256 && DK % 32 == 0 && DV % 64 == 0 && (KT == 16 || KT == 32), "shape");
+    static_assert(S >= 2 && S <= 4 && LW * (S - 2) + IPGK < 64, "ring");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t sK[S * STK];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV[S * STV];
+    __shared__ __attribute__((aligned(1024))) uint8_t sQ[S * STQ];
+    __shared__ int s_meta[S * MW];
+
+    const int lane = threadIdx.x & 63;
+    const int lr = lane & 15;
+    const int lg = lane >> 4;
+    const int worker = xcd_logical_index(blockIdx.x, gridDim.x);
+
+    const uint16_t *__restrict__ qg = (const uint16_t *)p.query;
+    const char *__restrict__ kg = (const char *)p.key_cache;
+    const char *__restrict__ vg = (const char *)p.value_cache;
+    const char *__restrict__ zg = (const char *)p.ws.zeros;
+    uint16_t *__restrict__ og = (uint16_t *)p.out;
+    const int G = p.group;
+    const int H = p.head_num;
+    const int bs = p.block_size;
+    const int bsh = p.bs_shift;
+    const uint32_t rsk = (uint32_t)p.kv_head_num * RBK;
+    const uint32_t rsv = (uint32_t)p.kv_head_num * RBV;
+    const uint32_t nb32 = p.num_blocks < 0x7fffffff ? (uint32_t)p.num_blocks : 0x7fffffffu;
+    const bool neg_scale = p.scale_log2 < 0.f;
+    const float sc = fmaxf(fabsf(p.scale_log2), 1e-30f);   // scale 0: every visible token weighs 1
+    const float grow_raw = 8.f / sc;
+    uint32_t err = 0;
+
+    // per-lane offsets of the loads (inside a 16-token group / the Q tile)
+    uint32_t voK[IPGK], voV[IPGV];
+    int qrow[IPGK], qlp[IPGK];
+#pragma unroll
+    for (int m = 0; m < IPGK; ++m) {
+        const int x = m * 1024 + 16 * lane;
+        const int row = x / RBK;
+        const int lp = ((x % RBK) >> 4) ^ (row & 7);
+        voK[m] = row * rsk + 16 * lp;
+        qrow[m] = row;
+        qlp[m] = lp;
+    }
+#pragma unroll
+    for (int m = 0; m < IPGV; ++m) {
+        const int x = m * 1024 + 16 * lane;
+        const int row = x / RBV;
+        voV[m] = row * rsv + 16 * (((x % RBV) >> 4) ^ (2 * (row & 3)));
+    }
+    // LDS read offsets (K and Q: row lr, piece 4 ks + lg; V: transposing read)
+    const int kq = 16 * (lg ^ (lr & 3));
+    const int kb2 = 64 * ((lr >> 2) & 1);
+    const int koE = lr * RBK + kq + kb2, koO = lr * RBK + kq - kb2;
+    int vo[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        vo[m] = (4 * lg + (lr >> 2)) * RBV + 32 * (m ^ (lr >> 2)) + 16 * ((lr & 3) >> 1) + 8 * (lr & 1);
+
+    // ------------------------------------------------------------ issue side
+    int ipiece = worker;
+    Cursor ic;
+    int iend;
+    if (ipiece >= p.partitions || !wg_range(p, ipiece, ic, iend))
+        return;
+    int idone = 0, ifirst = 1;
+    int ic1 = 0, icb = 0, invis = 0, inblk = 1, ikv = 0, iql = 0, it0 = 0, irows = 0;
+    const int32_t *ibt = p.block_tables;
+    const char *ikg = kg, *ivg = vg;
+    auto iseg = [&]() __attribute__((always_inline)) {
+        icb = ic.c;
+        ic1 = ic.nch < ic.c + (iend - ic.item) ? ic.nch : ic.c + (iend - ic.item);
+        ikv = sload(p.ws.kvlen, ic.b);
+        iql = sload(p.ws.qlen, ic.b);
+        it0 = sload(p.ws.cu_q, ic.b);
+        irows = iql * G - ic.qt * 16;
+        irows = irows < 16 ? irows : 16;
+        invis = tile_nvis(ikv, iql, G, ic.qt * 16 + irows - 1, p.causal);
+        inblk = invis > 0 ? div_bs(invis - 1, bs, bsh) + 1 : 1;
+        ibt = p.block_tables + (size_t)ic.b * p.max_blocks;
+        ikg = kg + (size_t)ic.g * RBK;
+        ivg = vg + (size_t)ic.g * RBV;
+    };
+    iseg();
+    int ibid[NTT];
+    auto ifetch = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < NTT; ++q) {
+            const int blk = div_bs(ic.c * KT + 16 * q, bs, bsh);
+            ibid[q] = sload(ibt, blk < inblk ? blk : inblk - 1);
+        }
+    };
+    ifetch();
+    int n_issued = 0;
+    // Issue the next chunk of the stream into stage st (nothing once done).
+    auto issue = [&](int st) __attribute__((always_inline)) {
+        if (idone)
+            return;
+        const bool seg_begin = ic.c == icb;
+        if (seg_begin) {
+            // Q tile of the segment (rows past the unit read the zero page)
+#pragma unroll
+            for (int m = 0; m < IPGK; ++m) {
+                const int rg = ic.qt * 16 + qrow[m];
+                const int t = it0 + rg / G;
+                const bool ok = qrow[m] < irows && t < p.num_q_tokens;
+                const char *src = ok ? (const char *)(qg + ((size_t)t * H + ic.g * G + rg % G) * DK + 8 * qlp[m])
+                                     : zg + 16 * qlp[m];
+                lds_load16(src, (lds_u8 *)sQ + st * STQ + m * 1024);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NTT; ++q) {
+            const int j0 = ic.c * KT + 16 * q;
+            const bool vis = j0 < invis;
+            const bool inb = (unsigned)ibid[q] < nb32;
+            err |= (vis && !inb) ? (uint32_t)PA_DEVERR_BLOCK_ID : 0u;
+            const size_t trow = (size_t)ibid[q] * bs + mod_bs(j0, bs, bsh);
+            const char *kbase = (vis && inb) ? ikg + trow * rsk : zg;
+            const char *vbase = (vis && inb) ? ivg + trow * rsv : zg;
+#pragma unroll
+            for (int m = 0; m < IPGK; ++m)
+                lds_load16(kbase + voK[m], (lds_u8 *)sK + st * STK + (q * IPGK + m) * 1024);
+#pragma unroll
+            for (int m = 0; m < IPGV; ++m)
+                lds_load16(vbase + voV[m], (lds_u8 *)sV + st * STV + (q * IPGV + m) * 1024);
+        }
+        const bool seg_end = ic.c + 1 == ic1;
+        if (lane == 0) {
+            int *md = s_meta + st * MW;
+            md[0] = ic.b;
+            md[1] = ic.g;
+            md[2] = ic.qt;
+            md[3] = ic.c;
+            md[4] = (seg_begin ? 1 : 0) | (seg_end ? 2 : 0) | ((icb == 0 && ic1 == ic.nch) ? 4 : 0) | (ifirst ? 8 : 0);
+            md[5] = ipiece;
+            md[6] = invis;
+            md[7] = ikv;
+            md[8] = iql;
+            md[9] = it0;
+            md[10] = irows;
+        }
+        ++n_issued;
+        // advance the issue position by one chunk
+        ++ic.c;
+        ++ic.item;
+        if (ic.c == ic1) {
+            ifirst = 0;
+            bool more = ic.item < iend;
+            if (more) {
+                cursor_next_unit(p, ic);
+                more = ic.b < p.batch;
+            }
+            idone = more ? 0 : 1;
+            if (!idone)
+                iseg();
+        }
+        if (!idone)
+            ifetch();
+    };
+
+    // ---------------------------------------------------------- compute side
+    u32x4 qb[KS];
+    f32x4 oacc[ND];
+    float m_run = -INFINITY, lsum = 0.f;
+    int lim = 0, min_lim = 0, nvis = 0, rows = 0, t0 = 0, kv = 0, ql = 0;
+
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k)
+        issue(k);
+
+    for (int k = 0; k < n_issued; ++k) {
+        const int st = k % S;
+        wait_ahead<LW, S - 2>(n_issued - 1 - k);   // chunk k (and any earlier Q tile) is in LDS
+        int md[11];
+#pragma unroll
+        for (int i = 0; i < 11; ++i)
+            md[i] = __builtin_amdgcn_readfirstlane(s_meta[st * MW + i]);
+        issue((k + S - 1) % S);
+        const int b = md[0], g = md[1], qt = md[2], c = md[3], fl = md[4];
+        const lds_u8 *kb = (const lds_u8 *)sK + st * STK;
+        const lds_u8 *vb = (const lds_u8 *)sV + st * STV;
+        if (fl & 1) {
+            // first chunk of a segment: its Q tile and row limits
+            nvis = md[6];
+            kv = md[7];
+            ql = md[8];
+            t0 = md[9];
+            rows = md[10];
+            const lds_u8 *qs = (const lds_u8 *)sQ + st * STQ;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                qb[ks] = *(const lds_u32x4 *)(qs + ((ks & 1) ? koO : koE) + 64 * ks);
+                if (neg_scale)   // exact: softmax(c s) = softmax(|c| (-s)) with -s = (-q) . k
+                    qb[ks] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+            }
+            const int prefix = kv - ql > 0 ? kv - ql : 0;
+            const int rg = qt * 16 + lr;
+            lim = p.causal ? (prefix + rg / G + 1 < kv ? prefix + rg / G + 1 : kv) : kv;
+            min_lim = p.causal ? tile_nvis(kv, ql, G, qt * 16, 1) : kv;
+#pragma unroll
+            for (int nd = 0; nd < ND; ++nd)
+                oacc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m_run = -INFINITY;
+            lsum = 0.f;
+        }
+
+        // S^T = K . Q^T
+        const int jb = c * KT;
+        f32x4 sacc[NTT];
+#pragma unroll
+        for (int n = 0; n < NTT; ++n)
+            sacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int n = 0; n < NTT; ++n) {
+                const u32x4 a = *(const lds_u32x4 *)(kb + ((ks & 1) ? koO : koE) + 16 * n * RBK + 64 * ks);
+                sacc[n] = Mfma<DT>::run(a, qb[ks], sacc[n]);
+            }
+        }
+        // mask, online softmax (raw scores, lazy reference)
+        float mx = -INFINITY;
+        const bool need_mask = jb + KT > min_lim;
+#pragma unroll
+        for (int n = 0; n < NTT; ++n) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (need_mask) {
+                    const int j = jb + 16 * n + 4 * lg + r;
+                    sacc[n][r] = j < lim ? sacc[n][r] : -INFINITY;
+                }
+                mx = fmaxf(mx, sacc[n][r]);
+            }
+        }
+        mx = xor_max<16>(mx);
+        mx = xor_max<32>(mx);
+        if (__any(mx > m_run + grow_raw)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * sc);
+            lsum *= alpha;
+            m_run = m_new;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * lg + r);
+#pragma unroll
+                for (int nd = 0; nd < ND; ++nd)
+                    oacc[nd][r] *= ar;
+            }
+        }
+        const float mref = m_run == -INFINITY ? 0.f : m_run * sc;
+        float ps = 0.f;
+#pragma unroll
+        for (int n = 0; n < NTT; ++n) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[n][r], sc, -mref));
+                sacc[n][r] = pv;
+                ps += pv;
+            }
+        }
+        lsum += ps;
+        // PV (V halves of tokens at or past nvis zeroed)
+        const bool tail = jb + KT > nvis;
+        if constexpr (KT == 16) {
+            const uint2 pa = uint2{pack2<DT>(sacc[0][0], sacc[0][1]), pack2<DT>(sacc[0][2], sacc[0][3])};
+            uint2 vm = {~0u, ~0u};
+            if (tail) {
+                const int tb = jb + 4 * lg;
+                vm.x = (tb < nvis ? 0xffffu : 0u) | (tb + 1 < nvis ? 0xffff0000u : 0u);
+                vm.y = (tb + 2 < nvis ? 0xffffu : 0u) | (tb + 3 < nvis ? 0xffff0000u : 0u);
+            }
+#pragma unroll
+            for (int nd = 0; nd < ND; ++nd) {
+                const v4i16 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + 32 * (nd & ~3)));
+                uint2 bv = __builtin_bit_cast(uint2, b0);
+                if (tail) {
+                    bv.x &= vm.x;
+                    bv.y &= vm.y;
+                }
+                oacc[nd] = Mfma16<DT>::run(pa, bv, oacc[nd]);
+            }
+        } else {
+            const u32x4 pa = u32x4{pack2<DT>(sacc[0][0], sacc[0][1]), pack2<DT>(sacc[0][2], sacc[0][3]),
+                                   pack2<DT>(sacc[1][0], sacc[1][1]), pack2<DT>(sacc[1][2], sacc[1][3])};
+            u32x4 vm = {~0u, ~0u, ~0u, ~0u};
+            if (tail) {
+                const int tb = jb + 4 * lg;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        vm[2 * h2 + e] = (tb + 16 * h2 + 2 * e < nvis ? 0xffffu : 0u) |
+                                         (tb + 16 * h2 + 2 * e + 1 < nvis ? 0xffff0000u : 0u);
+            }
+#pragma unroll
+            for (int nd = 0; nd < ND; ++nd) {
+                const int off = 32 * (nd & ~3);
+                const v4i16 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off));
+                const v4i16 b1 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off + 16 * RBV));
+                const uint2 lo = __builtin_bit_cast(uint2, b0), hi = __builtin_bit_cast(uint2, b1);
+                u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
+                if (tail)
+                    bv &= vm;
+                oacc[nd] = Mfma<DT>::run(pa, bv, oacc[nd]);
+            }
+        }
+
+        if (fl & 2) {
+            // last chunk of the segment: output or partial
+            const bool whole = fl & 4;
+            const int piece = md[5];
+            float *part = p.ws.partials + (size_t)(2 * piece + ((fl & 8) ? 0 : 1)) * p.partial_stride;
+            const float L = xor_sum<32>(xor_sum<16>(lsum));
+            const float Ms = m_run * sc;   // log2 domain
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float Lr = __shfl(L, 4 * lg + r);
+                const float Mr = __shfl(Ms, 4 * lg + r);
+                const int row_t = 4 * lg + r;
+                if (row_t >= rows)
+                    continue;
+                const int rg = qt * 16 + row_t;
+                const int t = t0 + rg / G;
+                const int h = g * G + rg % G;
+                if (whole) {
+                    if (t >= p.num_q_tokens)
+                        continue;
+                    const float inv = Lr > 0.f ? 1.f / Lr : 0.f;
+                    uint16_t *dst = og + ((size_t)t * H + h) * DV;
+#pragma unroll
+                    for (int nd = 0; nd < ND; ++nd)
+                        dst[16 * nd + lr] = to_bits<DT>(oacc[nd][r] * inv);
+                    if (lr == 0 && p.lse)
+                        p.lse[(size_t)t * H + h] = Lr > 0.f ? (Mr + log2f(Lr)) * 0.69314718055994531f : -INFINITY;
+                } else {
+#pragma unroll
+                    for (int nd = 0; nd < ND; ++nd)
+                        part[row_t * DV + 16 * nd + lr] = oacc[nd][r];
+                    if (lr == 0) {
+                        part[16 * DV + row_t] = Mr;
+                        part[16 * DV + 16 + row_t] = Lr;
+                    }
+                }
+            }
+        }
+    }
+    if (err)
+        set_error(p.ws.err, err);
+}
+
 // Variants per (Dk, Dv).  0: units of at most 16 rows (decode), memory-bound:
 // one wave per workgroup (no waiting on other waves), short chunks, three
 // stages.  1: up to 64 rows.  2: more rows, two 16-row
 // blocks per wave.  Dk = 576 has variant 0 only (64 rows per tile).
 struct TileShape {
-    int mb, kt, nw, cs, s;
+    int mb, kt, nw, cs, s;   // nw: waves that own rows
+    int threads;             // workgroup size
 };
 
 template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S>
 const void *pick(TileShape *t)
 {
-    *t = TileShape{MB, KT, NW, CS, S};
+    *t = TileShape{MB, KT, NW, CS, S, 64 * NW};
     return (const void *)&tile_kernel<DT, DK, DV, MB, KT, NW, CS, S>;
 }
 
@@ -654,11 +1018,9 @@ const void *kernel_for(int variant, TileShape *t)
         return variant == 0 ? pick<DT, DK, DV, 1, 16, 8, 2, 4>(t) : nullptr;
     } else {
         constexpr int KT = DK <= 128 ? 64 : 32;
-        if (variant == 0) {   // one wave per workgroup, several workgroups per CU
-            if constexpr (DK <= 128)
-                return pick<DT, DK, DV, 1, 32, 1, 1, 3>(t);
-            else
-                return pick<DT, DK, DV, 1, 16, 1, 1, 3>(t);
+        if (variant == 0) {   // one wave per workgroup, streaming across units
+            *t = TileShape{1, 16, 1, 1, 4, 64};
+            return (const void *)&stream_kernel<DT, DK, DV, 16, 4>;
         }
         if (variant == 1)
             return pick<DT, DK, DV, 1, KT, 4, 1, 2>(t);
@@ -712,7 +1074,7 @@ int tile_workers_per_cu(int dtype, int dk, int dv, int variant)
     TileShape t;
     const void *k = tile_kernel_ptr(dtype, dk, dv, variant, &t);
     int n = 0;
-    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * t.nw, 0) != hipSuccess || n < 1)
+    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, t.threads, 0) != hipSuccess || n < 1)
         return 1;
     return n;
 }
@@ -724,7 +1086,7 @@ hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s)
     if (!k)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&p};
-    return hipLaunchKernel(k, dim3(p.partitions), dim3(64 * t.nw), args, 0, s);
+    return hipLaunchKernel(k, dim3(p.partitions), dim3(t.threads), args, 0, s);
 }
 
 }  // namespace pa

@@ -44,12 +44,12 @@ DECODE_CASES = [
 
 
 @pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"G{c[1]//c[2]}_D{c[3]}_bs{c[4]}_{c[5]}")
-def test_decode_valu_parity(case):
+def test_decode_parity(case):
     lens, H, Hkv, D, bs, dt = case
     log(f"decode {case}")
     p = synth.custom(lens, H, Hkv, D, D, bs, dt, seed=sum(lens) % 1000)
     check_full(p, what=f"decode {case}")
-    if H // Hkv <= 8:   # the VALU kernel also for 5..8 rows (default there: MFMA)
+    if H // Hkv <= 8:   # the VALU kernel (built for up to 8 rows)
         check_full(p, flags=F.PA_FLAG_FORCE_VALU, what=f"decode valu {case}")
 
 
@@ -91,10 +91,11 @@ def test_scale_sign_and_degenerate_values(scale):
     p = synth.custom([300, 45], 8, 2, 128, 128, 64, "f16", "causal", q_seq_lens=[40, 45], scale=scale, seed=16)
     check_full(p, what=f"mfma scale {scale}")
     p = synth.custom([300, 45, 1000], 8, 2, 128, 128, 64, "bf16", scale=scale, seed=17)
-    check_full(p, what=f"valu scale {scale}")
+    check_full(p, what=f"decode scale {scale}")
+    check_full(p, flags=F.PA_FLAG_FORCE_VALU, what=f"valu scale {scale}")
 
 
-@pytest.mark.parametrize("flags", [0, F.PA_FLAG_FORCE_MFMA], ids=["valu", "mfma"])
+@pytest.mark.parametrize("flags", [F.PA_FLAG_FORCE_VALU, 0], ids=["valu", "mfma"])
 def test_split_units_merged_across_calls(flags):
     # Many small pieces: every unit is split over several parts, written by
     # workgroups that may sit on different XCDs and merged by the last one.
@@ -114,12 +115,13 @@ def test_split_units_merged_across_calls(flags):
     assert att.device_error() == 0
 
 
-def test_causal_small_rows_valu():
-    # qlen * G < 16 in causal mode takes the VALU kernel
-    log("causal valu")
+def test_causal_small_rows():
+    # qlen * G <= 16 in causal mode: one 16-row tile per unit (streaming kernel)
+    log("causal small rows")
     p = synth.custom([50, 9, 200], 8, 4, 128, 128, 16, "bf16", "causal", q_seq_lens=[7, 3, 5], seed=12)
-    check_full(p, what="causal valu")
-    check_full(p, flags=F.PA_FLAG_FORCE_MFMA, what="causal forced mfma")
+    check_full(p, what="causal small rows")
+    p = synth.custom([50, 9, 200], 8, 4, 128, 128, 16, "bf16", "causal", q_seq_lens=[4, 3, 1], seed=12)
+    check_full(p, flags=F.PA_FLAG_FORCE_VALU, what="causal valu")
 
 
 def test_no_mask_multi_token():
@@ -196,6 +198,8 @@ def test_poison_tails_and_slack():
         H, Hkv = (16, 1) if D == 576 else (8, 2)
         p = synth.custom([70, 200], H, Hkv, D, Dv, 64, dt, mask, q_seq_lens=ql, seed=23, max_blocks=8)
         clean, _, _ = run_hip(to_device(p))
+        valu = D != 576 and mask == "none"
+        clean_valu = run_hip(to_device(p), flags=F.PA_FLAG_FORCE_VALU)[0] if valu else None
         bs = 64
         used = set()
         for b in range(p.batch):
@@ -213,6 +217,8 @@ def test_poison_tails_and_slack():
                 p.value_cache[blk] = float("nan")
         dirty, _, att = run_hip(to_device(p))
         assert np.array_equal(clean, dirty), (D, mask)
+        if valu:
+            assert np.array_equal(clean_valu, run_hip(to_device(p), flags=F.PA_FLAG_FORCE_VALU)[0]), (D, "valu")
 
 
 def test_masked_positions_have_zero_weight():
@@ -236,6 +242,7 @@ def test_block_permutation_bit_exact():
         lens, H, Hkv, D, bs, dt = case
         p = synth.custom(lens, H, Hkv, D, D, bs, dt, seed=25)
         o1, l1, _ = run_hip(to_device(p))
+        v1, w1, _ = run_hip(to_device(p), flags=F.PA_FLAG_FORCE_VALU)
         perm = np.random.default_rng(4).permutation(p.num_blocks)
         inv = torch.from_numpy(np.argsort(perm).astype(np.int64))
         p2 = synth.Problem(**{**p.__dict__})
@@ -244,6 +251,8 @@ def test_block_permutation_bit_exact():
         p2.block_tables_np = perm[p.block_tables_np].astype(np.int32)
         o2, l2, _ = run_hip(to_device(p2))
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        v2, w2, _ = run_hip(to_device(p2), flags=F.PA_FLAG_FORCE_VALU)
+        assert np.array_equal(v1, v2) and np.array_equal(w1, w2)
 
 
 def test_deterministic_runs():
@@ -291,7 +300,8 @@ def test_empty_context_outputs_zero():
 
 def test_describe_paths():
     p = to_device(synth.custom([10], 32, 8, 128, 128, 128, "bf16", seed=30))
-    assert binding.for_problem(p).describe()["path"] == "valu"
+    assert binding.for_problem(p).describe()["path"] == "mfma"
+    assert binding.for_problem(p, flags=F.PA_FLAG_FORCE_VALU).describe()["path"] == "valu"
     p = to_device(synth.custom([10], 64, 1, 576, 512, 128, "bf16", seed=30))
     assert binding.for_problem(p).describe()["path"] == "mfma"
 
