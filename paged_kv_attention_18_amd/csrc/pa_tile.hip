@@ -996,9 +996,10 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
 }
 
 // Variants per (Dk, Dv).  0: units of at most 16 rows (decode), memory-bound:
-// one wave per workgroup (no waiting on other waves), short chunks, three
-// stages.  1: up to 64 rows.  2: more rows, two 16-row
-// blocks per wave.  Dk = 576 has variant 0 only (64 rows per tile).
+// the streaming kernel (one wave, 16-token chunks, four stages).  1: up to
+// 64 rows.  2: more rows, two 16-row blocks per wave.  Dk = 576 has variant
+// 0 only: 8 waves, 64 rows per tile, two waves per row group splitting Dv,
+// 32-token chunks, two stages (137 KB of LDS).
 struct TileShape {
     int mb, kt, nw, cs, s;   // nw: waves that own rows
     int threads;             // workgroup size
@@ -1015,7 +1016,7 @@ template <int DT, int DK, int DV>
 const void *kernel_for(int variant, TileShape *t)
 {
     if constexpr (DK > 256) {
-        return variant == 0 ? pick<DT, DK, DV, 1, 16, 8, 2, 4>(t) : nullptr;
+        return variant == 0 ? pick<DT, DK, DV, 1, 32, 8, 2, 2>(t) : nullptr;
     } else {
         constexpr int KT = DK <= 128 ? 64 : 32;
         if (variant == 0) {   // one wave per workgroup, streaming across units
