@@ -36,7 +36,7 @@ struct Workspace {
     int32_t *qlen;       // [max_batch]: sanitised q_seq_lens
     int32_t *kvlen;      // [max_batch]: sanitised context_lens
     int32_t *wg_b;       // [N]: sequence holding the first item of each piece
-    int32_t *splits;     // [N][8]: split units (b, g, qt, first item, end item; b < 0: none)
+    int32_t *splits;     // [N][8]: split units (b, g, qt, first item, end item, first query row, rows; b < 0: none)
     float *partials;     // [2 * N][R * (DV + 2)]
     const void *zeros;   // 16 token rows of zeros (K or V), read in place of a bad block
     uint32_t *err;       // device error word

@@ -25,14 +25,29 @@ namespace pa {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanLdsB = 2048;   // sequences kept in LDS for the piece phase
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(v, d);
+        v += lane >= d ? t : 0;
+    }
+    return v;
+}
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
 {
-    __shared__ int s_q[kPlanThreads];
-    __shared__ int s_w[kPlanThreads];
+    constexpr int NWV = kPlanThreads / 64;
+    __shared__ int s_wq[NWV], s_ww[NWV];
+    // per-sequence data for the piece phase (global arrays past kPlanLdsB)
+    __shared__ int s_wsb[kPlanLdsB + 1], s_kv[kPlanLdsB], s_ql[kPlanLdsB], s_ipg[kPlanLdsB], s_t0[kPlanLdsB];
     __shared__ int s_carry_q, s_carry_w;
     __shared__ uint32_t s_err;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
     if (tid == 0) {
         s_carry_q = 0;
         s_carry_w = 0;
@@ -45,10 +60,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
     const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
     for (int base = 0; base < p.batch; base += kPlanThreads) {
         const int b = base + tid;
-        int ql = 0, items = 0;
+        int ql = 0, kv = 0, ipg = 0, items = 0;
         uint32_t err = 0;
         if (b < p.batch) {
-            int kv = p.context_lens[b];
+            kv = p.context_lens[b];
             ql = p.q_seq_lens ? p.q_seq_lens[b] : 1;
             if (kv < 0) {
                 err |= PA_DEVERR_CTX;
@@ -69,7 +84,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
             if (p.causal && ql > kv)
                 err |= PA_DEVERR_QLEN;
             const int ntile = (ql * G + R - 1) / R;
-            int ipg = 0;
             for (int qt = 0; qt < ntile; ++qt)
                 ipg += unit_chunks(kv, ql, G, R, p.chunk, qt, p.causal);
             items = ipg * p.kv_head_num;
@@ -79,26 +93,38 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         }
         if (err)
             atomicOr(&s_err, err);
-        // inclusive scans of ql and items over this chunk of sequences
-        s_q[tid] = ql;
-        s_w[tid] = items;
-        __syncthreads();
-        for (int d = 1; d < kPlanThreads; d <<= 1) {
-            const int aq = tid >= d ? s_q[tid - d] : 0;
-            const int aw = tid >= d ? s_w[tid - d] : 0;
-            __syncthreads();
-            s_q[tid] += aq;
-            s_w[tid] += aw;
-            __syncthreads();
+        // exclusive prefix sums of ql and items: wave scans, then the wave totals
+        const int iq = wave_scan(ql, lane), iw = wave_scan(items, lane);
+        if (lane == 63) {
+            s_wq[wv] = iq;
+            s_ww[wv] = iw;
         }
+        __syncthreads();
+        if (tid == 0) {
+            int aq = s_carry_q, aw = s_carry_w;
+            for (int w = 0; w < NWV; ++w) {
+                const int tq = s_wq[w], tw = s_ww[w];
+                s_wq[w] = aq;
+                s_ww[w] = aw;
+                aq += tq;
+                aw += tw;
+            }
+            s_carry_q = aq;
+            s_carry_w = aw;
+        }
+        __syncthreads();
+        const int t0 = s_wq[wv] + iq - ql;
+        const int wsb = s_ww[wv] + iw - items;
         if (b < p.batch) {
-            p.ws.cu_q[b] = s_carry_q + s_q[tid] - ql;
-            p.ws.wsb[b] = s_carry_w + s_w[tid] - items;
-        }
-        __syncthreads();
-        if (tid == kPlanThreads - 1) {
-            s_carry_q += s_q[tid];
-            s_carry_w += s_w[tid];
+            p.ws.cu_q[b] = t0;
+            p.ws.wsb[b] = wsb;
+            if (b < kPlanLdsB) {
+                s_wsb[b] = wsb;
+                s_kv[b] = kv;
+                s_ql[b] = ql;
+                s_ipg[b] = ipg;
+                s_t0[b] = t0;
+            }
         }
         __syncthreads();
     }
@@ -116,53 +142,60 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
     }
     if (!p.no_split) {
         const int pe = per > 0 ? per : 1;
-        // Piece k starts at item k * pe: sequence b owns the pieces whose
-        // start lies in [wsb[b], wsb[b+1]).
+        const bool lds = p.batch <= kPlanLdsB;
+        if (tid == 0 && lds)
+            s_wsb[p.batch] = W;
         __syncthreads();
-        for (int base = 0; base < p.batch; base += kPlanThreads) {
-            const int b = base + tid;
-            if (b < p.batch) {
-                const int lo = p.ws.wsb[b], hi = p.ws.wsb[b + 1];
-                if (hi > lo)
-                    for (int k = (lo + pe - 1) / pe; k * pe < hi && k < p.pieces; ++k)
-                        p.ws.wg_b[k] = b;
-            }
-        }
-        __syncthreads();
-        // A unit is split when a piece boundary falls strictly inside it; it
-        // is listed once, at its first inner boundary k (entry k - 1).
-        for (int k = 1 + tid; k < p.pieces; k += kPlanThreads) {
-            int32_t *d = p.ws.splits + (size_t)(k - 1) * 8;
+        auto wsb_of = [&](int b) { return lds ? s_wsb[b] : p.ws.wsb[b]; };
+        // Piece k starts at item k * pe, in the last sequence b with
+        // wsb[b] <= k * pe.  Its split entry (entry k - 1) records the unit
+        // that boundary k cuts, if it falls strictly inside one.
+        const int nk = (W + pe - 1) / pe < p.pieces ? (W + pe - 1) / pe : p.pieces;
+        for (int k = tid; k < nk; k += kPlanThreads) {
             const int s = k * pe;
-            int b = -1, g = 0, qt = 0, us = 0, ue = 0;
-            if (s < W) {
-                const int bb = p.ws.wg_b[k];
-                const int kv = p.ws.kvlen[bb], ql = p.ws.qlen[bb], ipg = p.ws.ipg[bb];
-                int local = s - p.ws.wsb[bb];
-                const int gg = local / ipg;
-                local -= gg * ipg;
-                int u0 = p.ws.wsb[bb] + gg * ipg;
-                int t = 0, n = unit_chunks(kv, ql, G, R, p.chunk, 0, p.causal);
-                while (local >= n) {
-                    local -= n;
-                    u0 += n;
-                    ++t;
-                    n = unit_chunks(kv, ql, G, R, p.chunk, t, p.causal);
-                }
-                if (s > u0 && s - pe <= u0) {
-                    b = bb;
-                    g = gg;
-                    qt = t;
-                    us = u0;
-                    ue = u0 + n;
-                }
+            int lo = 0, hi = p.batch - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (wsb_of(mid) <= s)
+                    lo = mid;
+                else
+                    hi = mid - 1;
             }
-            d[0] = b;
-            d[1] = g;
-            d[2] = qt;
-            d[3] = us;
-            d[4] = ue;
+            const int b = lo;
+            p.ws.wg_b[k] = b;
+            if (k == 0)
+                continue;
+            const int kv = lds ? s_kv[b] : p.ws.kvlen[b];
+            const int ql = lds ? s_ql[b] : p.ws.qlen[b];
+            const int ipg = lds ? s_ipg[b] : p.ws.ipg[b];
+            const int t0 = lds ? s_t0[b] : p.ws.cu_q[b];
+            int local = s - wsb_of(b);
+            const int gg = local / ipg;
+            local -= gg * ipg;
+            int u0 = wsb_of(b) + gg * ipg;
+            int t = 0, n = unit_chunks(kv, ql, G, R, p.chunk, 0, p.causal);
+            while (local >= n) {
+                local -= n;
+                u0 += n;
+                ++t;
+                n = unit_chunks(kv, ql, G, R, p.chunk, t, p.causal);
+            }
+            int32_t *d = p.ws.splits + (size_t)(k - 1) * 8;
+            const bool split = s > u0 && s - pe <= u0;
+            int rows = ql * G - t * R;
+            rows = rows < R ? rows : R;
+            d[0] = split ? b : -1;
+            d[1] = gg;
+            d[2] = t;
+            d[3] = u0;
+            d[4] = u0 + n;
+            d[5] = t0;
+            d[6] = rows;
         }
+        // boundaries past the last item
+        for (int k = (W + pe - 1) / pe + tid; k < p.pieces; k += kPlanThreads)
+            if (k > 0)
+                p.ws.splits[(size_t)(k - 1) * 8] = -1;
     }
     if (tid == 0 && s_err)
         set_error(p.ws.err, s_err);
@@ -189,13 +222,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_group
     const int b = d[0];
     if (b < 0 || per <= 0)
         return;
-    const int g = d[1], qt = d[2], us = d[3], ue = d[4];
+    const int g = d[1], qt = d[2], us = d[3], ue = d[4], t0 = d[5], rows = d[6];
     const int rgp = blockIdx.x % row_groups;
     const int G = p.group;
     const int R = p.rows_per_tile;
     const int DV = p.head_size_v;
-    int rows = p.ws.qlen[b] * G - qt * R;
-    rows = rows < R ? rows : R;
     const int RPW = merge_rows_per_wg(DV);
     const int r0 = rgp * RPW;
     if (r0 >= rows)
@@ -235,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_group
         s_m[threadIdx.x] = M;
         s_inv[threadIdx.x] = L > 0.f ? 1.f / L : 0.f;
         const int rg = qt * R + r;
-        const int t = p.ws.cu_q[b] + rg / G;
+        const int t = t0 + rg / G;
         if (p.lse && t < p.num_q_tokens)
             p.lse[(size_t)t * p.head_num + g * G + rg % G] =
                 L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
@@ -243,7 +274,6 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_group
     __syncthreads();
     // four consecutive outputs per thread and step (DV is a multiple of 4)
     uint16_t *out = (uint16_t *)p.out;
-    const int t0 = p.ws.cu_q[b];
     for (int idx = 4 * threadIdx.x; idx < nr * DV; idx += 4 * kThreads) {
         const int rr = idx / DV;
         const int e = idx - rr * DV;
