@@ -250,7 +250,7 @@ def main():
     tokens = p.num_q_tokens
     kv_bytes = synth.kv_bytes(p)
     attn_ms = kms[1] / passes
-    kernel = "decode_kernel" if desc["path"] == "valu" else "tile_kernel"
+    kernel = {"valu": "decode_kernel", "mfma": "tile_kernel", "stream": "stream_kernel"}[desc["path"]]
     traffic = measured_traffic(w.name, kernel)
     flops = attention_flops(p)
     if flops / kv_bytes > RIDGE:

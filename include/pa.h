@@ -170,7 +170,8 @@ pa_status pa_read_timing(pa_handle *h, double ms[3], int32_t *count);
 
 /*
  * What pa_create chose, for logging and tests: *path is 0 for the VALU decode
- * kernel, 1 for the MFMA tile kernel (for a call with max_q_seq_len =
+ * kernel, 1 for the MFMA tile kernel, 2 for the MFMA streaming kernel (units
+ * of at most 16 rows), for a call with that max_q_seq_len (at most
  * cfg.max_q_seq_len); *rows_per_tile and *tokens_per_chunk describe its work
  * unit; *partitions is the attention grid size.
  */

@@ -150,7 +150,7 @@ def pa_describe(handle, max_q_seq_len):
     vals = [ctypes.c_int32() for _ in range(4)]
     _check(load_library().pa_describe(handle, max_q_seq_len, *[ctypes.byref(v) for v in vals]), "pa_describe")
     path, rows, chunk, parts = (v.value for v in vals)
-    return {"path": "valu" if path == 0 else "mfma", "rows_per_tile": rows, "tokens_per_chunk": chunk,
+    return {"path": {0: "valu", 1: "mfma", 2: "stream"}[path], "rows_per_tile": rows, "tokens_per_chunk": chunk,
             "partitions": parts}
 
 

@@ -279,8 +279,8 @@ pa_status pa_describe(const pa_handle *h, int32_t max_q_seq_len, int32_t *path, 
     if (!h || max_q_seq_len < 1 || max_q_seq_len > h->cfg.max_q_seq_len)
         return PA_ERR_INVALID_ARG;
     const Variant v = h->choose(max_q_seq_len);
-    if (path)
-        *path = v.path;
+    if (path)   // 2: the streaming variant of the matrix-core kernel
+        *path = v.path == 1 && pa::tile_streaming(h->cfg.head_size_k, h->cfg.head_size_v, v.tile_variant) ? 2 : v.path;
     if (rows_per_tile)
         *rows_per_tile = v.rows_per_tile;
     if (tokens_per_chunk)

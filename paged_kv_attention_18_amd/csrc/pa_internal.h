@@ -83,6 +83,7 @@ bool tile_supported(int dk, int dv, int variant);
 int tile_workers_per_cu(int dtype, int dk, int dv, int variant);   // resident workgroups per CU
 int tile_chunk(int dk, int dv, int variant);
 int tile_rows(int dk, int dv, int variant);
+bool tile_streaming(int dk, int dv, int variant);   // served by the one-wave streaming kernel
 int decode_chunk(int dk, int rows_pad);
 int decode_workers_per_cu(int dtype, int dk, int dv, int rows_pad);   // resident waves per CU
 

@@ -150,12 +150,14 @@ __device__ __forceinline__ void wait_ahead(int ahead)
 // Workgroups per CU the register budget is cut for: as many as fit in LDS
 // (at most 4; at most 2 with two 16-row blocks per wave, 1 at head sizes
 // above 128).
-template <int DK, int DV, int MB, int KT, int S>
+template <int DK, int DV, int MB, int KT, int S, int NW>
 constexpr int tile_min_wgs()
 {
     constexpr int lds = S * KT * 2 * (DK + DV) + 2048;
     constexpr int fit = (160 * 1024) / lds;
-    constexpr int cap = MB == 2 ? ((DK > 128 || DV > 128) ? 1 : 2) : 4;
+    // waves per SIMD the registers allow: 2 with two 16-row blocks, else 4
+    constexpr int waves = MB == 2 ? ((DK > 128 || DV > 128) ? 1 : 2) : 4;
+    constexpr int cap = 4 * waves / NW > 0 ? 4 * waves / NW : 1;
     return fit < 1 ? 1 : (fit > cap ? cap : fit);
 }
 
@@ -164,7 +166,7 @@ constexpr int tile_min_wgs()
 // S: LDS stages (chunks c + 1 .. c + S - 1 are in flight while c is
 // computed).
 template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S>
-__global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S>())) void tile_kernel(Params p)
+__global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW>())) void tile_kernel(Params p)
 {
     constexpr int RGS = NW / CS;                  // row groups
     constexpr int R = 16 * MB * RGS;              // rows per tile
@@ -1068,6 +1070,12 @@ int tile_rows(int dk, int dv, int variant)
 {
     TileShape t;
     return tile_kernel_ptr(0, dk, dv, variant, &t) ? 16 * t.mb * (t.nw / t.cs) : 0;
+}
+
+bool tile_streaming(int dk, int dv, int variant)
+{
+    TileShape t;
+    return tile_kernel_ptr(0, dk, dv, variant, &t) && t.nw == 1;
 }
 
 int tile_workers_per_cu(int dtype, int dk, int dv, int variant)

@@ -300,7 +300,7 @@ def test_empty_context_outputs_zero():
 
 def test_describe_paths():
     p = to_device(synth.custom([10], 32, 8, 128, 128, 128, "bf16", seed=30))
-    assert binding.for_problem(p).describe()["path"] == "mfma"
+    assert binding.for_problem(p).describe()["path"] == "stream"
     assert binding.for_problem(p, flags=F.PA_FLAG_FORCE_VALU).describe()["path"] == "valu"
     p = to_device(synth.custom([10], 64, 1, 576, 512, 128, "bf16", seed=30))
     assert binding.for_problem(p).describe()["path"] == "mfma"
