@@ -142,12 +142,19 @@ static int one_row(const problem *P, int b, int i, int h, double *z, double *o, 
     }
     for (int e = 0; e < Dv; ++e)
         o[e] = 0.0;
+    /* V row of token j: its own tensor, or (no value_cache) the first Dv
+     * elements of the token's K row.  The SparseAttnSharedkvMetadata page
+     * (function and parameter sections) feeds an attention whose K and V are
+     * one cache with one head count; with the MLA head sizes (576 for K, 512
+     * for V) the plain reading is that V is the leading part of the K row. */
+    const uint16_t *vsrc = P->value_cache ? P->value_cache : P->key_cache;
+    const int vstride = P->value_cache ? Dv : Dk;
     for (int j = 0; j < n; ++j) {
         int32_t phys = P->block_tables[(int64_t)b * P->max_num_blocks_per_seq + j / bs];
         int slot = j % bs;
-        const int64_t vrow = (((int64_t)phys * bs + slot) * Hkv + g) * Dv;
+        const int64_t vrow = (((int64_t)phys * bs + slot) * Hkv + g) * vstride;
         for (int e = 0; e < Dv; ++e)
-            o[e] += z[j] * elem(P->value_cache, vrow + e, P->dtype);
+            o[e] += z[j] * elem(vsrc, vrow + e, P->dtype);
     }
     for (int e = 0; e < Dv; ++e)
         o[e] /= wsum;
@@ -238,7 +245,9 @@ static int run_items(const problem *P, const int32_t *seq, const int32_t *pos, c
 /* Checks the problem description; fills P->row_start (caller frees). */
 static int setup(problem *P)
 {
-    if (!P->query || !P->key_cache || !P->value_cache || !P->block_tables || !P->context_lens)
+    if (!P->query || !P->key_cache || !P->block_tables || !P->context_lens)
+        return REF_BAD_ARG;
+    if (!P->value_cache && P->head_size_v > P->head_size_k)   /* V rows inside K rows */
         return REF_BAD_ARG;
     if (P->batch < 0 || P->head_num <= 0 || P->kv_head_num <= 0 || P->head_size_k <= 0 ||
         P->head_size_v <= 0 || P->block_size <= 0 || P->max_num_blocks_per_seq < 0 ||

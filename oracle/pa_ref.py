@@ -66,10 +66,13 @@ class Inputs:
     raw uint16 bit patterns, lengths and tables as int32."""
 
     def __init__(self, query, key_cache, value_cache, block_tables, context_lens, q_seq_lens,
-                 head_num, kv_head_num, dtype, mask, scale):
+                 head_num, kv_head_num, dtype, mask, scale, head_size_v=None):
         self.query = _bits(query)
         self.key_cache = _bits(key_cache)
-        self.value_cache = _bits(value_cache)
+        # value_cache None: the V row of a token is the first head_size_v
+        # elements of its K row (one cache for both)
+        self.value_cache = None if value_cache is None else _bits(value_cache)
+        self.head_size_v = int(self.value_cache.shape[3] if value_cache is not None else head_size_v)
         self.block_tables = np.ascontiguousarray(block_tables, dtype=np.int32)
         self.context_lens = np.ascontiguousarray(context_lens, dtype=np.int32)
         self.q_seq_lens = None if q_seq_lens is None else np.ascontiguousarray(q_seq_lens, dtype=np.int32)
@@ -84,7 +87,7 @@ class Inputs:
         """From a ``synth.Problem`` (tensors are copied to the host)."""
         w = p.workload
         return cls(p.query, p.key_cache, p.value_cache, p.block_tables_np, p.context_lens_np,
-                   p.q_seq_lens_np, w.head_num, w.kv_head_num, w.dtype, w.mask, w.scale)
+                   p.q_seq_lens_np, w.head_num, w.kv_head_num, w.dtype, w.mask, w.scale, w.head_size_v)
 
     @property
     def batch(self):
@@ -96,7 +99,7 @@ class Inputs:
 
     def _args(self):
         nb, bs, _, dk = self.key_cache.shape
-        dv = self.value_cache.shape[3]
+        dv = self.head_size_v
         mb = self.block_tables.shape[1] if self.block_tables.ndim == 2 else 0
         ptr = lambda a: None if a is None else a.ctypes.data
         return [ptr(self.query), ptr(self.key_cache), ptr(self.value_cache), ptr(self.block_tables),
@@ -116,7 +119,7 @@ def _bits(t):
 def forward(inp: Inputs, threads=None, lib=None):
     """All rows: returns (out float64 [T, H, Dv], lse float64 [T, H])."""
     lib = lib or load()
-    dv = inp.value_cache.shape[3]
+    dv = inp.head_size_v
     out = np.zeros((inp.num_q_tokens, inp.head_num, dv), dtype=np.float64)
     lse = np.zeros((inp.num_q_tokens, inp.head_num), dtype=np.float64)
     rc = lib.pa_ref_forward(*inp._args(), out.ctypes.data, lse.ctypes.data, threads or default_threads())
@@ -130,7 +133,7 @@ def rows(inp: Inputs, tokens, heads, threads=None, lib=None):
     lib = lib or load()
     tokens = np.ascontiguousarray(tokens, dtype=np.int32)
     heads = np.ascontiguousarray(heads, dtype=np.int32)
-    dv = inp.value_cache.shape[3]
+    dv = inp.head_size_v
     out = np.zeros((len(tokens), dv), dtype=np.float64)
     lse = np.zeros(len(tokens), dtype=np.float64)
     rc = lib.pa_ref_rows(*inp._args(), len(tokens), tokens.ctypes.data, heads.ctypes.data,

@@ -49,6 +49,7 @@ class Workload:
     num_blocks: Optional[int] = None   # fixed pool size; None -> used blocks + slack
     slack: float = 0.10
     seed: int = 0
+    shared_kv: bool = False    # V rows are the first head_size_v elements of the K rows
 
 
 def _tiny_lengths(rng):
@@ -88,6 +89,9 @@ WORKLOADS = {
                 1.0 / math.sqrt(128), _splitfuse_lengths, seed=1004),
     5: Workload("mla_decode", 128, 64, 1, 576, 512, 128, "bf16", "none", 1.0 / math.sqrt(576),
                 _mla_lengths, seed=1005),
+    # shared-KV form of the MLA decode: V is the first 512 elements of each K row
+    6: Workload("mla_shared_kv_decode", 128, 64, 1, 576, 512, 128, "bf16", "none", 1.0 / math.sqrt(576),
+                _mla_lengths, seed=1006, shared_kv=True),
 }
 
 
@@ -115,7 +119,7 @@ class Problem:
     block_tables: torch.Tensor       # int32 [B, max_num_blocks_per_seq]
     query: torch.Tensor              # [T, H, Dk]
     key_cache: torch.Tensor          # [num_blocks, block_size, Hkv, Dk]
-    value_cache: torch.Tensor        # [num_blocks, block_size, Hkv, Dv]
+    value_cache: Optional[torch.Tensor]   # [num_blocks, block_size, Hkv, Dv]; None with shared_kv
     context_lens_np: np.ndarray
     q_seq_lens_np: Optional[np.ndarray]
     block_tables_np: np.ndarray
@@ -190,11 +194,11 @@ def generate(w: Workload, device="cpu", seed: Optional[int] = None, values=True,
     if values:
         q = _normal(qshape, dt, seed * 16 + 1, device)
         kc = _normal(kshape, dt, seed * 16 + 2, device)
-        vc = _normal(vshape, dt, seed * 16 + 3, device)
+        vc = None if w.shared_kv else _normal(vshape, dt, seed * 16 + 3, device)
     else:
         q = torch.zeros(qshape, dtype=dt, device=device)
         kc = torch.zeros(kshape, dtype=dt, device=device)
-        vc = torch.zeros(vshape, dtype=dt, device=device)
+        vc = None if w.shared_kv else torch.zeros(vshape, dtype=dt, device=device)
     return Problem(
         workload=w,
         context_lens=torch.from_numpy(kv.copy()).to(device),
@@ -208,18 +212,20 @@ def generate(w: Workload, device="cpu", seed: Optional[int] = None, values=True,
 
 def custom(batch_lens, head_num, kv_head_num, head_size_k, head_size_v, block_size,
            dtype="f16", mask="none", scale=None, q_seq_lens=None, num_blocks=None,
-           slack=0.25, seed=7, name="custom", device="cpu", max_blocks=None) -> Problem:
+           slack=0.25, seed=7, name="custom", device="cpu", max_blocks=None, shared_kv=False) -> Problem:
     """A small hand-shaped problem (tests)."""
     if scale is None:
         scale = 1.0 / math.sqrt(head_size_k)
     w = Workload(name, len(batch_lens), head_num, kv_head_num, head_size_k, head_size_v,
                  block_size, dtype, mask, float(scale), fixed_lengths(batch_lens, q_seq_lens),
-                 num_blocks=num_blocks, slack=slack, seed=seed)
+                 num_blocks=num_blocks, slack=slack, seed=seed, shared_kv=shared_kv)
     return generate(w, device=device, max_blocks=max_blocks)
 
 
 def kv_bytes(p: Problem) -> int:
     """Key+value bytes the method must read: each visible (sequence, KV head,
-    token) row once, K and V head sizes at 2 bytes per element."""
+    token) row once, K and V head sizes at 2 bytes per element (only the K
+    row when V lives inside it)."""
     w = p.workload
-    return p.kv_tokens() * w.kv_head_num * (w.head_size_k + w.head_size_v) * 2
+    per_row = w.head_size_k if w.shared_kv else w.head_size_k + w.head_size_v
+    return p.kv_tokens() * w.kv_head_num * per_row * 2

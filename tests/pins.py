@@ -375,4 +375,35 @@ def pin_element_decoding(lib):
         assert np.array_equal(o[0, 0], want), dt
 
 
+def pin_shared_kv_is_sliced_v(lib):
+    """Shared K/V (no value cache; V is the first Dv elements of each K row,
+    the reading of the SparseAttnSharedkvMetadata page's single K/V cache) equals SDPA
+    with V cut from K by torch slicing, and the oracle with that V passed as
+    its own tensor, bit for bit.  Dv > Dk without a value cache is refused."""
+    for p in (synth.custom([37, 70, 5], 8, 2, 72, 64, 16, "bf16", seed=130, shared_kv=True),
+              synth.custom([40, 19], 4, 1, 48, 16, 16, "f16", "causal", q_seq_lens=[9, 19],
+                           seed=131, shared_kv=True)):
+        assert p.value_cache is None
+        o, l = run(lib, p)
+        p2 = synth.Problem(**{**p.__dict__})
+        p2.workload = synth.Workload(**{**p.workload.__dict__, "shared_kv": False})
+        p2.value_cache = p.key_cache[..., :p.workload.head_size_v].contiguous()
+        shifted = None
+        if p.workload.mask == "causal":     # row i sees tokens up to (kv - qlen) + i
+            shifted = lambda q, kv: torch.zeros(q, kv, dtype=torch.float64).masked_fill(
+                torch.ones(q, kv, dtype=torch.bool).triu(1 + max(0, kv - q)), -math.inf)
+        ro, rl = sdpa_reference(p2, shifted)
+        close(o, ro)
+        close(l, rl)
+        o2, l2 = run(lib, p2)
+        assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    bad = synth.custom([5], 2, 1, 16, 32, 16, "f16", seed=132, shared_kv=True)
+    try:
+        run(lib, bad)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("Dv > Dk with V inside K accepted")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

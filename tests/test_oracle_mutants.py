@@ -24,8 +24,8 @@ MUTANTS = [
     ("lse_no_log", "*lse = zmax + log(wsum);", "*lse = zmax + wsum;"),
     ("kv_layout_bhsd", "const int64_t krow = (((int64_t)phys * bs + slot) * Hkv + g) * Dk;",
      "const int64_t krow = (((int64_t)phys * Hkv + g) * bs + slot) * Dk;"),
-    ("v_layout_bhsd", "const int64_t vrow = (((int64_t)phys * bs + slot) * Hkv + g) * Dv;",
-     "const int64_t vrow = (((int64_t)phys * Hkv + g) * bs + slot) * Dv;"),
+    ("v_layout_bhsd", "const int64_t vrow = (((int64_t)phys * bs + slot) * Hkv + g) * vstride;",
+     "const int64_t vrow = (((int64_t)phys * Hkv + g) * bs + slot) * vstride;"),
     ("mean_not_softmax", "o[e] /= wsum;", "o[e] /= (double)n;"),
     ("row_offset_dropped", "const int64_t t = P->row_start[b] + i;", "const int64_t t = i;"),
     ("q_head_is_kv_head", "const uint16_t *q = P->query + (t * H + h) * (int64_t)Dk;",
@@ -37,8 +37,11 @@ MUTANTS = [
     ("table_row_stride",
      "int32_t phys = P->block_tables[(int64_t)b * P->max_num_blocks_per_seq + j / bs];\n        if (phys < 0",
      "int32_t phys = P->block_tables[(int64_t)b * (P->max_num_blocks_per_seq - 1) + j / bs];\n        if (phys < 0"),
-    ("v_uses_first_token", "o[e] += z[j] * elem(P->value_cache, vrow + e, P->dtype);",
-     "o[e] += z[j] * elem(P->value_cache, vrow - (int64_t)slot * Hkv * Dv + e, P->dtype);"),
+    ("v_uses_first_token", "o[e] += z[j] * elem(vsrc, vrow + e, P->dtype);",
+     "o[e] += z[j] * elem(vsrc, vrow - (int64_t)slot * Hkv * vstride + e, P->dtype);"),
+    ("shared_v_row_stride", "const int vstride = P->value_cache ? Dv : Dk;", "const int vstride = Dv;"),
+    ("shared_v_last_columns", "const uint16_t *vsrc = P->value_cache ? P->value_cache : P->key_cache;",
+     "const uint16_t *vsrc = P->value_cache ? P->value_cache : P->key_cache + (Dk - Dv);"),
     ("exp_without_shift_in_lse", "*lse = zmax + log(wsum);", "*lse = log(wsum);"),
 ]
 
