@@ -114,9 +114,10 @@ def cpu_baseline(p, target_s, threads):
             bt[i, :len(t)] = t
         idx = torch.tensor(blocks, dtype=torch.long, device=p.key_cache.device)
         qidx = torch.cat([torch.arange(int(cu[b]), int(cu[b + 1])) for b in seqs]).to(p.query.device)
-        return pa_ref.Inputs(p.query[qidx], p.key_cache[idx], p.value_cache[idx], bt, kv[seqs],
+        return pa_ref.Inputs(p.query[qidx], p.key_cache[idx],
+                             None if p.value_cache is None else p.value_cache[idx], bt, kv[seqs],
                              None if p.q_seq_lens_np is None else ql[seqs], w.head_num, w.kv_head_num,
-                             w.dtype, w.mask, w.scale)
+                             w.dtype, w.mask, w.scale, w.head_size_v)
 
     # calibrate the oracle's rate on the cheapest sequence
     b0 = int(np.argmin(cost))
@@ -186,10 +187,12 @@ def main():
 
     w = synth.WORKLOADS[int(args.workload)] if args.workload.isdigit() else synth.by_name(args.workload)
     p = synth.generate(w, device=dev)
-    cache_bytes = (p.key_cache.numel() + p.value_cache.numel()) * p.key_cache.element_size()
+    vc_numel = 0 if p.value_cache is None else p.value_cache.numel()
+    cache_bytes = (p.key_cache.numel() + vc_numel) * p.key_cache.element_size()
     copies = args.copies or max(3, math.ceil((1.5 * (1 << 30)) / cache_bytes))
     kcs = [p.key_cache] + [p.key_cache.clone() for _ in range(copies - 1)]
-    vcs = [p.value_cache] + [p.value_cache.clone() for _ in range(copies - 1)]
+    # shared K/V: no value cache (V is read from the K rows)
+    vcs = [None] * copies if p.value_cache is None else [p.value_cache] + [p.value_cache.clone() for _ in range(copies - 1)]
     att = binding.for_problem(p, flags=args.flags, num_partitions=args.partitions)
     desc = att.describe()
     out = torch.empty(p.num_q_tokens, w.head_num, w.head_size_v, dtype=p.query.dtype, device=dev)
@@ -281,7 +284,7 @@ def main():
         "config": {
             "workload": w.name, "batch": p.batch, "head_num": w.head_num, "kv_head_num": w.kv_head_num,
             "head_size_k": w.head_size_k, "head_size_v": w.head_size_v, "block_size": w.block_size,
-            "mask": w.mask, "query_tokens": tokens, "kv_tokens": p.kv_tokens(), "kv_bytes": kv_bytes,
+            "mask": w.mask, "shared_kv": w.shared_kv, "query_tokens": tokens, "kv_tokens": p.kv_tokens(), "kv_bytes": kv_bytes,
             "seed": w.seed, "kv_cache_copies": copies, "path": desc["path"],
             "partitions": desc["partitions"], "flags": args.flags, "parallelism": "none (1 GPU)",
         },

@@ -76,7 +76,10 @@ enum {
     PA_FLAG_FORCE_VALU = 1u << 0,  /* testing: require the VALU decode path (at most 8 rows per unit,
                                       i.e. max_q_seq_len * head_num / kv_head_num <= 8) */
     PA_FLAG_FORCE_MFMA = 1u << 1,  /* testing: take the MFMA tile path always */
-    PA_FLAG_NO_SPLIT = 1u << 2     /* testing: one worker per (sequence, KV head, row tile); no merge */
+    PA_FLAG_NO_SPLIT = 1u << 2,    /* testing: one worker per (sequence, KV head, row tile); no merge */
+    PA_FLAG_SHARED_KV = 1u << 3    /* one cache for K and V: the V row of a token is the leading
+                                      head_size_v elements of its K row (requires Dv <= Dk); see
+                                      pa_forward's value_cache */
 };
 
 /* Device error word bits (pa_get_device_error). */
@@ -115,7 +118,8 @@ typedef struct pa_handle pa_handle;
  * block_size % 16 == 0, block_size <= 256, and block_size <= 128 in causal
  * mode or when Dk or Dv > 256; num_blocks > 0; max_batch > 0;
  * max_num_blocks_per_seq > 0; max_q_seq_len > 0; dtype and mask in range;
- * scale finite; num_partitions >= 0.  PA_ERR_UNSUPPORTED: a (Dk, Dv) pair this
+ * scale finite; num_partitions >= 0; only PA_FLAG_* bits, not FORCE_VALU
+ * with FORCE_MFMA; Dv <= Dk with PA_FLAG_SHARED_KV.  PA_ERR_UNSUPPORTED: a (Dk, Dv) pair this
  * build has no kernels for (64/64, 128/128, 256/256, 576/512 are built), or a
  * device that is not gfx950.  On success *out receives the handle.
  */
@@ -126,7 +130,11 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out);
  * stream).  All tensors are device pointers, row-major, contiguous:
  *   query        [num_q_tokens, H, Dk]  dtype   (TND, rows of sequence b contiguous)
  *   key_cache    [num_blocks, block_size, Hkv, Dk]  dtype
- *   value_cache  [num_blocks, block_size, Hkv, Dv]  dtype
+ *   value_cache  [num_blocks, block_size, Hkv, Dv]  dtype; with PA_FLAG_SHARED_KV it must be
+ *                NULL or equal to key_cache, and V_j is elements [0, Dv) of key_cache's row
+ *                for token j (the single K/V cache of the SparseAttnSharedkvMetadata page,
+ *                function and parameter sections, with the MLA head sizes 576 / 512 of the
+ *                PagedAttentionOperation Constraints: V is the leading part of the K row)
  *   block_tables [batch, max_num_blocks_per_seq]  int32
  *   context_lens [batch]  int32   (kvSeqLen: history + current query tokens)
  *   q_seq_lens   [batch]  int32, or NULL for one query token per sequence
@@ -135,7 +143,9 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out);
  * batch in [0, max_batch]; max_q_seq_len in [1, cfg.max_q_seq_len] bounds
  * q_seq_lens (1 when q_seq_lens is NULL); num_q_tokens >= 0 equals the sum of
  * q_seq_lens (batch when NULL).  Returns PA_ERR_INVALID_ARG for a NULL
- * handle or tensor (q_seq_lens and lse excepted), a NULL q_seq_lens with
+ * handle or tensor (q_seq_lens, lse, and value_cache under PA_FLAG_SHARED_KV
+ * excepted), a value_cache other than NULL or key_cache under
+ * PA_FLAG_SHARED_KV, a NULL q_seq_lens with
  * num_q_tokens != batch, or sizes out of range; PA_ERR_HIP if a launch fails.
  */
 pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache,

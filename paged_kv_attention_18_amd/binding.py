@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_OOM = range(5)
 PA_F16, PA_BF16 = 0, 1
 PA_MASK_NONE, PA_MASK_CAUSAL = 0, 1
-PA_FLAG_FORCE_VALU, PA_FLAG_FORCE_MFMA, PA_FLAG_NO_SPLIT = 1, 2, 4
+PA_FLAG_FORCE_VALU, PA_FLAG_FORCE_MFMA, PA_FLAG_NO_SPLIT, PA_FLAG_SHARED_KV = 1, 2, 4, 8
 PA_DEVERR_BLOCK_ID, PA_DEVERR_TABLE_SHORT, PA_DEVERR_QLEN, PA_DEVERR_TOKENS, PA_DEVERR_CTX = 1, 2, 4, 8, 16
 
 EXPORTS = ("pa_create", "pa_forward", "pa_destroy", "pa_status_string", "pa_get_device_error",
@@ -210,8 +210,14 @@ class Attention:
         self._need(query, "query", self.dtype, (T, c.head_num, c.head_size_k))
         self._need(key_cache, "key_cache", self.dtype,
                    (c.num_blocks, c.block_size, c.kv_head_num, c.head_size_k))
-        self._need(value_cache, "value_cache", self.dtype,
-                   (c.num_blocks, c.block_size, c.kv_head_num, c.head_size_v))
+        shared = bool(c.flags & PA_FLAG_SHARED_KV)
+        if shared:
+            # one cache for K and V: pass None (or the key cache itself)
+            if value_cache is not None and value_cache is not key_cache:
+                raise ValueError("with PA_FLAG_SHARED_KV value_cache must be None or key_cache")
+        else:
+            self._need(value_cache, "value_cache", self.dtype,
+                       (c.num_blocks, c.block_size, c.kv_head_num, c.head_size_v))
         self._need(block_tables, "block_tables", torch.int32, (B, c.max_num_blocks_per_seq))
         self._need(context_lens, "context_lens", torch.int32, (B,))
         if q_seq_lens is not None:
@@ -229,7 +235,8 @@ class Attention:
             self._need(lse, "lse", torch.float32, (T, c.head_num))
         if stream is None:
             stream = torch.cuda.current_stream(query.device).cuda_stream
-        pa_forward(self.handle, query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        pa_forward(self.handle, query.data_ptr(), key_cache.data_ptr(),
+                   0 if shared else value_cache.data_ptr(),
                    block_tables.data_ptr(), context_lens.data_ptr(),
                    q_seq_lens.data_ptr() if q_seq_lens is not None else 0,
                    B, T, int(max_q_seq_len), out.data_ptr(), lse.data_ptr() if lse is not None else 0,
@@ -248,6 +255,8 @@ def for_problem(p, **kw):
                 max_batch=p.batch, max_num_blocks_per_seq=p.max_num_blocks_per_seq,
                 max_q_seq_len=max(1, p.max_q_seq_len), dtype=DTYPES[w.dtype], scale=w.scale, mask=w.mask)
     args.update(kw)
+    if w.shared_kv:
+        args["flags"] = args.get("flags", 0) | PA_FLAG_SHARED_KV
     return Attention(**args)
 
 

@@ -89,13 +89,14 @@ struct pa_handle {
         } else {
             v.path = 1;
             const int dk = cfg.head_size_k, dv = cfg.head_size_v;
+            const bool sh = (cfg.flags & PA_FLAG_SHARED_KV) != 0;
             int var = 0;
             if (rows > 16 && pa::tile_supported(dk, dv, 1))
-                var = (rows > pa::tile_rows(dk, dv, 1) && pa::tile_supported(dk, dv, 2)) ? 2 : 1;
+                var = (rows > pa::tile_rows(dk, dv, 1, sh) && pa::tile_supported(dk, dv, 2)) ? 2 : 1;
             v.tile_variant = var;
-            v.rows_per_tile = pa::tile_rows(dk, dv, var);
-            v.chunk = pa::tile_chunk(dk, dv, var);
-            v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var);
+            v.rows_per_tile = pa::tile_rows(dk, dv, var, sh);
+            v.chunk = pa::tile_chunk(dk, dv, var, sh);
+            v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var, sh);
             v.pieces_per_worker = var == 0 ? 1 : kMaxPiecesPerWorker;
         }
         if (cfg.num_partitions > 0)
@@ -136,8 +137,10 @@ static pa_status check_config(const pa_config *c)
         return PA_ERR_INVALID_ARG;
     if ((c->flags & PA_FLAG_FORCE_VALU) && (c->flags & PA_FLAG_FORCE_MFMA))
         return PA_ERR_INVALID_ARG;
-    if (c->flags & ~(uint32_t)(PA_FLAG_FORCE_VALU | PA_FLAG_FORCE_MFMA | PA_FLAG_NO_SPLIT))
+    if (c->flags & ~(uint32_t)(PA_FLAG_FORCE_VALU | PA_FLAG_FORCE_MFMA | PA_FLAG_NO_SPLIT | PA_FLAG_SHARED_KV))
         return PA_ERR_INVALID_ARG;
+    if ((c->flags & PA_FLAG_SHARED_KV) && c->head_size_v > c->head_size_k)
+        return PA_ERR_INVALID_ARG;   // V must fit inside the K row
     // Item indices are int32 on the device: bound the largest possible count.
     const int G = c->head_num / c->kv_head_num;
     const double tiles = std::ceil((double)c->max_q_seq_len * G / 16.0);
@@ -295,9 +298,13 @@ pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, con
                      int32_t batch, int32_t num_q_tokens, int32_t max_q_seq_len, void *out, float *lse,
                      void *stream)
 {
-    if (!h || !query || !key_cache || !value_cache || !block_tables || !context_lens || !out)
+    if (!h || !query || !key_cache || !block_tables || !context_lens || !out)
         return PA_ERR_INVALID_ARG;
     const pa_config &c = h->cfg;
+    const bool shared = (c.flags & PA_FLAG_SHARED_KV) != 0;
+    // shared K/V: value_cache is NULL or the key cache itself
+    if (shared ? (value_cache && value_cache != key_cache) : !value_cache)
+        return PA_ERR_INVALID_ARG;
     if (batch < 0 || batch > c.max_batch || num_q_tokens < 0)
         return PA_ERR_INVALID_ARG;
     if (!q_seq_lens) {
@@ -315,7 +322,10 @@ pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, con
     pa::Params p{};
     p.query = query;
     p.key_cache = key_cache;
-    p.value_cache = value_cache;
+    p.value_cache = shared ? key_cache : value_cache;
+    p.shared_kv = shared ? 1 : 0;
+    p.v_row_bytes = (uint32_t)c.kv_head_num * (uint32_t)(shared ? c.head_size_k : c.head_size_v) * 2u;
+    p.v_head_bytes = (uint32_t)(shared ? c.head_size_k : c.head_size_v) * 2u;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     p.q_seq_lens = q_seq_lens;

@@ -66,6 +66,11 @@ struct Params {
     int32_t no_split;
     int32_t max_tiles;                 // ceil(max_q * G / R)
     int32_t partial_stride;            // floats per partial slot = R * (DV + 2)
+    // V source: value_cache, or (shared K/V) the key cache itself, whose
+    // rows hold V as their leading Dv elements
+    int32_t shared_kv;
+    uint32_t v_row_bytes;              // bytes from one token row of the V source to the next
+    uint32_t v_head_bytes;             // bytes from one KV head to the next within a token row
     Workspace ws;
 };
 
@@ -79,10 +84,12 @@ hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s);
 bool decode_supported(int dk, int dv);
 // MFMA tile kernel variants: 0 for units of at most 16 rows, 1 for up to
 // tile_rows(.., 1) rows, 2 above; tile_supported says which exist.
+// `shared` selects the kernels that read V out of the K tile already in LDS
+// (shared K/V cache) where such kernels exist.
 bool tile_supported(int dk, int dv, int variant);
-int tile_workers_per_cu(int dtype, int dk, int dv, int variant);   // resident workgroups per CU
-int tile_chunk(int dk, int dv, int variant);
-int tile_rows(int dk, int dv, int variant);
+int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared);   // resident workgroups per CU
+int tile_chunk(int dk, int dv, int variant, bool shared);
+int tile_rows(int dk, int dv, int variant, bool shared);
 bool tile_streaming(int dk, int dv, int variant);   // served by the one-wave streaming kernel
 int decode_chunk(int dk, int rows_pad);
 int decode_workers_per_cu(int dtype, int dk, int dv, int rows_pad);   // resident waves per CU

@@ -149,11 +149,11 @@ __device__ __forceinline__ void wait_ahead(int ahead)
 
 // Workgroups per CU the register budget is cut for: as many as fit in LDS
 // (at most 4; at most 2 with two 16-row blocks per wave, 1 at head sizes
-// above 128).
-template <int DK, int DV, int MB, int KT, int S, int NW>
+// above 128).  SH: no V tiles in LDS.
+template <int DK, int DV, int MB, int KT, int S, int NW, bool SH>
 constexpr int tile_min_wgs()
 {
-    constexpr int lds = S * KT * 2 * (DK + DV) + 2048;
+    constexpr int lds = S * KT * 2 * (DK + (SH ? 0 : DV)) + 2048;
     constexpr int fit = (160 * 1024) / lds;
     // waves per SIMD the registers allow: 2 with two 16-row blocks, else 4
     constexpr int waves = MB == 2 ? ((DK > 128 || DV > 128) ? 1 : 2) : 4;
@@ -164,34 +164,40 @@ constexpr int tile_min_wgs()
 // DT: 0 f16 / 1 bf16.  MB: 16-row blocks per wave.  KT: tokens per chunk
 // (16, 32 or 64).  NW: waves.  CS: waves sharing a row group (column split).
 // S: LDS stages (chunks c + 1 .. c + S - 1 are in flight while c is
-// computed).
-template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S>
-__global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW>())) void tile_kernel(Params p)
+// computed).  SH: shared K/V cache -- V is the leading Dv elements of each
+// K row, so only K tiles are loaded and the PV product reads its operand
+// from the K tile (the K swizzle keeps those transposing reads free of
+// bank conflicts as well).
+template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH>
+__global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>())) void tile_kernel(Params p)
 {
     constexpr int RGS = NW / CS;                  // row groups
     constexpr int R = 16 * MB * RGS;              // rows per tile
     constexpr int RBK = 2 * DK, RBV = 2 * DV;     // LDS row bytes
+    constexpr int RBVL = SH ? RBK : RBV;          // LDS row bytes of the tile the V operand is read from
     constexpr int KS = DK / 32;
     constexpr int NTT = KT / 16;
     constexpr int ND = DV / 16 / CS;              // output column tiles per wave
     constexpr int IPGK = RBK / 64;                // 1 KiB LDS-load instructions per 16-token group (K)
-    constexpr int IPGV = RBV / 64;
+    constexpr int IPGV = SH ? 0 : RBV / 64;
     constexpr int MK = (IPGK + NW - 1) / NW;      // ... per wave per group
     constexpr int MV = (IPGV + NW - 1) / NW;
     constexpr int LW = NTT * (MK + MV);           // load instructions per wave per chunk, all waves alike
     constexpr bool PAD = MK * NW != IPGK || MV * NW != IPGV;
+    constexpr int VTB = SH ? 16 : KT * RBV;       // bytes of a V stage buffer
     static_assert(DK % 32 == 0 && DV % 64 == 0 && (KT == 16 || KT == 32 || KT == 64), "shape");
     static_assert(NW % CS == 0 && ND % 4 == 0 && S >= 2 && S <= 4, "split");
     static_assert(LW * (S - 2) < 64, "vmcnt range");
+    static_assert(!SH || DV <= DK, "V inside the K row");
 
     __shared__ __attribute__((aligned(1024))) uint8_t sK0[KT * RBK];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV0[KT * RBV];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV0[VTB];
     __shared__ __attribute__((aligned(1024))) uint8_t sK1[KT * RBK];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV1[KT * RBV];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV1[VTB];
     __shared__ __attribute__((aligned(1024))) uint8_t sK2[S > 2 ? KT * RBK : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV2[S > 2 ? KT * RBV : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV2[S > 2 ? VTB : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t sK3[S > 3 ? KT * RBK : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV3[S > 3 ? KT * RBV : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV3[S > 3 ? VTB : 16];
     // destination of the padding loads that keep every wave's count at LW
     __shared__ __attribute__((aligned(1024))) uint8_t sJunk[PAD ? 1024 : 16];
 
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW>())) v
     const int bs = p.block_size;
     const int bsh = p.bs_shift;
     const uint32_t rsk = (uint32_t)p.kv_head_num * RBK;   // bytes per token row of the cache
-    const uint32_t rsv = (uint32_t)p.kv_head_num * RBV;
+    const uint32_t rsv = p.v_row_bytes;
     const uint32_t nb32 = p.num_blocks < 0x7fffffff ? (uint32_t)p.num_blocks : 0x7fffffffu;
     // Scores are kept raw (q . k) and scaled on the way into exp2 by
     // sc = |scale| log2(e); a negative scale is folded into Q.
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW>())) v
     // Per-lane byte offset, inside a 16-token group of the cache, of the piece
     // that load instruction wave + NW m of the group moves; the piece is the
     // one whose LDS slot holds the swizzled layout.
-    uint32_t voK[MK], voV[MV];
+    uint32_t voK[MK], voV[MV > 0 ? MV : 1];
 #pragma unroll
     for (int m = 0; m < MK; ++m) {
         const int x = (wave + NW * m) * 1024 + 16 * lane;
@@ -256,11 +262,15 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW>())) v
     const int kb2 = 64 * ((lr >> 2) & 1);
     const int koE = lr * RBK + kq + kb2, koO = lr * RBK + kq - kb2;
     // V (B operand, transposing read): row 4 lg + lr / 4 (+ 16 n),
-    // columns col0 + 16 nd + 4 (lr % 4) .. + 3.
+    // columns col0 + 16 nd + 4 (lr % 4) .. + 3, i.e. 16-byte piece
+    // col0 / 8 + 2 nd + (lr % 4) / 2 of the row, moved by the tile's swizzle.
     int vo[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-        vo[m] = (4 * lg + (lr >> 2)) * RBV + 32 * (m ^ (lr >> 2)) + 16 * ((lr & 3) >> 1) + 8 * (lr & 1) + 2 * col0;
+    for (int m = 0; m < 4; ++m) {
+        const int vrow = 4 * lg + (lr >> 2);
+        const int vpiece = SH ? ((2 * m + ((lr & 3) >> 1)) ^ (vrow & 7)) : (2 * (m ^ (lr >> 2)) + ((lr & 3) >> 1));
+        vo[m] = vrow * RBVL + 16 * vpiece + 8 * (lr & 1) + 2 * col0;
+    }
 
     while (true) {
         const int b = cu.b, g = cu.g, qt = cu.qt;
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW>())) v
         const bool wave_active = wr0 < rows_tile;
         const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks;
         const char *kgh = kg + (size_t)g * RBK;
-        const char *vgh = vg + (size_t)g * RBV;
+        const char *vgh = vg + (size_t)g * p.v_head_bytes;
 
         // Q^T operand and the visible limit of this lane's rows
         u32x4 qb[MB][KS];
@@ -470,11 +480,11 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW>())) v
                     }
 #pragma unroll
                     for (int nd = 0; nd < ND; ++nd) {
-                        const int off = 32 * kk * RBV + 32 * (nd & ~3);
+                        const int off = 32 * kk * RBVL + 32 * (nd & ~3);
                         const v4i16 b0 =
                             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off));
                         const v4i16 b1 =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off + 16 * RBV));
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off + 16 * RBVL));
                         const uint2 lo = __builtin_bit_cast(uint2, b0), hi = __builtin_bit_cast(uint2, b1);
                         u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
                         if (tail)
@@ -498,7 +508,9 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW>())) v
                 return (lds_u8 *)sK3;
         };
         auto vbuf = [&](auto st) __attribute__((always_inline)) -> lds_u8 * {
-            if constexpr (decltype(st)::value == 0)
+            if constexpr (SH)
+                return kbuf(st);
+            else if constexpr (decltype(st)::value == 0)
                 return (lds_u8 *)sV0;
             else if constexpr (decltype(st)::value == 1)
                 return (lds_u8 *)sV1;
@@ -526,17 +538,17 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW>())) v
         wait_vm<0>();
         __syncthreads();
         fetch_bids(c0);
-        issue(c0, (lds_u8 *)sK0, (lds_u8 *)sV0);
+        issue(c0, kbuf(std::integral_constant<int, 0>{}), vbuf(std::integral_constant<int, 0>{}));
         if constexpr (S > 2) {
             if (c0 + 1 < c1) {
                 fetch_bids(c0 + 1);
-                issue(c0 + 1, (lds_u8 *)sK1, (lds_u8 *)sV1);
+                issue(c0 + 1, kbuf(std::integral_constant<int, 1>{}), vbuf(std::integral_constant<int, 1>{}));
             }
         }
         if constexpr (S > 3) {
             if (c0 + 2 < c1) {
                 fetch_bids(c0 + 2);
-                issue(c0 + 2, (lds_u8 *)sK2, (lds_u8 *)sV2);
+                issue(c0 + 2, kbuf(std::integral_constant<int, 2>{}), vbuf(std::integral_constant<int, 2>{}));
             }
         }
         if (c0 + S - 1 < c1)
@@ -670,7 +682,7 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
     const int bs = p.block_size;
     const int bsh = p.bs_shift;
     const uint32_t rsk = (uint32_t)p.kv_head_num * RBK;
-    const uint32_t rsv = (uint32_t)p.kv_head_num * RBV;
+    const uint32_t rsv = p.v_row_bytes;
     const uint32_t nb32 = p.num_blocks < 0x7fffffff ? (uint32_t)p.num_blocks : 0x7fffffffu;
     const bool neg_scale = p.scale_log2 < 0.f;
     const float sc = fmaxf(fabsf(p.scale_log2), 1e-30f);   // scale 0: every visible token weighs 1
@@ -726,7 +738,7 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
         inblk = invis > 0 ? div_bs(invis - 1, bs, bsh) + 1 : 1;
         ibt = p.block_tables + (size_t)ic.b * p.max_blocks;
         ikg = kg + (size_t)ic.g * RBK;
-        ivg = vg + (size_t)ic.g * RBV;
+        ivg = vg + (size_t)ic.g * p.v_head_bytes;
     };
     iseg();
     int ibid[NTT];
@@ -1001,24 +1013,31 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
 // the streaming kernel (one wave, 16-token chunks, four stages).  1: up to
 // 64 rows.  2: more rows, two 16-row blocks per wave.  Dk = 576 has variant
 // 0 only: 8 waves, 64 rows per tile, two waves per row group splitting Dv,
-// 32-token chunks, two stages (137 KB of LDS).
+// 32-token chunks, two stages (137 KB of LDS); with a shared K/V cache only
+// K tiles are staged, which leaves room for MLA_SHARED_STAGES stages.
+constexpr int MLA_SHARED_STAGES = 4;
+
 struct TileShape {
     int mb, kt, nw, cs, s;   // nw: waves that own rows
     int threads;             // workgroup size
 };
 
-template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S>
+template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH = false>
 const void *pick(TileShape *t)
 {
     *t = TileShape{MB, KT, NW, CS, S, 64 * NW};
-    return (const void *)&tile_kernel<DT, DK, DV, MB, KT, NW, CS, S>;
+    return (const void *)&tile_kernel<DT, DK, DV, MB, KT, NW, CS, S, SH>;
 }
 
 template <int DT, int DK, int DV>
-const void *kernel_for(int variant, TileShape *t)
+const void *kernel_for(int variant, bool shared, TileShape *t)
 {
     if constexpr (DK > 256) {
-        return variant == 0 ? pick<DT, DK, DV, 1, 32, 8, 2, 2>(t) : nullptr;
+        if (variant != 0)
+            return nullptr;
+        if (shared)
+            return pick<DT, DK, DV, 1, 32, 8, 2, MLA_SHARED_STAGES, true>(t);
+        return pick<DT, DK, DV, 1, 32, 8, 2, 2>(t);
     } else {
         constexpr int KT = DK <= 128 ? 64 : 32;
         if (variant == 0) {   // one wave per workgroup, streaming across units
@@ -1034,22 +1053,22 @@ const void *kernel_for(int variant, TileShape *t)
 }
 
 template <int DT>
-const void *kernel_dt(int dk, int dv, int variant, TileShape *t)
+const void *kernel_dt(int dk, int dv, int variant, bool shared, TileShape *t)
 {
     if (dk == 64 && dv == 64)
-        return kernel_for<DT, 64, 64>(variant, t);
+        return kernel_for<DT, 64, 64>(variant, shared, t);
     if (dk == 128 && dv == 128)
-        return kernel_for<DT, 128, 128>(variant, t);
+        return kernel_for<DT, 128, 128>(variant, shared, t);
     if (dk == 256 && dv == 256)
-        return kernel_for<DT, 256, 256>(variant, t);
+        return kernel_for<DT, 256, 256>(variant, shared, t);
     if (dk == 576 && dv == 512)
-        return kernel_for<DT, 576, 512>(variant, t);
+        return kernel_for<DT, 576, 512>(variant, shared, t);
     return nullptr;
 }
 
-const void *tile_kernel_ptr(int dtype, int dk, int dv, int variant, TileShape *t)
+const void *tile_kernel_ptr(int dtype, int dk, int dv, int variant, bool shared, TileShape *t)
 {
-    return dtype == 0 ? kernel_dt<0>(dk, dv, variant, t) : kernel_dt<1>(dk, dv, variant, t);
+    return dtype == 0 ? kernel_dt<0>(dk, dv, variant, shared, t) : kernel_dt<1>(dk, dv, variant, shared, t);
 }
 
 }  // namespace
@@ -1057,31 +1076,31 @@ const void *tile_kernel_ptr(int dtype, int dk, int dv, int variant, TileShape *t
 bool tile_supported(int dk, int dv, int variant)
 {
     TileShape t;
-    return tile_kernel_ptr(0, dk, dv, variant, &t) != nullptr;
+    return tile_kernel_ptr(0, dk, dv, variant, false, &t) != nullptr;
 }
 
-int tile_chunk(int dk, int dv, int variant)
+int tile_chunk(int dk, int dv, int variant, bool shared)
 {
     TileShape t;
-    return tile_kernel_ptr(0, dk, dv, variant, &t) ? t.kt : 0;
+    return tile_kernel_ptr(0, dk, dv, variant, shared, &t) ? t.kt : 0;
 }
 
-int tile_rows(int dk, int dv, int variant)
+int tile_rows(int dk, int dv, int variant, bool shared)
 {
     TileShape t;
-    return tile_kernel_ptr(0, dk, dv, variant, &t) ? 16 * t.mb * (t.nw / t.cs) : 0;
+    return tile_kernel_ptr(0, dk, dv, variant, shared, &t) ? 16 * t.mb * (t.nw / t.cs) : 0;
 }
 
 bool tile_streaming(int dk, int dv, int variant)
 {
     TileShape t;
-    return tile_kernel_ptr(0, dk, dv, variant, &t) && t.nw == 1;
+    return tile_kernel_ptr(0, dk, dv, variant, false, &t) && t.nw == 1;
 }
 
-int tile_workers_per_cu(int dtype, int dk, int dv, int variant)
+int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared)
 {
     TileShape t;
-    const void *k = tile_kernel_ptr(dtype, dk, dv, variant, &t);
+    const void *k = tile_kernel_ptr(dtype, dk, dv, variant, shared, &t);
     int n = 0;
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, t.threads, 0) != hipSuccess || n < 1)
         return 1;
@@ -1091,7 +1110,7 @@ int tile_workers_per_cu(int dtype, int dk, int dv, int variant)
 hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s)
 {
     TileShape t;
-    const void *k = tile_kernel_ptr(dtype, p.head_size_k, p.head_size_v, variant, &t);
+    const void *k = tile_kernel_ptr(dtype, p.head_size_k, p.head_size_v, variant, p.shared_kv != 0, &t);
     if (!k)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&p};

@@ -75,7 +75,8 @@ def test_config_struct_matches_header():
     dict(num_blocks=0), dict(max_batch=0), dict(max_num_blocks_per_seq=0), dict(max_q_seq_len=0),
     dict(dtype=7), dict(mask=3), dict(scale=float("inf")), dict(scale=float("nan")),
     dict(num_partitions=-1), dict(flags=binding.PA_FLAG_FORCE_VALU | binding.PA_FLAG_FORCE_MFMA),
-    dict(flags=64), dict(flags=8),
+    dict(flags=64), dict(flags=16),
+    dict(flags=binding.PA_FLAG_SHARED_KV, head_size_k=64, head_size_v=128),
 ])
 def test_create_rejects_invalid(lib, bad):
     assert create_status(lib, good_cfg(**bad)) == binding.PA_ERR_INVALID_ARG

@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
 
 Small problems are compared element by element; they span several chunks,
-several row tiles and ragged tails.  The five named workloads are compared at
+several row tiles and ragged tails.  The six named workloads are compared at
 full size on sampled rows, with the launch configuration the benchmark uses.
 Probes check gathering, masking and poison handling bit for bit."""
 import math
@@ -141,6 +141,77 @@ def test_mla_shape_f16_causal_small():
     log("mla causal")
     p = synth.custom([300, 70], 16, 1, 576, 512, 64, "f16", "causal", q_seq_lens=[5, 2], seed=15)
     check_full(p, what="mla causal")
+
+
+# ------------------------------------------------------- shared K/V cache
+SHARED_CASES = [
+    # (lens, H, Hkv, Dk, Dv, bs, dtype, mask, q_seq_lens)
+    ([1500, 77, 640, 33], 64, 1, 576, 512, 128, "bf16", "none", None),   # MLA decode: V from the K tile in LDS
+    ([300, 70], 16, 1, 576, 512, 64, "f16", "causal", [5, 2]),            # MLA, parallel decoding
+    ([700, 129, 2050, 5], 32, 8, 128, 128, 128, "bf16", "none", None),    # streaming kernel, V = K
+    ([80, 300], 8, 2, 64, 64, 16, "f16", "causal", [40, 100]),            # 400-row units (two blocks per wave)
+    ([90, 33], 8, 4, 64, 64, 32, "f16", "causal", [9, 12]),               # 24-48 row units
+]
+
+
+@pytest.mark.parametrize("case", SHARED_CASES, ids=lambda c: f"D{c[3]}_{c[4]}_H{c[1]}_{c[7]}")
+def test_shared_kv_parity(case):
+    """One cache for K and V (V = leading Dv elements of each K row): parity
+    with the oracle, and bit-identity with the same problem given V as its
+    own tensor cut from K (one worker per unit, so both runs add in the same
+    order)."""
+    lens, H, Hkv, Dk, Dv, bs, dt, mask, ql = case
+    log(f"shared kv {case}")
+    p = synth.custom(lens, H, Hkv, Dk, Dv, bs, dt, mask, q_seq_lens=ql, seed=40 + Dk, shared_kv=True)
+    assert p.value_cache is None
+    check_full(p, what=f"shared {case}")
+    shared_ns, shared_l, _ = run_hip(to_device(p), flags=F.PA_FLAG_NO_SPLIT)
+    p2 = synth.Problem(**{**p.__dict__})
+    p2.workload = synth.Workload(**{**p.workload.__dict__, "shared_kv": False})
+    p2.value_cache = p.key_cache[..., :Dv].contiguous()
+    sep_ns, sep_l, _ = run_hip(to_device(p2), flags=F.PA_FLAG_NO_SPLIT)
+    assert np.array_equal(shared_ns, sep_ns) and np.array_equal(shared_l, sep_l)
+    if Dk == Dv and mask == "none" and H // Hkv <= 8:
+        check_full(p, flags=F.PA_FLAG_FORCE_VALU, what=f"shared valu {case}")
+
+
+def test_shared_kv_poison_and_arguments():
+    """Shared K/V: NaN in K rows past each context and in unreferenced blocks
+    leaves the output bit-identical; a value_cache other than NULL or the key
+    cache is refused before any launch."""
+    log("shared kv poison")
+    p = synth.custom([70, 200, 129], 16, 1, 576, 512, 64, "bf16", seed=47, max_blocks=8, shared_kv=True)
+    pd = to_device(p)
+    clean, _, att = run_hip(pd)
+    assert att.describe()["path"] == "mfma"
+    bs = 64
+    used = set()
+    for b in range(p.batch):
+        n = int(p.context_lens_np[b])
+        nb = (n + bs - 1) // bs
+        used.update(p.block_tables_np[b, :nb].tolist())
+        if n % bs:
+            p.key_cache[int(p.block_tables_np[b, nb - 1]), n % bs:] = float("nan")
+        p.block_tables_np[b, nb:] = -1
+    for blk in range(p.num_blocks):
+        if blk not in used:
+            p.key_cache[blk] = float("nan")
+    dirty, _, _ = run_hip(to_device(p))
+    assert np.array_equal(clean, dirty)
+    # the same key cache object as value_cache is accepted, another tensor is not
+    o1 = att.forward(pd.query, pd.key_cache, pd.key_cache, pd.block_tables, pd.context_lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(o1.to(torch.float64).cpu().numpy(), clean)
+    other = pd.key_cache[..., :512].contiguous()
+    with pytest.raises(ValueError):
+        att.forward(pd.query, pd.key_cache, other, pd.block_tables, pd.context_lens)
+    lib = binding.load_library()
+    out = torch.empty((p.batch, 16, 512), dtype=pd.query.dtype, device="cuda")
+    st = lib.pa_forward(att.handle, pd.query.data_ptr(), pd.key_cache.data_ptr(), other.data_ptr(),
+                        pd.block_tables.data_ptr(), pd.context_lens.data_ptr(), None, p.batch, p.batch, 1,
+                        out.data_ptr(), None, None)
+    assert st == binding.PA_ERR_INVALID_ARG
+    assert att.device_error() == 0
 
 
 # ------------------------------------------------------------------ probes
@@ -321,7 +392,8 @@ def full_size_sampled(n, rows, seed=0):
     assert_lse_close(l[toks, heads], rl, w.name)
     # properties that hold at any size: finite everywhere, |o| <= max |V|
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
-    vmax = float(p.value_cache.abs().max())
+    vsrc = p.key_cache[..., :w.head_size_v] if w.shared_kv else p.value_cache
+    vmax = float(vsrc.abs().max())
     assert np.abs(o).max() <= vmax * (1 + 1e-2)
     log(f"workload {w.name}: max err {e:.2e}")
     return p, o, l
@@ -361,3 +433,7 @@ def test_workload_splitfuse_causal_sampled():
 
 def test_workload_mla_decode_sampled():
     full_size_sampled(5, 128, seed=3)
+
+
+def test_workload_mla_shared_kv_decode_sampled():
+    full_size_sampled(6, 128, seed=4)
