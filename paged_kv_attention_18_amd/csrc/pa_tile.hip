@@ -16,8 +16,9 @@
 //          ring of S stages, S - 1 chunks ahead of the one computed.  Each
 //          lane picks the global 16-byte piece that lands at its LDS slot,
 //          which realises an XOR swizzle of the pieces within a row (K:
-//          piece ^ (row & 7); V: piece ^ 2(row & 3)), so the operand reads
-//          below are free of bank conflicts.  A block id out of range reads
+//          piece ^ (row & 7); V: piece ^ 2(row & 7), or ^ (row & 7) for
+//          128-byte rows), so the operand reads below are free of bank
+//          conflicts.  A block id out of range reads
 //          a zero page (and is flagged); rows past the visible range are
 //          masked (P = 0, and their V operand halves are zeroed).
 //   S^T    = K . Q^T with v_mfma_f32_16x16x32_{f16,bf16}: K is the A operand
@@ -147,6 +148,23 @@ __device__ __forceinline__ void wait_ahead(int ahead)
     }
 }
 
+// XOR swizzle of the 16-byte pieces of V tile row r.  The PV operand is
+// read with ds_read_b64_tr_b16, whose 32-lane passes touch pieces 2 nd and
+// 2 nd + 1 of rows 8 i .. 8 i + 7; the swizzle spreads those 16 pieces over
+// all 64 banks: rows of a multiple of 256 bytes move by 2 (r % 8) pieces,
+// 128-byte rows (which alternate between the two bank halves) by r % 8.
+template <int RB>
+__device__ __forceinline__ int v_swz(int r)
+{
+    return RB % 256 == 0 ? 2 * (r & 7) : (r & 7);
+}
+// Per-lane read offsets the swizzle needs: one per nd % NVO.
+template <int RB>
+constexpr int v_offsets()
+{
+    return RB % 256 == 0 ? 8 : 4;
+}
+
 // Workgroups per CU the register budget is cut for: as many as fit in LDS
 // (at most 4; at most 2 with two 16-row blocks per wave, 1 at head sizes
 // above 128).  SH: no V tiles in LDS.
@@ -254,7 +272,7 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
     for (int m = 0; m < MV; ++m) {
         const int x = (wave + NW * m) * 1024 + 16 * lane;
         const int row = x / RBV;
-        voV[m] = (wave + NW * m) < IPGV ? row * rsv + 16 * (((x % RBV) >> 4) ^ (2 * (row & 3))) : 16 * lane;
+        voV[m] = (wave + NW * m) < IPGV ? row * rsv + 16 * (((x % RBV) >> 4) ^ v_swz<RBV>(row)) : 16 * lane;
     }
     // LDS read offsets.  K (A operand): row 16 n + lr, piece 4 ks + lg, which
     // the swizzle moves by +-64 bytes depending on bit 2 of the row.
@@ -263,12 +281,15 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
     const int koE = lr * RBK + kq + kb2, koO = lr * RBK + kq - kb2;
     // V (B operand, transposing read): row 4 lg + lr / 4 (+ 16 n),
     // columns col0 + 16 nd + 4 (lr % 4) .. + 3, i.e. 16-byte piece
-    // col0 / 8 + 2 nd + (lr % 4) / 2 of the row, moved by the tile's swizzle.
-    int vo[4];
+    // col0 / 8 + 2 nd + (lr % 4) / 2 of the row, moved by the tile's swizzle
+    // (the K swizzle when V is read from the K tile).  Column tile nd reads
+    // at vo[nd % NVO] + (nd / NVO) NVO 32 bytes.
+    constexpr int NVO = SH ? 4 : v_offsets<RBV>();
+    int vo[NVO];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < NVO; ++m) {
         const int vrow = 4 * lg + (lr >> 2);
-        const int vpiece = SH ? ((2 * m + ((lr & 3) >> 1)) ^ (vrow & 7)) : (2 * (m ^ (lr >> 2)) + ((lr & 3) >> 1));
+        const int vpiece = (2 * m + ((lr & 3) >> 1)) ^ (SH ? (vrow & 7) : v_swz<RBV>(vrow));
         vo[m] = vrow * RBVL + 16 * vpiece + 8 * (lr & 1) + 2 * col0;
     }
 
@@ -448,7 +469,7 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
 #pragma unroll
                 for (int nd = 0; nd < ND; ++nd) {
                     const v4i16 b0 =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + 32 * (nd & ~3)));
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + 32 * NVO * (nd / NVO)));
                     uint2 bv = __builtin_bit_cast(uint2, b0);
                     if (tail) {
                         bv.x &= vm.x;
@@ -480,11 +501,11 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
                     }
 #pragma unroll
                     for (int nd = 0; nd < ND; ++nd) {
-                        const int off = 32 * kk * RBVL + 32 * (nd & ~3);
+                        const int off = 32 * kk * RBVL + 32 * NVO * (nd / NVO);
                         const v4i16 b0 =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off));
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + off));
                         const v4i16 b1 =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off + 16 * RBVL));
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + off + 16 * RBVL));
                         const uint2 lo = __builtin_bit_cast(uint2, b0), hi = __builtin_bit_cast(uint2, b1);
                         u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
                         if (tail)
@@ -705,16 +726,19 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
     for (int m = 0; m < IPGV; ++m) {
         const int x = m * 1024 + 16 * lane;
         const int row = x / RBV;
-        voV[m] = row * rsv + 16 * (((x % RBV) >> 4) ^ (2 * (row & 3)));
+        voV[m] = row * rsv + 16 * (((x % RBV) >> 4) ^ v_swz<RBV>(row));
     }
     // LDS read offsets (K and Q: row lr, piece 4 ks + lg; V: transposing read)
     const int kq = 16 * (lg ^ (lr & 3));
     const int kb2 = 64 * ((lr >> 2) & 1);
     const int koE = lr * RBK + kq + kb2, koO = lr * RBK + kq - kb2;
-    int vo[4];
+    constexpr int NVO = v_offsets<RBV>();
+    int vo[NVO];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-        vo[m] = (4 * lg + (lr >> 2)) * RBV + 32 * (m ^ (lr >> 2)) + 16 * ((lr & 3) >> 1) + 8 * (lr & 1);
+    for (int m = 0; m < NVO; ++m) {
+        const int vrow = 4 * lg + (lr >> 2);
+        vo[m] = vrow * RBV + 16 * ((2 * m + ((lr & 3) >> 1)) ^ v_swz<RBV>(vrow)) + 8 * (lr & 1);
+    }
 
     // ------------------------------------------------------------ issue side
     int ipiece = worker;
@@ -931,7 +955,8 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
             }
 #pragma unroll
             for (int nd = 0; nd < ND; ++nd) {
-                const v4i16 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + 32 * (nd & ~3)));
+                const v4i16 b0 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + 32 * NVO * (nd / NVO)));
                 uint2 bv = __builtin_bit_cast(uint2, b0);
                 if (tail) {
                     bv.x &= vm.x;
@@ -954,10 +979,10 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
             }
 #pragma unroll
             for (int nd = 0; nd < ND; ++nd) {
-                const int off = 32 * (nd & ~3);
-                const v4i16 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off));
+                const int off = 32 * NVO * (nd / NVO);
+                const v4i16 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + off));
                 const v4i16 b1 =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd & 3] + off + 16 * RBV));
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + off + 16 * RBV));
                 const uint2 lo = __builtin_bit_cast(uint2, b0), hi = __builtin_bit_cast(uint2, b1);
                 u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
                 if (tail)
