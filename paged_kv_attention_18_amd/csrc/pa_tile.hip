@@ -1037,10 +1037,10 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
 // Variants per (Dk, Dv).  0: units of at most 16 rows (decode), memory-bound:
 // the streaming kernel (one wave, 16-token chunks, four stages).  1: up to
 // 64 rows.  2: more rows, two 16-row blocks per wave.  Dk = 576 has variant
-// 0 only: 8 waves, 64 rows per tile, two waves per row group splitting Dv,
-// 32-token chunks, two stages (137 KB of LDS); with a shared K/V cache only
-// K tiles are staged, which leaves room for MLA_SHARED_STAGES stages.
-constexpr int MLA_SHARED_STAGES = 4;
+// 0 only: 4 waves of 16 rows each own all 512 output columns (no duplicated
+// K . Q^T work), two workgroups per CU: 16-token chunks in two stages (69 KB
+// of LDS), or with a shared K/V cache, where only K tiles are staged,
+// 32-token chunks in two stages (74 KB).
 
 struct TileShape {
     int mb, kt, nw, cs, s;   // nw: waves that own rows
@@ -1061,8 +1061,8 @@ const void *kernel_for(int variant, bool shared, TileShape *t)
         if (variant != 0)
             return nullptr;
         if (shared)
-            return pick<DT, DK, DV, 1, 32, 8, 2, MLA_SHARED_STAGES, true>(t);
-        return pick<DT, DK, DV, 1, 32, 8, 2, 2>(t);
+            return pick<DT, DK, DV, 1, 32, 4, 1, 2, true>(t);
+        return pick<DT, DK, DV, 1, 16, 4, 1, 2>(t);
     } else {
         constexpr int KT = DK <= 128 ? 64 : 32;
         if (variant == 0) {   // one wave per workgroup, streaming across units

@@ -158,19 +158,25 @@ SHARED_CASES = [
 def test_shared_kv_parity(case):
     """One cache for K and V (V = leading Dv elements of each K row): parity
     with the oracle, and bit-identity with the same problem given V as its
-    own tensor cut from K (one worker per unit, so both runs add in the same
-    order)."""
+    own tensor cut from K when both kernels take the same chunk size (one
+    worker per unit, so both runs add in the same order)."""
     lens, H, Hkv, Dk, Dv, bs, dt, mask, ql = case
     log(f"shared kv {case}")
     p = synth.custom(lens, H, Hkv, Dk, Dv, bs, dt, mask, q_seq_lens=ql, seed=40 + Dk, shared_kv=True)
     assert p.value_cache is None
     check_full(p, what=f"shared {case}")
-    shared_ns, shared_l, _ = run_hip(to_device(p), flags=F.PA_FLAG_NO_SPLIT)
+    shared_ns, shared_l, att_s = run_hip(to_device(p), flags=F.PA_FLAG_NO_SPLIT)
     p2 = synth.Problem(**{**p.__dict__})
     p2.workload = synth.Workload(**{**p.workload.__dict__, "shared_kv": False})
     p2.value_cache = p.key_cache[..., :Dv].contiguous()
-    sep_ns, sep_l, _ = run_hip(to_device(p2), flags=F.PA_FLAG_NO_SPLIT)
-    assert np.array_equal(shared_ns, sep_ns) and np.array_equal(shared_l, sep_l)
+    sep_ns, sep_l, att_v = run_hip(to_device(p2), flags=F.PA_FLAG_NO_SPLIT)
+    if att_s.describe()["tokens_per_chunk"] == att_v.describe()["tokens_per_chunk"]:
+        assert np.array_equal(shared_ns, sep_ns) and np.array_equal(shared_l, sep_l)
+    else:   # another summation order: both within the tolerance of the oracle's result
+        ref_o, ref_l = oracle_full(p)
+        assert_close(shared_ns, ref_o, dt, "shared no-split")
+        assert_close(sep_ns, ref_o, dt, "separate no-split")
+        assert_lse_close(shared_l, ref_l, "shared no-split")
     if Dk == Dv and mask == "none" and H // Hkv <= 8:
         check_full(p, flags=F.PA_FLAG_FORCE_VALU, what=f"shared valu {case}")
 
