@@ -39,6 +39,14 @@
  *    row i sees tokens j <= prefix + i (PagedAttention Constraints, mask
  *    type 5 list).  Invisible tokens get weight exactly 0; with the pages'
  *    suggested fill of -10000 the additive form underflows to the same 0.
+ *  - Mask "band" (mask mode 4 of the SparseAttnSharedkvMetadata README,
+ *    parameter table, with win_left past tokens and win_right future tokens
+ *    per query; the page fixes 127 and 0): the query row i sits at position
+ *    prefix + i of its sequence, aligned as in the causal rule, and sees
+ *    tokens prefix + i - win_left <= j <= prefix + i + win_right, j < kv.
+ *    win_left counts the tokens before the query's own position, which is
+ *    itself visible (the page is silent on the query's own token; this is
+ *    the plain reading of a count of past tokens).
  *  - Query/output rows are packed (TND): sequence b's rows start at
  *    t0 = q_seq_lens[0] + ... + q_seq_lens[b-1], the prefix-sum convention of
  *    cu_seqlens_q (SparseAttnSharedkvMetadata README, parameter table).
@@ -52,7 +60,7 @@
 #include <string.h>
 
 enum { REF_F16 = 0, REF_BF16 = 1 };
-enum { REF_MASK_NONE = 0, REF_MASK_CAUSAL = 1 };
+enum { REF_MASK_NONE = 0, REF_MASK_CAUSAL = 1, REF_MASK_BAND = 2 };
 enum { REF_OK = 0, REF_BAD_ARG = -1, REF_BAD_BLOCK = -2, REF_BAD_LEN = -3, REF_NO_MEM = -4 };
 
 /* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
@@ -93,6 +101,7 @@ typedef struct {
     int64_t num_blocks;
     int32_t dtype, mask;
     double scale;
+    int32_t win_left, win_right;   /* band mask only */
     int64_t *row_start;  /* [batch + 1]: first packed query row of each sequence */
 } problem;
 
@@ -108,16 +117,26 @@ static int one_row(const problem *P, int b, int i, int h, double *z, double *o, 
     const int qlen = P->q_seq_lens ? P->q_seq_lens[b] : 1;
     const int kv = P->context_lens[b];
     const int prefix = kv - qlen > 0 ? kv - qlen : 0;
-    int n = kv;
-    if (P->mask == REF_MASK_CAUSAL && prefix + i + 1 < n)
-        n = prefix + i + 1;
+    /* the visible tokens are lo, lo + 1, ..., hi - 1 */
+    int64_t lo = 0, hi = kv;
+    if (P->mask == REF_MASK_CAUSAL && prefix + i + 1 < hi)
+        hi = prefix + i + 1;
+    if (P->mask == REF_MASK_BAND) {
+        const int64_t pos = (int64_t)prefix + i;    /* the query's own position */
+        if (pos - P->win_left > lo)
+            lo = pos - P->win_left;
+        if (pos + 1 + P->win_right < hi)
+            hi = pos + 1 + P->win_right;
+    }
+    const int n = hi > lo ? (int)(hi - lo) : 0;
 
     const uint16_t *q = P->query + (t * H + h) * (int64_t)Dk;
     for (int j = 0; j < n; ++j) {
-        int32_t phys = P->block_tables[(int64_t)b * P->max_num_blocks_per_seq + j / bs];
+        const int tok = (int)lo + j;
+        int32_t phys = P->block_tables[(int64_t)b * P->max_num_blocks_per_seq + tok / bs];
         if (phys < 0 || phys >= P->num_blocks)
             return REF_BAD_BLOCK;
-        int slot = j % bs;
+        int slot = tok % bs;
         const int64_t krow = (((int64_t)phys * bs + slot) * Hkv + g) * Dk;
         double dot = 0.0;
         for (int d = 0; d < Dk; ++d)
@@ -150,8 +169,9 @@ static int one_row(const problem *P, int b, int i, int h, double *z, double *o, 
     const uint16_t *vsrc = P->value_cache ? P->value_cache : P->key_cache;
     const int vstride = P->value_cache ? Dv : Dk;
     for (int j = 0; j < n; ++j) {
-        int32_t phys = P->block_tables[(int64_t)b * P->max_num_blocks_per_seq + j / bs];
-        int slot = j % bs;
+        const int tok = (int)lo + j;
+        int32_t phys = P->block_tables[(int64_t)b * P->max_num_blocks_per_seq + tok / bs];
+        int slot = tok % bs;
         const int64_t vrow = (((int64_t)phys * bs + slot) * Hkv + g) * vstride;
         for (int e = 0; e < Dv; ++e)
             o[e] += z[j] * elem(vsrc, vrow + e, P->dtype);
@@ -253,7 +273,8 @@ static int setup(problem *P)
         P->head_size_v <= 0 || P->block_size <= 0 || P->max_num_blocks_per_seq < 0 ||
         P->num_blocks < 0 || P->head_num % P->kv_head_num != 0 ||
         (P->dtype != REF_F16 && P->dtype != REF_BF16) ||
-        (P->mask != REF_MASK_NONE && P->mask != REF_MASK_CAUSAL))
+        (P->mask != REF_MASK_NONE && P->mask != REF_MASK_CAUSAL && P->mask != REF_MASK_BAND) ||
+        P->win_left < 0 || P->win_right < 0)
         return REF_BAD_ARG;
     P->row_start = (int64_t *)malloc(sizeof(int64_t) * (size_t)(P->batch + 1));
     if (!P->row_start)
@@ -281,7 +302,8 @@ static int setup(problem *P)
         const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_seq_lens,   \
         int32_t batch, int32_t num_q_tokens, int32_t head_num, int32_t kv_head_num,            \
         int32_t head_size_k, int32_t head_size_v, int32_t block_size, int64_t num_blocks,      \
-        int32_t max_num_blocks_per_seq, int32_t dtype, int32_t mask, double scale
+        int32_t max_num_blocks_per_seq, int32_t dtype, int32_t mask, double scale,            \
+        int32_t win_left, int32_t win_right
 
 #define FILL_PROBLEM(P)                                                                        \
     do {                                                                                       \
@@ -294,6 +316,7 @@ static int setup(problem *P)
         (P).block_size = block_size; (P).num_blocks = num_blocks;                              \
         (P).max_num_blocks_per_seq = max_num_blocks_per_seq; (P).dtype = dtype;                \
         (P).mask = mask; (P).scale = scale;                                                    \
+        (P).win_left = win_left; (P).win_right = win_right;                                    \
     } while (0)
 
 /*

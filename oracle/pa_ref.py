@@ -20,7 +20,7 @@ SRC = os.path.join(HERE, "pa_ref.c")
 LIB = os.path.join(HERE, "libpa_ref.so")
 
 F16, BF16 = 0, 1
-MASK_NONE, MASK_CAUSAL = 0, 1
+MASK_NONE, MASK_CAUSAL, MASK_BAND = 0, 1, 2
 ERRORS = {-1: "bad argument", -2: "block id out of range", -3: "bad lengths", -4: "out of memory"}
 
 _lock = threading.Lock()
@@ -45,7 +45,7 @@ def load(path=None):
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
-        common = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i64, i32, i32, i32, f64]
+        common = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i64, i32, i32, i32, f64, i32, i32]
         lib.pa_ref_forward.argtypes = common + [P, P, ctypes.c_int]
         lib.pa_ref_forward.restype = ctypes.c_int
         lib.pa_ref_rows.argtypes = common + [i64, P, P, P, P, ctypes.c_int]
@@ -66,7 +66,7 @@ class Inputs:
     raw uint16 bit patterns, lengths and tables as int32."""
 
     def __init__(self, query, key_cache, value_cache, block_tables, context_lens, q_seq_lens,
-                 head_num, kv_head_num, dtype, mask, scale, head_size_v=None):
+                 head_num, kv_head_num, dtype, mask, scale, head_size_v=None, window=(0, 0)):
         self.query = _bits(query)
         self.key_cache = _bits(key_cache)
         # value_cache None: the V row of a token is the first head_size_v
@@ -79,15 +79,18 @@ class Inputs:
         self.head_num = int(head_num)
         self.kv_head_num = int(kv_head_num)
         self.dtype = {"f16": F16, "bf16": BF16}.get(dtype, dtype)
-        self.mask = {"none": MASK_NONE, "causal": MASK_CAUSAL}.get(mask, mask)
+        self.mask = {"none": MASK_NONE, "causal": MASK_CAUSAL, "band": MASK_BAND}.get(mask, mask)
         self.scale = float(scale)
+        # band mask: (tokens before the query's position, tokens after it)
+        self.win_left, self.win_right = int(window[0]), int(window[1])
 
     @classmethod
     def from_problem(cls, p):
         """From a ``synth.Problem`` (tensors are copied to the host)."""
         w = p.workload
         return cls(p.query, p.key_cache, p.value_cache, p.block_tables_np, p.context_lens_np,
-                   p.q_seq_lens_np, w.head_num, w.kv_head_num, w.dtype, w.mask, w.scale, w.head_size_v)
+                   p.q_seq_lens_np, w.head_num, w.kv_head_num, w.dtype, w.mask, w.scale, w.head_size_v,
+                   (w.window_left, w.window_right))
 
     @property
     def batch(self):
@@ -104,7 +107,8 @@ class Inputs:
         ptr = lambda a: None if a is None else a.ctypes.data
         return [ptr(self.query), ptr(self.key_cache), ptr(self.value_cache), ptr(self.block_tables),
                 ptr(self.context_lens), ptr(self.q_seq_lens), self.batch, self.num_q_tokens,
-                self.head_num, self.kv_head_num, dk, dv, bs, nb, mb, self.dtype, self.mask, self.scale]
+                self.head_num, self.kv_head_num, dk, dv, bs, nb, mb, self.dtype, self.mask, self.scale,
+                self.win_left, self.win_right]
 
 
 def _bits(t):

@@ -43,13 +43,15 @@ class Workload:
     head_size_v: int
     block_size: int
     dtype: str                 # "f16" | "bf16"
-    mask: str                  # "none" | "causal"
+    mask: str                  # "none" | "causal" | "band"
     scale: float
     lengths: Callable          # rng -> (context_lens int32[B], q_seq_lens int32[B] or None)
     num_blocks: Optional[int] = None   # fixed pool size; None -> used blocks + slack
     slack: float = 0.10
     seed: int = 0
     shared_kv: bool = False    # V rows are the first head_size_v elements of the K rows
+    window_left: int = 0       # band mask: tokens before the query's position it sees
+    window_right: int = 0      # band mask: tokens after it
 
 
 def _tiny_lengths(rng):
@@ -143,6 +145,18 @@ class Problem:
     def kv_tokens(self) -> int:
         return int(self.context_lens_np.astype(np.int64).sum())
 
+    def read_tokens(self) -> int:
+        """Tokens some row of their sequence sees, summed over sequences: all
+        of them, except under a band mask, whose rows (at positions
+        prefix .. kv - 1) see nothing before prefix - window_left."""
+        kv = self.context_lens_np.astype(np.int64)
+        w = self.workload
+        if w.mask != "band":
+            return int(kv.sum())
+        ql = np.ones_like(kv) if self.q_seq_lens_np is None else self.q_seq_lens_np.astype(np.int64)
+        lo = np.maximum(0, np.maximum(0, kv - ql) - w.window_left)
+        return int(np.maximum(0, kv - lo).sum())
+
 
 def _normal(shape, dtype, seed, device, chunk_elems=1 << 26):
     """float32 N(0,1) from a seeded torch generator, rounded to ``dtype``."""
@@ -212,20 +226,22 @@ def generate(w: Workload, device="cpu", seed: Optional[int] = None, values=True,
 
 def custom(batch_lens, head_num, kv_head_num, head_size_k, head_size_v, block_size,
            dtype="f16", mask="none", scale=None, q_seq_lens=None, num_blocks=None,
-           slack=0.25, seed=7, name="custom", device="cpu", max_blocks=None, shared_kv=False) -> Problem:
+           slack=0.25, seed=7, name="custom", device="cpu", max_blocks=None, shared_kv=False,
+           window=(0, 0)) -> Problem:
     """A small hand-shaped problem (tests)."""
     if scale is None:
         scale = 1.0 / math.sqrt(head_size_k)
     w = Workload(name, len(batch_lens), head_num, kv_head_num, head_size_k, head_size_v,
                  block_size, dtype, mask, float(scale), fixed_lengths(batch_lens, q_seq_lens),
-                 num_blocks=num_blocks, slack=slack, seed=seed, shared_kv=shared_kv)
+                 num_blocks=num_blocks, slack=slack, seed=seed, shared_kv=shared_kv,
+                 window_left=int(window[0]), window_right=int(window[1]))
     return generate(w, device=device, max_blocks=max_blocks)
 
 
 def kv_bytes(p: Problem) -> int:
-    """Key+value bytes the method must read: each visible (sequence, KV head,
-    token) row once, K and V head sizes at 2 bytes per element (only the K
-    row when V lives inside it)."""
+    """Key+value bytes the method must read: each (sequence, KV head, token)
+    row that some query row sees, once, K and V head sizes at 2 bytes per
+    element (only the K row when V lives inside it)."""
     w = p.workload
     per_row = w.head_size_k if w.shared_kv else w.head_size_k + w.head_size_v
-    return p.kv_tokens() * w.kv_head_num * per_row * 2
+    return p.read_tokens() * w.kv_head_num * per_row * 2

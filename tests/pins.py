@@ -406,4 +406,98 @@ def pin_shared_kv_is_sliced_v(lib):
         raise AssertionError("Dv > Dk with V inside K accepted")
 
 
+def band_cases():
+    """Band-mask problems: decode with the pages' window (127 past tokens, 0
+    future), and several query tokens with a window reaching forward too."""
+    yield synth.custom([300, 17, 128, 129, 1000], 8, 2, 64, 64, 16, "f16", "band", seed=140, window=(127, 0))
+    yield synth.custom([200, 70, 33], 4, 1, 32, 48, 16, "bf16", "band", q_seq_lens=[40, 5, 33], seed=141,
+                       window=(20, 3))
+
+
+def _with_mask(p, mask, window=(0, 0)):
+    q = synth.Problem(**{**p.__dict__})
+    q.workload = synth.Workload(**{**p.workload.__dict__, "mask": mask, "window_left": window[0],
+                                   "window_right": window[1]})
+    return q
+
+
+def pin_band_extremes_are_causal_and_none(lib):
+    """A band reaching back past every sequence start is the causal mask when
+    it reaches no token ahead, and no mask at all when it also reaches past
+    every sequence end (bit for bit)."""
+    for p in band_cases():
+        o_c, l_c = run(lib, _with_mask(p, "causal"))
+        o_b, l_b = run(lib, _with_mask(p, "band", (10 ** 6, 0)))
+        assert np.array_equal(o_c, o_b) and np.array_equal(l_c, l_b)
+        o_n, l_n = run(lib, _with_mask(p, "none"))
+        o_b, l_b = run(lib, _with_mask(p, "band", (10 ** 6, 10 ** 6)))
+        assert np.array_equal(o_n, o_b) and np.array_equal(l_n, l_b)
+
+
+def _window_problem(p, b, lo, hi, query):
+    """One sequence holding only tokens lo .. hi - 1 of sequence b of p,
+    copied into fresh blocks with torch indexing, no mask, one query row."""
+    w = p.workload
+    n = hi - lo
+    bs = w.block_size
+    nblk = max(1, (n + bs - 1) // bs)
+    kc = gather_contiguous(p, b, p.key_cache)[lo:hi]
+    vsrc = p.key_cache[..., :w.head_size_v] if w.shared_kv else p.value_cache
+    vc = gather_contiguous(p, b, vsrc)[lo:hi]
+    def pack(rows):
+        out = torch.zeros(nblk * bs, rows.shape[1], rows.shape[2], dtype=rows.dtype)
+        out[:n] = rows
+        return out.reshape(nblk, bs, rows.shape[1], rows.shape[2])
+    d = synth.Problem(**{**p.__dict__})
+    d.workload = synth.Workload(**{**w.__dict__, "mask": "none", "shared_kv": False})
+    d.key_cache, d.value_cache = pack(kc), pack(vc)
+    d.num_blocks = nblk
+    d.block_tables_np = np.arange(nblk, dtype=np.int32)[None, :]
+    d.max_num_blocks_per_seq = nblk
+    d.context_lens_np = np.array([n], np.int32)
+    d.q_seq_lens_np = None
+    d.query = query
+    return d
+
+
+def pin_band_row_is_window_attention(lib):
+    """Row i of sequence b under the band mask is attention without a mask
+    over just the tokens of its window, copied out of the paged cache:
+    positions prefix + i - win_left .. prefix + i + win_right, cut to the
+    sequence (bit for bit)."""
+    for p in band_cases():
+        o, l = run(lib, p)
+        w = p.workload
+        ql = np.ones(p.batch, np.int64) if p.q_seq_lens_np is None else p.q_seq_lens_np.astype(np.int64)
+        t0 = 0
+        for b in range(p.batch):
+            kv = int(p.context_lens_np[b])
+            prefix = max(0, kv - int(ql[b]))
+            for i in range(int(ql[b])):
+                pos = prefix + i
+                lo, hi = max(0, pos - w.window_left), min(kv, pos + 1 + w.window_right)
+                d = _window_problem(p, b, lo, hi, p.query[t0 + i:t0 + i + 1])
+                od, ld = run(lib, d)
+                assert np.array_equal(od[0], o[t0 + i]) and np.array_equal(ld[0], l[t0 + i]), (b, i)
+            t0 += int(ql[b])
+
+
+def pin_band_lse_counts_window(lib):
+    """q = 0 makes every score 0, so exp(lse) counts the visible tokens: the
+    window's size, min(kv, pos + 1 + right) - max(0, pos - left)."""
+    for p in band_cases():
+        p.query.zero_()
+        _, l = run(lib, p)
+        w = p.workload
+        ql = np.ones(p.batch, np.int64) if p.q_seq_lens_np is None else p.q_seq_lens_np.astype(np.int64)
+        t0 = 0
+        for b in range(p.batch):
+            kv = int(p.context_lens_np[b])
+            for i in range(int(ql[b])):
+                pos = max(0, kv - int(ql[b])) + i
+                count = min(kv, pos + 1 + w.window_right) - max(0, pos - w.window_left)
+                assert np.all(np.rint(np.exp(l[t0 + i])) == count), (b, i)
+            t0 += int(ql[b])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -9,15 +9,23 @@ import pytest
 import pins
 from oracle import pa_ref
 
-# (name, exact snippet in pa_ref.c, mistaken replacement)
+# (name, exact snippet in pa_ref.c, mistaken replacement).  Every mutant keeps
+# the oracle's reads inside its buffers (a mistake that reads out of bounds
+# would crash the test process rather than fail a pin).
 MUTANTS = [
     ("gqa_modulo", "const int g = h / group;", "const int g = h % Hkv;"),
-    ("slot_shift", "int slot = j % bs;\n        const int64_t krow",
-     "int slot = (j + 1) % bs;\n        const int64_t krow"),
-    ("causal_off_by_one", "if (P->mask == REF_MASK_CAUSAL && prefix + i + 1 < n)\n        n = prefix + i + 1;",
-     "if (P->mask == REF_MASK_CAUSAL && prefix + i < n)\n        n = prefix + i;"),
-    ("causal_always", "if (P->mask == REF_MASK_CAUSAL && prefix + i + 1 < n)",
-     "if (prefix + i + 1 < n)"),
+    ("slot_shift", "int slot = tok % bs;\n        const int64_t krow",
+     "int slot = (tok + 1) % bs;\n        const int64_t krow"),
+    ("causal_off_by_one", "if (P->mask == REF_MASK_CAUSAL && prefix + i + 1 < hi)\n        hi = prefix + i + 1;",
+     "if (P->mask == REF_MASK_CAUSAL && prefix + i < hi)\n        hi = prefix + i;"),
+    ("causal_always", "if (P->mask == REF_MASK_CAUSAL && prefix + i + 1 < hi)",
+     "if (prefix + i + 1 < hi)"),
+    ("band_left_off_by_one", "if (pos - P->win_left > lo)\n            lo = pos - P->win_left;",
+     "if (pos - P->win_left + 1 > lo)\n            lo = pos - P->win_left + 1;"),
+    ("band_right_ignored", "if (pos + 1 + P->win_right < hi)\n            hi = pos + 1 + P->win_right;",
+     "if (pos + 1 < hi)\n            hi = pos + 1;"),
+    ("band_position_without_prefix", "const int64_t pos = (int64_t)prefix + i;", "const int64_t pos = i;"),
+    ("band_right_one_short", "            hi = pos + 1 + P->win_right;", "            hi = pos + P->win_right;"),
     ("prefix_plus_one", "const int prefix = kv - qlen > 0 ? kv - qlen : 0;",
      "const int prefix = kv - qlen + 1 > 0 ? kv - qlen + 1 : 0;"),
     ("no_scale", "z[j] = P->scale * dot;", "z[j] = dot;"),
@@ -35,8 +43,8 @@ MUTANTS = [
     ("f16_subnormal_scale", "v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
     ("bf16_shift", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = ((uint32_t)b << 16) | 0x8000u;"),
     ("table_row_stride",
-     "int32_t phys = P->block_tables[(int64_t)b * P->max_num_blocks_per_seq + j / bs];\n        if (phys < 0",
-     "int32_t phys = P->block_tables[(int64_t)b * (P->max_num_blocks_per_seq - 1) + j / bs];\n        if (phys < 0"),
+     "int32_t phys = P->block_tables[(int64_t)b * P->max_num_blocks_per_seq + tok / bs];\n        if (phys < 0",
+     "int32_t phys = P->block_tables[(int64_t)b * (P->max_num_blocks_per_seq - 1) + tok / bs];\n        if (phys < 0"),
     ("v_uses_first_token", "o[e] += z[j] * elem(vsrc, vrow + e, P->dtype);",
      "o[e] += z[j] * elem(vsrc, vrow - (int64_t)slot * Hkv * vstride + e, P->dtype);"),
     ("shared_v_row_stride", "const int vstride = P->value_cache ? Dv : Dk;", "const int vstride = Dv;"),
