@@ -76,10 +76,16 @@ def attention_flops(p):
     w = p.workload
     kv = p.context_lens_np.astype(np.int64)
     ql = np.ones(p.batch, np.int64) if p.q_seq_lens_np is None else p.q_seq_lens_np.astype(np.int64)
-    if w.mask == "causal":
+    if w.mask in ("causal", "band"):
         prefix = np.maximum(kv - ql, 0)
-        # sum over i < ql of min(prefix + i + 1, kv)
-        pairs = sum(int(np.minimum(prefix[b] + np.arange(ql[b]) + 1, kv[b]).sum()) for b in range(p.batch))
+        right = w.window_right if w.mask == "band" else 0
+        left = w.window_left if w.mask == "band" else None
+        pairs = 0
+        for b in range(p.batch):
+            pos = prefix[b] + np.arange(ql[b])          # row i sits at position prefix + i
+            hi = np.minimum(pos + 1 + right, kv[b])
+            lo = np.zeros_like(pos) if left is None else np.maximum(pos - left, 0)
+            pairs += int(np.maximum(hi - lo, 0).sum())
     else:
         pairs = int((ql * kv).sum())
     return pairs * w.head_num * 2 * (w.head_size_k + w.head_size_v)
@@ -98,7 +104,8 @@ def cpu_baseline(p, target_s, threads):
     ql = np.ones(p.batch, np.int64) if p.q_seq_lens_np is None else p.q_seq_lens_np.astype(np.int64)
     cu = np.concatenate([[0], np.cumsum(ql)])
     # oracle work per sequence ~ rows x visible tokens x (Dk + Dv)
-    cost = ql * kv * w.head_num * (w.head_size_k + w.head_size_v)
+    seen = np.minimum(kv, w.window_left + 1 + w.window_right) if w.mask == "band" else kv
+    cost = ql * seen * w.head_num * (w.head_size_k + w.head_size_v)
     order = np.random.default_rng(0).permutation(p.batch)
 
     def sub_problem(seqs):
@@ -117,7 +124,7 @@ def cpu_baseline(p, target_s, threads):
         return pa_ref.Inputs(p.query[qidx], p.key_cache[idx],
                              None if p.value_cache is None else p.value_cache[idx], bt, kv[seqs],
                              None if p.q_seq_lens_np is None else ql[seqs], w.head_num, w.kv_head_num,
-                             w.dtype, w.mask, w.scale, w.head_size_v)
+                             w.dtype, w.mask, w.scale, w.head_size_v, (w.window_left, w.window_right))
 
     # calibrate the oracle's rate on the cheapest sequence
     b0 = int(np.argmin(cost))

@@ -19,8 +19,15 @@
  *     (mask type 5), context_lens[b] counts history plus the current query
  *     tokens, prefix = max(0, context_lens[b] - q_seq_lens[b]), and row i
  *     sees tokens j <= prefix + i (the causal mask with its upper triangle,
- *     diagonal excluded, invisible; Constraints, mask type 5 list).  Masked
- *     tokens get weight exactly 0;
+ *     diagonal excluded, invisible; Constraints, mask type 5 list);
+ *     PA_MASK_BAND: a sliding window (mask mode 4 of the
+ *     SparseAttnSharedkvMetadata README, parameter table, with window_left
+ *     past and window_right future tokens; the page fixes 127 and 0): row i
+ *     sits at position prefix + i as in the causal mode and sees tokens
+ *     prefix + i - window_left <= j <= prefix + i + window_right.  Masked
+ *     tokens get weight exactly 0, and the chunks of KV blocks that no row
+ *     of a tile sees are neither planned nor read (block-table entries of
+ *     blocks wholly before a band are never used);
  *   - query and output rows are packed (TND): sequence b's rows start at
  *     t0 = q_seq_lens[0] + ... + q_seq_lens[b-1] (the cu_seqlens_q prefix-sum
  *     convention of the SparseAttnSharedkvMetadata README, parameter table);
@@ -42,7 +49,7 @@
  * Errors: functions return a pa_status synchronously.  Argument and shape
  * errors are reported before any device work is queued.  Problems that can
  * only be seen in device data (a block id outside [0, num_blocks), a table
- * too short for context_lens, q_seq_lens > context_lens in causal mode,
+ * too short for context_lens, q_seq_lens > context_lens in causal or band mode,
  * q_seq_lens that do not sum to num_q_tokens, negative lengths) never cause an
  * out-of-bounds access: the kernels clamp them and set a device error word
  * that pa_get_device_error reads back.
@@ -68,7 +75,8 @@ typedef enum { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
 
 typedef enum {
     PA_MASK_NONE = 0,    /* maskType UNDEFINED: all context_lens[b] tokens visible */
-    PA_MASK_CAUSAL = 1   /* mask type 5 (parallel decoding / splitfuse), prefix-aligned */
+    PA_MASK_CAUSAL = 1,  /* mask type 5 (parallel decoding / splitfuse), prefix-aligned */
+    PA_MASK_BAND = 2     /* sliding window (band mask mode 4), prefix-aligned like CAUSAL */
 } pa_mask;
 
 /* pa_config.flags */
@@ -107,6 +115,9 @@ typedef struct {
     pa_mask mask;
     uint32_t flags;                  /* PA_FLAG_* */
     int32_t num_partitions;          /* workgroups of the attention launch; 0 = chosen from the CU count */
+    int32_t window_left;             /* PA_MASK_BAND: tokens before a row's position it sees, in [0, 2^30];
+                                        ignored otherwise */
+    int32_t window_right;            /* PA_MASK_BAND: tokens after it, in [0, 2^30]; ignored otherwise */
 } pa_config;
 
 typedef struct pa_handle pa_handle;
@@ -116,12 +127,12 @@ typedef struct pa_handle pa_handle;
  * current HIP device.  Rules checked before any HIP call (PA_ERR_INVALID_ARG):
  * H, Hkv > 0 and H % Hkv == 0; 0 < Dk, Dv <= 576; block_size > 0,
  * block_size % 16 == 0, block_size <= 256, and block_size <= 128 in causal
- * mode or when Dk or Dv > 256; num_blocks > 0; max_batch > 0;
+ * mode or when Dk or Dv > 256; window sizes in [0, 2^30] in band mode; num_blocks > 0; max_batch > 0;
  * max_num_blocks_per_seq > 0; max_q_seq_len > 0; dtype and mask in range;
  * scale finite; num_partitions >= 0; only PA_FLAG_* bits, not FORCE_VALU
  * with FORCE_MFMA; Dv <= Dk with PA_FLAG_SHARED_KV.  PA_ERR_UNSUPPORTED: a (Dk, Dv) pair this
- * build has no kernels for (64/64, 128/128, 256/256, 576/512 are built), or a
- * device that is not gfx950.  On success *out receives the handle.
+ * build has no kernels for (64/64, 128/128, 256/256, 576/512 are built),
+ * PA_FLAG_FORCE_VALU with the band mask, or a device that is not gfx950.  On success *out receives the handle.
  */
 pa_status pa_create(const pa_config *cfg, pa_handle **out);
 

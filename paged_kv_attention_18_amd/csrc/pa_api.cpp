@@ -49,7 +49,7 @@ size_t partial_floats(int rows, int dv)
 }
 
 bool valid_dtype(int d) { return d == PA_F16 || d == PA_BF16; }
-bool valid_mask(int m) { return m == PA_MASK_NONE || m == PA_MASK_CAUSAL; }
+bool valid_mask(int m) { return m == PA_MASK_NONE || m == PA_MASK_CAUSAL || m == PA_MASK_BAND; }
 
 }  // namespace
 
@@ -96,7 +96,7 @@ struct pa_handle {
             v.tile_variant = var;
             v.rows_per_tile = pa::tile_rows(dk, dv, var, sh);
             v.chunk = pa::tile_chunk(dk, dv, var, sh);
-            v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var, sh);
+            v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var, sh, cfg.mask == PA_MASK_BAND);
             v.pieces_per_worker = var == 0 ? 1 : kMaxPiecesPerWorker;
         }
         if (cfg.num_partitions > 0)
@@ -141,6 +141,9 @@ static pa_status check_config(const pa_config *c)
         return PA_ERR_INVALID_ARG;
     if ((c->flags & PA_FLAG_SHARED_KV) && c->head_size_v > c->head_size_k)
         return PA_ERR_INVALID_ARG;   // V must fit inside the K row
+    if (c->mask == PA_MASK_BAND && (c->window_left < 0 || c->window_left > (1 << 30) || c->window_right < 0 ||
+                                    c->window_right > (1 << 30)))
+        return PA_ERR_INVALID_ARG;
     // Item indices are int32 on the device: bound the largest possible count.
     const int G = c->head_num / c->kv_head_num;
     const double tiles = std::ceil((double)c->max_q_seq_len * G / 16.0);
@@ -154,8 +157,8 @@ static pa_status check_config(const pa_config *c)
     const bool til = pa::tile_supported(c->head_size_k, c->head_size_v, 0);
     if (!dec && !til)
         return PA_ERR_UNSUPPORTED;
-    if ((c->flags & PA_FLAG_FORCE_VALU) && !dec)
-        return PA_ERR_UNSUPPORTED;
+    if ((c->flags & PA_FLAG_FORCE_VALU) && (!dec || c->mask == PA_MASK_BAND))
+        return PA_ERR_UNSUPPORTED;   // the VALU kernel has no lower visibility bound
     if ((c->flags & PA_FLAG_FORCE_MFMA) && !til)
         return PA_ERR_UNSUPPORTED;
     if (!til && (int64_t)c->max_q_seq_len * G > 8)
@@ -343,7 +346,10 @@ pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, con
     p.bs_shift = (c.block_size & (c.block_size - 1)) == 0 ? __builtin_ctz(c.block_size) : -1;
     p.max_blocks = c.max_num_blocks_per_seq;
     p.max_q = max_q_seq_len;
-    p.causal = c.mask == PA_MASK_CAUSAL;
+    p.causal = c.mask == PA_MASK_CAUSAL || c.mask == PA_MASK_BAND;
+    p.band = c.mask == PA_MASK_BAND;
+    p.win_left = p.band ? c.window_left : 0;
+    p.win_right = p.band ? c.window_right : 0;
     p.scale_log2 = c.scale * 1.4426950408889634f;
     p.rows_per_tile = v.rows_per_tile;
     p.chunk = v.chunk;

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
         const int rows = ql * G;
         const int t0 = p.ws.cu_q[b];
         const int prefix = kv - ql > 0 ? kv - ql : 0;
-        const int nvis = tile_nvis(kv, ql, G, rows - 1, p.causal);
+        const int nvis = tile_nvis(p, kv, ql, rows - 1);   // (no band mask: the host never picks this kernel for it)
         const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks;
         const size_t head_off = (size_t)g * D;
 
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
             m_run[k] = -INFINITY;
             l_part[k] = 0.f;
             const int r = own_row(k);
-            lim_own[k] = p.causal ? (prefix + r / G + 1 < kv ? prefix + r / G + 1 : kv) : kv;
+            lim_own[k] = row_hi(p, kv, prefix, r / G);
         }
 
         // Two register buffers: while the wave computes chunk c from one, the

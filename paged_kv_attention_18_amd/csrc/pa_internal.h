@@ -57,7 +57,9 @@ struct Params {
     int32_t block_size, bs_shift;      // bs_shift = log2(block_size) or -1
     int32_t max_blocks;                // block_tables row length
     int32_t max_q;                     // bound on q_seq_lens for this call
-    int32_t causal;
+    int32_t causal;                    // row-dependent upper limit (causal or band mask)
+    int32_t band;                      // band mask: row-dependent lower limit as well
+    int32_t win_left, win_right;       // band mask window (0, 0 otherwise)
     float scale_log2;                  // scale * log2(e)
     int32_t rows_per_tile;             // R
     int32_t chunk;                     // CT
@@ -85,14 +87,25 @@ bool decode_supported(int dk, int dv);
 // MFMA tile kernel variants: 0 for units of at most 16 rows, 1 for up to
 // tile_rows(.., 1) rows, 2 above; tile_supported says which exist.
 // `shared` selects the kernels that read V out of the K tile already in LDS
-// (shared K/V cache) where such kernels exist.
+// (shared K/V cache) where such kernels exist; `band` the kernels with a
+// lower visibility bound per row (band mask).
 bool tile_supported(int dk, int dv, int variant);
-int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared);   // resident workgroups per CU
+int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared, bool band);   // resident workgroups per CU
 int tile_chunk(int dk, int dv, int variant, bool shared);
 int tile_rows(int dk, int dv, int variant, bool shared);
 bool tile_streaming(int dk, int dv, int variant);   // served by the one-wave streaming kernel
 int decode_chunk(int dk, int rows_pad);
 int decode_workers_per_cu(int dtype, int dk, int dv, int rows_pad);   // resident waves per CU
+
+// Shape of a matrix-core kernel instance.
+struct TileShape {
+    int mb, kt, nw, cs, s;   // 16-row blocks per wave, tokens per chunk, waves owning rows,
+                             // waves sharing a row group, LDS stages
+    int threads;             // workgroup size
+};
+// Kernel instances without / with the band mask (nullptr: none for the shape).
+const void *tile_kernel_plain(int dtype, int dk, int dv, int variant, bool shared, TileShape *t);
+const void *tile_kernel_band(int dtype, int dk, int dv, int variant, bool shared, TileShape *t);
 
 constexpr int kThreads = 256;        // threads per attention workgroup
 constexpr int kBtWindow = 256;       // block-table entries staged in LDS at a time
@@ -104,24 +117,73 @@ constexpr int kBtWindow = 256;       // block-table entries staged in LDS at a t
 // select between two structs is lowered through memory).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Visible KV tokens of rows [r0, r1] of (b, g): a row (i, hh) sees tokens
-// j < kv, and in causal mode only j <= prefix + i.
-__device__ __forceinline__ int tile_nvis(int kv, int qlen, int G, int r1, int causal)
+// Visible KV tokens of query row i (0-based in its sequence; the row sits at
+// position prefix + i, prefix = max(0, kv - qlen)): j in [row_lo, row_hi).
+// No mask: [0, kv); causal: j <= prefix + i; band: prefix + i - win_left <=
+// j <= prefix + i + win_right (win_right = 0 in causal mode).
+__device__ __forceinline__ int row_hi(const Params &p, int kv, int prefix, int i)
 {
-    if (!causal)
+    if (!p.causal)
         return kv;
-    const int prefix = kv - qlen > 0 ? kv - qlen : 0;
-    const int lim = prefix + r1 / G + 1;
+    const int lim = prefix + i + 1 + p.win_right;
     return lim < kv ? lim : kv;
 }
 
-__device__ __forceinline__ int unit_chunks(int kv, int qlen, int G, int R, int CT, int qt, int causal)
+__device__ __forceinline__ int row_lo(const Params &p, int prefix, int i)
 {
-    const int rows = qlen * G;
-    int r1 = (qt + 1) * R;
+    if (!p.band)
+        return 0;
+    const int lo = prefix + i - p.win_left;
+    return lo > 0 ? lo : 0;
+}
+
+// The same with the mask kind fixed at compile time (BAND false: no lower
+// bound, and the upper one of the causal mask).
+template <bool BAND>
+__device__ __forceinline__ int row_hi_t(const Params &p, int kv, int prefix, int i)
+{
+    if (!p.causal)
+        return kv;
+    const int lim = prefix + i + 1 + (BAND ? p.win_right : 0);
+    return lim < kv ? lim : kv;
+}
+
+template <bool BAND>
+__device__ __forceinline__ int row_lo_t(const Params &p, int prefix, int i)
+{
+    if constexpr (!BAND)
+        return 0;
+    const int lo = prefix + i - p.win_left;
+    return lo > 0 ? lo : 0;
+}
+
+__device__ __forceinline__ int seq_prefix(int kv, int qlen)
+{
+    return kv - qlen > 0 ? kv - qlen : 0;
+}
+
+// Tokens up to which some row of rows [.., r1] of (b, g) looks (exclusive):
+// the limit of row r1, the largest.
+__device__ __forceinline__ int tile_nvis(const Params &p, int kv, int qlen, int r1)
+{
+    return row_hi(p, kv, seq_prefix(kv, qlen), r1 / p.group);
+}
+
+// The row tile qt of (b, g) covers chunks [first, first + count) of its
+// sequence: from the chunk holding the lowest visible token of its first
+// row (0 unless banded) to the one holding the last token its last row sees.
+__device__ __forceinline__ int unit_first_chunk(const Params &p, int kv, int qlen, int qt)
+{
+    return row_lo(p, seq_prefix(kv, qlen), (qt * p.rows_per_tile) / p.group) / p.chunk;
+}
+
+__device__ __forceinline__ int unit_chunks(const Params &p, int kv, int qlen, int qt)
+{
+    const int rows = qlen * p.group;
+    int r1 = (qt + 1) * p.rows_per_tile;
     r1 = (r1 < rows ? r1 : rows) - 1;
-    const int n = tile_nvis(kv, qlen, G, r1, causal);
-    const int c = (n + CT - 1) / CT;
+    const int n = tile_nvis(p, kv, qlen, r1);
+    const int c = (n + p.chunk - 1) / p.chunk - unit_first_chunk(p, kv, qlen, qt);
     return c > 1 ? c : 1;
 }
 
@@ -355,11 +417,11 @@ __device__ __forceinline__ void cursor_seek(const Params &p, Cursor &cu, int b, 
     local -= cu.g * ipg;
     cu.ntile = seq_tiles(p, ql);
     int qt = 0;
-    int n = unit_chunks(kv, ql, p.group, p.rows_per_tile, p.chunk, 0, p.causal);
+    int n = unit_chunks(p, kv, ql, 0);
     while (local >= n) {
         local -= n;
         ++qt;
-        n = unit_chunks(kv, ql, p.group, p.rows_per_tile, p.chunk, qt, p.causal);
+        n = unit_chunks(p, kv, ql, qt);
     }
     cu.qt = qt;
     cu.c = local;
@@ -384,8 +446,7 @@ __device__ __forceinline__ void cursor_next_unit(const Params &p, Cursor &cu)
             cu.ntile = seq_tiles(p, sload(p.ws.qlen, cu.b));
         }
     }
-    cu.nch = unit_chunks(sload(p.ws.kvlen, cu.b), sload(p.ws.qlen, cu.b), p.group, p.rows_per_tile, p.chunk,
-                         cu.qt, p.causal);
+    cu.nch = unit_chunks(p, sload(p.ws.kvlen, cu.b), sload(p.ws.qlen, cu.b), cu.qt);
 }
 
 // The item range of piece w (balanced mode) or of the unit of workgroup w
@@ -415,13 +476,13 @@ __device__ __forceinline__ bool wg_range(const Params &p, int w, Cursor &cu, int
     const int kv = sload(p.ws.kvlen, b);
     int start = sload(p.ws.wsb, b) + g * sload(p.ws.ipg, b);
     for (int t = 0; t < qt; ++t)
-        start += unit_chunks(kv, ql, p.group, p.rows_per_tile, p.chunk, t, p.causal);
+        start += unit_chunks(p, kv, ql, t);
     cu.b = b;
     cu.g = g;
     cu.qt = qt;
     cu.c = 0;
     cu.ntile = seq_tiles(p, ql);
-    cu.nch = unit_chunks(kv, ql, p.group, p.rows_per_tile, p.chunk, qt, p.causal);
+    cu.nch = unit_chunks(p, kv, ql, qt);
     cu.item = start;
     end = start + cu.nch;
     return true;

@@ -81,11 +81,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
                 err |= PA_DEVERR_QLEN;
                 ql = p.max_q;
             }
-            if (p.causal && ql > kv)
+            if (p.causal && ql > kv)   // causal and band rows sit at positions kv - ql .. kv - 1
                 err |= PA_DEVERR_QLEN;
             const int ntile = (ql * G + R - 1) / R;
             for (int qt = 0; qt < ntile; ++qt)
-                ipg += unit_chunks(kv, ql, G, R, p.chunk, qt, p.causal);
+                ipg += unit_chunks(p, kv, ql, qt);
             items = ipg * p.kv_head_num;
             p.ws.qlen[b] = ql;
             p.ws.kvlen[b] = kv;
@@ -173,12 +173,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
             const int gg = local / ipg;
             local -= gg * ipg;
             int u0 = wsb_of(b) + gg * ipg;
-            int t = 0, n = unit_chunks(kv, ql, G, R, p.chunk, 0, p.causal);
+            int t = 0, n = unit_chunks(p, kv, ql, 0);
             while (local >= n) {
                 local -= n;
                 u0 += n;
                 ++t;
-                n = unit_chunks(kv, ql, G, R, p.chunk, t, p.causal);
+                n = unit_chunks(p, kv, ql, t);
             }
             int32_t *d = p.ws.splits + (size_t)(k - 1) * 8;
             const bool split = s > u0 && s - pe <= u0;

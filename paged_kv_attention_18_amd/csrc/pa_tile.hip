@@ -1,1099 +1,21 @@
-// pa_tile.hip -- paged attention on the matrix cores (gfx950 MFMA).
-//
-// For units of 5 rows or more: parallel decoding / splitfuse chunks with the
-// prefix-aligned causal mask (Ascend ATB PagedAttentionOperation,
-// Constraints, mask type 5 list), decode with GQA groups of 8 or more, and a
-// wide GQA group on one KV head with 576/512 key/value head sizes (which the
-// same Constraints allow at block_size <= 128).  Rows are padded to 16.
-//
-// A workgroup of NW waves owns a tile of rows of one (sequence, KV head).  The
-// waves form NW / CS row groups of 16 * MB rows; the CS waves of a row group
-// share its rows and split the Dv output columns (CS = 2 halves the output
-// accumulator per wave for Dv = 512).  Per KT-token chunk:
-//
-//   stage  K and V rows are copied from the paged cache straight into LDS
-//          with global_load_lds_dwordx4 (no registers, no ALU work) into a
-//          ring of S stages, S - 1 chunks ahead of the one computed.  Each
-//          lane picks the global 16-byte piece that lands at its LDS slot,
-//          which realises an XOR swizzle of the pieces within a row (K:
-//          piece ^ (row & 7); V: piece ^ 2(row & 7), or ^ (row & 7) for
-//          128-byte rows), so the operand reads below are free of bank
-//          conflicts.  A block id out of range reads
-//          a zero page (and is flagged); rows past the visible range are
-//          masked (P = 0, and their V operand halves are zeroed).
-//   S^T    = K . Q^T with v_mfma_f32_16x16x32_{f16,bf16}: K is the A operand
-//          (ds_read_b128), Q^T the B operand, held in registers for the whole
-//          unit.  The accumulator gives every lane one query row and 4 + 4
-//          tokens, which is exactly the A-operand layout P needs for the next
-//          product, so P never leaves registers.
-//   mask   select -inf where j >= kv or (causal) j > prefix + i; chunks that
-//          lie wholly inside every row's visible range skip the test, and
-//          chunks wholly outside are never planned.
-//   PV     O += P . V with the same instruction (16x16x16 for 16-token
-//          chunks); the V operand is read from the row-major tile with
-//          ds_read_b64_tr_b16 (a transposing LDS read: within each 16-lane
-//          group, lane i receives element i % 4 of the 8-byte chunks
-//          addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4).
-//
-// Every wave issues the same number of LDS loads per chunk, so the wait for
-// chunk c is an exact vmcnt count, followed by one barrier.  Row statistics
-// (running max and sum, log2 domain) stay per wave; at the end of a unit's
-// range O is normalised into the output, or written as an fp32 partial for
-// the merge kernel.
-#include "pa_internal.h"
-
-#include <type_traits>
+// pa_tile.hip -- the matrix-core kernels without the band mask, and the host
+// side of their selection, occupancy and launch.  The kernels themselves are
+// described in pa_tile_kernels.h.
+#include "pa_tile_kernels.h"
 
 namespace pa {
 
+const void *tile_kernel_plain(int dtype, int dk, int dv, int variant, bool shared, TileShape *t)
+{
+    return kernel_select<false>(dtype, dk, dv, variant, shared, t);
+}
+
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-template <int DT>
-struct Mfma;
-
-template <>
-struct Mfma<0> {
-    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
-    static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c)
-    {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c,
-                                                      0, 0, 0);
-    }
-};
-
-template <>
-struct Mfma<1> {
-    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
-    static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c)
-    {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c,
-                                                       0, 0, 0);
-    }
-};
-
-// Two 16-bit values packed as (lo, hi), round to nearest even.
-template <int DT>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+const void *tile_kernel_ptr(int dtype, int dk, int dv, int variant, bool shared, TileShape *t, bool band = false)
 {
-    if constexpr (DT == 0) {
-        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-        const h2 v = {(_Float16)lo, (_Float16)hi};
-        return __builtin_bit_cast(uint32_t, v);
-    } else {
-        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-        const b2 v = {(__bf16)lo, (__bf16)hi};
-        return __builtin_bit_cast(uint32_t, v);
-    }
-}
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes
-// land at dst + 16 l (global_load_lds_dwordx4, LDS base in M0).  Issued from
-// inline assembly so that the compiler does not add waits of its own for
-// these stores; the kernel waits for them explicitly (vmcnt + barrier)
-// before it reads the LDS they fill.
-__device__ __forceinline__ void lds_load16(const void *src, lds_u8 *dst)
-{
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
-}
-
-template <int DT>
-struct Mfma16;   // 16 x 16 x 16 products (PV over 16-token chunks)
-
-template <>
-struct Mfma16<0> {
-    typedef _Float16 v4 __attribute__((ext_vector_type(4)));
-    static __device__ __forceinline__ f32x4 run(uint2 a, uint2 b, f32x4 c)
-    {
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4, a), __builtin_bit_cast(v4, b), c, 0, 0, 0);
-    }
-};
-
-template <>
-struct Mfma16<1> {
-    static __device__ __forceinline__ f32x4 run(uint2 a, uint2 b, f32x4 c)
-    {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, a), __builtin_bit_cast(v4i16, b), c,
-                                                         0, 0, 0);
-    }
-};
-
-// s_waitcnt with vmcnt(n) only (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Wait until at most LW * min(ahead, A) vector memory instructions of this
-// wave are outstanding.
-template <int LW, int A>
-__device__ __forceinline__ void wait_ahead(int ahead)
-{
-    if constexpr (A == 0) {
-        wait_vm<0>();
-    } else {
-        if (ahead >= A)
-            wait_vm<LW * A>();
-        else
-            wait_ahead<LW, A - 1>(ahead);
-    }
-}
-
-// XOR swizzle of the 16-byte pieces of V tile row r.  The PV operand is
-// read with ds_read_b64_tr_b16, whose 32-lane passes touch pieces 2 nd and
-// 2 nd + 1 of rows 8 i .. 8 i + 7; the swizzle spreads those 16 pieces over
-// all 64 banks: rows of a multiple of 256 bytes move by 2 (r % 8) pieces,
-// 128-byte rows (which alternate between the two bank halves) by r % 8.
-template <int RB>
-__device__ __forceinline__ int v_swz(int r)
-{
-    return RB % 256 == 0 ? 2 * (r & 7) : (r & 7);
-}
-// Per-lane read offsets the swizzle needs: one per nd % NVO.
-template <int RB>
-constexpr int v_offsets()
-{
-    return RB % 256 == 0 ? 8 : 4;
-}
-
-// Workgroups per CU the register budget is cut for: as many as fit in LDS
-// (at most 4; at most 2 with two 16-row blocks per wave, 1 at head sizes
-// above 128).  SH: no V tiles in LDS.
-template <int DK, int DV, int MB, int KT, int S, int NW, bool SH>
-constexpr int tile_min_wgs()
-{
-    constexpr int lds = S * KT * 2 * (DK + (SH ? 0 : DV)) + 2048;
-    constexpr int fit = (160 * 1024) / lds;
-    // waves per SIMD the registers allow: 2 with two 16-row blocks, else 4
-    constexpr int waves = MB == 2 ? ((DK > 128 || DV > 128) ? 1 : 2) : 4;
-    constexpr int cap = 4 * waves / NW > 0 ? 4 * waves / NW : 1;
-    return fit < 1 ? 1 : (fit > cap ? cap : fit);
-}
-
-// DT: 0 f16 / 1 bf16.  MB: 16-row blocks per wave.  KT: tokens per chunk
-// (16, 32 or 64).  NW: waves.  CS: waves sharing a row group (column split).
-// S: LDS stages (chunks c + 1 .. c + S - 1 are in flight while c is
-// computed).  SH: shared K/V cache -- V is the leading Dv elements of each
-// K row, so only K tiles are loaded and the PV product reads its operand
-// from the K tile (the K swizzle keeps those transposing reads free of
-// bank conflicts as well).
-template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH>
-__global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>())) void tile_kernel(Params p)
-{
-    constexpr int RGS = NW / CS;                  // row groups
-    constexpr int R = 16 * MB * RGS;              // rows per tile
-    constexpr int RBK = 2 * DK, RBV = 2 * DV;     // LDS row bytes
-    constexpr int RBVL = SH ? RBK : RBV;          // LDS row bytes of the tile the V operand is read from
-    constexpr int KS = DK / 32;
-    constexpr int NTT = KT / 16;
-    constexpr int ND = DV / 16 / CS;              // output column tiles per wave
-    constexpr int IPGK = RBK / 64;                // 1 KiB LDS-load instructions per 16-token group (K)
-    constexpr int IPGV = SH ? 0 : RBV / 64;
-    constexpr int MK = (IPGK + NW - 1) / NW;      // ... per wave per group
-    constexpr int MV = (IPGV + NW - 1) / NW;
-    constexpr int LW = NTT * (MK + MV);           // load instructions per wave per chunk, all waves alike
-    constexpr bool PAD = MK * NW != IPGK || MV * NW != IPGV;
-    constexpr int VTB = SH ? 16 : KT * RBV;       // bytes of a V stage buffer
-    static_assert(DK % 32 == 0 && DV % 64 == 0 && (KT == 16 || KT == 32 || KT == 64), "shape");
-    static_assert(NW % CS == 0 && ND % 4 == 0 && S >= 2 && S <= 4, "split");
-    static_assert(LW * (S - 2) < 64, "vmcnt range");
-    static_assert(!SH || DV <= DK, "V inside the K row");
-
-    __shared__ __attribute__((aligned(1024))) uint8_t sK0[KT * RBK];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV0[VTB];
-    __shared__ __attribute__((aligned(1024))) uint8_t sK1[KT * RBK];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV1[VTB];
-    __shared__ __attribute__((aligned(1024))) uint8_t sK2[S > 2 ? KT * RBK : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV2[S > 2 ? VTB : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t sK3[S > 3 ? KT * RBK : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV3[S > 3 ? VTB : 16];
-    // destination of the padding loads that keep every wave's count at LW
-    __shared__ __attribute__((aligned(1024))) uint8_t sJunk[PAD ? 1024 : 16];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rgi = wave / CS;          // row group
-    const int csl = wave % CS;          // column slice
-    const int col0 = csl * (DV / CS);
-    const int lr = lane & 15;
-    const int lg = lane >> 4;
-
-    int piece = xcd_logical_index(blockIdx.x, gridDim.x);
-    Cursor cu;
-    int end;
-    if (piece >= p.partitions || !wg_range(p, piece, cu, end))
-        return;
-    __shared__ int s_piece;
-
-    const uint16_t *__restrict__ qg = (const uint16_t *)p.query;
-    const char *__restrict__ kg = (const char *)p.key_cache;
-    const char *__restrict__ vg = (const char *)p.value_cache;
-    const char *__restrict__ zg = (const char *)p.ws.zeros;
-    uint16_t *__restrict__ og = (uint16_t *)p.out;
-    const int G = p.group;
-    const int H = p.head_num;
-    const int bs = p.block_size;
-    const int bsh = p.bs_shift;
-    const uint32_t rsk = (uint32_t)p.kv_head_num * RBK;   // bytes per token row of the cache
-    const uint32_t rsv = p.v_row_bytes;
-    const uint32_t nb32 = p.num_blocks < 0x7fffffff ? (uint32_t)p.num_blocks : 0x7fffffffu;
-    // Scores are kept raw (q . k) and scaled on the way into exp2 by
-    // sc = |scale| log2(e); a negative scale is folded into Q.
-    const bool neg_scale = p.scale_log2 < 0.f;
-    const float sc = fmaxf(fabsf(p.scale_log2), 1e-30f);   // scale 0: every visible token weighs 1
-    // The running max used as exp2 reference is only moved when a row's
-    // max grows by more than 2^8 (P stays below 256, exact in the
-    // 16-bit operand types); a moved reference rescales O and the sum.
-    const float grow_raw = 8.f / sc;
-    uint32_t err = 0;
-    bool first_seg = true;
-
-    // Per-lane byte offset, inside a 16-token group of the cache, of the piece
-    // that load instruction wave + NW m of the group moves; the piece is the
-    // one whose LDS slot holds the swizzled layout.
-    uint32_t voK[MK], voV[MV > 0 ? MV : 1];
-#pragma unroll
-    for (int m = 0; m < MK; ++m) {
-        const int x = (wave + NW * m) * 1024 + 16 * lane;
-        const int row = x / RBK;
-        voK[m] = (wave + NW * m) < IPGK ? row * rsk + 16 * (((x % RBK) >> 4) ^ (row & 7)) : 16 * lane;
-    }
-#pragma unroll
-    for (int m = 0; m < MV; ++m) {
-        const int x = (wave + NW * m) * 1024 + 16 * lane;
-        const int row = x / RBV;
-        voV[m] = (wave + NW * m) < IPGV ? row * rsv + 16 * (((x % RBV) >> 4) ^ v_swz<RBV>(row)) : 16 * lane;
-    }
-    // LDS read offsets.  K (A operand): row 16 n + lr, piece 4 ks + lg, which
-    // the swizzle moves by +-64 bytes depending on bit 2 of the row.
-    const int kq = 16 * (lg ^ (lr & 3));
-    const int kb2 = 64 * ((lr >> 2) & 1);
-    const int koE = lr * RBK + kq + kb2, koO = lr * RBK + kq - kb2;
-    // V (B operand, transposing read): row 4 lg + lr / 4 (+ 16 n),
-    // columns col0 + 16 nd + 4 (lr % 4) .. + 3, i.e. 16-byte piece
-    // col0 / 8 + 2 nd + (lr % 4) / 2 of the row, moved by the tile's swizzle
-    // (the K swizzle when V is read from the K tile).  Column tile nd reads
-    // at vo[nd % NVO] + (nd / NVO) NVO 32 bytes.
-    constexpr int NVO = SH ? 4 : v_offsets<RBV>();
-    int vo[NVO];
-#pragma unroll
-    for (int m = 0; m < NVO; ++m) {
-        const int vrow = 4 * lg + (lr >> 2);
-        const int vpiece = (2 * m + ((lr & 3) >> 1)) ^ (SH ? (vrow & 7) : v_swz<RBV>(vrow));
-        vo[m] = vrow * RBVL + 16 * vpiece + 8 * (lr & 1) + 2 * col0;
-    }
-
-    while (true) {
-        const int b = cu.b, g = cu.g, qt = cu.qt;
-        const int c0 = cu.c;
-        const int c1 = cu.nch < c0 + (end - cu.item) ? cu.nch : c0 + (end - cu.item);
-        const bool whole = (c0 == 0 && c1 == cu.nch);
-        const int kv = sload(p.ws.kvlen, b);
-        const int ql = sload(p.ws.qlen, b);
-        const int rows = ql * G;
-        int rows_tile = rows - qt * R;
-        rows_tile = rows_tile < R ? rows_tile : R;
-        const int t0 = sload(p.ws.cu_q, b);
-        const int prefix = kv - ql > 0 ? kv - ql : 0;
-        const int nvis = tile_nvis(kv, ql, G, qt * R + rows_tile - 1, p.causal);
-        const int nblk = nvis > 0 ? div_bs(nvis - 1, bs, bsh) + 1 : 1;
-        // the fewest visible tokens of any row of the tile (masking threshold)
-        const int min_lim = p.causal ? tile_nvis(kv, ql, G, qt * R, 1) : kv;
-        const int wr0 = rgi * 16 * MB;
-        const bool wave_active = wr0 < rows_tile;
-        const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks;
-        const char *kgh = kg + (size_t)g * RBK;
-        const char *vgh = vg + (size_t)g * p.v_head_bytes;
-
-        // Q^T operand and the visible limit of this lane's rows
-        u32x4 qb[MB][KS];
-        int lim[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int row_t = wr0 + 16 * mb + lr;
-            const int rg = qt * R + row_t;
-            const int t = t0 + rg / G;
-            const bool ok = row_t < rows_tile && t < p.num_q_tokens;
-            lim[mb] = p.causal ? (prefix + rg / G + 1 < kv ? prefix + rg / G + 1 : kv) : kv;
-            const uint16_t *src = qg + ((size_t)t * H + g * G + rg % G) * DK + 8 * lg;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                qb[mb][ks] = ok ? *(const u32x4 *)(src + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
-                if (neg_scale)   // exact: softmax(c s) = softmax(|c| (-s)) with -s = (-q) . k
-                    qb[mb][ks] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-            }
-        }
-
-        f32x4 oacc[MB][ND];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int nd = 0; nd < ND; ++nd)
-                oacc[mb][nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float m_run[MB], lsum[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            m_run[mb] = -INFINITY;
-            lsum[mb] = 0.f;
-        }
-
-        // Block id of each 16-token group of a chunk (clamped table index;
-        // range-checked when used).
-        int bid[NTT];
-        auto fetch_bids = [&](int c) __attribute__((always_inline)) {
-#pragma unroll
-            for (int q = 0; q < NTT; ++q) {
-                const int blk = div_bs(c * KT + 16 * q, bs, bsh);
-                bid[q] = sload(bt, blk < nblk ? blk : nblk - 1);
-            }
-        };
-        // Issue the LDS loads of chunk c: exactly LW instructions per wave.
-        // Groups wholly past the visible range read the zero page; their
-        // rows are masked in compute anyway.
-        auto issue = [&](int c, lds_u8 *kb, lds_u8 *vb) __attribute__((always_inline)) {
-#pragma unroll
-            for (int q = 0; q < NTT; ++q) {
-                const int j0 = c * KT + 16 * q;
-                const bool vis = j0 < nvis;
-                const bool inb = (unsigned)bid[q] < nb32;
-                err |= (vis && !inb) ? (uint32_t)PA_DEVERR_BLOCK_ID : 0u;
-                const size_t trow = (size_t)bid[q] * bs + mod_bs(j0, bs, bsh);
-                const char *kbase = (vis && inb) ? kgh + trow * rsk : zg;
-                const char *vbase = (vis && inb) ? vgh + trow * rsv : zg;
-#pragma unroll
-                for (int m = 0; m < MK; ++m) {
-                    const int i = wave + NW * m;
-                    lds_u8 *dst = (!PAD || i < IPGK) ? kb + (q * IPGK + i) * 1024 : (lds_u8 *)sJunk;
-                    const char *src = (!PAD || i < IPGK) ? kbase : zg;
-                    lds_load16(src + voK[m], dst);
-                }
-#pragma unroll
-                for (int m = 0; m < MV; ++m) {
-                    const int i = wave + NW * m;
-                    lds_u8 *dst = (!PAD || i < IPGV) ? vb + (q * IPGV + i) * 1024 : (lds_u8 *)sJunk;
-                    const char *src = (!PAD || i < IPGV) ? vbase : zg;
-                    lds_load16(src + voV[m], dst);
-                }
-            }
-        };
-
-        // one chunk from (kb, vb): S^T, mask, online softmax, PV
-        auto compute = [&](const lds_u8 *kb, const lds_u8 *vb, int c) __attribute__((always_inline)) {
-            if (!wave_active)
-                return;
-            const int jb = c * KT;
-            f32x4 sacc[MB][NTT];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int n = 0; n < NTT; ++n)
-                    sacc[mb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int n = 0; n < NTT; ++n) {
-                    const u32x4 a = *(const lds_u32x4 *)(kb + ((ks & 1) ? koO : koE) + 16 * n * RBK + 64 * ks);
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        sacc[mb][n] = Mfma<DT>::run(a, qb[mb][ks], sacc[mb][n]);
-                }
-            }
-            const bool need_mask = jb + KT > min_lim;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int n = 0; n < NTT; ++n) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (need_mask) {
-                            const int j = jb + 16 * n + 4 * lg + r;
-                            sacc[mb][n][r] = j < lim[mb] ? sacc[mb][n][r] : -INFINITY;
-                        }
-                        mx = fmaxf(mx, sacc[mb][n][r]);
-                    }
-                }
-                mx = xor_max<16>(mx);
-                mx = xor_max<32>(mx);
-                if (__any(mx > m_run[mb] + grow_raw)) {
-                    const float m_new = fmaxf(m_run[mb], mx);
-                    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run[mb] - m_new) * sc);
-                    lsum[mb] *= alpha;
-                    m_run[mb] = m_new;
-                    // O rows 4 lg + r take the factor of the lane holding that row
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float ar = __shfl(alpha, 4 * lg + r);
-#pragma unroll
-                        for (int nd = 0; nd < ND; ++nd)
-                            oacc[mb][nd][r] *= ar;
-                    }
-                }
-                const float mref = m_run[mb] == -INFINITY ? 0.f : m_run[mb] * sc;
-                float ps = 0.f;
-#pragma unroll
-                for (int n = 0; n < NTT; ++n) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][n][r], sc, -mref));
-                        sacc[mb][n][r] = pv;
-                        ps += pv;
-                    }
-                }
-                lsum[mb] += ps;
-            }
-            // V rows of tokens at or past nvis may be stale or unwritten
-            // cache slots: zero their operand halves (P is 0 there).
-            const bool tail = jb + KT > nvis;
-            if constexpr (KT == 16) {
-                uint2 pa[MB];
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    pa[mb] = uint2{pack2<DT>(sacc[mb][0][0], sacc[mb][0][1]), pack2<DT>(sacc[mb][0][2], sacc[mb][0][3])};
-                uint2 vm = {~0u, ~0u};
-                if (tail) {
-                    const int tb = jb + 4 * lg;
-                    vm.x = (tb < nvis ? 0xffffu : 0u) | (tb + 1 < nvis ? 0xffff0000u : 0u);
-                    vm.y = (tb + 2 < nvis ? 0xffffu : 0u) | (tb + 3 < nvis ? 0xffff0000u : 0u);
-                }
-#pragma unroll
-                for (int nd = 0; nd < ND; ++nd) {
-                    const v4i16 b0 =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + 32 * NVO * (nd / NVO)));
-                    uint2 bv = __builtin_bit_cast(uint2, b0);
-                    if (tail) {
-                        bv.x &= vm.x;
-                        bv.y &= vm.y;
-                    }
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        oacc[mb][nd] = Mfma16<DT>::run(pa[mb], bv, oacc[mb][nd]);
-                }
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < KT / 32; ++kk) {
-                    u32x4 pa[MB];
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        const f32x4 s0 = sacc[mb][2 * kk], s1 = sacc[mb][2 * kk + 1];
-                        pa[mb] = u32x4{pack2<DT>(s0[0], s0[1]), pack2<DT>(s0[2], s0[3]),
-                                       pack2<DT>(s1[0], s1[1]), pack2<DT>(s1[2], s1[3])};
-                    }
-                    u32x4 vm = {~0u, ~0u, ~0u, ~0u};
-                    if (tail) {
-                        const int tb = jb + 32 * kk + 4 * lg;
-#pragma unroll
-                        for (int h = 0; h < 2; ++h)
-#pragma unroll
-                            for (int e = 0; e < 2; ++e)
-                                vm[2 * h + e] = (tb + 16 * h + 2 * e < nvis ? 0xffffu : 0u) |
-                                                (tb + 16 * h + 2 * e + 1 < nvis ? 0xffff0000u : 0u);
-                    }
-#pragma unroll
-                    for (int nd = 0; nd < ND; ++nd) {
-                        const int off = 32 * kk * RBVL + 32 * NVO * (nd / NVO);
-                        const v4i16 b0 =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + off));
-                        const v4i16 b1 =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + off + 16 * RBVL));
-                        const uint2 lo = __builtin_bit_cast(uint2, b0), hi = __builtin_bit_cast(uint2, b1);
-                        u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
-                        if (tail)
-                            bv &= vm;
-#pragma unroll
-                        for (int mb = 0; mb < MB; ++mb)
-                            oacc[mb][nd] = Mfma<DT>::run(pa[mb], bv, oacc[mb][nd]);
-                    }
-                }
-            }
-        };
-
-        auto kbuf = [&](auto st) __attribute__((always_inline)) -> lds_u8 * {
-            if constexpr (decltype(st)::value == 0)
-                return (lds_u8 *)sK0;
-            else if constexpr (decltype(st)::value == 1)
-                return (lds_u8 *)sK1;
-            else if constexpr (decltype(st)::value == 2)
-                return (lds_u8 *)sK2;
-            else
-                return (lds_u8 *)sK3;
-        };
-        auto vbuf = [&](auto st) __attribute__((always_inline)) -> lds_u8 * {
-            if constexpr (SH)
-                return kbuf(st);
-            else if constexpr (decltype(st)::value == 0)
-                return (lds_u8 *)sV0;
-            else if constexpr (decltype(st)::value == 1)
-                return (lds_u8 *)sV1;
-            else if constexpr (decltype(st)::value == 2)
-                return (lds_u8 *)sV2;
-            else
-                return (lds_u8 *)sV3;
-        };
-        // one pipeline step: chunk c sits in stage st
-        auto step = [&](auto st, int c) __attribute__((always_inline)) {
-            constexpr int ST = decltype(st)::value;
-            constexpr int NX = (ST + S - 1) % S;   // stage of chunk c + S - 1
-            wait_ahead<LW, S - 2>(c1 - 1 - c);     // this wave's loads of chunk c are in LDS
-            __builtin_amdgcn_s_barrier();          // ... and every wave's; stage NX is free
-            if (c + S - 1 < c1)
-                issue(c + S - 1, kbuf(std::integral_constant<int, NX>{}), vbuf(std::integral_constant<int, NX>{}));
-            compute(kbuf(st), vbuf(st), c);
-            if (c + S < c1)
-                fetch_bids(c + S);                 // scalar loads land during the next wait
-        };
-
-        // Q in registers before the LDS loads start: the vector memory
-        // counter then covers only those loads.  All waves are done reading
-        // every stage (previous segment).
-        wait_vm<0>();
-        __syncthreads();
-        fetch_bids(c0);
-        issue(c0, kbuf(std::integral_constant<int, 0>{}), vbuf(std::integral_constant<int, 0>{}));
-        if constexpr (S > 2) {
-            if (c0 + 1 < c1) {
-                fetch_bids(c0 + 1);
-                issue(c0 + 1, kbuf(std::integral_constant<int, 1>{}), vbuf(std::integral_constant<int, 1>{}));
-            }
-        }
-        if constexpr (S > 3) {
-            if (c0 + 2 < c1) {
-                fetch_bids(c0 + 2);
-                issue(c0 + 2, kbuf(std::integral_constant<int, 2>{}), vbuf(std::integral_constant<int, 2>{}));
-            }
-        }
-        if (c0 + S - 1 < c1)
-            fetch_bids(c0 + S - 1);
-        for (int c = c0; c < c1; c += S) {
-            step(std::integral_constant<int, 0>{}, c);
-            if (c + 1 >= c1)
-                break;
-            step(std::integral_constant<int, 1>{}, c + 1);
-            if constexpr (S > 2) {
-                if (c + 2 >= c1)
-                    break;
-                step(std::integral_constant<int, 2>{}, c + 2);
-            }
-            if constexpr (S > 3) {
-                if (c + 3 >= c1)
-                    break;
-                step(std::integral_constant<int, 3>{}, c + 3);
-            }
-        }
-
-        // -------------------------------------------------------- finalise
-        if (wave_active) {
-            const int slot = first_seg ? 0 : 1;
-            float *part = p.ws.partials + (size_t)(2 * piece + slot) * p.partial_stride;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const float L = xor_sum<32>(xor_sum<16>(lsum[mb]));
-                const float Ms = m_run[mb] * sc;   // log2 domain
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float Lr = __shfl(L, 4 * lg + r);
-                    const float Mr = __shfl(Ms, 4 * lg + r);
-                    const int row_t = wr0 + 16 * mb + 4 * lg + r;
-                    if (row_t >= rows_tile)
-                        continue;
-                    const int rg = qt * R + row_t;
-                    const int t = t0 + rg / G;
-                    const int h = g * G + rg % G;
-                    if (whole) {
-                        if (t >= p.num_q_tokens)
-                            continue;
-                        const float inv = Lr > 0.f ? 1.f / Lr : 0.f;
-                        uint16_t *dst = og + ((size_t)t * H + h) * DV;
-#pragma unroll
-                        for (int nd = 0; nd < ND; ++nd)
-                            dst[col0 + 16 * nd + lr] = to_bits<DT>(oacc[mb][nd][r] * inv);
-                        if (lr == 0 && csl == 0 && p.lse)
-                            p.lse[(size_t)t * H + h] =
-                                Lr > 0.f ? (Mr + log2f(Lr)) * 0.69314718055994531f : -INFINITY;
-                    } else {
-#pragma unroll
-                        for (int nd = 0; nd < ND; ++nd)
-                            part[row_t * DV + col0 + 16 * nd + lr] = oacc[mb][nd][r];
-                        if (lr == 0 && csl == 0) {
-                            part[R * DV + row_t] = Mr;
-                            part[R * DV + R + row_t] = Lr;
-                        }
-                    }
-                }
-            }
-        }
-
-        first_seg = false;
-        cu.item += c1 - c0;
-        bool more = cu.item < end;
-        if (more) {
-            cursor_next_unit(p, cu);
-            more = cu.b < p.batch;
-        }
-        if (!more) {
-            // this piece is done: take the next one, if any
-            if (p.no_split || p.pieces <= p.partitions)
-                break;
-            if (threadIdx.x == 0)
-                s_piece = grab_piece(p);
-            __syncthreads();
-            piece = s_piece;
-            if (!wg_range(p, piece, cu, end))
-                break;
-            first_seg = true;
-        }
-    }
-    if (err)
-        set_error(p.ws.err, err);
-}
-
-// ---------------------------------------------------------------------------
-// Streaming kernel for units of at most 16 rows (decode).  One wave is a
-// worker with its own S-stage LDS ring, and the ring does not drain between
-// units or pieces: the wave issues chunk k + S - 1 of its stream (whatever
-// unit or piece it belongs to) while it computes chunk k.  The first chunk
-// of every segment also carries the segment's 16 x Dk Q tile into its stage,
-// and each stage carries the chunk's segment parameters in a small LDS
-// record, so the compute side never waits for a lookup.  A worker keeps
-// one piece: taking further pieces from a shared counter needs the atomic's
-// return, and waiting for it is a wait on every load of the in-order vector
-// memory counter, which drains the ring.
-template <int DT, int DK, int DV, int KT, int S>
-__global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
-{
-    constexpr int RBK = 2 * DK, RBV = 2 * DV;     // LDS row bytes
-    constexpr int KS = DK / 32;
-    constexpr int NTT = KT / 16;
-    constexpr int ND = DV / 16;
-    constexpr int IPGK = RBK / 64;                // 1 KiB loads per 16 rows of K (and of the Q tile)
-    constexpr int IPGV = RBV / 64;
-    constexpr int LW = NTT * (IPGK + IPGV);       // loads per chunk (plus IPGK for a Q tile)
-    constexpr int STK = KT * RBK, STV = KT * RBV, STQ = 16 * RBK;
-    constexpr int MW = 12;                        // ints per stage record
-    static_assert(DK <= 256 && DV <= 256 && DK % 32 == 0 && DV % 64 == 0 && (KT == 16 || KT == 32), "shape");
-    static_assert(S >= 2 && S <= 4 && LW * (S - 2) + IPGK < 64, "ring");
-
-    __shared__ __attribute__((aligned(1024))) uint8_t sK[S * STK];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV[S * STV];
-    __shared__ __attribute__((aligned(1024))) uint8_t sQ[S * STQ];
-    __shared__ int s_meta[S * MW];
-
-    const int lane = threadIdx.x & 63;
-    const int lr = lane & 15;
-    const int lg = lane >> 4;
-    const int worker = xcd_logical_index(blockIdx.x, gridDim.x);
-
-    const uint16_t *__restrict__ qg = (const uint16_t *)p.query;
-    const char *__restrict__ kg = (const char *)p.key_cache;
-    const char *__restrict__ vg = (const char *)p.value_cache;
-    const char *__restrict__ zg = (const char *)p.ws.zeros;
-    uint16_t *__restrict__ og = (uint16_t *)p.out;
-    const int G = p.group;
-    const int H = p.head_num;
-    const int bs = p.block_size;
-    const int bsh = p.bs_shift;
-    const uint32_t rsk = (uint32_t)p.kv_head_num * RBK;
-    const uint32_t rsv = p.v_row_bytes;
-    const uint32_t nb32 = p.num_blocks < 0x7fffffff ? (uint32_t)p.num_blocks : 0x7fffffffu;
-    const bool neg_scale = p.scale_log2 < 0.f;
-    const float sc = fmaxf(fabsf(p.scale_log2), 1e-30f);   // scale 0: every visible token weighs 1
-    const float grow_raw = 8.f / sc;
-    uint32_t err = 0;
-
-    // per-lane offsets of the loads (inside a 16-token group / the Q tile)
-    uint32_t voK[IPGK], voV[IPGV];
-    int qrow[IPGK], qlp[IPGK];
-#pragma unroll
-    for (int m = 0; m < IPGK; ++m) {
-        const int x = m * 1024 + 16 * lane;
-        const int row = x / RBK;
-        const int lp = ((x % RBK) >> 4) ^ (row & 7);
-        voK[m] = row * rsk + 16 * lp;
-        qrow[m] = row;
-        qlp[m] = lp;
-    }
-#pragma unroll
-    for (int m = 0; m < IPGV; ++m) {
-        const int x = m * 1024 + 16 * lane;
-        const int row = x / RBV;
-        voV[m] = row * rsv + 16 * (((x % RBV) >> 4) ^ v_swz<RBV>(row));
-    }
-    // LDS read offsets (K and Q: row lr, piece 4 ks + lg; V: transposing read)
-    const int kq = 16 * (lg ^ (lr & 3));
-    const int kb2 = 64 * ((lr >> 2) & 1);
-    const int koE = lr * RBK + kq + kb2, koO = lr * RBK + kq - kb2;
-    constexpr int NVO = v_offsets<RBV>();
-    int vo[NVO];
-#pragma unroll
-    for (int m = 0; m < NVO; ++m) {
-        const int vrow = 4 * lg + (lr >> 2);
-        vo[m] = vrow * RBV + 16 * ((2 * m + ((lr & 3) >> 1)) ^ v_swz<RBV>(vrow)) + 8 * (lr & 1);
-    }
-
-    // ------------------------------------------------------------ issue side
-    int ipiece = worker;
-    Cursor ic;
-    int iend;
-    if (ipiece >= p.partitions || !wg_range(p, ipiece, ic, iend))
-        return;
-    int idone = 0, ifirst = 1;
-    int ic1 = 0, icb = 0, invis = 0, inblk = 1, ikv = 0, iql = 0, it0 = 0, irows = 0;
-    const int32_t *ibt = p.block_tables;
-    const char *ikg = kg, *ivg = vg;
-    auto iseg = [&]() __attribute__((always_inline)) {
-        icb = ic.c;
-        ic1 = ic.nch < ic.c + (iend - ic.item) ? ic.nch : ic.c + (iend - ic.item);
-        ikv = sload(p.ws.kvlen, ic.b);
-        iql = sload(p.ws.qlen, ic.b);
-        it0 = sload(p.ws.cu_q, ic.b);
-        irows = iql * G - ic.qt * 16;
-        irows = irows < 16 ? irows : 16;
-        invis = tile_nvis(ikv, iql, G, ic.qt * 16 + irows - 1, p.causal);
-        inblk = invis > 0 ? div_bs(invis - 1, bs, bsh) + 1 : 1;
-        ibt = p.block_tables + (size_t)ic.b * p.max_blocks;
-        ikg = kg + (size_t)ic.g * RBK;
-        ivg = vg + (size_t)ic.g * p.v_head_bytes;
-    };
-    iseg();
-    int ibid[NTT];
-    auto ifetch = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < NTT; ++q) {
-            const int blk = div_bs(ic.c * KT + 16 * q, bs, bsh);
-            ibid[q] = sload(ibt, blk < inblk ? blk : inblk - 1);
-        }
-    };
-    ifetch();
-    int n_issued = 0;
-    // Issue the next chunk of the stream into stage st (nothing once done).
-    auto issue = [&](int st) __attribute__((always_inline)) {
-        if (idone)
-            return;
-        const bool seg_begin = ic.c == icb;
-        if (seg_begin) {
-            // Q tile of the segment (rows past the unit read the zero page)
-#pragma unroll
-            for (int m = 0; m < IPGK; ++m) {
-                const int rg = ic.qt * 16 + qrow[m];
-                const int t = it0 + rg / G;
-                const bool ok = qrow[m] < irows && t < p.num_q_tokens;
-                const char *src = ok ? (const char *)(qg + ((size_t)t * H + ic.g * G + rg % G) * DK + 8 * qlp[m])
-                                     : zg + 16 * qlp[m];
-                lds_load16(src, (lds_u8 *)sQ + st * STQ + m * 1024);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < NTT; ++q) {
-            const int j0 = ic.c * KT + 16 * q;
-            const bool vis = j0 < invis;
-            const bool inb = (unsigned)ibid[q] < nb32;
-            err |= (vis && !inb) ? (uint32_t)PA_DEVERR_BLOCK_ID : 0u;
-            const size_t trow = (size_t)ibid[q] * bs + mod_bs(j0, bs, bsh);
-            const char *kbase = (vis && inb) ? ikg + trow * rsk : zg;
-            const char *vbase = (vis && inb) ? ivg + trow * rsv : zg;
-#pragma unroll
-            for (int m = 0; m < IPGK; ++m)
-                lds_load16(kbase + voK[m], (lds_u8 *)sK + st * STK + (q * IPGK + m) * 1024);
-#pragma unroll
-            for (int m = 0; m < IPGV; ++m)
-                lds_load16(vbase + voV[m], (lds_u8 *)sV + st * STV + (q * IPGV + m) * 1024);
-        }
-        const bool seg_end = ic.c + 1 == ic1;
-        if (lane == 0) {
-            int *md = s_meta + st * MW;
-            md[0] = ic.b;
-            md[1] = ic.g;
-            md[2] = ic.qt;
-            md[3] = ic.c;
-            md[4] = (seg_begin ? 1 : 0) | (seg_end ? 2 : 0) | ((icb == 0 && ic1 == ic.nch) ? 4 : 0) | (ifirst ? 8 : 0);
-            md[5] = ipiece;
-            md[6] = invis;
-            md[7] = ikv;
-            md[8] = iql;
-            md[9] = it0;
-            md[10] = irows;
-        }
-        ++n_issued;
-        // advance the issue position by one chunk
-        ++ic.c;
-        ++ic.item;
-        if (ic.c == ic1) {
-            ifirst = 0;
-            bool more = ic.item < iend;
-            if (more) {
-                cursor_next_unit(p, ic);
-                more = ic.b < p.batch;
-            }
-            idone = more ? 0 : 1;
-            if (!idone)
-                iseg();
-        }
-        if (!idone)
-            ifetch();
-    };
-
-    // ---------------------------------------------------------- compute side
-    u32x4 qb[KS];
-    f32x4 oacc[ND];
-    float m_run = -INFINITY, lsum = 0.f;
-    int lim = 0, min_lim = 0, nvis = 0, rows = 0, t0 = 0, kv = 0, ql = 0;
-
-#pragma unroll
-    for (int k = 0; k < S - 1; ++k)
-        issue(k);
-
-    for (int k = 0; k < n_issued; ++k) {
-        const int st = k % S;
-        wait_ahead<LW, S - 2>(n_issued - 1 - k);   // chunk k (and any earlier Q tile) is in LDS
-        int md[11];
-#pragma unroll
-        for (int i = 0; i < 11; ++i)
-            md[i] = __builtin_amdgcn_readfirstlane(s_meta[st * MW + i]);
-        issue((k + S - 1) % S);
-        const int b = md[0], g = md[1], qt = md[2], c = md[3], fl = md[4];
-        const lds_u8 *kb = (const lds_u8 *)sK + st * STK;
-        const lds_u8 *vb = (const lds_u8 *)sV + st * STV;
-        if (fl & 1) {
-            // first chunk of a segment: its Q tile and row limits
-            nvis = md[6];
-            kv = md[7];
-            ql = md[8];
-            t0 = md[9];
-            rows = md[10];
-            const lds_u8 *qs = (const lds_u8 *)sQ + st * STQ;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                qb[ks] = *(const lds_u32x4 *)(qs + ((ks & 1) ? koO : koE) + 64 * ks);
-                if (neg_scale)   // exact: softmax(c s) = softmax(|c| (-s)) with -s = (-q) . k
-                    qb[ks] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-            }
-            const int prefix = kv - ql > 0 ? kv - ql : 0;
-            const int rg = qt * 16 + lr;
-            lim = p.causal ? (prefix + rg / G + 1 < kv ? prefix + rg / G + 1 : kv) : kv;
-            min_lim = p.causal ? tile_nvis(kv, ql, G, qt * 16, 1) : kv;
-#pragma unroll
-            for (int nd = 0; nd < ND; ++nd)
-                oacc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-            m_run = -INFINITY;
-            lsum = 0.f;
-        }
-
-        // S^T = K . Q^T
-        const int jb = c * KT;
-        f32x4 sacc[NTT];
-#pragma unroll
-        for (int n = 0; n < NTT; ++n)
-            sacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int n = 0; n < NTT; ++n) {
-                const u32x4 a = *(const lds_u32x4 *)(kb + ((ks & 1) ? koO : koE) + 16 * n * RBK + 64 * ks);
-                sacc[n] = Mfma<DT>::run(a, qb[ks], sacc[n]);
-            }
-        }
-        // mask, online softmax (raw scores, lazy reference)
-        float mx = -INFINITY;
-        const bool need_mask = jb + KT > min_lim;
-#pragma unroll
-        for (int n = 0; n < NTT; ++n) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (need_mask) {
-                    const int j = jb + 16 * n + 4 * lg + r;
-                    sacc[n][r] = j < lim ? sacc[n][r] : -INFINITY;
-                }
-                mx = fmaxf(mx, sacc[n][r]);
-            }
-        }
-        mx = xor_max<16>(mx);
-        mx = xor_max<32>(mx);
-        if (__any(mx > m_run + grow_raw)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * sc);
-            lsum *= alpha;
-            m_run = m_new;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ar = __shfl(alpha, 4 * lg + r);
-#pragma unroll
-                for (int nd = 0; nd < ND; ++nd)
-                    oacc[nd][r] *= ar;
-            }
-        }
-        const float mref = m_run == -INFINITY ? 0.f : m_run * sc;
-        float ps = 0.f;
-#pragma unroll
-        for (int n = 0; n < NTT; ++n) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[n][r], sc, -mref));
-                sacc[n][r] = pv;
-                ps += pv;
-            }
-        }
-        lsum += ps;
-        // PV (V halves of tokens at or past nvis zeroed)
-        const bool tail = jb + KT > nvis;
-        if constexpr (KT == 16) {
-            const uint2 pa = uint2{pack2<DT>(sacc[0][0], sacc[0][1]), pack2<DT>(sacc[0][2], sacc[0][3])};
-            uint2 vm = {~0u, ~0u};
-            if (tail) {
-                const int tb = jb + 4 * lg;
-                vm.x = (tb < nvis ? 0xffffu : 0u) | (tb + 1 < nvis ? 0xffff0000u : 0u);
-                vm.y = (tb + 2 < nvis ? 0xffffu : 0u) | (tb + 3 < nvis ? 0xffff0000u : 0u);
-            }
-#pragma unroll
-            for (int nd = 0; nd < ND; ++nd) {
-                const v4i16 b0 =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + 32 * NVO * (nd / NVO)));
-                uint2 bv = __builtin_bit_cast(uint2, b0);
-                if (tail) {
-                    bv.x &= vm.x;
-                    bv.y &= vm.y;
-                }
-                oacc[nd] = Mfma16<DT>::run(pa, bv, oacc[nd]);
-            }
-        } else {
-            const u32x4 pa = u32x4{pack2<DT>(sacc[0][0], sacc[0][1]), pack2<DT>(sacc[0][2], sacc[0][3]),
-                                   pack2<DT>(sacc[1][0], sacc[1][1]), pack2<DT>(sacc[1][2], sacc[1][3])};
-            u32x4 vm = {~0u, ~0u, ~0u, ~0u};
-            if (tail) {
-                const int tb = jb + 4 * lg;
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int e = 0; e < 2; ++e)
-                        vm[2 * h2 + e] = (tb + 16 * h2 + 2 * e < nvis ? 0xffffu : 0u) |
-                                         (tb + 16 * h2 + 2 * e + 1 < nvis ? 0xffff0000u : 0u);
-            }
-#pragma unroll
-            for (int nd = 0; nd < ND; ++nd) {
-                const int off = 32 * NVO * (nd / NVO);
-                const v4i16 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + off));
-                const v4i16 b1 =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + off + 16 * RBV));
-                const uint2 lo = __builtin_bit_cast(uint2, b0), hi = __builtin_bit_cast(uint2, b1);
-                u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
-                if (tail)
-                    bv &= vm;
-                oacc[nd] = Mfma<DT>::run(pa, bv, oacc[nd]);
-            }
-        }
-
-        if (fl & 2) {
-            // last chunk of the segment: output or partial
-            const bool whole = fl & 4;
-            const int piece = md[5];
-            float *part = p.ws.partials + (size_t)(2 * piece + ((fl & 8) ? 0 : 1)) * p.partial_stride;
-            const float L = xor_sum<32>(xor_sum<16>(lsum));
-            const float Ms = m_run * sc;   // log2 domain
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float Lr = __shfl(L, 4 * lg + r);
-                const float Mr = __shfl(Ms, 4 * lg + r);
-                const int row_t = 4 * lg + r;
-                if (row_t >= rows)
-                    continue;
-                const int rg = qt * 16 + row_t;
-                const int t = t0 + rg / G;
-                const int h = g * G + rg % G;
-                if (whole) {
-                    if (t >= p.num_q_tokens)
-                        continue;
-                    const float inv = Lr > 0.f ? 1.f / Lr : 0.f;
-                    uint16_t *dst = og + ((size_t)t * H + h) * DV;
-#pragma unroll
-                    for (int nd = 0; nd < ND; ++nd)
-                        dst[16 * nd + lr] = to_bits<DT>(oacc[nd][r] * inv);
-                    if (lr == 0 && p.lse)
-                        p.lse[(size_t)t * H + h] = Lr > 0.f ? (Mr + log2f(Lr)) * 0.69314718055994531f : -INFINITY;
-                } else {
-#pragma unroll
-                    for (int nd = 0; nd < ND; ++nd)
-                        part[row_t * DV + 16 * nd + lr] = oacc[nd][r];
-                    if (lr == 0) {
-                        part[16 * DV + row_t] = Mr;
-                        part[16 * DV + 16 + row_t] = Lr;
-                    }
-                }
-            }
-        }
-    }
-    if (err)
-        set_error(p.ws.err, err);
-}
-
-// Variants per (Dk, Dv).  0: units of at most 16 rows (decode), memory-bound:
-// the streaming kernel (one wave, 16-token chunks, four stages).  1: up to
-// 64 rows.  2: more rows, two 16-row blocks per wave.  Dk = 576 has variant
-// 0 only: 4 waves of 16 rows each own all 512 output columns (no duplicated
-// K . Q^T work), two workgroups per CU: 16-token chunks in two stages (69 KB
-// of LDS), or with a shared K/V cache, where only K tiles are staged,
-// 32-token chunks in two stages (74 KB).
-
-struct TileShape {
-    int mb, kt, nw, cs, s;   // nw: waves that own rows
-    int threads;             // workgroup size
-};
-
-template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH = false>
-const void *pick(TileShape *t)
-{
-    *t = TileShape{MB, KT, NW, CS, S, 64 * NW};
-    return (const void *)&tile_kernel<DT, DK, DV, MB, KT, NW, CS, S, SH>;
-}
-
-template <int DT, int DK, int DV>
-const void *kernel_for(int variant, bool shared, TileShape *t)
-{
-    if constexpr (DK > 256) {
-        if (variant != 0)
-            return nullptr;
-        if (shared)
-            return pick<DT, DK, DV, 1, 32, 4, 1, 2, true>(t);
-        return pick<DT, DK, DV, 1, 16, 4, 1, 2>(t);
-    } else {
-        constexpr int KT = DK <= 128 ? 64 : 32;
-        if (variant == 0) {   // one wave per workgroup, streaming across units
-            *t = TileShape{1, 16, 1, 1, 4, 64};
-            return (const void *)&stream_kernel<DT, DK, DV, 16, 4>;
-        }
-        if (variant == 1)
-            return pick<DT, DK, DV, 1, KT, 4, 1, 2>(t);
-        if (variant == 2)
-            return pick<DT, DK, DV, 2, KT, 4, 1, 2>(t);
-        return nullptr;
-    }
-}
-
-template <int DT>
-const void *kernel_dt(int dk, int dv, int variant, bool shared, TileShape *t)
-{
-    if (dk == 64 && dv == 64)
-        return kernel_for<DT, 64, 64>(variant, shared, t);
-    if (dk == 128 && dv == 128)
-        return kernel_for<DT, 128, 128>(variant, shared, t);
-    if (dk == 256 && dv == 256)
-        return kernel_for<DT, 256, 256>(variant, shared, t);
-    if (dk == 576 && dv == 512)
-        return kernel_for<DT, 576, 512>(variant, shared, t);
-    return nullptr;
-}
-
-const void *tile_kernel_ptr(int dtype, int dk, int dv, int variant, bool shared, TileShape *t)
-{
-    return dtype == 0 ? kernel_dt<0>(dk, dv, variant, shared, t) : kernel_dt<1>(dk, dv, variant, shared, t);
+    return band ? tile_kernel_band(dtype, dk, dv, variant, shared, t)
+                : tile_kernel_plain(dtype, dk, dv, variant, shared, t);
 }
 
 }  // namespace
@@ -1122,10 +44,10 @@ bool tile_streaming(int dk, int dv, int variant)
     return tile_kernel_ptr(0, dk, dv, variant, false, &t) && t.nw == 1;
 }
 
-int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared)
+int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared, bool band)
 {
     TileShape t;
-    const void *k = tile_kernel_ptr(dtype, dk, dv, variant, shared, &t);
+    const void *k = tile_kernel_ptr(dtype, dk, dv, variant, shared, &t, band);
     int n = 0;
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, t.threads, 0) != hipSuccess || n < 1)
         return 1;
@@ -1135,7 +57,7 @@ int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared)
 hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s)
 {
     TileShape t;
-    const void *k = tile_kernel_ptr(dtype, p.head_size_k, p.head_size_v, variant, p.shared_kv != 0, &t);
+    const void *k = tile_kernel_ptr(dtype, p.head_size_k, p.head_size_v, variant, p.shared_kv != 0, &t, p.band != 0);
     if (!k)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&p};

@@ -15,11 +15,12 @@ Recipe (one seed per workload):
     id as the pages require of every entry;
   * blocks that no sequence references (the slack) keep their random values.
 
-The five named workloads follow the shapes, dtypes, length mixes and mask
-modes of the operator's documented use: decode (one query token per sequence),
-GQA decode, long skewed decode, parallel decoding / splitfuse with the causal
-mask aligned at prefix = kvSeqLen - qSeqLen, and single-KV-head decode with
-576/512 key/value head sizes.
+The named workloads follow the shapes, dtypes, length mixes and mask modes of
+the operator's documented use: decode (one query token per sequence), GQA
+decode, long skewed decode, parallel decoding / splitfuse with the causal
+mask aligned at prefix = kvSeqLen - qSeqLen, single-KV-head decode with
+576/512 key/value head sizes (also with one cache for K and V), and the band
+mask with a 127-token window (decode and splitfuse).
 """
 from __future__ import annotations
 
@@ -94,6 +95,13 @@ WORKLOADS = {
     # shared-KV form of the MLA decode: V is the first 512 elements of each K row
     6: Workload("mla_shared_kv_decode", 128, 64, 1, 576, 512, 128, "bf16", "none", 1.0 / math.sqrt(576),
                 _mla_lengths, seed=1006, shared_kv=True),
+    # band (sliding-window) mask with the window the pages fix (127 past
+    # tokens, none ahead): the shared-KV decode of 64 query heads on one KV
+    # head, and the splitfuse mix on the GQA shape
+    7: Workload("band_shared_kv_decode", 128, 64, 1, 576, 512, 128, "bf16", "band", 1.0 / math.sqrt(576),
+                _mla_lengths, seed=1007, shared_kv=True, window_left=127, window_right=0),
+    8: Workload("splitfuse_band", 32, 32, 8, 128, 128, 128, "f16", "band", 1.0 / math.sqrt(128),
+                _splitfuse_lengths, seed=1008, window_left=127, window_right=0),
 }
 
 

@@ -77,12 +77,16 @@ def test_config_struct_matches_header():
     dict(num_partitions=-1), dict(flags=binding.PA_FLAG_FORCE_VALU | binding.PA_FLAG_FORCE_MFMA),
     dict(flags=64), dict(flags=16),
     dict(flags=binding.PA_FLAG_SHARED_KV, head_size_k=64, head_size_v=128),
+    dict(mask=binding.PA_MASK_BAND, window_left=-1), dict(mask=binding.PA_MASK_BAND, window_right=-5),
+    dict(mask=binding.PA_MASK_BAND, window_left=(1 << 30) + 1),
 ])
 def test_create_rejects_invalid(lib, bad):
     assert create_status(lib, good_cfg(**bad)) == binding.PA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("shape", [dict(head_size_k=96, head_size_v=96), dict(head_size_k=128, head_size_v=64)])
+@pytest.mark.parametrize("shape", [dict(head_size_k=96, head_size_v=96), dict(head_size_k=128, head_size_v=64),
+                                   dict(mask=binding.PA_MASK_BAND, window_left=127,
+                                        flags=binding.PA_FLAG_FORCE_VALU)])
 def test_create_unsupported_shape(lib, shape):
     assert create_status(lib, good_cfg(**shape)) == binding.PA_ERR_UNSUPPORTED
 

@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
 
 Small problems are compared element by element; they span several chunks,
-several row tiles and ragged tails.  The six named workloads are compared at
+several row tiles and ragged tails.  The named workloads are compared at
 full size on sampled rows, with the launch configuration the benchmark uses.
 Probes check gathering, masking and poison handling bit for bit."""
 import math
@@ -218,6 +218,81 @@ def test_shared_kv_poison_and_arguments():
                         out.data_ptr(), None, None)
     assert st == binding.PA_ERR_INVALID_ARG
     assert att.device_error() == 0
+
+
+# ------------------------------------------------------------------- band mask
+BAND_CASES = [
+    # (lens, H, Hkv, Dk, Dv, bs, dtype, q_seq_lens, (left, right), shared)
+    ([300, 17, 128, 129, 1000, 2050], 32, 8, 128, 128, 128, "bf16", None, (127, 0), False),   # streaming
+    ([90, 47, 33, 400], 8, 2, 64, 64, 16, "f16", None, (5, 0), False),       # window inside one chunk
+    ([200, 70, 33], 8, 2, 64, 64, 16, "f16", [40, 5, 33], (20, 3), False),    # rows see ahead too
+    ([900, 300], 32, 8, 128, 128, 128, "f16", [512, 8], (127, 0), False),     # long chunk, most blocks skipped
+    ([1500, 77, 640], 64, 1, 576, 512, 128, "bf16", None, (127, 0), True),    # the pages' shape: 64 heads, 1 KV head
+    ([300, 70], 16, 1, 576, 512, 64, "f16", [5, 2], (40, 2), False),
+]
+
+
+@pytest.mark.parametrize("case", BAND_CASES, ids=lambda c: f"D{c[3]}_H{c[1]}_w{c[8][0]}_{c[8][1]}")
+def test_band_parity(case):
+    """Band mask: parity with the oracle, balanced and one worker per unit."""
+    lens, H, Hkv, Dk, Dv, bs, dt, ql, win, shared = case
+    log(f"band {case}")
+    p = synth.custom(lens, H, Hkv, Dk, Dv, bs, dt, "band", q_seq_lens=ql, seed=50 + Dk, shared_kv=shared,
+                     window=win)
+    check_full(p, what=f"band {case}")
+    check_full(p, flags=F.PA_FLAG_NO_SPLIT, what=f"band no-split {case}")
+
+
+def test_band_wide_windows_equal_causal_and_none():
+    """A window reaching past every sequence start is the causal mask when it
+    reaches nothing ahead, and no mask when it reaches past every end: the
+    same plan and arithmetic, so bit for bit."""
+    log("band limits")
+    for ql in ([7, 30], None):
+        p = synth.custom([200, 77], 16, 4, 128, 128, 64, "bf16", "causal" if ql else "none", q_seq_lens=ql,
+                         seed=57)
+        ref, ref_l, _ = run_hip(to_device(p))
+        q = synth.Problem(**{**p.__dict__})
+        q.workload = synth.Workload(**{**p.workload.__dict__, "mask": "band", "window_left": 1 << 30,
+                                       "window_right": 0 if ql else 1 << 30})
+        o, l, att = run_hip(to_device(q))
+        assert np.array_equal(ref, o) and np.array_equal(ref_l, l)
+        assert att.device_error() == 0
+
+
+def test_band_skips_blocks_before_the_window():
+    """Blocks wholly before every row's window are never read: their table
+    entries may be invalid and their contents NaN; NaN in the tokens of a
+    window's first block that lie before the window changes nothing either.
+    exp(lse) with q = 0 counts each row's window."""
+    log("band skips")
+    p = synth.custom([700, 129, 1000], 16, 4, 128, 128, 16, "f16", "band", q_seq_lens=[3, 1, 9], seed=58,
+                     window=(100, 0))
+    clean, clean_l, _ = run_hip(to_device(p))
+    bs = 16
+    for b in range(p.batch):
+        kv, q = int(p.context_lens_np[b]), int(p.q_seq_lens_np[b])
+        lo = max(0, kv - q - 100)          # lowest token any row of b sees
+        for blk in range(lo // bs):        # blocks wholly before it
+            p.key_cache[int(p.block_tables_np[b, blk])] = float("nan")
+            p.value_cache[int(p.block_tables_np[b, blk])] = float("nan")
+            p.block_tables_np[b, blk] = -7
+        first = int(p.block_tables_np[b, lo // bs])
+        p.key_cache[first, :lo % bs] = float("nan")
+        p.value_cache[first, :lo % bs] = float("nan")
+    o, l, att = run_hip(to_device(p))
+    assert np.array_equal(clean, o) and np.array_equal(clean_l, l)
+    assert att.device_error() == 0
+    p.query.zero_()
+    _, l, _ = run_hip(to_device(p))
+    t0 = 0
+    for b in range(p.batch):
+        kv, q = int(p.context_lens_np[b]), int(p.q_seq_lens_np[b])
+        for i in range(q):
+            pos = kv - q + i
+            count = min(kv, pos + 1) - max(0, pos - 100)
+            assert np.all(np.abs(np.exp(l[t0 + i]) - count) <= 1e-3 * count), (b, i)
+        t0 += q
 
 
 # ------------------------------------------------------------------ probes
@@ -443,3 +518,18 @@ def test_workload_mla_decode_sampled():
 
 def test_workload_mla_shared_kv_decode_sampled():
     full_size_sampled(6, 128, seed=4)
+
+
+def test_workload_band_shared_kv_decode_sampled():
+    full_size_sampled(7, 256, seed=5)
+
+
+def test_workload_splitfuse_band_sampled():
+    p, o, l = full_size_sampled(8, 256, seed=6)
+    # rows at the starts and ends of the prefill chunks
+    cu = np.concatenate([[0], np.cumsum(p.q_seq_lens_np)])
+    big = np.flatnonzero(p.q_seq_lens_np == 512)[:3]
+    toks = np.concatenate([[cu[b], cu[b] + 1, cu[b] + 200, cu[b + 1] - 1] for b in big]).astype(np.int32)
+    heads = (np.arange(len(toks)) * 5 % 32).astype(np.int32)
+    ro, rl = pa_ref.rows(pa_ref.Inputs.from_problem(p), toks, heads)
+    assert_close(o[toks, heads], ro, "f16", "splitfuse band chunk rows")
