@@ -47,6 +47,19 @@
  *    win_left counts the tokens before the query's own position, which is
  *    itself visible (the page is silent on the query's own token; this is
  *    the plain reading of a count of past tokens).
+ *  - Mask "tensor" (the shared compressed mask of mask type 5: one fp16
+ *    [2048, 2048] matrix for all sequences and heads, 0 where visible and a
+ *    large negative value such as -10000 above the diagonal; the operator
+ *    aligns it with prefix = max(0, kvSeqLen - qSeqLen) and adapts to
+ *    sequences longer than 2048 -- PagedAttention Constraints, mask type 5
+ *    list): the matrix is added to the scaled scores, row i of a sequence
+ *    against token j reading element [i][j - prefix].  History tokens
+ *    (j < prefix) are visible with nothing added.  Outside the matrix
+ *    (i >= 2048 or j - prefix >= 2048) the causal rule holds: visible with
+ *    nothing added if j - prefix <= i, invisible otherwise.  (The reading
+ *    of the alignment: the prefix shifts the columns, so the matrix covers
+ *    the current query tokens whatever the history length; for the pages'
+ *    triangular matrix every alignment gives the causal mask.)
  *  - Query/output rows are packed (TND): sequence b's rows start at
  *    t0 = q_seq_lens[0] + ... + q_seq_lens[b-1], the prefix-sum convention of
  *    cu_seqlens_q (SparseAttnSharedkvMetadata README, parameter table).
@@ -60,7 +73,8 @@
 #include <string.h>
 
 enum { REF_F16 = 0, REF_BF16 = 1 };
-enum { REF_MASK_NONE = 0, REF_MASK_CAUSAL = 1, REF_MASK_BAND = 2 };
+enum { REF_MASK_NONE = 0, REF_MASK_CAUSAL = 1, REF_MASK_BAND = 2, REF_MASK_TENSOR = 3 };
+enum { REF_MASK_DIM = 2048 };   /* the shared mask matrix is REF_MASK_DIM x REF_MASK_DIM */
 enum { REF_OK = 0, REF_BAD_ARG = -1, REF_BAD_BLOCK = -2, REF_BAD_LEN = -3, REF_NO_MEM = -4 };
 
 /* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
@@ -102,6 +116,7 @@ typedef struct {
     int32_t dtype, mask;
     double scale;
     int32_t win_left, win_right;   /* band mask only */
+    const uint16_t *mask_tensor;   /* tensor mask only: fp16 [REF_MASK_DIM][REF_MASK_DIM] */
     int64_t *row_start;  /* [batch + 1]: first packed query row of each sequence */
 } problem;
 
@@ -142,18 +157,25 @@ static int one_row(const problem *P, int b, int i, int h, double *z, double *o, 
         for (int d = 0; d < Dk; ++d)
             dot += elem(q, d, P->dtype) * elem(P->key_cache, krow + d, P->dtype);
         z[j] = P->scale * dot;
+        if (P->mask == REF_MASK_TENSOR) {
+            const int64_t c = (int64_t)tok - prefix;   /* column of the shifted mask */
+            if (c >= 0 && c < REF_MASK_DIM && i < REF_MASK_DIM)
+                z[j] += from_f16_bits(P->mask_tensor[(int64_t)i * REF_MASK_DIM + c]);
+            else if (c > i)
+                z[j] = -INFINITY;                     /* causal rule outside the matrix */
+        }
     }
 
-    if (n == 0) {
+    double zmax = -INFINITY;
+    for (int j = 0; j < n; ++j)
+        if (z[j] > zmax)
+            zmax = z[j];
+    if (n == 0 || zmax == -INFINITY) {   /* no visible token */
         for (int e = 0; e < Dv; ++e)
             o[e] = 0.0;
         *lse = -INFINITY;
         return REF_OK;
     }
-    double zmax = z[0];
-    for (int j = 1; j < n; ++j)
-        if (z[j] > zmax)
-            zmax = z[j];
     double wsum = 0.0;
     for (int j = 0; j < n; ++j) {
         z[j] = exp(z[j] - zmax);    /* z now holds the unnormalised weight */
@@ -273,8 +295,9 @@ static int setup(problem *P)
         P->head_size_v <= 0 || P->block_size <= 0 || P->max_num_blocks_per_seq < 0 ||
         P->num_blocks < 0 || P->head_num % P->kv_head_num != 0 ||
         (P->dtype != REF_F16 && P->dtype != REF_BF16) ||
-        (P->mask != REF_MASK_NONE && P->mask != REF_MASK_CAUSAL && P->mask != REF_MASK_BAND) ||
-        P->win_left < 0 || P->win_right < 0)
+        (P->mask != REF_MASK_NONE && P->mask != REF_MASK_CAUSAL && P->mask != REF_MASK_BAND &&
+         P->mask != REF_MASK_TENSOR) ||
+        P->win_left < 0 || P->win_right < 0 || (P->mask == REF_MASK_TENSOR && !P->mask_tensor))
         return REF_BAD_ARG;
     P->row_start = (int64_t *)malloc(sizeof(int64_t) * (size_t)(P->batch + 1));
     if (!P->row_start)
@@ -303,7 +326,7 @@ static int setup(problem *P)
         int32_t batch, int32_t num_q_tokens, int32_t head_num, int32_t kv_head_num,            \
         int32_t head_size_k, int32_t head_size_v, int32_t block_size, int64_t num_blocks,      \
         int32_t max_num_blocks_per_seq, int32_t dtype, int32_t mask, double scale,            \
-        int32_t win_left, int32_t win_right
+        int32_t win_left, int32_t win_right, const uint16_t *mask_tensor
 
 #define FILL_PROBLEM(P)                                                                        \
     do {                                                                                       \
@@ -317,6 +340,7 @@ static int setup(problem *P)
         (P).max_num_blocks_per_seq = max_num_blocks_per_seq; (P).dtype = dtype;                \
         (P).mask = mask; (P).scale = scale;                                                    \
         (P).win_left = win_left; (P).win_right = win_right;                                    \
+        (P).mask_tensor = mask_tensor;                                                         \
     } while (0)
 
 /*

@@ -53,6 +53,7 @@ class Workload:
     shared_kv: bool = False    # V rows are the first head_size_v elements of the K rows
     window_left: int = 0       # band mask: tokens before the query's position it sees
     window_right: int = 0      # band mask: tokens after it
+    mask_fill: float = -10000.0   # tensor mask: the value above the diagonal of the shared matrix
 
 
 def _tiny_lengths(rng):
@@ -135,6 +136,7 @@ class Problem:
     block_tables_np: np.ndarray
     num_blocks: int
     max_num_blocks_per_seq: int
+    mask_tensor: Optional[torch.Tensor] = None   # tensor mask: fp16 [MASK_DIM, MASK_DIM]
 
     @property
     def batch(self) -> int:
@@ -164,6 +166,26 @@ class Problem:
         ql = np.ones_like(kv) if self.q_seq_lens_np is None else self.q_seq_lens_np.astype(np.int64)
         lo = np.maximum(0, np.maximum(0, kv - ql) - w.window_left)
         return int(np.maximum(0, kv - lo).sum())
+
+
+MASK_DIM = 2048   # side of the shared mask matrix of the tensor mask
+
+
+def causal_mask_tensor(fill=-10000.0, device="cpu"):
+    """The shared compressed mask as the pages describe it: fp16
+    [MASK_DIM, MASK_DIM], ``fill`` above the diagonal, 0 on and below it."""
+    m = torch.zeros(MASK_DIM, MASK_DIM, dtype=torch.float16, device=device)
+    return m.masked_fill(torch.ones(MASK_DIM, MASK_DIM, dtype=torch.bool, device=device).triu(1), fill)
+
+
+def random_mask_tensor(seed, device="cpu", scale=2.0, neg_inf_frac=0.05):
+    """A mask matrix of seeded N(0, scale^2) values (fp16) with a fraction of
+    -inf entries: arbitrary additive values, not only 0 / large negative."""
+    m = _normal((MASK_DIM, MASK_DIM), torch.float32, seed, device) * scale
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) + 1)
+    holes = torch.rand(MASK_DIM, MASK_DIM, generator=gen, device=device) < neg_inf_frac
+    return m.masked_fill(holes, float("-inf")).to(torch.float16)
 
 
 def _normal(shape, dtype, seed, device, chunk_elems=1 << 26):
@@ -229,6 +251,7 @@ def generate(w: Workload, device="cpu", seed: Optional[int] = None, values=True,
         query=q, key_cache=kc, value_cache=vc,
         context_lens_np=kv, q_seq_lens_np=None if ql is None else np.asarray(ql, np.int32),
         block_tables_np=tables, num_blocks=nb, max_num_blocks_per_seq=int(tables.shape[1]),
+        mask_tensor=causal_mask_tensor(w.mask_fill, device) if w.mask == "tensor" else None,
     )
 
 

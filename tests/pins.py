@@ -500,4 +500,63 @@ def pin_band_lse_counts_window(lib):
             t0 += int(ql[b])
 
 
+def _tensor_mask_problem(p, m):
+    q = _with_mask(p, "tensor")
+    q.mask_tensor = m
+    return q
+
+
+def shifted_mask(m, q, kv):
+    """The additive [q, kv] mask a sequence's rows take from the shared
+    matrix m, built with torch indexing: 0 over the history (columns below
+    prefix), m[i, j - prefix] inside the matrix, and outside it 0 on and
+    below the diagonal, -inf above it."""
+    prefix = max(0, kv - q)
+    D = m.shape[0]
+    out = torch.zeros(q, kv, dtype=torch.float64)
+    i = torch.arange(q)[:, None]
+    c = torch.arange(kv)[None, :] - prefix
+    inside = (c >= 0) & (c < D) & (i < D)
+    mf = m.to(torch.float64)
+    out[inside] = mf[i.expand(q, kv)[inside], c.expand(q, kv)[inside]]
+    out[(~inside) & (c > i)] = -math.inf
+    return out
+
+
+def pin_tensor_mask_pages_matrix_is_causal(lib):
+    """The pages' shared matrix (-10000 or -60000 above the diagonal) gives
+    exactly the causal result: the masked weights underflow to 0."""
+    for fill in (-10000.0, -60000.0):
+        m = synth.causal_mask_tensor(fill)
+        for p in causal_cases():
+            o, l = run(lib, p)
+            ot, lt = run(lib, _tensor_mask_problem(p, m))
+            assert np.array_equal(o, ot) and np.array_equal(l, lt), fill
+
+
+def pin_tensor_mask_is_additive(lib):
+    """Arbitrary matrix values (N(0, 4), some -inf) are added to the scaled
+    scores: torch SDPA with the shifted additive mask."""
+    m = synth.random_mask_tensor(150)
+    for p in list(causal_cases())[:2] + [
+            synth.custom([30, 50], 4, 2, 32, 32, 16, "f16", "causal", q_seq_lens=[3, 6], seed=151)]:
+        pt = _tensor_mask_problem(p, m)
+        o, l = run(lib, pt)
+        ro, rl = sdpa_reference(pt, lambda q, kv: shifted_mask(m, q, kv))
+        close(o, ro)
+        close(l, rl)
+
+
+def pin_tensor_mask_beyond_the_matrix(lib):
+    """Rows past the matrix (query index >= 2048) and columns past it follow
+    the causal rule, as the pages say longer sequences are handled."""
+    m = synth.random_mask_tensor(152)
+    p = synth.custom([2150], 1, 1, 16, 16, 16, "f16", "causal", q_seq_lens=[2100], seed=153)
+    pt = _tensor_mask_problem(p, m)
+    o, l = run(lib, pt, threads=4)
+    ro, rl = sdpa_reference(pt, lambda q, kv: shifted_mask(m, q, kv))
+    close(o, ro, rtol=1e-10, atol=1e-11)
+    close(l, rl, rtol=1e-10, atol=1e-11)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

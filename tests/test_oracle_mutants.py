@@ -51,6 +51,10 @@ MUTANTS = [
     ("shared_v_last_columns", "const uint16_t *vsrc = P->value_cache ? P->value_cache : P->key_cache;",
      "const uint16_t *vsrc = P->value_cache ? P->value_cache : P->key_cache + (Dk - Dv);"),
     ("exp_without_shift_in_lse", "*lse = zmax + log(wsum);", "*lse = log(wsum);"),
+    ("tensor_bias_subtracted", "z[j] += from_f16_bits(P->mask_tensor", "z[j] -= from_f16_bits(P->mask_tensor"),
+    ("tensor_transposed", "P->mask_tensor[(int64_t)i * REF_MASK_DIM + c]", "P->mask_tensor[(int64_t)c * REF_MASK_DIM + i]"),
+    ("tensor_columns_not_shifted", "const int64_t c = (int64_t)tok - prefix;", "const int64_t c = (int64_t)tok;"),
+    ("tensor_all_visible_outside", "else if (c > i)\n                z[j] = -INFINITY;", "else if (0)\n                z[j] = -INFINITY;"),
 ]
 
 
@@ -74,4 +78,5 @@ def test_mutant_is_caught(tmp_path, name, old, new):
             pin(lib)
         except (AssertionError, ValueError):
             caught.append(pin.__name__)
+            break   # one pin that fails is enough
     assert caught, f"mutant {name} passes every pin"
