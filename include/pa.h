@@ -27,7 +27,16 @@
  *     prefix + i - window_left <= j <= prefix + i + window_right.  Masked
  *     tokens get weight exactly 0, and the chunks of KV blocks that no row
  *     of a tile sees are neither planned nor read (block-table entries of
- *     blocks wholly before a band are never used);
+ *     blocks wholly before a band are never used); PA_MASK_TENSOR: the
+ *     shared compressed mask of mask type 5 (Constraints, mask type 5
+ *     list: one fp16 [2048, 2048] matrix for all sequences and heads, 0 where
+ *     visible, a large negative value such as -10000 above the diagonal,
+ *     aligned by the prefix, longer sequences handled) is added to the
+ *     scaled scores: row i against token j adds element [i][j - prefix];
+ *     history tokens (j < prefix) are visible with nothing added; outside
+ *     the matrix (i >= 2048 or j - prefix >= 2048) token j is visible with
+ *     nothing added if j - prefix <= i and invisible otherwise.  Every
+ *     token j < context_lens[b] is computed (the matrix decides its weight);
  *   - query and output rows are packed (TND): sequence b's rows start at
  *     t0 = q_seq_lens[0] + ... + q_seq_lens[b-1] (the cu_seqlens_q prefix-sum
  *     convention of the SparseAttnSharedkvMetadata README, parameter table);
@@ -76,7 +85,8 @@ typedef enum { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
 typedef enum {
     PA_MASK_NONE = 0,    /* maskType UNDEFINED: all context_lens[b] tokens visible */
     PA_MASK_CAUSAL = 1,  /* mask type 5 (parallel decoding / splitfuse), prefix-aligned */
-    PA_MASK_BAND = 2     /* sliding window (band mask mode 4), prefix-aligned like CAUSAL */
+    PA_MASK_BAND = 2,    /* sliding window (band mask mode 4), prefix-aligned like CAUSAL */
+    PA_MASK_TENSOR = 3   /* the shared compressed mask matrix (mask type 5), see pa_config.mask_tensor */
 } pa_mask;
 
 /* pa_config.flags */
@@ -118,6 +128,9 @@ typedef struct {
     int32_t window_left;             /* PA_MASK_BAND: tokens before a row's position it sees, in [0, 2^30];
                                         ignored otherwise */
     int32_t window_right;            /* PA_MASK_BAND: tokens after it, in [0, 2^30]; ignored otherwise */
+    const void *mask_tensor;         /* PA_MASK_TENSOR: device pointer to the shared fp16 [2048, 2048]
+                                        mask matrix, owned by the caller and kept alive and unchanged
+                                        while the handle is used; ignored otherwise */
 } pa_config;
 
 typedef struct pa_handle pa_handle;
@@ -127,12 +140,14 @@ typedef struct pa_handle pa_handle;
  * current HIP device.  Rules checked before any HIP call (PA_ERR_INVALID_ARG):
  * H, Hkv > 0 and H % Hkv == 0; 0 < Dk, Dv <= 576; block_size > 0,
  * block_size % 16 == 0, block_size <= 256, and block_size <= 128 in causal
- * mode or when Dk or Dv > 256; window sizes in [0, 2^30] in band mode; num_blocks > 0; max_batch > 0;
+ * mode or when Dk or Dv > 256; window sizes in [0, 2^30] in band mode;
+ * a non-NULL mask_tensor in tensor mode; num_blocks > 0; max_batch > 0;
  * max_num_blocks_per_seq > 0; max_q_seq_len > 0; dtype and mask in range;
  * scale finite; num_partitions >= 0; only PA_FLAG_* bits, not FORCE_VALU
  * with FORCE_MFMA; Dv <= Dk with PA_FLAG_SHARED_KV.  PA_ERR_UNSUPPORTED: a (Dk, Dv) pair this
  * build has no kernels for (64/64, 128/128, 256/256, 576/512 are built),
- * PA_FLAG_FORCE_VALU with the band mask, or a device that is not gfx950.  On success *out receives the handle.
+ * PA_FLAG_FORCE_VALU with any mask other than PA_MASK_NONE, or a device
+ * that is not gfx950.  On success *out receives the handle.
  */
 pa_status pa_create(const pa_config *cfg, pa_handle **out);
 

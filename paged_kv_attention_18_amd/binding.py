@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_OOM = range(5)
 PA_F16, PA_BF16 = 0, 1
-PA_MASK_NONE, PA_MASK_CAUSAL, PA_MASK_BAND = 0, 1, 2
+PA_MASK_NONE, PA_MASK_CAUSAL, PA_MASK_BAND, PA_MASK_TENSOR = 0, 1, 2, 3
 PA_FLAG_FORCE_VALU, PA_FLAG_FORCE_MFMA, PA_FLAG_NO_SPLIT, PA_FLAG_SHARED_KV = 1, 2, 4, 8
 PA_DEVERR_BLOCK_ID, PA_DEVERR_TABLE_SHORT, PA_DEVERR_QLEN, PA_DEVERR_TOKENS, PA_DEVERR_CTX = 1, 2, 4, 8, 16
 
@@ -46,6 +46,7 @@ class pa_config(ctypes.Structure):
         ("num_partitions", ctypes.c_int32),
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
+        ("mask_tensor", ctypes.c_void_p),
     ]
 
 
@@ -165,17 +166,23 @@ class Attention:
 
     def __init__(self, head_num, kv_head_num, head_size_k, head_size_v, block_size, num_blocks,
                  max_batch, max_num_blocks_per_seq, max_q_seq_len=1, dtype=torch.float16,
-                 scale=None, mask="none", flags=0, num_partitions=0, window=(0, 0)):
+                 scale=None, mask="none", flags=0, num_partitions=0, window=(0, 0), mask_tensor=None):
         if dtype not in _TORCH_DT:
             raise ValueError("dtype must be torch.float16 or torch.bfloat16")
         if scale is None:
             scale = head_size_k ** -0.5
         self.dtype = dtype
+        if mask == "tensor":
+            # the shared fp16 [2048, 2048] matrix; kept referenced by the handle
+            self._need(mask_tensor, "mask_tensor", torch.float16, (2048, 2048))
+        self.mask_tensor = mask_tensor if mask == "tensor" else None
         self.cfg = pa_config(head_num, kv_head_num, head_size_k, head_size_v, block_size, num_blocks,
                              max_batch, max_num_blocks_per_seq, max_q_seq_len, _TORCH_DT[dtype],
                              float(scale),
-                             {"none": PA_MASK_NONE, "causal": PA_MASK_CAUSAL, "band": PA_MASK_BAND}[mask],
-                             int(flags), int(num_partitions), int(window[0]), int(window[1]))
+                             {"none": PA_MASK_NONE, "causal": PA_MASK_CAUSAL, "band": PA_MASK_BAND,
+                              "tensor": PA_MASK_TENSOR}[mask],
+                             int(flags), int(num_partitions), int(window[0]), int(window[1]),
+                             self.mask_tensor.data_ptr() if self.mask_tensor is not None else None)
         self.handle = pa_create(self.cfg)
 
     def close(self):
@@ -257,7 +264,7 @@ def for_problem(p, **kw):
                 head_size_v=w.head_size_v, block_size=w.block_size, num_blocks=p.num_blocks,
                 max_batch=p.batch, max_num_blocks_per_seq=p.max_num_blocks_per_seq,
                 max_q_seq_len=max(1, p.max_q_seq_len), dtype=DTYPES[w.dtype], scale=w.scale, mask=w.mask,
-                window=(w.window_left, w.window_right))
+                window=(w.window_left, w.window_right), mask_tensor=p.mask_tensor)
     args.update(kw)
     if w.shared_kv:
         args["flags"] = args.get("flags", 0) | PA_FLAG_SHARED_KV

@@ -49,7 +49,9 @@ size_t partial_floats(int rows, int dv)
 }
 
 bool valid_dtype(int d) { return d == PA_F16 || d == PA_BF16; }
-bool valid_mask(int m) { return m == PA_MASK_NONE || m == PA_MASK_CAUSAL || m == PA_MASK_BAND; }
+bool valid_mask(int m) { return m == PA_MASK_NONE || m == PA_MASK_CAUSAL || m == PA_MASK_BAND || m == PA_MASK_TENSOR; }
+
+int kernel_mode(int mask) { return mask == PA_MASK_BAND ? 1 : (mask == PA_MASK_TENSOR ? 2 : 0); }
 
 }  // namespace
 
@@ -90,13 +92,15 @@ struct pa_handle {
             v.path = 1;
             const int dk = cfg.head_size_k, dv = cfg.head_size_v;
             const bool sh = (cfg.flags & PA_FLAG_SHARED_KV) != 0;
+            const int mode = kernel_mode(cfg.mask);   // the kernels' shapes depend on the mode
             int var = 0;
-            if (rows > 16 && pa::tile_supported(dk, dv, 1))
-                var = (rows > pa::tile_rows(dk, dv, 1, sh) && pa::tile_supported(dk, dv, 2)) ? 2 : 1;
+            if (rows > 16 && pa::tile_supported(dk, dv, 1))   // (no variant 2 with the tensor mask)
+                var = (rows > pa::tile_rows(dk, dv, 1, sh, mode) && pa::tile_supported(dk, dv, 2) &&
+                       cfg.mask != PA_MASK_TENSOR) ? 2 : 1;
             v.tile_variant = var;
-            v.rows_per_tile = pa::tile_rows(dk, dv, var, sh);
-            v.chunk = pa::tile_chunk(dk, dv, var, sh);
-            v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var, sh, cfg.mask == PA_MASK_BAND);
+            v.rows_per_tile = pa::tile_rows(dk, dv, var, sh, mode);
+            v.chunk = pa::tile_chunk(dk, dv, var, sh, mode);
+            v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var, sh, mode);
             v.pieces_per_worker = var == 0 ? 1 : kMaxPiecesPerWorker;
         }
         if (cfg.num_partitions > 0)
@@ -144,6 +148,8 @@ static pa_status check_config(const pa_config *c)
     if (c->mask == PA_MASK_BAND && (c->window_left < 0 || c->window_left > (1 << 30) || c->window_right < 0 ||
                                     c->window_right > (1 << 30)))
         return PA_ERR_INVALID_ARG;
+    if (c->mask == PA_MASK_TENSOR && !c->mask_tensor)
+        return PA_ERR_INVALID_ARG;
     // Item indices are int32 on the device: bound the largest possible count.
     const int G = c->head_num / c->kv_head_num;
     const double tiles = std::ceil((double)c->max_q_seq_len * G / 16.0);
@@ -157,8 +163,11 @@ static pa_status check_config(const pa_config *c)
     const bool til = pa::tile_supported(c->head_size_k, c->head_size_v, 0);
     if (!dec && !til)
         return PA_ERR_UNSUPPORTED;
-    if ((c->flags & PA_FLAG_FORCE_VALU) && (!dec || c->mask == PA_MASK_BAND))
-        return PA_ERR_UNSUPPORTED;   // the VALU kernel has no lower visibility bound
+    // The VALU kernel serves decode without a mask only: it has neither a
+    // lower visibility bound nor the matrix, and its causal mode is switched
+    // off (a GPU memory fault was seen once in a causal run, cause not found).
+    if ((c->flags & PA_FLAG_FORCE_VALU) && (!dec || c->mask != PA_MASK_NONE))
+        return PA_ERR_UNSUPPORTED;
     if ((c->flags & PA_FLAG_FORCE_MFMA) && !til)
         return PA_ERR_UNSUPPORTED;
     if (!til && (int64_t)c->max_q_seq_len * G > 8)
@@ -350,6 +359,8 @@ pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, con
     p.band = c.mask == PA_MASK_BAND;
     p.win_left = p.band ? c.window_left : 0;
     p.win_right = p.band ? c.window_right : 0;
+    p.tmask = c.mask == PA_MASK_TENSOR;
+    p.mask_tensor = p.tmask ? (const uint16_t *)c.mask_tensor : nullptr;
     p.scale_log2 = c.scale * 1.4426950408889634f;
     p.rows_per_tile = v.rows_per_tile;
     p.chunk = v.chunk;

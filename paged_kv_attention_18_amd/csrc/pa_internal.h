@@ -60,6 +60,8 @@ struct Params {
     int32_t causal;                    // row-dependent upper limit (causal or band mask)
     int32_t band;                      // band mask: row-dependent lower limit as well
     int32_t win_left, win_right;       // band mask window (0, 0 otherwise)
+    int32_t tmask;                     // tensor mask: the shared matrix is added to the scores
+    const uint16_t *mask_tensor;       // fp16 [2048, 2048] (tensor mask only)
     float scale_log2;                  // scale * log2(e)
     int32_t rows_per_tile;             // R
     int32_t chunk;                     // CT
@@ -87,12 +89,12 @@ bool decode_supported(int dk, int dv);
 // MFMA tile kernel variants: 0 for units of at most 16 rows, 1 for up to
 // tile_rows(.., 1) rows, 2 above; tile_supported says which exist.
 // `shared` selects the kernels that read V out of the K tile already in LDS
-// (shared K/V cache) where such kernels exist; `band` the kernels with a
-// lower visibility bound per row (band mask).
+// (shared K/V cache) where such kernels exist; `mode` the kernels of a mask
+// kind with code of its own (0 none / causal, 1 band, 2 tensor).
 bool tile_supported(int dk, int dv, int variant);
-int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared, bool band);   // resident workgroups per CU
-int tile_chunk(int dk, int dv, int variant, bool shared);
-int tile_rows(int dk, int dv, int variant, bool shared);
+int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared, int mode);   // resident workgroups per CU
+int tile_chunk(int dk, int dv, int variant, bool shared, int mode);
+int tile_rows(int dk, int dv, int variant, bool shared, int mode);
 bool tile_streaming(int dk, int dv, int variant);   // served by the one-wave streaming kernel
 int decode_chunk(int dk, int rows_pad);
 int decode_workers_per_cu(int dtype, int dk, int dv, int rows_pad);   // resident waves per CU
@@ -106,6 +108,7 @@ struct TileShape {
 // Kernel instances without / with the band mask (nullptr: none for the shape).
 const void *tile_kernel_plain(int dtype, int dk, int dv, int variant, bool shared, TileShape *t);
 const void *tile_kernel_band(int dtype, int dk, int dv, int variant, bool shared, TileShape *t);
+const void *tile_kernel_tensor(int dtype, int dk, int dv, int variant, bool shared, TileShape *t);
 
 constexpr int kThreads = 256;        // threads per attention workgroup
 constexpr int kBtWindow = 256;       // block-table entries staged in LDS at a time

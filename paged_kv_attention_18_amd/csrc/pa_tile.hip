@@ -7,15 +7,18 @@ namespace pa {
 
 const void *tile_kernel_plain(int dtype, int dk, int dv, int variant, bool shared, TileShape *t)
 {
-    return kernel_select<false>(dtype, dk, dv, variant, shared, t);
+    return kernel_select<MODE_PLAIN>(dtype, dk, dv, variant, shared, t);
 }
 
 namespace {
 
-const void *tile_kernel_ptr(int dtype, int dk, int dv, int variant, bool shared, TileShape *t, bool band = false)
+const void *tile_kernel_ptr(int dtype, int dk, int dv, int variant, bool shared, TileShape *t, int mode = MODE_PLAIN)
 {
-    return band ? tile_kernel_band(dtype, dk, dv, variant, shared, t)
-                : tile_kernel_plain(dtype, dk, dv, variant, shared, t);
+    if (mode == MODE_BAND)
+        return tile_kernel_band(dtype, dk, dv, variant, shared, t);
+    if (mode == MODE_TENSOR)
+        return tile_kernel_tensor(dtype, dk, dv, variant, shared, t);
+    return tile_kernel_plain(dtype, dk, dv, variant, shared, t);
 }
 
 }  // namespace
@@ -26,16 +29,16 @@ bool tile_supported(int dk, int dv, int variant)
     return tile_kernel_ptr(0, dk, dv, variant, false, &t) != nullptr;
 }
 
-int tile_chunk(int dk, int dv, int variant, bool shared)
+int tile_chunk(int dk, int dv, int variant, bool shared, int mode)
 {
     TileShape t;
-    return tile_kernel_ptr(0, dk, dv, variant, shared, &t) ? t.kt : 0;
+    return tile_kernel_ptr(0, dk, dv, variant, shared, &t, mode) ? t.kt : 0;
 }
 
-int tile_rows(int dk, int dv, int variant, bool shared)
+int tile_rows(int dk, int dv, int variant, bool shared, int mode)
 {
     TileShape t;
-    return tile_kernel_ptr(0, dk, dv, variant, shared, &t) ? 16 * t.mb * (t.nw / t.cs) : 0;
+    return tile_kernel_ptr(0, dk, dv, variant, shared, &t, mode) ? 16 * t.mb * (t.nw / t.cs) : 0;
 }
 
 bool tile_streaming(int dk, int dv, int variant)
@@ -44,10 +47,10 @@ bool tile_streaming(int dk, int dv, int variant)
     return tile_kernel_ptr(0, dk, dv, variant, false, &t) && t.nw == 1;
 }
 
-int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared, bool band)
+int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared, int mode)
 {
     TileShape t;
-    const void *k = tile_kernel_ptr(dtype, dk, dv, variant, shared, &t, band);
+    const void *k = tile_kernel_ptr(dtype, dk, dv, variant, shared, &t, mode);
     int n = 0;
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, t.threads, 0) != hipSuccess || n < 1)
         return 1;
@@ -57,8 +60,10 @@ int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared, boo
 hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s)
 {
     TileShape t;
-    const void *k = tile_kernel_ptr(dtype, p.head_size_k, p.head_size_v, variant, p.shared_kv != 0, &t, p.band != 0);
-    if (!k)
+    const int mode = p.band ? MODE_BAND : (p.tmask ? MODE_TENSOR : MODE_PLAIN);
+    const void *k = tile_kernel_ptr(dtype, p.head_size_k, p.head_size_v, variant, p.shared_kv != 0, &t, mode);
+    // the plan was made for this kernel's chunk and tile sizes
+    if (!k || t.kt != p.chunk || 16 * t.mb * (t.nw / t.cs) != p.rows_per_tile)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&p};
     return hipLaunchKernel(k, dim3(p.partitions), dim3(t.threads), args, 0, s);

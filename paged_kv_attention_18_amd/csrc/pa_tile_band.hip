@@ -6,7 +6,7 @@ namespace pa {
 
 const void *tile_kernel_band(int dtype, int dk, int dv, int variant, bool shared, TileShape *t)
 {
-    return kernel_select<true>(dtype, dk, dv, variant, shared, t);
+    return kernel_select<MODE_BAND>(dtype, dk, dv, variant, shared, t);
 }
 
 }  // namespace pa

@@ -110,6 +110,37 @@ __device__ __forceinline__ void lds_load16(const void *src, lds_u8 *dst)
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
 }
 
+// 4 bytes per lane from global memory into LDS (lane l -> dst + 4 l); the
+// source must be 4-byte aligned.  Waited for like lds_load16.
+__device__ __forceinline__ void lds_load4(const void *src, lds_u8 *dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+}
+
+// Kernel modes: the mask kinds that need code of their own.
+enum { MODE_PLAIN = 0, MODE_BAND = 1, MODE_TENSOR = 2 };
+constexpr int kMaskDim = 2048;   // side of the shared mask matrix (tensor mask)
+
+// Tensor mask: per chunk, the slice of the shared matrix a tile needs is
+// staged in LDS next to the K/V tiles, one row per query index of the tile
+// (at most R), KT + 2 columns from an even start (dword-aligned loads).
+template <int KT>
+constexpr int slab_row_dwords()
+{
+    return (KT + 2) / 2;
+}
+template <int R, int KT>
+constexpr int slab_bytes()
+{
+    return ((R * slab_row_dwords<KT>() + 63) / 64) * 256;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
 template <int DT>
 struct Mfma16;   // 16 x 16 x 16 products (PV over 16-token chunks)
 
@@ -173,14 +204,16 @@ constexpr int v_offsets()
 
 // Workgroups per CU the register budget is cut for: as many as fit in LDS
 // (at most 4; at most 2 with two 16-row blocks per wave, 1 at head sizes
-// above 128).  SH: no V tiles in LDS.
-template <int DK, int DV, int MB, int KT, int S, int NW, bool SH>
+// above 128).  SH: no V tiles in LDS.  TM: a tensor-mask slab per stage.
+template <int DK, int DV, int MB, int KT, int S, int NW, int CS, bool SH, bool TM>
 constexpr int tile_min_wgs()
 {
-    constexpr int lds = S * KT * 2 * (DK + (SH ? 0 : DV)) + 2048;
+    constexpr int lds = S * KT * 2 * (DK + (SH ? 0 : DV)) + 2048 +
+                        (TM ? S * slab_bytes<16 * MB * (NW / CS), KT>() : 0);
     constexpr int fit = (160 * 1024) / lds;
-    // waves per SIMD the registers allow: 2 with two 16-row blocks, else 4
-    constexpr int waves = MB == 2 ? ((DK > 128 || DV > 128) ? 1 : 2) : 4;
+    // waves per SIMD the registers allow: 2 with two 16-row blocks (1 at
+    // head sizes above 128), 2 at head sizes above 256, else 4
+    constexpr int waves = MB == 2 ? ((DK > 128 || DV > 128) ? 1 : 2) : (DK > 256 || DV > 256 ? 2 : 4);
     constexpr int cap = 4 * waves / NW > 0 ? 4 * waves / NW : 1;
     return fit < 1 ? 1 : (fit > cap ? cap : fit);
 }
@@ -191,12 +224,18 @@ constexpr int tile_min_wgs()
 // computed).  SH: shared K/V cache -- V is the leading Dv elements of each
 // K row, so only K tiles are loaded and the PV product reads its operand
 // from the K tile (the K swizzle keeps those transposing reads free of
-// bank conflicts as well).  BAND: band mask (rows also have a lower
+// bank conflicts as well).  MODE_BAND: band mask (rows also have a lower
 // visibility bound, and a unit starts at the chunk of its lowest visible
-// token); without it the lower bounds are the constant 0.
-template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH, bool BAND>
-__global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>())) void tile_kernel(Params p)
+// token); otherwise the lower bounds are the constant 0.  MODE_TENSOR: the
+// shared mask matrix is added to the scaled scores (row i, token j: element
+// [i][j - prefix]; history visible with nothing added; the causal rule
+// outside the matrix); the matrix slice of each chunk is staged in LDS with
+// the chunk, and the online softmax runs on scaled log2-domain scores.
+template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH, int MODE>
+__global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, CS, SH, MODE == MODE_TENSOR>()))
+void tile_kernel(Params p)
 {
+    constexpr bool BAND = MODE == MODE_BAND, TMASK = MODE == MODE_TENSOR;
     constexpr int RGS = NW / CS;                  // row groups
     constexpr int R = 16 * MB * RGS;              // rows per tile
     constexpr int RBK = 2 * DK, RBV = 2 * DV;     // LDS row bytes
@@ -211,6 +250,8 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
     constexpr int LW = NTT * (MK + MV);           // load instructions per wave per chunk, all waves alike
     constexpr bool PAD = MK * NW != IPGK || MV * NW != IPGV;
     constexpr int VTB = SH ? 16 : KT * RBV;       // bytes of a V stage buffer
+    constexpr int SDW = slab_row_dwords<KT>();
+    constexpr int SLB = TMASK ? slab_bytes<R, KT>() : 16;   // bytes of a mask slab stage
     static_assert(DK % 32 == 0 && DV % 64 == 0 && (KT == 16 || KT == 32 || KT == 64), "shape");
     static_assert(NW % CS == 0 && ND % 4 == 0 && S >= 2 && S <= 4, "split");
     static_assert(LW * (S - 2) < 64, "vmcnt range");
@@ -224,6 +265,10 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
     __shared__ __attribute__((aligned(1024))) uint8_t sV2[S > 2 ? VTB : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t sK3[S > 3 ? KT * RBK : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t sV3[S > 3 ? VTB : 16];
+    __shared__ __attribute__((aligned(256))) uint8_t sM0[SLB];
+    __shared__ __attribute__((aligned(256))) uint8_t sM1[SLB];
+    __shared__ __attribute__((aligned(256))) uint8_t sM2[S > 2 ? SLB : 16];
+    __shared__ __attribute__((aligned(256))) uint8_t sM3[S > 3 ? SLB : 16];
     // destination of the padding loads that keep every wave's count at LW
     __shared__ __attribute__((aligned(1024))) uint8_t sJunk[PAD ? 1024 : 16];
 
@@ -247,6 +292,7 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
     const char *__restrict__ kg = (const char *)p.key_cache;
     const char *__restrict__ vg = (const char *)p.value_cache;
     const char *__restrict__ zg = (const char *)p.ws.zeros;
+    const char *__restrict__ mg = (const char *)p.mask_tensor;
     uint16_t *__restrict__ og = (uint16_t *)p.out;
     const int G = p.group;
     const int H = p.head_num;
@@ -258,7 +304,10 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
     // Scores are kept raw (q . k) and scaled on the way into exp2 by
     // sc = |scale| log2(e); a negative scale is folded into Q.
     const bool neg_scale = p.scale_log2 < 0.f;
-    const float sc = fmaxf(fabsf(p.scale_log2), 1e-30f);   // scale 0: every visible token weighs 1
+    const float scq = fmaxf(fabsf(p.scale_log2), 1e-30f);   // scale 0: every visible token weighs 1
+    // Softmax domain: raw scores scaled by sc on the way into exp2 (with the
+    // tensor mask the scores are scaled first, and sc is 1).
+    const float sc = TMASK ? 1.f : scq;
     // The running max used as exp2 reference is only moved when a row's
     // max grows by more than 2^8 (P stays below 256, exact in the
     // 16-bit operand types); a moved reference rescales O and the sum.
@@ -325,6 +374,14 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
         const int min_lim = row_hi_t<BAND>(p, kv, prefix, (qt * R) / G);
         const int lo_tile = row_lo_t<BAND>(p, prefix, (qt * R) / G);
         const int max_lo = row_lo_t<BAND>(p, prefix, (qt * R + rows_tile - 1) / G);
+        // tensor mask: query indices [i0, i0 + nim) of the tile have matrix rows
+        const int i0 = (qt * R) / G;
+        int nim = 0;
+        if constexpr (TMASK) {
+            const int i1 = (qt * R + rows_tile - 1) / G;
+            nim = (i1 < kMaskDim - 1 ? i1 : kMaskDim - 1) - i0 + 1;
+            nim = nim > 0 ? nim : 0;
+        }
         const int wr0 = rgi * 16 * MB;
         const bool wave_active = wr0 < rows_tile;
         const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks;
@@ -378,7 +435,25 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
         // Groups wholly outside the tile's visible range read the zero page
         // (their block-table entries are not used); their rows are masked in
         // compute anyway.
-        auto issue = [&](int c, lds_u8 *kb, lds_u8 *vb) __attribute__((always_inline)) {
+        auto issue = [&](int c, lds_u8 *kb, lds_u8 *vb, lds_u8 *mb_) __attribute__((always_inline)) {
+            if constexpr (TMASK) {
+                // the matrix slice of chunk c (beyond the fixed LW loads per
+                // wave; extra loads only make the waits for later chunks
+                // wait longer)
+                const int c0m = c * KT - prefix;
+                if (c0m < kMaskDim && c0m + KT > 0 && nim > 0) {
+                    int cs = c0m & ~1;
+                    cs = cs < 0 ? 0 : (cs > kMaskDim - 2 * SDW ? kMaskDim - 2 * SDW : cs);
+                    const int ntot = nim * SDW;
+                    const int nin = (ntot + 63) / 64;
+                    for (int m = wave; m < nin; m += NW) {
+                        const int x = m * 64 + lane;
+                        const int r = x / SDW;
+                        const char *src = x < ntot ? mg + ((size_t)(i0 + r) * kMaskDim + cs) * 2 + 4 * (x - r * SDW) : mg;
+                        lds_load4(src, mb_ + m * 256);
+                    }
+                }
+            }
 #pragma unroll
             for (int q = 0; q < NTT; ++q) {
                 const int j0 = c * KT + 16 * q;
@@ -406,7 +481,7 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
         };
 
         // one chunk from (kb, vb): S^T, mask, online softmax, PV
-        auto compute = [&](const lds_u8 *kb, const lds_u8 *vb, int c) __attribute__((always_inline)) {
+        auto compute = [&](const lds_u8 *kb, const lds_u8 *vb, const lds_u8 *mb_, int c) __attribute__((always_inline)) {
             if (!wave_active)
                 return;
             const int jb = c * KT;
@@ -424,6 +499,38 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb)
                         sacc[mb][n] = Mfma<DT>::run(a, qb[mb][ks], sacc[mb][n]);
+                }
+            }
+            if constexpr (TMASK) {
+                // scaled log2-domain scores plus the matrix (log2 e times
+                // its value); outside the matrix the causal rule
+                const int c0m = jb - prefix;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int n = 0; n < NTT; ++n)
+                        sacc[mb][n] *= scq;
+                if (c0m + KT > 0) {
+                    int cs = c0m & ~1;
+                    cs = cs < 0 ? 0 : (cs > kMaskDim - 2 * SDW ? kMaskDim - 2 * SDW : cs);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const int i = (qt * R + wr0 + 16 * mb + lr) / G;
+                        const lds_u8 *row = mb_ + (i - i0) * (4 * SDW);
+#pragma unroll
+                        for (int n = 0; n < NTT; ++n) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int cj = c0m + 16 * n + 4 * lg + r;
+                                if ((unsigned)cj < (unsigned)kMaskDim && i < kMaskDim) {
+                                    const uint16_t hb = *(const __attribute__((address_space(3))) uint16_t *)(row + 2 * (cj - cs));
+                                    sacc[mb][n][r] = __builtin_fmaf(f16_bits_to_f32(hb), 1.4426950408889634f, sacc[mb][n][r]);
+                                } else if (cj > i) {
+                                    sacc[mb][n][r] = -INFINITY;
+                                }
+                            }
+                        }
+                    }
                 }
             }
             const bool need_mask = jb + KT > min_lim || (BAND && jb < max_lo);
@@ -549,6 +656,16 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
             else
                 return (lds_u8 *)sK3;
         };
+        auto mbuf = [&](auto st) __attribute__((always_inline)) -> lds_u8 * {
+            if constexpr (decltype(st)::value == 0)
+                return (lds_u8 *)sM0;
+            else if constexpr (decltype(st)::value == 1)
+                return (lds_u8 *)sM1;
+            else if constexpr (decltype(st)::value == 2)
+                return (lds_u8 *)sM2;
+            else
+                return (lds_u8 *)sM3;
+        };
         auto vbuf = [&](auto st) __attribute__((always_inline)) -> lds_u8 * {
             if constexpr (SH)
                 return kbuf(st);
@@ -568,8 +685,9 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
             wait_ahead<LW, S - 2>(c1 - 1 - c);     // this wave's loads of chunk c are in LDS
             __builtin_amdgcn_s_barrier();          // ... and every wave's; stage NX is free
             if (c + S - 1 < c1)
-                issue(c + S - 1, kbuf(std::integral_constant<int, NX>{}), vbuf(std::integral_constant<int, NX>{}));
-            compute(kbuf(st), vbuf(st), c);
+                issue(c + S - 1, kbuf(std::integral_constant<int, NX>{}), vbuf(std::integral_constant<int, NX>{}),
+                      mbuf(std::integral_constant<int, NX>{}));
+            compute(kbuf(st), vbuf(st), mbuf(st), c);
             if (c + S < c1)
                 fetch_bids(c + S);                 // scalar loads land during the next wait
         };
@@ -580,17 +698,20 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
         wait_vm<0>();
         __syncthreads();
         fetch_bids(c0);
-        issue(c0, kbuf(std::integral_constant<int, 0>{}), vbuf(std::integral_constant<int, 0>{}));
+        issue(c0, kbuf(std::integral_constant<int, 0>{}), vbuf(std::integral_constant<int, 0>{}),
+              mbuf(std::integral_constant<int, 0>{}));
         if constexpr (S > 2) {
             if (c0 + 1 < c1) {
                 fetch_bids(c0 + 1);
-                issue(c0 + 1, kbuf(std::integral_constant<int, 1>{}), vbuf(std::integral_constant<int, 1>{}));
+                issue(c0 + 1, kbuf(std::integral_constant<int, 1>{}), vbuf(std::integral_constant<int, 1>{}),
+                      mbuf(std::integral_constant<int, 1>{}));
             }
         }
         if constexpr (S > 3) {
             if (c0 + 2 < c1) {
                 fetch_bids(c0 + 2);
-                issue(c0 + 2, kbuf(std::integral_constant<int, 2>{}), vbuf(std::integral_constant<int, 2>{}));
+                issue(c0 + 2, kbuf(std::integral_constant<int, 2>{}), vbuf(std::integral_constant<int, 2>{}),
+                      mbuf(std::integral_constant<int, 2>{}));
             }
         }
         if (c0 + S - 1 < c1)
@@ -688,10 +809,13 @@ __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, SH>()
 // record, so the compute side never waits for a lookup.  A worker keeps
 // one piece: taking further pieces from a shared counter needs the atomic's
 // return, and waiting for it is a wait on every load of the in-order vector
-// memory counter, which drains the ring.  BAND as for the tile kernel.
-template <int DT, int DK, int DV, int KT, int S, bool BAND>
+// memory counter, which drains the ring.  MODE as for the tile kernel.
+template <int DT, int DK, int DV, int KT, int S, int MODE>
 __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
 {
+    constexpr bool BAND = MODE == MODE_BAND, TMASK = MODE == MODE_TENSOR;
+    constexpr int SDW = slab_row_dwords<KT>();
+    constexpr int SLB = TMASK ? slab_bytes<16, KT>() : 0;   // bytes of a mask slab stage
     constexpr int RBK = 2 * DK, RBV = 2 * DV;     // LDS row bytes
     constexpr int KS = DK / 32;
     constexpr int NTT = KT / 16;
@@ -707,6 +831,7 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
     __shared__ __attribute__((aligned(1024))) uint8_t sK[S * STK];
     __shared__ __attribute__((aligned(1024))) uint8_t sV[S * STV];
     __shared__ __attribute__((aligned(1024))) uint8_t sQ[S * STQ];
+    __shared__ __attribute__((aligned(256))) uint8_t sMk[TMASK ? S * SLB : 16];
     __shared__ int s_meta[S * MW];
 
     const int lane = threadIdx.x & 63;
@@ -718,6 +843,7 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
     const char *__restrict__ kg = (const char *)p.key_cache;
     const char *__restrict__ vg = (const char *)p.value_cache;
     const char *__restrict__ zg = (const char *)p.ws.zeros;
+    const char *__restrict__ mg = (const char *)p.mask_tensor;
     uint16_t *__restrict__ og = (uint16_t *)p.out;
     const int G = p.group;
     const int H = p.head_num;
@@ -727,7 +853,8 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
     const uint32_t rsv = p.v_row_bytes;
     const uint32_t nb32 = p.num_blocks < 0x7fffffff ? (uint32_t)p.num_blocks : 0x7fffffffu;
     const bool neg_scale = p.scale_log2 < 0.f;
-    const float sc = fmaxf(fabsf(p.scale_log2), 1e-30f);   // scale 0: every visible token weighs 1
+    const float scq = fmaxf(fabsf(p.scale_log2), 1e-30f);   // scale 0: every visible token weighs 1
+    const float sc = TMASK ? 1.f : scq;   // scores already scaled with the tensor mask
     const float grow_raw = 8.f / sc;
     uint32_t err = 0;
 
@@ -803,6 +930,28 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
     auto issue = [&](int st) __attribute__((always_inline)) {
         if (idone)
             return;
+        if constexpr (TMASK) {
+            // the matrix slice of the chunk: rows of the unit's query
+            // indices, KT + 2 columns from an even start (extra loads, see
+            // the tile kernel)
+            const int c0m = (icf + ic.c) * KT - seq_prefix(ikv, iql);
+            const int i0 = (ic.qt * 16) / G;
+            int i1 = (ic.qt * 16 + irows - 1) / G;
+            i1 = i1 < kMaskDim - 1 ? i1 : kMaskDim - 1;
+            const int nim = i1 - i0 + 1;
+            if (c0m < kMaskDim && c0m + KT > 0 && nim > 0) {
+                int cs = c0m & ~1;
+                cs = cs < 0 ? 0 : (cs > kMaskDim - 2 * SDW ? kMaskDim - 2 * SDW : cs);
+                const int ntot = nim * SDW;
+                const int nin = (ntot + 63) / 64;
+                for (int m = 0; m < nin; ++m) {
+                    const int x = m * 64 + lane;
+                    const int r = x / SDW;
+                    const char *src = x < ntot ? mg + ((size_t)(i0 + r) * kMaskDim + cs) * 2 + 4 * (x - r * SDW) : mg;
+                    lds_load4(src, (lds_u8 *)sMk + st * SLB + m * 256);
+                }
+            }
+        }
         const bool seg_begin = ic.c == icb;
         if (seg_begin) {
             // Q tile of the segment (rows past the unit read the zero page)
@@ -929,6 +1078,33 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
             for (int n = 0; n < NTT; ++n) {
                 const u32x4 a = *(const lds_u32x4 *)(kb + ((ks & 1) ? koO : koE) + 16 * n * RBK + 64 * ks);
                 sacc[n] = Mfma<DT>::run(a, qb[ks], sacc[n]);
+            }
+        }
+        if constexpr (TMASK) {
+            // scaled log2-domain scores plus the matrix; the causal rule
+            // outside it
+            const int c0m = jb - seq_prefix(kv, ql);
+#pragma unroll
+            for (int n = 0; n < NTT; ++n)
+                sacc[n] *= scq;
+            if (c0m + KT > 0) {
+                int cs = c0m & ~1;
+                cs = cs < 0 ? 0 : (cs > kMaskDim - 2 * SDW ? kMaskDim - 2 * SDW : cs);
+                const int i = (qt * 16 + lr) / G;
+                const lds_u8 *row = (const lds_u8 *)sMk + st * SLB + (i - (qt * 16) / G) * (4 * SDW);
+#pragma unroll
+                for (int n = 0; n < NTT; ++n) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int cj = c0m + 16 * n + 4 * lg + r;
+                        if ((unsigned)cj < (unsigned)kMaskDim && i < kMaskDim) {
+                            const uint16_t hb = *(const __attribute__((address_space(3))) uint16_t *)(row + 2 * (cj - cs));
+                            sacc[n][r] = __builtin_fmaf(f16_bits_to_f32(hb), 1.4426950408889634f, sacc[n][r]);
+                        } else if (cj > i) {
+                            sacc[n][r] = -INFINITY;
+                        }
+                    }
+                }
             }
         }
         // mask, online softmax (raw scores, lazy reference)
@@ -1074,56 +1250,68 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
 // of LDS), or with a shared K/V cache, where only K tiles are staged,
 // 32-token chunks in two stages (74 KB).
 
-template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH, bool BAND>
+template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH, int MODE>
 const void *pick(TileShape *t)
 {
     *t = TileShape{MB, KT, NW, CS, S, 64 * NW};
-    return (const void *)&tile_kernel<DT, DK, DV, MB, KT, NW, CS, S, SH, BAND>;
+    return (const void *)&tile_kernel<DT, DK, DV, MB, KT, NW, CS, S, SH, MODE>;
 }
 
-template <int DT, int DK, int DV, bool BAND>
+// The tensor mask has variants 0 and 1 only (variant 1 with 32-token
+// chunks, which leaves LDS room for the matrix slices); the host takes
+// variant 1 for every unit of more than 16 rows.
+template <int DT, int DK, int DV, int MODE>
 const void *kernel_for(int variant, bool shared, TileShape *t)
 {
     if constexpr (DK > 256) {
         if (variant != 0)
             return nullptr;
-        if (shared)
-            return pick<DT, DK, DV, 1, 32, 4, 1, 2, true, BAND>(t);
-        return pick<DT, DK, DV, 1, 16, 4, 1, 2, false, BAND>(t);
+        if (shared) {
+            if constexpr (MODE == MODE_TENSOR)
+                return pick<DT, DK, DV, 1, 16, 4, 1, 2, true, MODE>(t);
+            else
+                return pick<DT, DK, DV, 1, 32, 4, 1, 2, true, MODE>(t);
+        }
+        return pick<DT, DK, DV, 1, 16, 4, 1, 2, false, MODE>(t);
     } else {
         constexpr int KT = DK <= 128 ? 64 : 32;
         if (variant == 0) {   // one wave per workgroup, streaming across units
             *t = TileShape{1, 16, 1, 1, 4, 64};
-            return (const void *)&stream_kernel<DT, DK, DV, 16, 4, BAND>;
+            return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE>;
         }
-        if (variant == 1)
-            return pick<DT, DK, DV, 1, KT, 4, 1, 2, false, BAND>(t);
-        if (variant == 2)
-            return pick<DT, DK, DV, 2, KT, 4, 1, 2, false, BAND>(t);
+        if constexpr (MODE == MODE_TENSOR) {
+            if (variant == 1)
+                return pick<DT, DK, DV, 1, 32, 4, 1, 2, false, MODE>(t);
+        } else {
+            if (variant == 1)
+                return pick<DT, DK, DV, 1, KT, 4, 1, 2, false, MODE>(t);
+            if (variant == 2)
+                return pick<DT, DK, DV, 2, KT, 4, 1, 2, false, MODE>(t);
+        }
         return nullptr;
     }
 }
 
-template <int DT, bool BAND>
+template <int DT, int MODE>
 const void *kernel_dt(int dk, int dv, int variant, bool shared, TileShape *t)
 {
     if (dk == 64 && dv == 64)
-        return kernel_for<DT, 64, 64, BAND>(variant, shared, t);
+        return kernel_for<DT, 64, 64, MODE>(variant, shared, t);
     if (dk == 128 && dv == 128)
-        return kernel_for<DT, 128, 128, BAND>(variant, shared, t);
+        return kernel_for<DT, 128, 128, MODE>(variant, shared, t);
     if (dk == 256 && dv == 256)
-        return kernel_for<DT, 256, 256, BAND>(variant, shared, t);
+        return kernel_for<DT, 256, 256, MODE>(variant, shared, t);
     if (dk == 576 && dv == 512)
-        return kernel_for<DT, 576, 512, BAND>(variant, shared, t);
+        return kernel_for<DT, 576, 512, MODE>(variant, shared, t);
     return nullptr;
 }
 
 // The kernel (and its shape) for a configuration, from this translation
 // unit's instantiations.
-template <bool BAND>
+template <int MODE>
 const void *kernel_select(int dtype, int dk, int dv, int variant, bool shared, TileShape *t)
 {
-    return dtype == 0 ? kernel_dt<0, BAND>(dk, dv, variant, shared, t) : kernel_dt<1, BAND>(dk, dv, variant, shared, t);
+    return dtype == 0 ? kernel_dt<0, MODE>(dk, dv, variant, shared, t) : kernel_dt<1, MODE>(dk, dv, variant, shared, t);
 }
 
 }  // namespace

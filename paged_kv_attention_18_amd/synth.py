@@ -19,8 +19,9 @@ The named workloads follow the shapes, dtypes, length mixes and mask modes of
 the operator's documented use: decode (one query token per sequence), GQA
 decode, long skewed decode, parallel decoding / splitfuse with the causal
 mask aligned at prefix = kvSeqLen - qSeqLen, single-KV-head decode with
-576/512 key/value head sizes (also with one cache for K and V), and the band
-mask with a 127-token window (decode and splitfuse).
+576/512 key/value head sizes (also with one cache for K and V), the band
+mask with a 127-token window (decode and splitfuse), and splitfuse with the
+shared compressed mask matrix.
 """
 from __future__ import annotations
 
@@ -103,6 +104,11 @@ WORKLOADS = {
                 _mla_lengths, seed=1007, shared_kv=True, window_left=127, window_right=0),
     8: Workload("splitfuse_band", 32, 32, 8, 128, 128, 128, "f16", "band", 1.0 / math.sqrt(128),
                 _splitfuse_lengths, seed=1008, window_left=127, window_right=0),
+    # the splitfuse mix with the pages' own mask interface: the shared
+    # compressed 2048 x 2048 matrix (-10000 above the diagonal) added to the
+    # scores, every context token computed
+    9: Workload("splitfuse_tensor_mask", 32, 32, 8, 128, 128, 128, "f16", "tensor", 1.0 / math.sqrt(128),
+                _splitfuse_lengths, seed=1009),
 }
 
 

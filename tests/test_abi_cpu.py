@@ -73,7 +73,8 @@ def test_config_struct_matches_header():
     dict(block_size=256, mask=binding.PA_MASK_CAUSAL),
     dict(block_size=256, head_size_k=576, head_size_v=512),
     dict(num_blocks=0), dict(max_batch=0), dict(max_num_blocks_per_seq=0), dict(max_q_seq_len=0),
-    dict(dtype=7), dict(mask=3), dict(scale=float("inf")), dict(scale=float("nan")),
+    dict(dtype=7), dict(mask=4), dict(mask=binding.PA_MASK_TENSOR),   # (no matrix given)
+    dict(scale=float("inf")), dict(scale=float("nan")),
     dict(num_partitions=-1), dict(flags=binding.PA_FLAG_FORCE_VALU | binding.PA_FLAG_FORCE_MFMA),
     dict(flags=64), dict(flags=16),
     dict(flags=binding.PA_FLAG_SHARED_KV, head_size_k=64, head_size_v=128),
@@ -86,7 +87,8 @@ def test_create_rejects_invalid(lib, bad):
 
 @pytest.mark.parametrize("shape", [dict(head_size_k=96, head_size_v=96), dict(head_size_k=128, head_size_v=64),
                                    dict(mask=binding.PA_MASK_BAND, window_left=127,
-                                        flags=binding.PA_FLAG_FORCE_VALU)])
+                                        flags=binding.PA_FLAG_FORCE_VALU),
+                                   dict(mask=binding.PA_MASK_CAUSAL, flags=binding.PA_FLAG_FORCE_VALU)])
 def test_create_unsupported_shape(lib, shape):
     assert create_status(lib, good_cfg(**shape)) == binding.PA_ERR_UNSUPPORTED
 
