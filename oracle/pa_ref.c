@@ -60,6 +60,19 @@
  *    of the alignment: the prefix shifts the columns, so the matrix covers
  *    the current query tokens whatever the history length; for the pages'
  *    triangular matrix every alignment gives the causal mask.)
+ *  - Mask "sparse" (the compressed-KV stream of the SparseAttnSharedkvMetadata
+ *    README, parameter table: cmp_kv, the compression of ori_kv, from which
+ *    an index selector keeps cmp_topk tokens, 512 there, under mask mode 3,
+ *    rightDownCausal): the cache holds the compressed tokens, contextLens
+ *    counts them, and every query token t of sequence b carries, per KV
+ *    head g, a list of topk indices into them.  Row i of b (query head h,
+ *    KV head g) attends over the listed tokens c with 0 <= c < kv and
+ *    c <= prefix + i -- the causal mask aligned at the bottom right of the
+ *    (query, compressed token) matrix, as rightDownCausal reads.  Entries
+ *    outside that range (e.g. -1 padding of a short list) are skipped; every
+ *    other entry contributes once (a selector's list holds distinct
+ *    indices; a repeated entry would count twice).  The selector itself
+ *    is not described on the page; its lists are inputs here.
  *  - Query/output rows are packed (TND): sequence b's rows start at
  *    t0 = q_seq_lens[0] + ... + q_seq_lens[b-1], the prefix-sum convention of
  *    cu_seqlens_q (SparseAttnSharedkvMetadata README, parameter table).
@@ -73,7 +86,7 @@
 #include <string.h>
 
 enum { REF_F16 = 0, REF_BF16 = 1 };
-enum { REF_MASK_NONE = 0, REF_MASK_CAUSAL = 1, REF_MASK_BAND = 2, REF_MASK_TENSOR = 3 };
+enum { REF_MASK_NONE = 0, REF_MASK_CAUSAL = 1, REF_MASK_BAND = 2, REF_MASK_TENSOR = 3, REF_MASK_SPARSE = 4 };
 enum { REF_MASK_DIM = 2048 };   /* the shared mask matrix is REF_MASK_DIM x REF_MASK_DIM */
 enum { REF_OK = 0, REF_BAD_ARG = -1, REF_BAD_BLOCK = -2, REF_BAD_LEN = -3, REF_NO_MEM = -4 };
 
@@ -117,6 +130,8 @@ typedef struct {
     double scale;
     int32_t win_left, win_right;   /* band mask only */
     const uint16_t *mask_tensor;   /* tensor mask only: fp16 [REF_MASK_DIM][REF_MASK_DIM] */
+    const int32_t *topk_idx;       /* sparse only: [num_q_tokens][kv_head_num][topk] */
+    int32_t topk;
     int64_t *row_start;  /* [batch + 1]: first packed query row of each sequence */
 } problem;
 
@@ -143,11 +158,21 @@ static int one_row(const problem *P, int b, int i, int h, double *z, double *o, 
         if (pos + 1 + P->win_right < hi)
             hi = pos + 1 + P->win_right;
     }
-    const int n = hi > lo ? (int)(hi - lo) : 0;
+    int n = hi > lo ? (int)(hi - lo) : 0;
+    /* sparse: the entries of the row's list instead of a token range */
+    const int32_t *list = NULL;
+    if (P->mask == REF_MASK_SPARSE) {
+        list = P->topk_idx + (t * Hkv + g) * (int64_t)P->topk;
+        n = P->topk;
+    }
 
     const uint16_t *q = P->query + (t * H + h) * (int64_t)Dk;
     for (int j = 0; j < n; ++j) {
-        const int tok = (int)lo + j;
+        const int tok = list ? list[j] : (int)lo + j;
+        if (list && (tok < 0 || tok >= kv || tok > prefix + i)) {   /* skipped entry */
+            z[j] = -INFINITY;
+            continue;
+        }
         int32_t phys = P->block_tables[(int64_t)b * P->max_num_blocks_per_seq + tok / bs];
         if (phys < 0 || phys >= P->num_blocks)
             return REF_BAD_BLOCK;
@@ -191,7 +216,9 @@ static int one_row(const problem *P, int b, int i, int h, double *z, double *o, 
     const uint16_t *vsrc = P->value_cache ? P->value_cache : P->key_cache;
     const int vstride = P->value_cache ? Dv : Dk;
     for (int j = 0; j < n; ++j) {
-        const int tok = (int)lo + j;
+        const int tok = list ? list[j] : (int)lo + j;
+        if (list && (tok < 0 || tok >= kv || tok > prefix + i))    /* skipped entry */
+            continue;
         int32_t phys = P->block_tables[(int64_t)b * P->max_num_blocks_per_seq + tok / bs];
         int slot = tok % bs;
         const int64_t vrow = (((int64_t)phys * bs + slot) * Hkv + g) * vstride;
@@ -266,7 +293,7 @@ static int run_items(const problem *P, const int32_t *seq, const int32_t *pos, c
     W.n_items = n_items;
     W.out = out;
     W.lse = lse;
-    W.max_kv = max_kv;
+    W.max_kv = P->mask == REF_MASK_SPARSE && P->topk > max_kv ? P->topk : max_kv;
     pthread_mutex_init(&W.lock, NULL);
     if (num_threads < 1)
         num_threads = 1;
@@ -296,8 +323,9 @@ static int setup(problem *P)
         P->num_blocks < 0 || P->head_num % P->kv_head_num != 0 ||
         (P->dtype != REF_F16 && P->dtype != REF_BF16) ||
         (P->mask != REF_MASK_NONE && P->mask != REF_MASK_CAUSAL && P->mask != REF_MASK_BAND &&
-         P->mask != REF_MASK_TENSOR) ||
-        P->win_left < 0 || P->win_right < 0 || (P->mask == REF_MASK_TENSOR && !P->mask_tensor))
+         P->mask != REF_MASK_TENSOR && P->mask != REF_MASK_SPARSE) ||
+        P->win_left < 0 || P->win_right < 0 || (P->mask == REF_MASK_TENSOR && !P->mask_tensor) ||
+        (P->mask == REF_MASK_SPARSE && (!P->topk_idx || P->topk <= 0)))
         return REF_BAD_ARG;
     P->row_start = (int64_t *)malloc(sizeof(int64_t) * (size_t)(P->batch + 1));
     if (!P->row_start)
@@ -326,7 +354,8 @@ static int setup(problem *P)
         int32_t batch, int32_t num_q_tokens, int32_t head_num, int32_t kv_head_num,            \
         int32_t head_size_k, int32_t head_size_v, int32_t block_size, int64_t num_blocks,      \
         int32_t max_num_blocks_per_seq, int32_t dtype, int32_t mask, double scale,            \
-        int32_t win_left, int32_t win_right, const uint16_t *mask_tensor
+        int32_t win_left, int32_t win_right, const uint16_t *mask_tensor,                      \
+        const int32_t *topk_idx, int32_t topk
 
 #define FILL_PROBLEM(P)                                                                        \
     do {                                                                                       \
@@ -340,7 +369,7 @@ static int setup(problem *P)
         (P).max_num_blocks_per_seq = max_num_blocks_per_seq; (P).dtype = dtype;                \
         (P).mask = mask; (P).scale = scale;                                                    \
         (P).win_left = win_left; (P).win_right = win_right;                                    \
-        (P).mask_tensor = mask_tensor;                                                         \
+        (P).mask_tensor = mask_tensor; (P).topk_idx = topk_idx; (P).topk = topk;               \
     } while (0)
 
 /*

@@ -20,7 +20,7 @@ SRC = os.path.join(HERE, "pa_ref.c")
 LIB = os.path.join(HERE, "libpa_ref.so")
 
 F16, BF16 = 0, 1
-MASK_NONE, MASK_CAUSAL, MASK_BAND, MASK_TENSOR = 0, 1, 2, 3
+MASK_NONE, MASK_CAUSAL, MASK_BAND, MASK_TENSOR, MASK_SPARSE = 0, 1, 2, 3, 4
 MASK_DIM = 2048   # the shared mask matrix of the tensor mask is MASK_DIM x MASK_DIM fp16
 ERRORS = {-1: "bad argument", -2: "block id out of range", -3: "bad lengths", -4: "out of memory"}
 
@@ -46,7 +46,7 @@ def load(path=None):
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
-        common = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i64, i32, i32, i32, f64, i32, i32, P]
+        common = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i64, i32, i32, i32, f64, i32, i32, P, P, i32]
         lib.pa_ref_forward.argtypes = common + [P, P, ctypes.c_int]
         lib.pa_ref_forward.restype = ctypes.c_int
         lib.pa_ref_rows.argtypes = common + [i64, P, P, P, P, ctypes.c_int]
@@ -68,7 +68,7 @@ class Inputs:
 
     def __init__(self, query, key_cache, value_cache, block_tables, context_lens, q_seq_lens,
                  head_num, kv_head_num, dtype, mask, scale, head_size_v=None, window=(0, 0),
-                 mask_tensor=None):
+                 mask_tensor=None, topk_idx=None):
         self.query = _bits(query)
         self.key_cache = _bits(key_cache)
         # value_cache None: the V row of a token is the first head_size_v
@@ -82,7 +82,12 @@ class Inputs:
         self.kv_head_num = int(kv_head_num)
         self.dtype = {"f16": F16, "bf16": BF16}.get(dtype, dtype)
         self.mask = {"none": MASK_NONE, "causal": MASK_CAUSAL, "band": MASK_BAND,
-                     "tensor": MASK_TENSOR}.get(mask, mask)
+                     "tensor": MASK_TENSOR, "sparse": MASK_SPARSE}.get(mask, mask)
+        # sparse: int32 [num_q_tokens, kv_head_num, topk] lists of token indices
+        self.topk_idx = None
+        if topk_idx is not None:
+            ti = topk_idx.detach().cpu().numpy() if hasattr(topk_idx, "detach") else topk_idx
+            self.topk_idx = np.ascontiguousarray(ti, dtype=np.int32)
         # tensor mask: fp16 [MASK_DIM, MASK_DIM] added to the scaled scores
         self.mask_tensor = None if mask_tensor is None else _bits(mask_tensor)
         if self.mask_tensor is not None:
@@ -97,7 +102,7 @@ class Inputs:
         w = p.workload
         return cls(p.query, p.key_cache, p.value_cache, p.block_tables_np, p.context_lens_np,
                    p.q_seq_lens_np, w.head_num, w.kv_head_num, w.dtype, w.mask, w.scale, w.head_size_v,
-                   (w.window_left, w.window_right), getattr(p, "mask_tensor", None))
+                   (w.window_left, w.window_right), getattr(p, "mask_tensor", None), getattr(p, "topk_idx", None))
 
     @property
     def batch(self):
@@ -115,7 +120,8 @@ class Inputs:
         return [ptr(self.query), ptr(self.key_cache), ptr(self.value_cache), ptr(self.block_tables),
                 ptr(self.context_lens), ptr(self.q_seq_lens), self.batch, self.num_q_tokens,
                 self.head_num, self.kv_head_num, dk, dv, bs, nb, mb, self.dtype, self.mask, self.scale,
-                self.win_left, self.win_right, ptr(self.mask_tensor)]
+                self.win_left, self.win_right, ptr(self.mask_tensor), ptr(self.topk_idx),
+                0 if self.topk_idx is None else int(self.topk_idx.shape[-1])]
 
 
 def _bits(t):

@@ -55,6 +55,7 @@ class Workload:
     window_left: int = 0       # band mask: tokens before the query's position it sees
     window_right: int = 0      # band mask: tokens after it
     mask_fill: float = -10000.0   # tensor mask: the value above the diagonal of the shared matrix
+    topk: int = 0              # sparse mask: entries per (query token, KV head) list
 
 
 def _tiny_lengths(rng):
@@ -109,6 +110,11 @@ WORKLOADS = {
     # scores, every context token computed
     9: Workload("splitfuse_tensor_mask", 32, 32, 8, 128, 128, 128, "f16", "tensor", 1.0 / math.sqrt(128),
                 _splitfuse_lengths, seed=1009),
+    # sparse top-k decode over a compressed cache (compression ratio 4 of the
+    # MLA decode's lengths; 512 entries per list, as the pages fix cmp_topk),
+    # 64 query heads on one shared K/V head
+    10: Workload("sparse_topk_decode", 128, 64, 1, 576, 512, 128, "bf16", "sparse", 1.0 / math.sqrt(576),
+                 lambda rng: (_mla_lengths(rng)[0] // 4, None), seed=1010, shared_kv=True, topk=512),
 }
 
 
@@ -143,6 +149,7 @@ class Problem:
     num_blocks: int
     max_num_blocks_per_seq: int
     mask_tensor: Optional[torch.Tensor] = None   # tensor mask: fp16 [MASK_DIM, MASK_DIM]
+    topk_idx: Optional[torch.Tensor] = None      # sparse mask: int32 [T, Hkv, topk], -1 = unused
 
     @property
     def batch(self) -> int:
@@ -160,6 +167,21 @@ class Problem:
 
     def kv_tokens(self) -> int:
         return int(self.context_lens_np.astype(np.int64).sum())
+
+    def sparse_entries(self) -> int:
+        """Sparse mask: list entries that select a visible token, over every
+        (query token, KV head) list."""
+        idx = self.topk_idx.detach().cpu().numpy()
+        kv = self.context_lens_np.astype(np.int64)
+        ql = np.ones_like(kv) if self.q_seq_lens_np is None else self.q_seq_lens_np.astype(np.int64)
+        total, t0 = 0, 0
+        for b in range(self.batch):
+            for i in range(int(ql[b])):
+                lim = min(int(kv[b]), max(0, int(kv[b] - ql[b])) + i + 1)
+                e = idx[t0 + i]
+                total += int(((e >= 0) & (e < lim)).sum())
+            t0 += int(ql[b])
+        return total
 
     def read_tokens(self) -> int:
         """Tokens some row of their sequence sees, summed over sequences: all
@@ -192,6 +214,26 @@ def random_mask_tensor(seed, device="cpu", scale=2.0, neg_inf_frac=0.05):
     gen.manual_seed(int(seed) + 1)
     holes = torch.rand(MASK_DIM, MASK_DIM, generator=gen, device=device) < neg_inf_frac
     return m.masked_fill(holes, float("-inf")).to(torch.float16)
+
+
+def topk_lists(kv, ql, kv_heads, topk, rng):
+    """Synthetic selector output: for every query token (row i of its
+    sequence) and KV head, min(topk, n) distinct indices drawn uniformly from
+    the n = min(kv, prefix + i + 1) compressed tokens the row may see, in
+    random order, padded with -1."""
+    T = int(kv.shape[0]) if ql is None else int(np.asarray(ql, np.int64).sum())
+    out = np.full((T, kv_heads, topk), -1, dtype=np.int32)
+    qls = np.ones_like(kv) if ql is None else np.asarray(ql, np.int64)
+    t = 0
+    for b in range(kv.shape[0]):
+        prefix = max(0, int(kv[b]) - int(qls[b]))
+        for i in range(int(qls[b])):
+            n = min(int(kv[b]), prefix + i + 1)
+            m = min(topk, n)
+            for g in range(kv_heads):
+                out[t, g, :m] = rng.choice(n, size=m, replace=False)
+            t += 1
+    return out
 
 
 def _normal(shape, dtype, seed, device, chunk_elems=1 << 26):
@@ -258,20 +300,23 @@ def generate(w: Workload, device="cpu", seed: Optional[int] = None, values=True,
         context_lens_np=kv, q_seq_lens_np=None if ql is None else np.asarray(ql, np.int32),
         block_tables_np=tables, num_blocks=nb, max_num_blocks_per_seq=int(tables.shape[1]),
         mask_tensor=causal_mask_tensor(w.mask_fill, device) if w.mask == "tensor" else None,
+        topk_idx=torch.from_numpy(topk_lists(kv, ql, w.kv_head_num, w.topk,
+                                             np.random.Generator(np.random.PCG64(seed * 16 + 4)))).to(device)
+        if w.mask == "sparse" else None,
     )
 
 
 def custom(batch_lens, head_num, kv_head_num, head_size_k, head_size_v, block_size,
            dtype="f16", mask="none", scale=None, q_seq_lens=None, num_blocks=None,
            slack=0.25, seed=7, name="custom", device="cpu", max_blocks=None, shared_kv=False,
-           window=(0, 0)) -> Problem:
+           window=(0, 0), topk=0) -> Problem:
     """A small hand-shaped problem (tests)."""
     if scale is None:
         scale = 1.0 / math.sqrt(head_size_k)
     w = Workload(name, len(batch_lens), head_num, kv_head_num, head_size_k, head_size_v,
                  block_size, dtype, mask, float(scale), fixed_lengths(batch_lens, q_seq_lens),
                  num_blocks=num_blocks, slack=slack, seed=seed, shared_kv=shared_kv,
-                 window_left=int(window[0]), window_right=int(window[1]))
+                 window_left=int(window[0]), window_right=int(window[1]), topk=int(topk))
     return generate(w, device=device, max_blocks=max_blocks)
 
 
@@ -281,4 +326,6 @@ def kv_bytes(p: Problem) -> int:
     element (only the K row when V lives inside it)."""
     w = p.workload
     per_row = w.head_size_k if w.shared_kv else w.head_size_k + w.head_size_v
+    if w.mask == "sparse":   # the rows the lists select, once per list
+        return p.sparse_entries() * per_row * 2
     return p.read_tokens() * w.kv_head_num * per_row * 2

@@ -559,4 +559,123 @@ def pin_tensor_mask_beyond_the_matrix(lib):
     close(l, rl, rtol=1e-10, atol=1e-11)
 
 
+def sparse_cases():
+    """Sparse-list problems: decode and several query tokens, two KV heads.
+    The last two entries of every multi-token list are overwritten with
+    indices the row must skip: one past its causal limit (when the sequence
+    has such a token) and one past the sequence."""
+    yield synth.custom([300, 17, 128, 129], 8, 2, 64, 64, 16, "f16", "sparse", seed=160, topk=40)
+    p = synth.custom([200, 70, 33], 4, 2, 32, 48, 16, "bf16", "sparse", q_seq_lens=[40, 5, 33], seed=161,
+                     topk=24)
+    idx = p.topk_idx.numpy()
+    t = 0
+    for b in range(p.batch):
+        kv, q = int(p.context_lens_np[b]), int(p.q_seq_lens_np[b])
+        for i in range(q):
+            pos = max(0, kv - q) + i
+            idx[t, :, -2] = pos + 1 if pos + 1 < kv else -1
+            idx[t, :, -1] = kv + 3
+            t += 1
+    p.topk_idx = torch.from_numpy(idx)
+    yield p
+
+
+def pin_sparse_sorted_full_lists_are_causal(lib):
+    """Lists holding every token a row may see, in ascending order, give the
+    causal result bit for bit (the compressed-axis rule is the causal rule)."""
+    for p in sparse_cases():
+        w = p.workload
+        kv = p.context_lens_np
+        ql = np.ones_like(kv) if p.q_seq_lens_np is None else p.q_seq_lens_np
+        K = int(kv.max())
+        idx = np.full((p.num_q_tokens, w.kv_head_num, K), -1, np.int32)
+        t = 0
+        for b in range(p.batch):
+            prefix = max(0, int(kv[b]) - int(ql[b]))
+            for i in range(int(ql[b])):
+                n = min(int(kv[b]), prefix + i + 1)
+                idx[t, :, :n] = np.arange(n)
+                t += 1
+        ps = synth.Problem(**{**p.__dict__})
+        ps.workload = synth.Workload(**{**w.__dict__, "topk": K})
+        ps.topk_idx = torch.from_numpy(idx)
+        o, l = run(lib, ps)
+        oc, lc = run(lib, _with_mask(p, "causal"))
+        assert np.array_equal(o, oc) and np.array_equal(l, lc)
+
+
+def pin_sparse_row_is_attention_over_its_list(lib):
+    """Each row equals unmasked attention over just the tokens its list
+    selects, copied out of the paged cache in list order (bit for bit)."""
+    for p in sparse_cases():
+        o, l = run(lib, p)
+        w = p.workload
+        G = w.head_num // w.kv_head_num
+        idx = p.topk_idx.numpy()
+        ql = np.ones(p.batch, np.int64) if p.q_seq_lens_np is None else p.q_seq_lens_np.astype(np.int64)
+        t0 = 0
+        for b in range(p.batch):
+            kv = int(p.context_lens_np[b])
+            prefix = max(0, kv - int(ql[b]))
+            for i in range(int(ql[b])):
+                for g in range(w.kv_head_num):
+                    sel = [int(c) for c in idx[t0 + i, g] if 0 <= c < kv and c <= prefix + i]
+                    heads = list(range(g * G, (g + 1) * G))
+                    d = _list_problem(p, b, g, sel, p.query[t0 + i:t0 + i + 1, heads[0]:heads[-1] + 1])
+                    od, ld = run(lib, d)
+                    assert np.array_equal(od[0], o[t0 + i, heads]) and np.array_equal(ld[0], l[t0 + i, heads])
+            t0 += int(ql[b])
+
+
+def _list_problem(p, b, g, sel, query):
+    """One sequence of KV head g's rows of tokens `sel` (in that order) of
+    sequence b, copied into fresh blocks with torch indexing; one KV head."""
+    w = p.workload
+    n = len(sel)
+    bs = w.block_size
+    nblk = max(1, (n + bs - 1) // bs)
+    rows_k = gather_contiguous(p, b, p.key_cache)[:, g:g + 1]
+    vsrc = p.key_cache[..., :w.head_size_v] if w.shared_kv else p.value_cache
+    rows_v = gather_contiguous(p, b, vsrc)[:, g:g + 1]
+    ids = torch.tensor(sel, dtype=torch.long)
+    def pack(rows):
+        out = torch.zeros(nblk * bs, 1, rows.shape[2], dtype=rows.dtype)
+        out[:n] = rows[ids] if n else out[:0]
+        return out.reshape(nblk, bs, 1, rows.shape[2])
+    d = synth.Problem(**{**p.__dict__})
+    d.workload = synth.Workload(**{**w.__dict__, "mask": "none", "shared_kv": False,
+                                   "head_num": query.shape[1], "kv_head_num": 1, "topk": 0})
+    d.key_cache, d.value_cache = pack(rows_k), pack(rows_v)
+    d.num_blocks = nblk
+    d.block_tables_np = np.arange(nblk, dtype=np.int32)[None, :]
+    d.max_num_blocks_per_seq = nblk
+    d.context_lens_np = np.array([n], np.int32)
+    d.q_seq_lens_np = None
+    d.query = query.contiguous()
+    d.topk_idx = None
+    return d
+
+
+def pin_sparse_lse_counts_entries(lib):
+    """q = 0: exp(lse) counts the list entries that select a visible token."""
+    for p in sparse_cases():
+        p.query.zero_()
+        _, l = run(lib, p)
+        w = p.workload
+        G = w.head_num // w.kv_head_num
+        idx = p.topk_idx.numpy()
+        ql = np.ones(p.batch, np.int64) if p.q_seq_lens_np is None else p.q_seq_lens_np.astype(np.int64)
+        t0 = 0
+        for b in range(p.batch):
+            kv = int(p.context_lens_np[b])
+            for i in range(int(ql[b])):
+                lim = min(kv, max(0, kv - int(ql[b])) + i + 1)
+                for h in range(w.head_num):
+                    e = idx[t0 + i, h // G]
+                    count = int(((e >= 0) & (e < lim)).sum())
+                    got = np.exp(l[t0 + i, h])
+                    assert (count == 0 and got == 0) or np.rint(got) == count, (b, i, h)
+            t0 += int(ql[b])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

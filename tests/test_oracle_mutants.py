@@ -51,6 +51,12 @@ MUTANTS = [
     ("shared_v_last_columns", "const uint16_t *vsrc = P->value_cache ? P->value_cache : P->key_cache;",
      "const uint16_t *vsrc = P->value_cache ? P->value_cache : P->key_cache + (Dk - Dv);"),
     ("exp_without_shift_in_lse", "*lse = zmax + log(wsum);", "*lse = log(wsum);"),
+    ("sparse_causal_ignored", "if (list && (tok < 0 || tok >= kv || tok > prefix + i)) {",
+     "if (list && (tok < 0 || tok >= kv)) {"),
+    ("sparse_causal_off_by_one", "if (list && (tok < 0 || tok >= kv || tok > prefix + i)) {",
+     "if (list && (tok < 0 || tok >= kv || tok >= prefix + i)) {"),
+    ("sparse_list_of_head_0", "list = P->topk_idx + (t * Hkv + g) * (int64_t)P->topk;",
+     "list = P->topk_idx + (t * Hkv) * (int64_t)P->topk;"),
     ("tensor_bias_subtracted", "z[j] += from_f16_bits(P->mask_tensor", "z[j] -= from_f16_bits(P->mask_tensor"),
     ("tensor_transposed", "P->mask_tensor[(int64_t)i * REF_MASK_DIM + c]", "P->mask_tensor[(int64_t)c * REF_MASK_DIM + i]"),
     ("tensor_columns_not_shifted", "const int64_t c = (int64_t)tok - prefix;", "const int64_t c = (int64_t)tok;"),
