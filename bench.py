@@ -86,6 +86,9 @@ def attention_flops(p):
             hi = np.minimum(pos + 1 + right, kv[b])
             lo = np.zeros_like(pos) if left is None else np.maximum(pos - left, 0)
             pairs += int(np.maximum(hi - lo, 0).sum())
+    elif w.mask == "sparse":
+        # list entries that select a visible token, for each query head of the KV head
+        return p.sparse_entries() * (w.head_num // w.kv_head_num) * 2 * (w.head_size_k + w.head_size_v)
     else:
         pairs = int((ql * kv).sum())
     return pairs * w.head_num * 2 * (w.head_size_k + w.head_size_v)
@@ -105,6 +108,8 @@ def cpu_baseline(p, target_s, threads):
     cu = np.concatenate([[0], np.cumsum(ql)])
     # oracle work per sequence ~ rows x visible tokens x (Dk + Dv)
     seen = np.minimum(kv, w.window_left + 1 + w.window_right) if w.mask == "band" else kv
+    if w.mask == "sparse":
+        seen = np.minimum(kv, w.topk)
     cost = ql * seen * w.head_num * (w.head_size_k + w.head_size_v)
     order = np.random.default_rng(0).permutation(p.batch)
 
@@ -124,7 +129,8 @@ def cpu_baseline(p, target_s, threads):
         return pa_ref.Inputs(p.query[qidx], p.key_cache[idx],
                              None if p.value_cache is None else p.value_cache[idx], bt, kv[seqs],
                              None if p.q_seq_lens_np is None else ql[seqs], w.head_num, w.kv_head_num,
-                             w.dtype, w.mask, w.scale, w.head_size_v, (w.window_left, w.window_right))
+                             w.dtype, w.mask, w.scale, w.head_size_v, (w.window_left, w.window_right),
+                             p.mask_tensor, None if p.topk_idx is None else p.topk_idx[qidx])
 
     # calibrate the oracle's rate on the cheapest sequence
     b0 = int(np.argmin(cost))
@@ -207,7 +213,7 @@ def main():
 
     def step(k):
         att.forward(p.query, kcs[k % copies], vcs[k % copies], p.block_tables, p.context_lens,
-                    p.q_seq_lens, max_q_seq_len=ql_max, out=out)
+                    p.q_seq_lens, max_q_seq_len=ql_max, out=out, topk_indices=p.topk_idx)
 
     for k in range(args.warmup):
         step(k)

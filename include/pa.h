@@ -86,7 +86,9 @@ typedef enum {
     PA_MASK_NONE = 0,    /* maskType UNDEFINED: all context_lens[b] tokens visible */
     PA_MASK_CAUSAL = 1,  /* mask type 5 (parallel decoding / splitfuse), prefix-aligned */
     PA_MASK_BAND = 2,    /* sliding window (band mask mode 4), prefix-aligned like CAUSAL */
-    PA_MASK_TENSOR = 3   /* the shared compressed mask matrix (mask type 5), see pa_config.mask_tensor */
+    PA_MASK_TENSOR = 3,  /* the shared compressed mask matrix (mask type 5), see pa_config.mask_tensor */
+    PA_MASK_SPARSE = 4   /* per-query-token lists of selected tokens (compressed-KV top-k), see
+                            pa_forward_sparse */
 } pa_mask;
 
 /* pa_config.flags */
@@ -131,6 +133,7 @@ typedef struct {
     const void *mask_tensor;         /* PA_MASK_TENSOR: device pointer to the shared fp16 [2048, 2048]
                                         mask matrix, owned by the caller and kept alive and unchanged
                                         while the handle is used; ignored otherwise */
+    int32_t topk;                    /* PA_MASK_SPARSE: entries per list (> 0); ignored otherwise */
 } pa_config;
 
 typedef struct pa_handle pa_handle;
@@ -141,13 +144,15 @@ typedef struct pa_handle pa_handle;
  * H, Hkv > 0 and H % Hkv == 0; 0 < Dk, Dv <= 576; block_size > 0,
  * block_size % 16 == 0, block_size <= 256, and block_size <= 128 in causal
  * mode or when Dk or Dv > 256; window sizes in [0, 2^30] in band mode;
- * a non-NULL mask_tensor in tensor mode; num_blocks > 0; max_batch > 0;
+ * a non-NULL mask_tensor in tensor mode; topk > 0 in sparse mode; num_blocks > 0; max_batch > 0;
  * max_num_blocks_per_seq > 0; max_q_seq_len > 0; dtype and mask in range;
  * scale finite; num_partitions >= 0; only PA_FLAG_* bits, not FORCE_VALU
  * with FORCE_MFMA; Dv <= Dk with PA_FLAG_SHARED_KV.  PA_ERR_UNSUPPORTED: a (Dk, Dv) pair this
  * build has no kernels for (64/64, 128/128, 256/256, 576/512 are built),
- * PA_FLAG_FORCE_VALU with any mask other than PA_MASK_NONE, or a device
- * that is not gfx950.  On success *out receives the handle.
+ * PA_FLAG_FORCE_VALU with any mask other than PA_MASK_NONE, sparse mode
+ * unless head_num / kv_head_num is a multiple of 64 (the matrix-core tiles
+ * of 64 rows must each hold one query token), or a device that is not
+ * gfx950.  On success *out receives the handle.
  */
 pa_status pa_create(const pa_config *cfg, pa_handle **out);
 
@@ -179,6 +184,28 @@ pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache,
                      const int32_t *context_lens, const int32_t *q_seq_lens, int32_t batch,
                      int32_t num_q_tokens, int32_t max_q_seq_len, void *out, float *lse,
                      void *stream);
+
+/*
+ * The sparse mode (PA_MASK_SPARSE handles only; pa_forward refuses them and
+ * this call refuses other handles, PA_ERR_INVALID_ARG).  The compressed-KV
+ * stream of the SparseAttnSharedkvMetadata README (parameter table: cmp_kv,
+ * cmp_topk selected tokens -- 512 there -- under mask mode 3,
+ * rightDownCausal): the caches hold the compressed tokens and context_lens
+ * counts them; every query token t and KV head g carries a list
+ *   topk_indices [num_q_tokens, Hkv, cfg.topk]  int32 (device)
+ * of token indices.  Row i of sequence b (query head h, KV head g) attends
+ * over the listed tokens c with 0 <= c < context_lens[b] and c <= prefix + i
+ * (prefix = max(0, context_lens[b] - q_seq_lens[b]): the causal mask aligned
+ * at the bottom right of the query x compressed-token matrix); other
+ * entries (such as -1 padding of a short list) are skipped, and each
+ * remaining entry contributes once (lists from a selector hold distinct
+ * indices).  A row without a remaining entry gets out = 0, lse = -inf.
+ * Every other argument and rule is pa_forward's.
+ */
+pa_status pa_forward_sparse(pa_handle *h, const void *query, const void *key_cache, const void *value_cache,
+                            const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_seq_lens,
+                            const int32_t *topk_indices, int32_t batch, int32_t num_q_tokens, int32_t max_q_seq_len,
+                            void *out, float *lse, void *stream);
 
 /* Frees the workspace and the handle (synchronises the device first).  NULL is a no-op. */
 pa_status pa_destroy(pa_handle *h);

@@ -20,12 +20,12 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_OOM = range(5)
 PA_F16, PA_BF16 = 0, 1
-PA_MASK_NONE, PA_MASK_CAUSAL, PA_MASK_BAND, PA_MASK_TENSOR = 0, 1, 2, 3
+PA_MASK_NONE, PA_MASK_CAUSAL, PA_MASK_BAND, PA_MASK_TENSOR, PA_MASK_SPARSE = 0, 1, 2, 3, 4
 PA_FLAG_FORCE_VALU, PA_FLAG_FORCE_MFMA, PA_FLAG_NO_SPLIT, PA_FLAG_SHARED_KV = 1, 2, 4, 8
 PA_DEVERR_BLOCK_ID, PA_DEVERR_TABLE_SHORT, PA_DEVERR_QLEN, PA_DEVERR_TOKENS, PA_DEVERR_CTX = 1, 2, 4, 8, 16
 
-EXPORTS = ("pa_create", "pa_forward", "pa_destroy", "pa_status_string", "pa_get_device_error",
-           "pa_set_timing", "pa_read_timing", "pa_describe")
+EXPORTS = ("pa_create", "pa_forward", "pa_forward_sparse", "pa_destroy", "pa_status_string",
+           "pa_get_device_error", "pa_set_timing", "pa_read_timing", "pa_describe")
 
 
 class pa_config(ctypes.Structure):
@@ -47,6 +47,7 @@ class pa_config(ctypes.Structure):
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
         ("mask_tensor", ctypes.c_void_p),
+        ("topk", ctypes.c_int32),
     ]
 
 
@@ -75,6 +76,8 @@ def load_library(path=LIB_PATH):
         lib.pa_create.restype = ctypes.c_int
         lib.pa_forward.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, P, P, P]
         lib.pa_forward.restype = ctypes.c_int
+        lib.pa_forward_sparse.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, P, P, P]
+        lib.pa_forward_sparse.restype = ctypes.c_int
         lib.pa_destroy.argtypes = [P]
         lib.pa_destroy.restype = ctypes.c_int
         lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -122,6 +125,15 @@ def pa_forward(handle, query, key_cache, value_cache, block_tables, context_lens
                           stream or None), "pa_forward")
 
 
+def pa_forward_sparse(handle, query, key_cache, value_cache, block_tables, context_lens, q_seq_lens,
+                      topk_indices, batch, num_q_tokens, max_q_seq_len, out, lse, stream):
+    """Pointer-level call of the sparse mode (device addresses or 0)."""
+    lib = load_library()
+    _check(lib.pa_forward_sparse(handle, query, key_cache, value_cache, block_tables, context_lens,
+                                 q_seq_lens or None, topk_indices, batch, num_q_tokens, max_q_seq_len, out,
+                                 lse or None, stream or None), "pa_forward_sparse")
+
+
 def pa_destroy(handle):
     if handle:
         _check(load_library().pa_destroy(handle), "pa_destroy")
@@ -166,7 +178,7 @@ class Attention:
 
     def __init__(self, head_num, kv_head_num, head_size_k, head_size_v, block_size, num_blocks,
                  max_batch, max_num_blocks_per_seq, max_q_seq_len=1, dtype=torch.float16,
-                 scale=None, mask="none", flags=0, num_partitions=0, window=(0, 0), mask_tensor=None):
+                 scale=None, mask="none", flags=0, num_partitions=0, window=(0, 0), mask_tensor=None, topk=0):
         if dtype not in _TORCH_DT:
             raise ValueError("dtype must be torch.float16 or torch.bfloat16")
         if scale is None:
@@ -180,9 +192,9 @@ class Attention:
                              max_batch, max_num_blocks_per_seq, max_q_seq_len, _TORCH_DT[dtype],
                              float(scale),
                              {"none": PA_MASK_NONE, "causal": PA_MASK_CAUSAL, "band": PA_MASK_BAND,
-                              "tensor": PA_MASK_TENSOR}[mask],
+                              "tensor": PA_MASK_TENSOR, "sparse": PA_MASK_SPARSE}[mask],
                              int(flags), int(num_partitions), int(window[0]), int(window[1]),
-                             self.mask_tensor.data_ptr() if self.mask_tensor is not None else None)
+                             self.mask_tensor.data_ptr() if self.mask_tensor is not None else None, int(topk))
         self.handle = pa_create(self.cfg)
 
     def close(self):
@@ -213,7 +225,7 @@ class Attention:
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
     def forward(self, query, key_cache, value_cache, block_tables, context_lens, q_seq_lens=None,
-                max_q_seq_len=None, out=None, lse=None, return_lse=False, stream=None):
+                max_q_seq_len=None, out=None, lse=None, return_lse=False, stream=None, topk_indices=None):
         c = self.cfg
         T = query.shape[0] if query.dim() == 3 else -1
         B = context_lens.shape[0]
@@ -245,12 +257,16 @@ class Attention:
             self._need(lse, "lse", torch.float32, (T, c.head_num))
         if stream is None:
             stream = torch.cuda.current_stream(query.device).cuda_stream
-        pa_forward(self.handle, query.data_ptr(), key_cache.data_ptr(),
-                   0 if shared else value_cache.data_ptr(),
-                   block_tables.data_ptr(), context_lens.data_ptr(),
-                   q_seq_lens.data_ptr() if q_seq_lens is not None else 0,
-                   B, T, int(max_q_seq_len), out.data_ptr(), lse.data_ptr() if lse is not None else 0,
-                   stream)
+        args = (self.handle, query.data_ptr(), key_cache.data_ptr(), 0 if shared else value_cache.data_ptr(),
+                block_tables.data_ptr(), context_lens.data_ptr(),
+                q_seq_lens.data_ptr() if q_seq_lens is not None else 0)
+        tail = (B, T, int(max_q_seq_len), out.data_ptr(), lse.data_ptr() if lse is not None else 0, stream)
+        if c.mask == PA_MASK_SPARSE:
+            # per (query token, KV head) lists of selected token indices
+            self._need(topk_indices, "topk_indices", torch.int32, (T, c.kv_head_num, c.topk))
+            pa_forward_sparse(*args, topk_indices.data_ptr(), *tail)
+        else:
+            pa_forward(*args, *tail)
         return (out, lse) if (return_lse or lse is not None) else out
 
     __call__ = forward
@@ -264,7 +280,7 @@ def for_problem(p, **kw):
                 head_size_v=w.head_size_v, block_size=w.block_size, num_blocks=p.num_blocks,
                 max_batch=p.batch, max_num_blocks_per_seq=p.max_num_blocks_per_seq,
                 max_q_seq_len=max(1, p.max_q_seq_len), dtype=DTYPES[w.dtype], scale=w.scale, mask=w.mask,
-                window=(w.window_left, w.window_right), mask_tensor=p.mask_tensor)
+                window=(w.window_left, w.window_right), mask_tensor=p.mask_tensor, topk=w.topk)
     args.update(kw)
     if w.shared_kv:
         args["flags"] = args.get("flags", 0) | PA_FLAG_SHARED_KV
@@ -273,4 +289,4 @@ def for_problem(p, **kw):
 
 def run_problem(att, p, **kw):
     return att.forward(p.query, p.key_cache, p.value_cache, p.block_tables, p.context_lens,
-                       p.q_seq_lens, max_q_seq_len=max(1, p.max_q_seq_len), **kw)
+                       p.q_seq_lens, max_q_seq_len=max(1, p.max_q_seq_len), topk_indices=p.topk_idx, **kw)

@@ -49,9 +49,18 @@ size_t partial_floats(int rows, int dv)
 }
 
 bool valid_dtype(int d) { return d == PA_F16 || d == PA_BF16; }
-bool valid_mask(int m) { return m == PA_MASK_NONE || m == PA_MASK_CAUSAL || m == PA_MASK_BAND || m == PA_MASK_TENSOR; }
+bool valid_mask(int m)
+{
+    return m == PA_MASK_NONE || m == PA_MASK_CAUSAL || m == PA_MASK_BAND || m == PA_MASK_TENSOR || m == PA_MASK_SPARSE;
+}
 
-int kernel_mode(int mask) { return mask == PA_MASK_BAND ? 1 : (mask == PA_MASK_TENSOR ? 2 : 0); }
+int kernel_mode(int mask)
+{
+    return mask == PA_MASK_BAND ? 1 : (mask == PA_MASK_TENSOR ? 2 : (mask == PA_MASK_SPARSE ? 3 : 0));
+}
+
+// Sparse lists: every 64-row tile must hold the rows of one query token.
+constexpr int kSparseTileRows = 64;
 
 }  // namespace
 
@@ -94,9 +103,11 @@ struct pa_handle {
             const bool sh = (cfg.flags & PA_FLAG_SHARED_KV) != 0;
             const int mode = kernel_mode(cfg.mask);   // the kernels' shapes depend on the mode
             int var = 0;
-            if (rows > 16 && pa::tile_supported(dk, dv, 1))   // (no variant 2 with the tensor mask)
+            // (no variant 2 with the tensor mask; sparse lists: variant 1
+            // below 576, the one 576/512 variant above)
+            if ((rows > 16 || cfg.mask == PA_MASK_SPARSE) && pa::tile_supported(dk, dv, 1))
                 var = (rows > pa::tile_rows(dk, dv, 1, sh, mode) && pa::tile_supported(dk, dv, 2) &&
-                       cfg.mask != PA_MASK_TENSOR) ? 2 : 1;
+                       cfg.mask != PA_MASK_TENSOR && cfg.mask != PA_MASK_SPARSE) ? 2 : 1;
             v.tile_variant = var;
             v.rows_per_tile = pa::tile_rows(dk, dv, var, sh, mode);
             v.chunk = pa::tile_chunk(dk, dv, var, sh, mode);
@@ -150,6 +161,8 @@ static pa_status check_config(const pa_config *c)
         return PA_ERR_INVALID_ARG;
     if (c->mask == PA_MASK_TENSOR && !c->mask_tensor)
         return PA_ERR_INVALID_ARG;
+    if (c->mask == PA_MASK_SPARSE && c->topk <= 0)
+        return PA_ERR_INVALID_ARG;
     // Item indices are int32 on the device: bound the largest possible count.
     const int G = c->head_num / c->kv_head_num;
     const double tiles = std::ceil((double)c->max_q_seq_len * G / 16.0);
@@ -170,6 +183,8 @@ static pa_status check_config(const pa_config *c)
         return PA_ERR_UNSUPPORTED;
     if ((c->flags & PA_FLAG_FORCE_MFMA) && !til)
         return PA_ERR_UNSUPPORTED;
+    if (c->mask == PA_MASK_SPARSE && (!til || G % kSparseTileRows != 0))
+        return PA_ERR_UNSUPPORTED;   // the rows of a tile must share one query token's list
     if (!til && (int64_t)c->max_q_seq_len * G > 8)
         return PA_ERR_UNSUPPORTED;   // only the VALU kernel exists for this shape
     if ((c->flags & PA_FLAG_FORCE_VALU) && (int64_t)c->max_q_seq_len * G > 8)
@@ -305,14 +320,17 @@ pa_status pa_describe(const pa_handle *h, int32_t max_q_seq_len, int32_t *path, 
     return PA_OK;
 }
 
-pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, const void *value_cache,
-                     const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_seq_lens,
-                     int32_t batch, int32_t num_q_tokens, int32_t max_q_seq_len, void *out, float *lse,
-                     void *stream)
+static pa_status forward_impl(pa_handle *h, const void *query, const void *key_cache, const void *value_cache,
+                              const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_seq_lens,
+                              const int32_t *topk_indices, int32_t batch, int32_t num_q_tokens, int32_t max_q_seq_len,
+                              void *out, float *lse, void *stream)
 {
     if (!h || !query || !key_cache || !block_tables || !context_lens || !out)
         return PA_ERR_INVALID_ARG;
     const pa_config &c = h->cfg;
+    // the sparse mode takes its lists through pa_forward_sparse only
+    if ((c.mask == PA_MASK_SPARSE) != (topk_indices != nullptr))
+        return PA_ERR_INVALID_ARG;
     const bool shared = (c.flags & PA_FLAG_SHARED_KV) != 0;
     // shared K/V: value_cache is NULL or the key cache itself
     if (shared ? (value_cache && value_cache != key_cache) : !value_cache)
@@ -361,6 +379,9 @@ pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, con
     p.win_right = p.band ? c.window_right : 0;
     p.tmask = c.mask == PA_MASK_TENSOR;
     p.mask_tensor = p.tmask ? (const uint16_t *)c.mask_tensor : nullptr;
+    p.sparse = c.mask == PA_MASK_SPARSE;
+    p.topk = p.sparse ? c.topk : 0;
+    p.topk_idx = p.sparse ? topk_indices : nullptr;
     p.scale_log2 = c.scale * 1.4426950408889634f;
     p.rows_per_tile = v.rows_per_tile;
     p.chunk = v.chunk;
@@ -394,6 +415,26 @@ pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, con
         ++h->timed;
     }
     return PA_OK;
+}
+
+pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, const void *value_cache,
+                     const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_seq_lens,
+                     int32_t batch, int32_t num_q_tokens, int32_t max_q_seq_len, void *out, float *lse,
+                     void *stream)
+{
+    return forward_impl(h, query, key_cache, value_cache, block_tables, context_lens, q_seq_lens, nullptr, batch,
+                        num_q_tokens, max_q_seq_len, out, lse, stream);
+}
+
+pa_status pa_forward_sparse(pa_handle *h, const void *query, const void *key_cache, const void *value_cache,
+                            const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_seq_lens,
+                            const int32_t *topk_indices, int32_t batch, int32_t num_q_tokens, int32_t max_q_seq_len,
+                            void *out, float *lse, void *stream)
+{
+    if (!topk_indices)
+        return PA_ERR_INVALID_ARG;
+    return forward_impl(h, query, key_cache, value_cache, block_tables, context_lens, q_seq_lens, topk_indices,
+                        batch, num_q_tokens, max_q_seq_len, out, lse, stream);
 }
 
 pa_status pa_get_device_error(pa_handle *h, uint32_t *code, int32_t clear)

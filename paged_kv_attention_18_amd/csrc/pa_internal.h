@@ -62,6 +62,9 @@ struct Params {
     int32_t win_left, win_right;       // band mask window (0, 0 otherwise)
     int32_t tmask;                     // tensor mask: the shared matrix is added to the scores
     const uint16_t *mask_tensor;       // fp16 [2048, 2048] (tensor mask only)
+    int32_t sparse;                    // sparse lists: a unit's tokens are its query token's list entries
+    int32_t topk;                      // entries per list
+    const int32_t *topk_idx;           // [num_q_tokens, kv_head_num, topk] (sparse only)
     float scale_log2;                  // scale * log2(e)
     int32_t rows_per_tile;             // R
     int32_t chunk;                     // CT
@@ -90,7 +93,7 @@ bool decode_supported(int dk, int dv);
 // tile_rows(.., 1) rows, 2 above; tile_supported says which exist.
 // `shared` selects the kernels that read V out of the K tile already in LDS
 // (shared K/V cache) where such kernels exist; `mode` the kernels of a mask
-// kind with code of its own (0 none / causal, 1 band, 2 tensor).
+// kind with code of its own (0 none / causal, 1 band, 2 tensor, 3 sparse).
 bool tile_supported(int dk, int dv, int variant);
 int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared, int mode);   // resident workgroups per CU
 int tile_chunk(int dk, int dv, int variant, bool shared, int mode);
@@ -109,6 +112,7 @@ struct TileShape {
 const void *tile_kernel_plain(int dtype, int dk, int dv, int variant, bool shared, TileShape *t);
 const void *tile_kernel_band(int dtype, int dk, int dv, int variant, bool shared, TileShape *t);
 const void *tile_kernel_tensor(int dtype, int dk, int dv, int variant, bool shared, TileShape *t);
+const void *tile_kernel_sparse(int dtype, int dk, int dv, int variant, bool shared, TileShape *t);
 
 constexpr int kThreads = 256;        // threads per attention workgroup
 constexpr int kBtWindow = 256;       // block-table entries staged in LDS at a time
@@ -182,6 +186,8 @@ __device__ __forceinline__ int unit_first_chunk(const Params &p, int kv, int qle
 
 __device__ __forceinline__ int unit_chunks(const Params &p, int kv, int qlen, int qt)
 {
+    if (p.sparse)   // the entries of the query token's list
+        return (p.topk + p.chunk - 1) / p.chunk;
     const int rows = qlen * p.group;
     int r1 = (qt + 1) * p.rows_per_tile;
     r1 = (r1 < rows ? r1 : rows) - 1;

@@ -18,6 +18,8 @@ const void *tile_kernel_ptr(int dtype, int dk, int dv, int variant, bool shared,
         return tile_kernel_band(dtype, dk, dv, variant, shared, t);
     if (mode == MODE_TENSOR)
         return tile_kernel_tensor(dtype, dk, dv, variant, shared, t);
+    if (mode == MODE_SPARSE)
+        return tile_kernel_sparse(dtype, dk, dv, variant, shared, t);
     return tile_kernel_plain(dtype, dk, dv, variant, shared, t);
 }
 
@@ -60,7 +62,7 @@ int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared, int
 hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s)
 {
     TileShape t;
-    const int mode = p.band ? MODE_BAND : (p.tmask ? MODE_TENSOR : MODE_PLAIN);
+    const int mode = p.band ? MODE_BAND : (p.tmask ? MODE_TENSOR : (p.sparse ? MODE_SPARSE : MODE_PLAIN));
     const void *k = tile_kernel_ptr(dtype, p.head_size_k, p.head_size_v, variant, p.shared_kv != 0, &t, mode);
     // the plan was made for this kernel's chunk and tile sizes
     if (!k || t.kt != p.chunk || 16 * t.mb * (t.nw / t.cs) != p.rows_per_tile)

@@ -119,7 +119,7 @@ __device__ __forceinline__ void lds_load4(const void *src, lds_u8 *dst)
 }
 
 // Kernel modes: the mask kinds that need code of their own.
-enum { MODE_PLAIN = 0, MODE_BAND = 1, MODE_TENSOR = 2 };
+enum { MODE_PLAIN = 0, MODE_BAND = 1, MODE_TENSOR = 2, MODE_SPARSE = 3 };
 constexpr int kMaskDim = 2048;   // side of the shared mask matrix (tensor mask)
 
 // Tensor mask: per chunk, the slice of the shared matrix a tile needs is
@@ -212,8 +212,8 @@ constexpr int tile_min_wgs()
                         (TM ? S * slab_bytes<16 * MB * (NW / CS), KT>() : 0);
     constexpr int fit = (160 * 1024) / lds;
     // waves per SIMD the registers allow: 2 with two 16-row blocks (1 at
-    // head sizes above 128), 2 at head sizes above 256, else 4
-    constexpr int waves = MB == 2 ? ((DK > 128 || DV > 128) ? 1 : 2) : (DK > 256 || DV > 256 ? 2 : 4);
+    // head sizes above 128), 2 at head sizes above 128, else 4
+    constexpr int waves = MB == 2 ? ((DK > 128 || DV > 128) ? 1 : 2) : (DK > 128 || DV > 128 ? 2 : 4);
     constexpr int cap = 4 * waves / NW > 0 ? 4 * waves / NW : 1;
     return fit < 1 ? 1 : (fit > cap ? cap : fit);
 }
@@ -231,11 +231,18 @@ constexpr int tile_min_wgs()
 // [i][j - prefix]; history visible with nothing added; the causal rule
 // outside the matrix); the matrix slice of each chunk is staged in LDS with
 // the chunk, and the online softmax runs on scaled log2-domain scores.
+// MODE_SPARSE: the KV tokens of a unit are the entries of its query token's
+// list (all rows of a tile belong to one query token): chunk c holds list
+// entries 16 c .. 16 c + 15, each lane's LDS-load piece comes from the
+// cache row of its entry's token (the rows of a chunk sit one per lane and
+// each lane takes its own with ds_bpermute), and a per-chunk bit mask marks
+// the entries that select a visible token.
 template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH, int MODE>
 __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, CS, SH, MODE == MODE_TENSOR>()))
 void tile_kernel(Params p)
 {
-    constexpr bool BAND = MODE == MODE_BAND, TMASK = MODE == MODE_TENSOR;
+    constexpr bool BAND = MODE == MODE_BAND, TMASK = MODE == MODE_TENSOR, SPARSE = MODE == MODE_SPARSE;
+    static_assert(!SPARSE || KT == 16, "sparse lists are taken 16 entries per chunk");
     constexpr int RGS = NW / CS;                  // row groups
     constexpr int R = 16 * MB * RGS;              // rows per tile
     constexpr int RBK = 2 * DK, RBV = 2 * DV;     // LDS row bytes
@@ -318,18 +325,24 @@ void tile_kernel(Params p)
     // Per-lane byte offset, inside a 16-token group of the cache, of the piece
     // that load instruction wave + NW m of the group moves; the piece is the
     // one whose LDS slot holds the swizzled layout.
+    // (sparse: the row part is per token -- tK / tV name the token of the
+    // group the piece belongs to, voK / voV keep only the piece offset)
     uint32_t voK[MK], voV[MV > 0 ? MV : 1];
+    int tK[MK], tV[MV > 0 ? MV : 1];
 #pragma unroll
     for (int m = 0; m < MK; ++m) {
         const int x = (wave + NW * m) * 1024 + 16 * lane;
         const int row = x / RBK;
-        voK[m] = (wave + NW * m) < IPGK ? row * rsk + 16 * (((x % RBK) >> 4) ^ (row & 7)) : 16 * lane;
+        tK[m] = row;
+        voK[m] = (wave + NW * m) < IPGK ? (SPARSE ? 0u : row * rsk) + 16 * (((x % RBK) >> 4) ^ (row & 7)) : 16 * lane;
     }
 #pragma unroll
     for (int m = 0; m < MV; ++m) {
         const int x = (wave + NW * m) * 1024 + 16 * lane;
         const int row = x / RBV;
-        voV[m] = (wave + NW * m) < IPGV ? row * rsv + 16 * (((x % RBV) >> 4) ^ v_swz<RBV>(row)) : 16 * lane;
+        tV[m] = row;
+        voV[m] = (wave + NW * m) < IPGV ? (SPARSE ? 0u : row * rsv) + 16 * (((x % RBV) >> 4) ^ v_swz<RBV>(row))
+                                        : 16 * lane;
     }
     // LDS read offsets.  K (A operand): row 16 n + lr, piece 4 ks + lg, which
     // the swizzle moves by +-64 bytes depending on bit 2 of the row.
@@ -369,7 +382,7 @@ void tile_kernel(Params p)
         // tokens [lo_tile, nvis) are seen by some row of the tile; every row
         // sees [max_lo, min_lim) (the thresholds below which, and from which
         // on, a chunk needs the per-element mask)
-        const int nvis = row_hi_t<BAND>(p, kv, prefix, (qt * R + rows_tile - 1) / G);
+        const int nvis = SPARSE ? kv : row_hi_t<BAND>(p, kv, prefix, (qt * R + rows_tile - 1) / G);
         const int nblk = nvis > 0 ? div_bs(nvis - 1, bs, bsh) + 1 : 1;
         const int min_lim = row_hi_t<BAND>(p, kv, prefix, (qt * R) / G);
         const int lo_tile = row_lo_t<BAND>(p, prefix, (qt * R) / G);
@@ -424,11 +437,41 @@ void tile_kernel(Params p)
         // Block id of each 16-token group of a chunk (clamped table index;
         // range-checked when used).
         int bid[NTT];
+        // sparse: the tile's query token, its list, the tokens it may see
+        // (c < lim_c), and for the fetched chunk the cache row of entry t in
+        // lane t (srow) and the entries that select a visible token (sbits)
+        const int itok = (qt * R) / G;
+        const bool lst_ok = SPARSE && t0 + itok < p.num_q_tokens;
+        const int lim_c = prefix + itok + 1 < kv ? prefix + itok + 1 : kv;
+        const int32_t *lst = SPARSE ? p.topk_idx + ((size_t)(t0 + itok) * p.kv_head_num + g) * p.topk : nullptr;
+        int srow = 0;
+        uint32_t sbits = 0;
+        uint32_t smask[S];
         auto fetch_bids = [&](int c) __attribute__((always_inline)) {
+            if constexpr (SPARSE) {
+                uint32_t bits = 0;
+                int rv = 0;
 #pragma unroll
-            for (int q = 0; q < NTT; ++q) {
-                const int blk = div_bs(c * KT + 16 * q, bs, bsh);
-                bid[q] = sload(bt, blk < nblk ? blk : nblk - 1);
+                for (int t = 0; t < 16; ++t) {
+                    const int k = c * 16 + t;
+                    const int ci = (lst_ok && k < p.topk) ? sload(lst, k) : -1;
+                    const bool valid = ci >= 0 && ci < lim_c;
+                    const int blk = sload(bt, valid ? div_bs(ci, bs, bsh) : 0);
+                    const bool inb = (unsigned)blk < nb32;
+                    err |= (valid && !inb) ? (uint32_t)PA_DEVERR_BLOCK_ID : 0u;
+                    const bool ok = valid && inb;
+                    bits |= ok ? (1u << t) : 0u;
+                    const int row = ok ? (int)((uint32_t)blk * (uint32_t)bs + (uint32_t)mod_bs(ci, bs, bsh)) : 0;
+                    rv = lane == t ? row : rv;
+                }
+                srow = rv;
+                sbits = bits;
+            } else {
+#pragma unroll
+                for (int q = 0; q < NTT; ++q) {
+                    const int blk = div_bs(c * KT + 16 * q, bs, bsh);
+                    bid[q] = sload(bt, blk < nblk ? blk : nblk - 1);
+                }
             }
         };
         // Issue the LDS loads of chunk c: exactly LW instructions per wave.
@@ -453,6 +496,29 @@ void tile_kernel(Params p)
                         lds_load4(src, mb_ + m * 256);
                     }
                 }
+            }
+            if constexpr (SPARSE) {
+                // one 16-entry group: each lane's piece from its entry's row
+                // (invalid entries read row 0 of block 0 and are masked)
+#pragma unroll
+                for (int m = 0; m < MK; ++m) {
+                    const int i = wave + NW * m;
+                    const bool real = !PAD || i < IPGK;
+                    lds_u8 *dst = real ? kb + i * 1024 : (lds_u8 *)sJunk;
+                    const uint32_t rl = (uint32_t)__builtin_amdgcn_ds_bpermute(tK[m] * 4, srow);
+                    const char *src = real ? kgh + (size_t)rl * rsk + voK[m] : zg + voK[m];
+                    lds_load16(src, dst);
+                }
+#pragma unroll
+                for (int m = 0; m < MV; ++m) {
+                    const int i = wave + NW * m;
+                    const bool real = !PAD || i < IPGV;
+                    lds_u8 *dst = real ? vb + i * 1024 : (lds_u8 *)sJunk;
+                    const uint32_t rl = (uint32_t)__builtin_amdgcn_ds_bpermute(tV[m] * 4, srow);
+                    const char *src = real ? vgh + (size_t)rl * rsv + voV[m] : zg + voV[m];
+                    lds_load16(src, dst);
+                }
+                return;
             }
 #pragma unroll
             for (int q = 0; q < NTT; ++q) {
@@ -481,7 +547,8 @@ void tile_kernel(Params p)
         };
 
         // one chunk from (kb, vb): S^T, mask, online softmax, PV
-        auto compute = [&](const lds_u8 *kb, const lds_u8 *vb, const lds_u8 *mb_, int c) __attribute__((always_inline)) {
+        auto compute = [&](const lds_u8 *kb, const lds_u8 *vb, const lds_u8 *mb_, int c, uint32_t vbits)
+                           __attribute__((always_inline)) {
             if (!wave_active)
                 return;
             const int jb = c * KT;
@@ -533,7 +600,7 @@ void tile_kernel(Params p)
                     }
                 }
             }
-            const bool need_mask = jb + KT > min_lim || (BAND && jb < max_lo);
+            const bool need_mask = SPARSE || jb + KT > min_lim || (BAND && jb < max_lo);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 float mx = -INFINITY;
@@ -543,7 +610,9 @@ void tile_kernel(Params p)
                     for (int r = 0; r < 4; ++r) {
                         if (need_mask) {
                             const int j = jb + 16 * n + 4 * lg + r;
-                            sacc[mb][n][r] = (j < lim[mb] && (!BAND || j >= lo_r[mb])) ? sacc[mb][n][r] : -INFINITY;
+                            const bool vis = SPARSE ? ((vbits >> (16 * n + 4 * lg + r)) & 1u) != 0
+                                                    : (j < lim[mb] && (!BAND || j >= lo_r[mb]));
+                            sacc[mb][n][r] = vis ? sacc[mb][n][r] : -INFINITY;
                         }
                         mx = fmaxf(mx, sacc[mb][n][r]);
                     }
@@ -579,9 +648,12 @@ void tile_kernel(Params p)
             }
             // V rows of tokens outside [lo_tile, nvis) may be stale or
             // unwritten cache slots: zero their operand halves (P is 0 there).
-            const bool tail = jb + KT > nvis || (BAND && jb < lo_tile);
+            const bool tail = SPARSE || jb + KT > nvis || (BAND && jb < lo_tile);
             auto tok_ok = [&](int t) __attribute__((always_inline)) {
-                return BAND ? (unsigned)(t - lo_tile) < (unsigned)(nvis - lo_tile) : t < nvis;
+                if constexpr (SPARSE)
+                    return ((vbits >> (t - jb)) & 1u) != 0;
+                else
+                    return BAND ? (unsigned)(t - lo_tile) < (unsigned)(nvis - lo_tile) : t < nvis;
             };
             if constexpr (KT == 16) {
                 uint2 pa[MB];
@@ -684,10 +756,12 @@ void tile_kernel(Params p)
             constexpr int NX = (ST + S - 1) % S;   // stage of chunk c + S - 1
             wait_ahead<LW, S - 2>(c1 - 1 - c);     // this wave's loads of chunk c are in LDS
             __builtin_amdgcn_s_barrier();          // ... and every wave's; stage NX is free
-            if (c + S - 1 < c1)
+            if (c + S - 1 < c1) {
                 issue(c + S - 1, kbuf(std::integral_constant<int, NX>{}), vbuf(std::integral_constant<int, NX>{}),
                       mbuf(std::integral_constant<int, NX>{}));
-            compute(kbuf(st), vbuf(st), mbuf(st), c);
+                smask[NX] = sbits;
+            }
+            compute(kbuf(st), vbuf(st), mbuf(st), c, smask[ST]);
             if (c + S < c1)
                 fetch_bids(c + S);                 // scalar loads land during the next wait
         };
@@ -700,11 +774,13 @@ void tile_kernel(Params p)
         fetch_bids(c0);
         issue(c0, kbuf(std::integral_constant<int, 0>{}), vbuf(std::integral_constant<int, 0>{}),
               mbuf(std::integral_constant<int, 0>{}));
+        smask[0] = sbits;
         if constexpr (S > 2) {
             if (c0 + 1 < c1) {
                 fetch_bids(c0 + 1);
                 issue(c0 + 1, kbuf(std::integral_constant<int, 1>{}), vbuf(std::integral_constant<int, 1>{}),
                       mbuf(std::integral_constant<int, 1>{}));
+                smask[1] = sbits;
             }
         }
         if constexpr (S > 3) {
@@ -712,6 +788,7 @@ void tile_kernel(Params p)
                 fetch_bids(c0 + 2);
                 issue(c0 + 2, kbuf(std::integral_constant<int, 2>{}), vbuf(std::integral_constant<int, 2>{}),
                       mbuf(std::integral_constant<int, 2>{}));
+                smask[2] = sbits;
             }
         }
         if (c0 + S - 1 < c1)
@@ -1267,7 +1344,7 @@ const void *kernel_for(int variant, bool shared, TileShape *t)
         if (variant != 0)
             return nullptr;
         if (shared) {
-            if constexpr (MODE == MODE_TENSOR)
+            if constexpr (MODE == MODE_TENSOR || MODE == MODE_SPARSE)
                 return pick<DT, DK, DV, 1, 16, 4, 1, 2, true, MODE>(t);
             else
                 return pick<DT, DK, DV, 1, 32, 4, 1, 2, true, MODE>(t);
@@ -1275,18 +1352,24 @@ const void *kernel_for(int variant, bool shared, TileShape *t)
         return pick<DT, DK, DV, 1, 16, 4, 1, 2, false, MODE>(t);
     } else {
         constexpr int KT = DK <= 128 ? 64 : 32;
-        if (variant == 0) {   // one wave per workgroup, streaming across units
-            *t = TileShape{1, 16, 1, 1, 4, 64};
-            return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE>;
-        }
-        if constexpr (MODE == MODE_TENSOR) {
+        if constexpr (MODE == MODE_SPARSE) {
+            // 64-row tiles of 16-entry chunks only (no streaming kernel)
             if (variant == 1)
-                return pick<DT, DK, DV, 1, 32, 4, 1, 2, false, MODE>(t);
+                return pick<DT, DK, DV, 1, 16, 4, 1, 2, false, MODE>(t);
         } else {
-            if (variant == 1)
-                return pick<DT, DK, DV, 1, KT, 4, 1, 2, false, MODE>(t);
-            if (variant == 2)
-                return pick<DT, DK, DV, 2, KT, 4, 1, 2, false, MODE>(t);
+            if (variant == 0) {   // one wave per workgroup, streaming across units
+                *t = TileShape{1, 16, 1, 1, 4, 64};
+                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE>;
+            }
+            if constexpr (MODE == MODE_TENSOR) {
+                if (variant == 1)
+                    return pick<DT, DK, DV, 1, 32, 4, 1, 2, false, MODE>(t);
+            } else {
+                if (variant == 1)
+                    return pick<DT, DK, DV, 1, KT, 4, 1, 2, false, MODE>(t);
+                if (variant == 2)
+                    return pick<DT, DK, DV, 2, KT, 4, 1, 2, false, MODE>(t);
+            }
         }
         return nullptr;
     }

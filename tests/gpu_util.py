@@ -25,7 +25,8 @@ def log(msg):
 def to_device(p: synth.Problem, device="cuda"):
     """The same problem with its tensors on the GPU (values copied bit for bit)."""
     q = synth.Problem(**{**p.__dict__})
-    for name in ("context_lens", "q_seq_lens", "block_tables", "query", "key_cache", "value_cache", "mask_tensor"):
+    for name in ("context_lens", "q_seq_lens", "block_tables", "query", "key_cache", "value_cache", "mask_tensor",
+                 "topk_idx"):
         t = getattr(p, name)
         if t is not None:
             setattr(q, name, t.to(device))

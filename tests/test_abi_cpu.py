@@ -80,6 +80,7 @@ def test_config_struct_matches_header():
     dict(flags=binding.PA_FLAG_SHARED_KV, head_size_k=64, head_size_v=128),
     dict(mask=binding.PA_MASK_BAND, window_left=-1), dict(mask=binding.PA_MASK_BAND, window_right=-5),
     dict(mask=binding.PA_MASK_BAND, window_left=(1 << 30) + 1),
+    dict(mask=binding.PA_MASK_SPARSE, topk=0),
 ])
 def test_create_rejects_invalid(lib, bad):
     assert create_status(lib, good_cfg(**bad)) == binding.PA_ERR_INVALID_ARG
@@ -88,7 +89,8 @@ def test_create_rejects_invalid(lib, bad):
 @pytest.mark.parametrize("shape", [dict(head_size_k=96, head_size_v=96), dict(head_size_k=128, head_size_v=64),
                                    dict(mask=binding.PA_MASK_BAND, window_left=127,
                                         flags=binding.PA_FLAG_FORCE_VALU),
-                                   dict(mask=binding.PA_MASK_CAUSAL, flags=binding.PA_FLAG_FORCE_VALU)])
+                                   dict(mask=binding.PA_MASK_CAUSAL, flags=binding.PA_FLAG_FORCE_VALU),
+                                   dict(mask=binding.PA_MASK_SPARSE, topk=16)])   # G 4: not a multiple of 64
 def test_create_unsupported_shape(lib, shape):
     assert create_status(lib, good_cfg(**shape)) == binding.PA_ERR_UNSUPPORTED
 
@@ -105,6 +107,8 @@ def test_create_without_gpu_reports_hip_error(lib):
 
 def test_forward_null_handle(lib):
     st = lib.pa_forward(None, 1, 1, 1, 1, 1, None, 1, 1, 1, 1, None, None)
+    assert st == binding.PA_ERR_INVALID_ARG
+    st = lib.pa_forward_sparse(None, 1, 1, 1, 1, 1, None, 1, 1, 1, 1, 1, None, None)
     assert st == binding.PA_ERR_INVALID_ARG
 
 

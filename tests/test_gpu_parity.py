@@ -335,6 +335,69 @@ def test_tensor_mask_beyond_the_matrix():
     check_full(p, what="tensor beyond")
 
 
+# ------------------------------------------------------------------ sparse lists
+SPARSE_CASES = [
+    # (lens, H, Hkv, Dk, Dv, bs, dtype, q_seq_lens, topk, shared)
+    ([300, 17, 1000, 70], 64, 1, 128, 128, 16, "bf16", None, 40, False),
+    ([200, 70, 33], 128, 2, 64, 64, 16, "f16", [4, 5, 3], 24, False),
+    ([1500, 77, 640], 64, 1, 576, 512, 128, "bf16", None, 512, True),     # the pages' shape: cmp_topk 512
+    ([300, 70], 64, 1, 576, 512, 64, "f16", [3, 2], 100, False),
+]
+
+
+def _sparse_problem(case, seed):
+    lens, H, Hkv, Dk, Dv, bs, dt, ql, topk, shared = case
+    p = synth.custom(lens, H, Hkv, Dk, Dv, bs, dt, "sparse", q_seq_lens=ql, seed=seed, shared_kv=shared, topk=topk)
+    # the last two entries of every list: one past the row's causal limit
+    # (where the sequence has one) and one past the sequence -- both skipped
+    idx = p.topk_idx.numpy()
+    qls = np.ones(p.batch, np.int64) if p.q_seq_lens_np is None else p.q_seq_lens_np
+    t = 0
+    for b in range(p.batch):
+        kv, q = int(p.context_lens_np[b]), int(qls[b])
+        for i in range(q):
+            pos = max(0, kv - q) + i
+            idx[t, :, -2] = pos + 1 if pos + 1 < kv else -1
+            idx[t, :, -1] = kv + 3
+            t += 1
+    p.topk_idx = torch.from_numpy(idx)
+    return p
+
+
+@pytest.mark.parametrize("case", SPARSE_CASES, ids=lambda c: f"D{c[3]}_H{c[1]}_k{c[8]}")
+def test_sparse_parity(case):
+    """Sparse lists over a compressed cache: parity with the oracle, balanced
+    and one worker per unit."""
+    log(f"sparse {case}")
+    p = _sparse_problem(case, 70 + case[3])
+    check_full(p, what=f"sparse {case}")
+    check_full(p, flags=F.PA_FLAG_NO_SPLIT, what=f"sparse no-split {case}")
+
+
+def test_sparse_reads_only_listed_rows():
+    """Cache rows no list selects may hold NaN and blocks holding none of
+    them may have invalid table entries: the output does not change, and no
+    error is flagged."""
+    log("sparse poison")
+    p = _sparse_problem(SPARSE_CASES[0], 75)
+    clean, _, _ = run_hip(to_device(p))
+    bs = p.workload.block_size
+    idx = p.topk_idx.numpy()
+    for b in range(p.batch):
+        kv = int(p.context_lens_np[b])
+        sel = set(int(c) for c in idx[b, 0] if 0 <= c < kv)
+        for j in range(kv):
+            if j not in sel:
+                p.key_cache[int(p.block_tables_np[b, j // bs]), j % bs] = float("nan")
+                p.value_cache[int(p.block_tables_np[b, j // bs]), j % bs] = float("nan")
+        for blk in range((kv + bs - 1) // bs):
+            if not any(blk * bs <= c < (blk + 1) * bs for c in sel):
+                p.block_tables_np[b, blk] = -9
+    dirty, _, att = run_hip(to_device(p))
+    assert np.array_equal(clean, dirty)
+    assert att.device_error() == 0
+
+
 # ------------------------------------------------------------------ probes
 def test_one_hot_gather_bit_exact():
     """K zero except the row of logical token t*, q one-hot: out is V[t*] bit for bit."""
@@ -566,6 +629,10 @@ def test_workload_band_shared_kv_decode_sampled():
 
 def test_workload_splitfuse_tensor_mask_sampled():
     full_size_sampled(9, 192, seed=7)
+
+
+def test_workload_sparse_topk_decode_sampled():
+    full_size_sampled(10, 128, seed=8)
 
 
 def test_workload_splitfuse_band_sampled():
