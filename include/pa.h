@@ -151,8 +151,8 @@ typedef struct pa_handle pa_handle;
  * build has no kernels for (64/64, 128/128, 256/256, 576/512 are built),
  * PA_FLAG_FORCE_VALU with any mask other than PA_MASK_NONE, sparse mode
  * unless head_num / kv_head_num is a multiple of 64 (the matrix-core tiles
- * of 64 rows must each hold one query token), or a device that is not
- * gfx950.  On success *out receives the handle.
+ * of 64 rows must each hold one query token) and topk <= 2048 (a list is
+ * resolved to cache rows in LDS), or a device that is not gfx950.  On success *out receives the handle.
  */
 pa_status pa_create(const pa_config *cfg, pa_handle **out);
 

@@ -183,8 +183,8 @@ static pa_status check_config(const pa_config *c)
         return PA_ERR_UNSUPPORTED;
     if ((c->flags & PA_FLAG_FORCE_MFMA) && !til)
         return PA_ERR_UNSUPPORTED;
-    if (c->mask == PA_MASK_SPARSE && (!til || G % kSparseTileRows != 0))
-        return PA_ERR_UNSUPPORTED;   // the rows of a tile must share one query token's list
+    if (c->mask == PA_MASK_SPARSE && (!til || G % kSparseTileRows != 0 || c->topk > 2048))
+        return PA_ERR_UNSUPPORTED;   // a tile's rows share one query token's list, staged whole in LDS
     if (!til && (int64_t)c->max_q_seq_len * G > 8)
         return PA_ERR_UNSUPPORTED;   // only the VALU kernel exists for this shape
     if ((c->flags & PA_FLAG_FORCE_VALU) && (int64_t)c->max_q_seq_len * G > 8)

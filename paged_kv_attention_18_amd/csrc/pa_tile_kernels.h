@@ -121,6 +121,7 @@ __device__ __forceinline__ void lds_load4(const void *src, lds_u8 *dst)
 // Kernel modes: the mask kinds that need code of their own.
 enum { MODE_PLAIN = 0, MODE_BAND = 1, MODE_TENSOR = 2, MODE_SPARSE = 3 };
 constexpr int kMaskDim = 2048;   // side of the shared mask matrix (tensor mask)
+constexpr int kSparseMaxTopk = 2048;   // list entries a segment stages in LDS (sparse lists)
 
 // Tensor mask: per chunk, the slice of the shared matrix a tile needs is
 // staged in LDS next to the K/V tiles, one row per query index of the tile
@@ -233,10 +234,12 @@ constexpr int tile_min_wgs()
 // the chunk, and the online softmax runs on scaled log2-domain scores.
 // MODE_SPARSE: the KV tokens of a unit are the entries of its query token's
 // list (all rows of a tile belong to one query token): chunk c holds list
-// entries 16 c .. 16 c + 15, each lane's LDS-load piece comes from the
-// cache row of its entry's token (the rows of a chunk sit one per lane and
-// each lane takes its own with ds_bpermute), and a per-chunk bit mask marks
-// the entries that select a visible token.
+// entries 16 c .. 16 c + 15.  At the start of a segment the workgroup
+// resolves all its entries to cache rows (list entry, then block id) into
+// LDS, so the chunk loop never waits for a lookup; each lane's LDS-load
+// piece comes from the cache row of its entry's token (the rows of a chunk
+// sit one per lane and each lane takes its own with ds_bpermute), and a
+// per-chunk bit mask marks the entries that select a visible token.
 template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH, int MODE>
 __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, CS, SH, MODE == MODE_TENSOR>()))
 void tile_kernel(Params p)
@@ -278,6 +281,8 @@ void tile_kernel(Params p)
     __shared__ __attribute__((aligned(256))) uint8_t sM3[S > 3 ? SLB : 16];
     // destination of the padding loads that keep every wave's count at LW
     __shared__ __attribute__((aligned(1024))) uint8_t sJunk[PAD ? 1024 : 16];
+    // sparse: the cache row of every list entry of the segment (-1: skipped)
+    __shared__ int s_rows[SPARSE ? kSparseMaxTopk : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -449,23 +454,10 @@ void tile_kernel(Params p)
         uint32_t smask[S];
         auto fetch_bids = [&](int c) __attribute__((always_inline)) {
             if constexpr (SPARSE) {
-                uint32_t bits = 0;
-                int rv = 0;
-#pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    const int k = c * 16 + t;
-                    const int ci = (lst_ok && k < p.topk) ? sload(lst, k) : -1;
-                    const bool valid = ci >= 0 && ci < lim_c;
-                    const int blk = sload(bt, valid ? div_bs(ci, bs, bsh) : 0);
-                    const bool inb = (unsigned)blk < nb32;
-                    err |= (valid && !inb) ? (uint32_t)PA_DEVERR_BLOCK_ID : 0u;
-                    const bool ok = valid && inb;
-                    bits |= ok ? (1u << t) : 0u;
-                    const int row = ok ? (int)((uint32_t)blk * (uint32_t)bs + (uint32_t)mod_bs(ci, bs, bsh)) : 0;
-                    rv = lane == t ? row : rv;
-                }
-                srow = rv;
-                sbits = bits;
+                // entry 16 c + lane's row from the segment's table (lanes < 16)
+                const int rv = lane < 16 ? s_rows[(c - c0) * 16 + lane] : -1;
+                sbits = (uint32_t)__ballot(rv >= 0);
+                srow = rv >= 0 ? rv : 0;
             } else {
 #pragma unroll
                 for (int q = 0; q < NTT; ++q) {
@@ -771,6 +763,26 @@ void tile_kernel(Params p)
         // every stage (previous segment).
         wait_vm<0>();
         __syncthreads();
+        if constexpr (SPARSE) {
+            // resolve the segment's list entries to cache rows (two dependent
+            // loads each, all entries at once), before any LDS load is issued
+            for (int k = c0 * 16 + tid; k < c1 * 16; k += 64 * NW) {
+                int row = -1;
+                if (lst_ok && k < p.topk) {
+                    const int ci = lst[k];
+                    if (ci >= 0 && ci < lim_c) {
+                        const int blk = bt[div_bs(ci, bs, bsh)];
+                        if ((unsigned)blk < nb32)
+                            row = (int)((uint32_t)blk * (uint32_t)bs + (uint32_t)mod_bs(ci, bs, bsh));
+                        else
+                            err |= (uint32_t)PA_DEVERR_BLOCK_ID;
+                    }
+                }
+                s_rows[k - c0 * 16] = row;
+            }
+            wait_vm<0>();
+            __syncthreads();
+        }
         fetch_bids(c0);
         issue(c0, kbuf(std::integral_constant<int, 0>{}), vbuf(std::integral_constant<int, 0>{}),
               mbuf(std::integral_constant<int, 0>{}));
