@@ -147,13 +147,20 @@ def cpu_baseline(p, target_s, threads):
         acc += cost[b]
     seqs.sort()
     inp = sub_problem(seqs)
+    # repeat a sample that finishes early (the whole workload can take well
+    # under a second), so the rate is not one short, noisy interval
+    reps = 0
     t = time.perf_counter()
-    pa_ref.forward(inp, threads=threads)
-    dt = time.perf_counter() - t
+    while True:
+        pa_ref.forward(inp, threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt >= min(3.0, target_s):
+            break
     tokens = int(ql[seqs].sum())
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tokens * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(seqs)} of {p.batch} sequences ({tokens} query tokens, all {w.head_num} heads, "
-                      f"{int(kv[seqs].sum())} KV tokens), fp64, {dt:.1f} s wall"}
+                      f"{int(kv[seqs].sum())} KV tokens), fp64, {reps} run(s) in {dt:.1f} s wall"}
 
 
 def main():
