@@ -510,6 +510,42 @@ def test_block_permutation_bit_exact():
         assert np.array_equal(v1, v2) and np.array_equal(w1, w2)
 
 
+def test_hip_graph_replays_match_eager():
+    """pa_forward captured in a HIP graph (through torch's graph capture):
+    every replay, with other GPU work and synchronisations in between,
+    gives the eager result bit for bit (decode with split units, and a
+    causal splitfuse mix on the matrix cores)."""
+    log("graph replay")
+    for p_cpu in (synth.custom([3000, 100, 2049, 700], 32, 8, 128, 128, 128, "bf16", seed=27),
+                  synth.custom([600, 90], 8, 2, 128, 128, 64, "f16", "causal", q_seq_lens=[130, 6], seed=28)):
+        p = to_device(p_cpu)
+        att = binding.for_problem(p)
+        T, H, Dv = p.num_q_tokens, p.workload.head_num, p.workload.head_size_v
+        ref_o, ref_l = binding.run_problem(att, p, return_lse=True)
+        ref_o, ref_l = ref_o.clone(), ref_l.clone()
+        out = torch.empty(T, H, Dv, dtype=p.query.dtype, device="cuda")
+        lse = torch.empty(T, H, dtype=torch.float32, device="cuda")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            binding.run_problem(att, p, out=out, lse=lse)   # warm-up on the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                binding.run_problem(att, p, out=out, lse=lse)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            out.fill_(float("nan"))
+            lse.zero_()
+            junk = torch.randn(1 << 20, device="cuda").sum()   # other work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), rep
+            del junk
+        assert att.device_error() == 0
+
+
 def test_deterministic_runs():
     log("determinism")
     p = to_device(synth.custom([3000, 100, 2049], 32, 8, 128, 128, 128, "bf16", seed=26))
