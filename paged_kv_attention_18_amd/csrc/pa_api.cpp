@@ -62,6 +62,9 @@ int kernel_mode(int mask)
 // Sparse lists: every 64-row tile must hold the rows of one query token.
 constexpr int kSparseTileRows = 64;
 
+// Kernel variant of the streaming kernel that plans for itself.
+constexpr int kSelfPlanVariant = 3;
+
 }  // namespace
 
 struct pa_handle {
@@ -112,6 +115,11 @@ struct pa_handle {
             v.rows_per_tile = pa::tile_rows(dk, dv, var, sh, mode);
             v.chunk = pa::tile_chunk(dk, dv, var, sh, mode);
             v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var, sh, mode);
+            if (var == 0 && pa::tile_supported(dk, dv, kSelfPlanVariant)) {
+                // the self-planning twin of the streaming kernel runs the same grid
+                const int w3 = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, kSelfPlanVariant, sh, mode);
+                v.partitions = w3 < v.partitions ? w3 : v.partitions;
+            }
             v.pieces_per_worker = var == 0 ? 1 : kMaxPiecesPerWorker;
         }
         if (cfg.num_partitions > 0)
@@ -392,17 +400,25 @@ static pa_status forward_impl(pa_handle *h, const void *query, const void *key_c
     p.pieces = p.no_split ? 0 : p.partitions * v.pieces_per_worker;
     p.partial_stride = (int32_t)partial_floats(v.rows_per_tile, c.head_size_v);
     p.ws = h->ws;
+    // The streaming kernel cuts its own pieces when the lengths fit in a
+    // wave's registers: one launch fewer, and no wait on plan data when a
+    // worker starts or moves to the next unit.
+    p.self_plan = (v.path == 1 && v.tile_variant == 0 && !p.no_split && batch <= pa::kSelfPlanMaxBatch &&
+                   p.pieces == p.partitions && max_q_seq_len <= 16 &&
+                   pa::tile_supported(c.head_size_k, c.head_size_v, kSelfPlanVariant))
+                      ? 1
+                      : 0;
 
     const bool timed = h->timing && h->timed < kMaxTimedPasses;
     hipEvent_t *ev = timed ? &h->events[4 * h->timed] : nullptr;
     if (timed && hipEventRecord(ev[0], s) != hipSuccess)
         return PA_ERR_HIP;
-    if (pa::launch_plan(p, s) != hipSuccess)
+    if (!p.self_plan && pa::launch_plan(p, s) != hipSuccess)
         return PA_ERR_HIP;
     if (timed && hipEventRecord(ev[1], s) != hipSuccess)
         return PA_ERR_HIP;
     hipError_t e = v.path == 0 ? pa::launch_decode(p, c.dtype, v.rows_pad, s)
-                               : pa::launch_tile(p, c.dtype, v.tile_variant, s);
+                               : pa::launch_tile(p, c.dtype, p.self_plan ? kSelfPlanVariant : v.tile_variant, s);
     if (e != hipSuccess)
         return PA_ERR_HIP;
     if (timed && hipEventRecord(ev[2], s) != hipSuccess)

@@ -78,8 +78,15 @@ struct Params {
     int32_t shared_kv;
     uint32_t v_row_bytes;              // bytes from one token row of the V source to the next
     uint32_t v_head_bytes;             // bytes from one KV head to the next within a token row
+    // The streaming kernel plans for itself (no plan kernel): every wave
+    // reads the lengths and cuts the pieces as the plan kernel would, and
+    // writes the header and the split entry of its own piece.
+    int32_t self_plan;
     Workspace ws;
 };
+
+// Largest batch a self-planning launch takes (four sequences per lane).
+constexpr int kSelfPlanMaxBatch = 256;
 
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const Params &p, hipStream_t s);
@@ -90,7 +97,8 @@ hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s);
 // Shapes and occupancy used by the host to pick kernels and size the grid.
 bool decode_supported(int dk, int dv);
 // MFMA tile kernel variants: 0 for units of at most 16 rows, 1 for up to
-// tile_rows(.., 1) rows, 2 above; tile_supported says which exist.
+// tile_rows(.., 1) rows, 2 above, 3 as 0 but planning for itself
+// (Params::self_plan); tile_supported says which exist.
 // `shared` selects the kernels that read V out of the K tile already in LDS
 // (shared K/V cache) where such kernels exist; `mode` the kernels of a mask
 // kind with code of its own (0 none / causal, 1 band, 2 tensor, 3 sparse).
@@ -495,6 +503,107 @@ __device__ __forceinline__ bool wg_range(const Params &p, int w, Cursor &cu, int
     cu.item = start;
     end = start + cu.nch;
     return true;
+}
+
+// ------------------------------------------------------------ planning
+// The planner's reading of the lengths and its cut into pieces, shared by the
+// plan kernel and the self-planning streaming kernel so both cut alike.
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(v, d);
+        v += lane >= d ? t : 0;
+    }
+    return v;
+}
+
+// Longest context the block table can address.
+__device__ __forceinline__ int seq_cap(const Params &p)
+{
+    const int64_t cap64 = (int64_t)p.max_blocks * p.block_size;
+    return cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
+}
+
+// Clamps one sequence's lengths into range; returns the error bits of what
+// was out of range.
+__device__ __forceinline__ uint32_t sanitize_seq(const Params &p, int cap, int &kv, int &ql)
+{
+    uint32_t err = 0;
+    if (kv < 0) {
+        err |= PA_DEVERR_CTX;
+        kv = 0;
+    }
+    if (kv > cap) {
+        err |= PA_DEVERR_TABLE_SHORT;
+        kv = cap;
+    }
+    if (ql < 0) {
+        err |= PA_DEVERR_QLEN;
+        ql = 0;
+    }
+    if (ql > p.max_q) {
+        err |= PA_DEVERR_QLEN;
+        ql = p.max_q;
+    }
+    if (p.causal && ql > kv)   // causal and band rows sit at positions kv - ql .. kv - 1
+        err |= PA_DEVERR_QLEN;
+    return err;
+}
+
+// Items of one (sequence, KV head): the chunks of all its row tiles.
+__device__ __forceinline__ int seq_items_per_group(const Params &p, int kv, int ql)
+{
+    const int ntile = seq_tiles(p, ql);
+    int ipg = 0;
+    for (int qt = 0; qt < ntile; ++qt)
+        ipg += unit_chunks(p, kv, ql, qt);
+    return ipg;
+}
+
+// Piece k begins at item s = k * pe, inside sequence b (first item wsb,
+// items per KV head ipg, first packed query row t0).  Returns the cursor at
+// s and, when `write` and k > 0, writes split entry k - 1: the unit that
+// boundary k cuts, if s falls strictly inside it and the unit began in
+// piece k - 1 (a unit cut several times is listed once).
+__device__ __forceinline__ Cursor piece_start(const Params &p, int k, int s, int pe, int b, int kv, int ql, int ipg,
+                                              int wsb, int t0, bool write)
+{
+    int local = s - wsb;
+    const int gg = local / ipg;
+    local -= gg * ipg;
+    int u0 = wsb + gg * ipg;
+    int t = 0, n = unit_chunks(p, kv, ql, 0);
+    while (local >= n) {
+        local -= n;
+        u0 += n;
+        ++t;
+        n = unit_chunks(p, kv, ql, t);
+    }
+    if (write && k > 0) {
+        int32_t *d = p.ws.splits + (size_t)(k - 1) * 8;
+        const bool split = s > u0 && s - pe <= u0;
+        int rows = ql * p.group - t * p.rows_per_tile;
+        rows = rows < p.rows_per_tile ? rows : p.rows_per_tile;
+        d[0] = split ? b : -1;
+        d[1] = gg;
+        d[2] = t;
+        d[3] = u0;
+        d[4] = u0 + n;
+        d[5] = t0;
+        d[6] = rows;
+    }
+    Cursor cu;
+    cu.b = b;
+    cu.g = gg;
+    cu.qt = t;
+    cu.c = local;
+    cu.nch = n;
+    cu.ntile = seq_tiles(p, ql);
+    cu.item = s;
+    return cu;
 }
 
 // Next piece for a worker that finished its current one (one lane calls).

@@ -27,17 +27,6 @@ namespace {
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanLdsB = 2048;   // sequences kept in LDS for the piece phase
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_scan(int v, int lane)
-{
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(v, d);
-        v += lane >= d ? t : 0;
-    }
-    return v;
-}
-
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
 {
     constexpr int NWV = kPlanThreads / 64;
@@ -54,10 +43,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         s_err = 0;
     }
     __syncthreads();
-    const int G = p.group;
-    const int R = p.rows_per_tile;
-    const int64_t cap64 = (int64_t)p.max_blocks * p.block_size;
-    const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
+    const int cap = seq_cap(p);
     for (int base = 0; base < p.batch; base += kPlanThreads) {
         const int b = base + tid;
         int ql = 0, kv = 0, ipg = 0, items = 0;
@@ -65,27 +51,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         if (b < p.batch) {
             kv = p.context_lens[b];
             ql = p.q_seq_lens ? p.q_seq_lens[b] : 1;
-            if (kv < 0) {
-                err |= PA_DEVERR_CTX;
-                kv = 0;
-            }
-            if (kv > cap) {
-                err |= PA_DEVERR_TABLE_SHORT;
-                kv = cap;
-            }
-            if (ql < 0) {
-                err |= PA_DEVERR_QLEN;
-                ql = 0;
-            }
-            if (ql > p.max_q) {
-                err |= PA_DEVERR_QLEN;
-                ql = p.max_q;
-            }
-            if (p.causal && ql > kv)   // causal and band rows sit at positions kv - ql .. kv - 1
-                err |= PA_DEVERR_QLEN;
-            const int ntile = (ql * G + R - 1) / R;
-            for (int qt = 0; qt < ntile; ++qt)
-                ipg += unit_chunks(p, kv, ql, qt);
+            err = sanitize_seq(p, cap, kv, ql);
+            ipg = seq_items_per_group(p, kv, ql);
             items = ipg * p.kv_head_num;
             p.ws.qlen[b] = ql;
             p.ws.kvlen[b] = kv;
@@ -169,28 +136,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
             const int ql = lds ? s_ql[b] : p.ws.qlen[b];
             const int ipg = lds ? s_ipg[b] : p.ws.ipg[b];
             const int t0 = lds ? s_t0[b] : p.ws.cu_q[b];
-            int local = s - wsb_of(b);
-            const int gg = local / ipg;
-            local -= gg * ipg;
-            int u0 = wsb_of(b) + gg * ipg;
-            int t = 0, n = unit_chunks(p, kv, ql, 0);
-            while (local >= n) {
-                local -= n;
-                u0 += n;
-                ++t;
-                n = unit_chunks(p, kv, ql, t);
-            }
-            int32_t *d = p.ws.splits + (size_t)(k - 1) * 8;
-            const bool split = s > u0 && s - pe <= u0;
-            int rows = ql * G - t * R;
-            rows = rows < R ? rows : R;
-            d[0] = split ? b : -1;
-            d[1] = gg;
-            d[2] = t;
-            d[3] = u0;
-            d[4] = u0 + n;
-            d[5] = t0;
-            d[6] = rows;
+            (void)piece_start(p, k, s, pe, b, kv, ql, ipg, wsb_of(b), t0, true);
         }
         // boundaries past the last item
         for (int k = (W + pe - 1) / pe + tid; k < p.pieces; k += kPlanThreads)

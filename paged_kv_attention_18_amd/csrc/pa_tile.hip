@@ -67,6 +67,11 @@ hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s)
     // the plan was made for this kernel's chunk and tile sizes
     if (!k || t.kt != p.chunk || 16 * t.mb * (t.nw / t.cs) != p.rows_per_tile)
         return hipErrorInvalidValue;
+    // only the streaming kernel's variant 3 plans for itself, for at most
+    // kSelfPlanMaxBatch sequences of at most 16 query tokens, one piece per wave
+    if ((p.self_plan != 0) != (variant == 3) ||
+        (p.self_plan && (t.nw != 1 || p.batch > kSelfPlanMaxBatch || p.pieces != p.partitions || p.max_q > 16)))
+        return hipErrorInvalidValue;
     void *args[] = {(void *)&p};
     return hipLaunchKernel(k, dim3(p.partitions), dim3(t.threads), args, 0, s);
 }

@@ -899,7 +899,12 @@ void tile_kernel(Params p)
 // one piece: taking further pieces from a shared counter needs the atomic's
 // return, and waiting for it is a wait on every load of the in-order vector
 // memory counter, which drains the ring.  MODE as for the tile kernel.
-template <int DT, int DK, int DV, int KT, int S, int MODE>
+// SELF: the kernel plans for itself (no plan kernel, at most
+// kSelfPlanMaxBatch sequences): every wave reads and sums the lengths as the
+// plan kernel does, finds its piece, writes the header (wave 0) and its
+// piece's split entry, and keeps the sequences' lengths in LDS, so neither
+// the start nor a move to the next unit waits for plan data in memory.
+template <int DT, int DK, int DV, int KT, int S, int MODE, bool SELF>
 __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
 {
     constexpr bool BAND = MODE == MODE_BAND, TMASK = MODE == MODE_TENSOR;
@@ -922,6 +927,10 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
     __shared__ __attribute__((aligned(1024))) uint8_t sQ[S * STQ];
     __shared__ __attribute__((aligned(256))) uint8_t sMk[TMASK ? S * SLB : 16];
     __shared__ int s_meta[S * MW];
+    // SELF: context length, first packed query row and query length
+    // (at most 16 here) of each sequence
+    __shared__ int s_skv[SELF ? kSelfPlanMaxBatch : 1], s_st0[SELF ? kSelfPlanMaxBatch : 1];
+    __shared__ uint8_t s_sql[SELF ? kSelfPlanMaxBatch : 4];
 
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15;
@@ -977,12 +986,144 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
         vo[m] = vrow * RBV + 16 * ((2 * m + ((lr & 3) >> 1)) ^ v_swz<RBV>(vrow)) + 8 * (lr & 1);
     }
 
-    // ------------------------------------------------------------ issue side
+    // ------------------------------------------------------------ the piece
+    // Sequence lengths: the plan kernel's arrays, or (SELF) this wave's LDS.
+    auto lds_int = [&](const int *a, int b) __attribute__((always_inline)) {
+        return __builtin_amdgcn_readfirstlane(a[b]);
+    };
+    auto seq_kv = [&](int b) __attribute__((always_inline)) {
+        if constexpr (SELF)
+            return lds_int(s_skv, b);
+        else
+            return sload(p.ws.kvlen, b);
+    };
+    auto seq_ql = [&](int b) __attribute__((always_inline)) {
+        if constexpr (SELF)
+            return (int)__builtin_amdgcn_readfirstlane((int)s_sql[b]);
+        else
+            return sload(p.ws.qlen, b);
+    };
+    auto seq_t0 = [&](int b) __attribute__((always_inline)) {
+        if constexpr (SELF)
+            return lds_int(s_st0, b);
+        else
+            return sload(p.ws.cu_q, b);
+    };
+    auto seq_has_items = [&](int b) __attribute__((always_inline)) {
+        if constexpr (SELF)   // a sequence has items iff it has query rows
+            return seq_ql(b) > 0;
+        else
+            return sload(p.ws.ipg, b) > 0;
+    };
+
     int ipiece = worker;
     Cursor ic;
     int iend;
-    if (ipiece >= p.partitions || !wg_range(p, ipiece, ic, iend))
+    if (ipiece >= p.partitions)
         return;
+    if constexpr (SELF) {
+        // up to four sequences per lane: b = lane + 64 i
+        const int cap = seq_cap(p);
+        int kvr[4] = {0, 0, 0, 0}, qlr[4] = {0, 0, 0, 0}, ipr[4] = {0, 0, 0, 0}, t0r[4] = {0, 0, 0, 0};
+        int wsbr[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = lane + 64 * i;
+            if (64 * i < p.batch && b < p.batch) {
+                kvr[i] = p.context_lens[b];
+                qlr[i] = p.q_seq_lens ? p.q_seq_lens[b] : 1;
+            }
+        }
+        uint32_t serr = 0;
+        int cq = 0, cw = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (64 * i >= p.batch)
+                break;
+            const int b = lane + 64 * i;
+            if (b < p.batch) {
+                serr |= sanitize_seq(p, cap, kvr[i], qlr[i]);
+                ipr[i] = seq_items_per_group(p, kvr[i], qlr[i]);
+            }
+            const int items = ipr[i] * p.kv_head_num;
+            const int iq = wave_scan(qlr[i], lane), iw = wave_scan(items, lane);
+            t0r[i] = cq + iq - qlr[i];
+            wsbr[i] = cw + iw - items;
+            cq += __builtin_amdgcn_readlane(iq, 63);
+            cw += __builtin_amdgcn_readlane(iw, 63);
+            if (b < p.batch) {
+                s_skv[b] = kvr[i];
+                s_st0[b] = t0r[i];
+                s_sql[b] = (uint8_t)qlr[i];
+            }
+        }
+        const int W = cw;
+        const int per = (W + p.pieces - 1) / p.pieces;
+        const int pe = per > 0 ? per : 1;
+        if (ipiece == 0) {
+            // the header and the error word, as the plan kernel writes them
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1)
+                serr |= __shfl_xor(serr, d);
+            if (cq != p.num_q_tokens)
+                serr |= PA_DEVERR_TOKENS;
+            if (lane == 0) {
+                p.ws.hdr[0] = W;
+                p.ws.hdr[1] = pe;
+                p.ws.hdr[2] = p.pieces;
+                p.ws.hdr[3] = 0;
+                if (serr)
+                    set_error(p.ws.err, serr);
+            }
+        }
+        const int s0 = ipiece * pe;
+        if (s0 >= W) {
+            // a boundary past the last item cuts nothing
+            if (ipiece > 0 && lane == 0)
+                p.ws.splits[(size_t)(ipiece - 1) * 8] = -1;
+            return;
+        }
+        // the sequence holding item s0: the last one whose first item is <= s0
+        int b0 = 0;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+            const uint64_t m = __ballot(lane + 64 * i < p.batch && wsbr[i] <= s0);
+            if (m) {
+                b0 = 64 * i + 63 - __builtin_clzll(m);
+                break;
+            }
+        }
+        const int i0 = b0 >> 6, l0 = b0 & 63;
+        auto pick4 = [&](const int(&r)[4]) __attribute__((always_inline)) {
+            return __builtin_amdgcn_readlane(i0 == 0 ? r[0] : (i0 == 1 ? r[1] : (i0 == 2 ? r[2] : r[3])), l0);
+        };
+        ic = piece_start(p, ipiece, s0, pe, b0, pick4(kvr), pick4(qlr), pick4(ipr), pick4(wsbr), pick4(t0r),
+                         lane == 0);
+        iend = s0 + pe < W ? s0 + pe : W;
+    } else {
+        if (!wg_range(p, ipiece, ic, iend))
+            return;
+    }
+    // the first chunk of the next unit (skipping sequences without rows);
+    // the caller has already advanced ic.item past the current unit
+    auto next_unit = [&]() __attribute__((always_inline)) {
+        ic.c = 0;
+        if (++ic.qt >= ic.ntile) {
+            ic.qt = 0;
+            if (++ic.g >= p.kv_head_num) {
+                ic.g = 0;
+                do {
+                    ++ic.b;
+                } while (ic.b < p.batch && !seq_has_items(ic.b));
+                if (ic.b >= p.batch)
+                    return;
+                ic.ntile = seq_tiles(p, seq_ql(ic.b));
+            }
+        }
+        ic.nch = unit_chunks(p, seq_kv(ic.b), seq_ql(ic.b), ic.qt);
+    };
+
+    // ------------------------------------------------------------ issue side
     int idone = 0, ifirst = 1;
     int ic1 = 0, icb = 0, invis = 0, inblk = 1, ikv = 0, iql = 0, it0 = 0, irows = 0;
     int icf = 0, ilo = 0;   // first chunk of the unit (from the sequence start), lowest visible token
@@ -991,9 +1132,9 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
     auto iseg = [&]() __attribute__((always_inline)) {
         icb = ic.c;
         ic1 = ic.nch < ic.c + (iend - ic.item) ? ic.nch : ic.c + (iend - ic.item);
-        ikv = sload(p.ws.kvlen, ic.b);
-        iql = sload(p.ws.qlen, ic.b);
-        it0 = sload(p.ws.cu_q, ic.b);
+        ikv = seq_kv(ic.b);
+        iql = seq_ql(ic.b);
+        it0 = seq_t0(ic.b);
         irows = iql * G - ic.qt * 16;
         irows = irows < 16 ? irows : 16;
         invis = row_hi_t<BAND>(p, ikv, seq_prefix(ikv, iql), (ic.qt * 16 + irows - 1) / G);
@@ -1094,7 +1235,7 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
             ifirst = 0;
             bool more = ic.item < iend;
             if (more) {
-                cursor_next_unit(p, ic);
+                next_unit();
                 more = ic.b < p.batch;
             }
             idone = more ? 0 : 1;
@@ -1371,7 +1512,11 @@ const void *kernel_for(int variant, bool shared, TileShape *t)
         } else {
             if (variant == 0) {   // one wave per workgroup, streaming across units
                 *t = TileShape{1, 16, 1, 1, 4, 64};
-                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE>;
+                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, false>;
+            }
+            if (variant == 3) {   // the same, planning for itself
+                *t = TileShape{1, 16, 1, 1, 4, 64};
+                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, true>;
             }
             if constexpr (MODE == MODE_TENSOR) {
                 if (variant == 1)

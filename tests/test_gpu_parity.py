@@ -569,6 +569,37 @@ def test_bad_block_id_is_flagged_not_read():
     assert att.device_error() == 0          # cleared by the previous read
 
 
+# The streaming kernel cuts its own pieces for up to 256 sequences (four per
+# lane of its wave) and takes the plan kernel's above; both cuts must give the
+# oracle's answer, at the register boundaries too.
+@pytest.mark.parametrize("batch", [63, 64, 65, 128, 256, 257, 400])
+def test_decode_batch_sizes_around_self_planning(batch):
+    log(f"decode batch {batch}")
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(1, 300, size=batch).tolist()
+    p = synth.custom(lens, 8, 2, 64, 64, 16, "f16", seed=batch)
+    check_full(p, what=f"batch {batch}")
+
+
+def test_stream_sequences_without_rows():
+    log("sequences without query rows")
+    p = synth.custom([40, 70, 5, 130, 64, 1, 333], 8, 4, 128, 128, 16, "bf16",
+                     q_seq_lens=[1, 0, 2, 0, 4, 0, 3], seed=31)
+    assert binding.for_problem(to_device(p)).describe()["path"] == "stream"
+    check_full(p, what="rows 0")
+
+
+def test_token_count_mismatch_is_flagged():
+    log("token count mismatch")
+    p = synth.custom([30, 40], 8, 2, 64, 64, 16, "f16", q_seq_lens=[2, 3], seed=32)
+    g = to_device(p)
+    ref_o, _ = oracle_full(p)
+    g.query = g.query[:4].contiguous()   # the lengths ask for 5 query tokens
+    o, _, att = run_hip(g)
+    assert att.device_error() & F.PA_DEVERR_TOKENS
+    assert_close(o, ref_o[:4], "f16", "rows that exist")
+
+
 def test_bad_lengths_are_clamped_and_flagged():
     log("bad lengths")
     p = synth.custom([100, 50], 4, 2, 64, 64, 16, "f16", seed=28)
