@@ -171,6 +171,12 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(0) only.
+__device__ __forceinline__ void wait_lgkm0()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
 // Wait until at most LW * min(ahead, A) vector memory instructions of this
 // wave are outstanding.
 template <int LW, int A>
@@ -889,23 +895,28 @@ void tile_kernel(Params p)
 }
 
 // ---------------------------------------------------------------------------
-// Streaming kernel for units of at most 16 rows (decode).  One wave is a
-// worker with its own S-stage LDS ring, and the ring does not drain between
-// units or pieces: the wave issues chunk k + S - 1 of its stream (whatever
-// unit or piece it belongs to) while it computes chunk k.  The first chunk
-// of every segment also carries the segment's 16 x Dk Q tile into its stage,
+// Streaming kernel for units of at most 16 rows (decode).  A workgroup of
+// two waves is a worker with an S-stage LDS ring: wave 0 issues the loads
+// (chunk k + S - 1 of its stream, whatever unit or piece it belongs to),
+// wave 1 computes chunk k, and one barrier per chunk hands a landed stage
+// to wave 1 and the stage wave 1 has finished back to wave 0.  The ring does
+// not drain between units, and the compute side's latencies (softmax, the
+// start and end of a segment, its output stores) never hold back a load:
+// the stores sit on the other wave's memory counter.  The first chunk of
+// every segment also carries the segment's 16 x Dk Q tile into its stage,
 // and each stage carries the chunk's segment parameters in a small LDS
-// record, so the compute side never waits for a lookup.  A worker keeps
-// one piece: taking further pieces from a shared counter needs the atomic's
+// record, so the compute side never waits for a lookup.  A worker keeps one
+// piece: taking further pieces from a shared counter needs the atomic's
 // return, and waiting for it is a wait on every load of the in-order vector
 // memory counter, which drains the ring.  MODE as for the tile kernel.
 // SELF: the kernel plans for itself (no plan kernel, at most
-// kSelfPlanMaxBatch sequences): every wave reads and sums the lengths as the
-// plan kernel does, finds its piece, writes the header (wave 0) and its
-// piece's split entry, and keeps the sequences' lengths in LDS, so neither
-// the start nor a move to the next unit waits for plan data in memory.
+// kSelfPlanMaxBatch sequences): the issuing wave reads and sums the lengths
+// as the plan kernel does, finds its piece, writes the header (worker 0)
+// and its piece's split entry, and keeps the sequences' lengths in LDS, so
+// neither the start nor a move to the next unit waits for plan data in
+// memory.
 template <int DT, int DK, int DV, int KT, int S, int MODE, bool SELF>
-__global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
+__global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
 {
     constexpr bool BAND = MODE == MODE_BAND, TMASK = MODE == MODE_TENSOR;
     constexpr int SDW = slab_row_dwords<KT>();
@@ -932,9 +943,11 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
     __shared__ int s_skv[SELF ? kSelfPlanMaxBatch : 1], s_st0[SELF ? kSelfPlanMaxBatch : 1];
     __shared__ uint8_t s_sql[SELF ? kSelfPlanMaxBatch : 4];
 
+    __shared__ int s_n;   // chunks of the worker's piece
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15;
     const int lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // 0 issues, 1 computes
     const int worker = xcd_logical_index(blockIdx.x, gridDim.x);
 
     const uint16_t *__restrict__ qg = (const uint16_t *)p.query;
@@ -1017,10 +1030,12 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
     };
 
     int ipiece = worker;
-    Cursor ic;
-    int iend;
+    Cursor ic{};
+    int iend = 0;
     if (ipiece >= p.partitions)
         return;
+    if (wave == 0) {
+    bool have = true;
     if constexpr (SELF) {
         // up to four sequences per lane: b = lane + 64 i
         const int cap = seq_cap(p);
@@ -1077,12 +1092,11 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
             }
         }
         const int s0 = ipiece * pe;
-        if (s0 >= W) {
-            // a boundary past the last item cuts nothing
-            if (ipiece > 0 && lane == 0)
-                p.ws.splits[(size_t)(ipiece - 1) * 8] = -1;
-            return;
-        }
+        have = s0 < W;
+        // a boundary past the last item cuts nothing
+        if (!have && ipiece > 0 && lane == 0)
+            p.ws.splits[(size_t)(ipiece - 1) * 8] = -1;
+        if (have) {
         // the sequence holding item s0: the last one whose first item is <= s0
         int b0 = 0;
 #pragma unroll
@@ -1100,10 +1114,19 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
         ic = piece_start(p, ipiece, s0, pe, b0, pick4(kvr), pick4(qlr), pick4(ipr), pick4(wsbr), pick4(t0r),
                          lane == 0);
         iend = s0 + pe < W ? s0 + pe : W;
+        }
     } else {
-        if (!wg_range(p, ipiece, ic, iend))
-            return;
+        have = wg_range(p, ipiece, ic, iend);
     }
+    if (lane == 0)
+        s_n = have ? iend - ic.item : 0;
+    }
+    // both waves learn the piece's length (0: no work) from wave 0
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    const int n = __builtin_amdgcn_readfirstlane(s_n);
+    if (n <= 0)
+        return;
     // the first chunk of the next unit (skipping sequences without rows);
     // the caller has already advanced ic.item past the current unit
     auto next_unit = [&]() __attribute__((always_inline)) {
@@ -1145,7 +1168,6 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
         ikg = kg + (size_t)ic.g * RBK;
         ivg = vg + (size_t)ic.g * p.v_head_bytes;
     };
-    iseg();
     int ibid[NTT];
     auto ifetch = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -1154,7 +1176,6 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
             ibid[q] = sload(ibt, blk < inblk ? blk : inblk - 1);
         }
     };
-    ifetch();
     int n_issued = 0;
     // Issue the next chunk of the stream into stage st (nothing once done).
     auto issue = [&](int st) __attribute__((always_inline)) {
@@ -1253,18 +1274,32 @@ __global__ __launch_bounds__(64, 3) void stream_kernel(Params p)
     int lim = 0, min_lim = 0, nvis = 0, rows = 0, t0 = 0, kv = 0, ql = 0;
     int lo_r = 0, max_lo = 0, lo_tile = 0;
 
+    if (wave == 0) {
+        // the issuing wave: n barriers, one per chunk, as the computing wave
+        iseg();
+        ifetch();
 #pragma unroll
-    for (int k = 0; k < S - 1; ++k)
-        issue(k);
+        for (int k = 0; k < S - 1; ++k)
+            issue(k);
+        for (int k = 0; k < n; ++k) {
+            wait_ahead<LW, S - 2>(n - 1 - k);   // chunk k (and any earlier Q tile) is in LDS
+            wait_lgkm0();                       // and its stage record
+            __builtin_amdgcn_s_barrier();       // wave 1 has finished chunk k - 1 ...
+            issue((k + S - 1) % S);             // ... whose stage this load fills
+        }
+        if (err)
+            set_error(p.ws.err, err);
+        return;
+    }
 
-    for (int k = 0; k < n_issued; ++k) {
+    for (int k = 0; k < n; ++k) {
         const int st = k % S;
-        wait_ahead<LW, S - 2>(n_issued - 1 - k);   // chunk k (and any earlier Q tile) is in LDS
+        wait_lgkm0();                  // this wave's reads of chunk k - 1 are done
+        __builtin_amdgcn_s_barrier();  // chunk k has landed
         int md[12];
 #pragma unroll
         for (int i = 0; i < 12; ++i)
             md[i] = __builtin_amdgcn_readfirstlane(s_meta[st * MW + i]);
-        issue((k + S - 1) % S);
         const int b = md[0], g = md[1], qt = md[2], c = md[3], fl = md[4];
         const lds_u8 *kb = (const lds_u8 *)sK + st * STK;
         const lds_u8 *vb = (const lds_u8 *)sV + st * STV;
@@ -1511,11 +1546,11 @@ const void *kernel_for(int variant, bool shared, TileShape *t)
                 return pick<DT, DK, DV, 1, 16, 4, 1, 2, false, MODE>(t);
         } else {
             if (variant == 0) {   // one wave per workgroup, streaming across units
-                *t = TileShape{1, 16, 1, 1, 4, 64};
+                *t = TileShape{1, 16, 1, 1, 4, 128};
                 return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, false>;
             }
             if (variant == 3) {   // the same, planning for itself
-                *t = TileShape{1, 16, 1, 1, 4, 64};
+                *t = TileShape{1, 16, 1, 1, 4, 128};
                 return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, true>;
             }
             if constexpr (MODE == MODE_TENSOR) {
