@@ -156,13 +156,15 @@ __host__ __device__ inline int merge_rows_per_wg(int dv)
 
 // One workgroup per (split unit, group of rows).  Piece k's partial of a
 // unit is in slot 0 if the unit started at or before the piece, else in slot 1.
-// The loads of up to KB parts are issued together before any is used, so
-// each batch of parts costs one memory round trip.
+// Each thread owns four consecutive outputs of one row and combines the
+// parts online (running max, rescaled sum and accumulator), reading a part's
+// m, l and its four accumulator values together: the loads of up to KB
+// parts are issued before any is used, so each batch of parts costs one
+// memory round trip and the row statistics need no pass of their own.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_groups)
 {
     constexpr int KB = 4;
-    __shared__ float s_m[64], s_inv[64];
     const int per = p.ws.hdr[1];
     const int32_t *d = p.ws.splits + (size_t)(blockIdx.x / row_groups) * 8;
     const int b = d[0];
@@ -184,73 +186,56 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_group
         k = k < last ? k : last;
         return p.ws.partials + (size_t)(2 * k + (k * per >= us ? 0 : 1)) * p.partial_stride;
     };
-    // row statistics: M = max_p m_p, L = sum_p l_p 2^(m_p - M), by an online
-    // combination over the parts
-    if (threadIdx.x < nr) {
-        const int r = r0 + threadIdx.x;
+    uint16_t *out = (uint16_t *)p.out;
+    // four consecutive outputs per thread and step (DV is a multiple of 4)
+    for (int idx = 4 * threadIdx.x; idx < nr * DV; idx += 4 * kThreads) {
+        const int rr = idx / DV;
+        const int e = idx - rr * DV;
+        const int r = r0 + rr;
         float M = -INFINITY, L = 0.f;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int k0 = first; k0 <= last; k0 += KB) {
             float mk[KB], lk[KB];
+            float4 a[KB];
 #pragma unroll
             for (int i = 0; i < KB; ++i) {
                 const float *pt = part_of(k0 + i);
                 mk[i] = pt[R * DV + r];
                 lk[i] = pt[R * DV + R + r];
+                a[i] = *(const float4 *)(pt + r * DV + e);
             }
 #pragma unroll
             for (int i = 0; i < KB; ++i) {
                 if (k0 + i > last || mk[i] == -INFINITY)
                     continue;
                 if (mk[i] > M) {
-                    L = L * exp2f(M - mk[i]) + lk[i];
+                    const float sc = exp2f(M - mk[i]);   // 0 while M is -inf
+                    L = L * sc + lk[i];
+                    acc[0] = acc[0] * sc + a[i].x;
+                    acc[1] = acc[1] * sc + a[i].y;
+                    acc[2] = acc[2] * sc + a[i].z;
+                    acc[3] = acc[3] * sc + a[i].w;
                     M = mk[i];
                 } else {
-                    L += lk[i] * exp2f(mk[i] - M);
+                    const float w = exp2f(mk[i] - M);
+                    L += lk[i] * w;
+                    acc[0] += w * a[i].x;
+                    acc[1] += w * a[i].y;
+                    acc[2] += w * a[i].z;
+                    acc[3] += w * a[i].w;
                 }
-            }
-        }
-        s_m[threadIdx.x] = M;
-        s_inv[threadIdx.x] = L > 0.f ? 1.f / L : 0.f;
-        const int rg = qt * R + r;
-        const int t = t0 + rg / G;
-        if (p.lse && t < p.num_q_tokens)
-            p.lse[(size_t)t * p.head_num + g * G + rg % G] =
-                L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
-    }
-    __syncthreads();
-    // four consecutive outputs per thread and step (DV is a multiple of 4)
-    uint16_t *out = (uint16_t *)p.out;
-    for (int idx = 4 * threadIdx.x; idx < nr * DV; idx += 4 * kThreads) {
-        const int rr = idx / DV;
-        const int e = idx - rr * DV;
-        const int r = r0 + rr;
-        const float M = s_m[rr];
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = first; k0 <= last; k0 += KB) {
-            float mk[KB];
-            float4 a[KB];
-#pragma unroll
-            for (int i = 0; i < KB; ++i) {
-                const float *pt = part_of(k0 + i);
-                mk[i] = pt[R * DV + r];
-                a[i] = *(const float4 *)(pt + r * DV + e);
-            }
-#pragma unroll
-            for (int i = 0; i < KB; ++i) {
-                const float w = (k0 + i > last || mk[i] == -INFINITY) ? 0.f : exp2f(mk[i] - M);
-                acc[0] += w * a[i].x;
-                acc[1] += w * a[i].y;
-                acc[2] += w * a[i].z;
-                acc[3] += w * a[i].w;
             }
         }
         const int rg = qt * R + r;
         const int t = t0 + rg / G;
         if (t < p.num_q_tokens) {
-            const float inv = s_inv[rr];
+            const float inv = L > 0.f ? 1.f / L : 0.f;
             const uint32_t w0 = (uint32_t)to_bits<DT>(acc[0] * inv) | ((uint32_t)to_bits<DT>(acc[1] * inv) << 16);
             const uint32_t w1 = (uint32_t)to_bits<DT>(acc[2] * inv) | ((uint32_t)to_bits<DT>(acc[3] * inv) << 16);
             *(uint2 *)(out + ((size_t)t * p.head_num + g * G + rg % G) * DV + e) = uint2{w0, w1};
+            if (e == 0 && p.lse)
+                p.lse[(size_t)t * p.head_num + g * G + rg % G] =
+                    L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
         }
     }
 }

@@ -1037,36 +1037,43 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     if (wave == 0) {
     bool have = true;
     if constexpr (SELF) {
-        // up to four sequences per lane: b = lane + 64 i
+        // up to four consecutive sequences per lane: b = spl * lane + i,
+        // summed in the lane first and then over the wave (one scan each for
+        // query tokens and items, whatever the batch)
         const int cap = seq_cap(p);
+        const int spl = (p.batch + 63) >> 6;
         int kvr[4] = {0, 0, 0, 0}, qlr[4] = {0, 0, 0, 0}, ipr[4] = {0, 0, 0, 0}, t0r[4] = {0, 0, 0, 0};
         int wsbr[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int b = lane + 64 * i;
-            if (64 * i < p.batch && b < p.batch) {
+            const int b = spl * lane + i;
+            if (i < spl && b < p.batch) {
                 kvr[i] = p.context_lens[b];
                 qlr[i] = p.q_seq_lens ? p.q_seq_lens[b] : 1;
             }
         }
         uint32_t serr = 0;
-        int cq = 0, cw = 0;
+        int lq = 0, lw = 0;   // the lane's running sums
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (64 * i >= p.batch)
-                break;
-            const int b = lane + 64 * i;
-            if (b < p.batch) {
+            const int b = spl * lane + i;
+            if (i < spl && b < p.batch) {
                 serr |= sanitize_seq(p, cap, kvr[i], qlr[i]);
                 ipr[i] = seq_items_per_group(p, kvr[i], qlr[i]);
             }
-            const int items = ipr[i] * p.kv_head_num;
-            const int iq = wave_scan(qlr[i], lane), iw = wave_scan(items, lane);
-            t0r[i] = cq + iq - qlr[i];
-            wsbr[i] = cw + iw - items;
-            cq += __builtin_amdgcn_readlane(iq, 63);
-            cw += __builtin_amdgcn_readlane(iw, 63);
-            if (b < p.batch) {
+            t0r[i] = lq;
+            wsbr[i] = lw;
+            lq += qlr[i];
+            lw += ipr[i] * p.kv_head_num;
+        }
+        const int iq = wave_scan(lq, lane), iw = wave_scan(lw, lane);
+        const int cq = __builtin_amdgcn_readlane(iq, 63), cw = __builtin_amdgcn_readlane(iw, 63);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = spl * lane + i;
+            t0r[i] += iq - lq;
+            wsbr[i] += iw - lw;
+            if (i < spl && b < p.batch) {
                 s_skv[b] = kvr[i];
                 s_st0[b] = t0r[i];
                 s_sql[b] = (uint8_t)qlr[i];
@@ -1097,17 +1104,17 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
         if (!have && ipiece > 0 && lane == 0)
             p.ws.splits[(size_t)(ipiece - 1) * 8] = -1;
         if (have) {
-        // the sequence holding item s0: the last one whose first item is <= s0
-        int b0 = 0;
+        // the sequence holding item s0: the last one whose first item is
+        // <= s0 (first items grow with b, so a lane's qualifying sequences
+        // are a prefix of its own)
+        int nle = 0;
 #pragma unroll
-        for (int i = 3; i >= 0; --i) {
-            const uint64_t m = __ballot(lane + 64 * i < p.batch && wsbr[i] <= s0);
-            if (m) {
-                b0 = 64 * i + 63 - __builtin_clzll(m);
-                break;
-            }
-        }
-        const int i0 = b0 >> 6, l0 = b0 & 63;
+        for (int i = 0; i < 4; ++i)
+            nle += (i < spl && spl * lane + i < p.batch && wsbr[i] <= s0) ? 1 : 0;
+        const uint64_t m = __ballot(nle > 0);   // lane 0 always qualifies (b = 0)
+        const int l0 = 63 - __builtin_clzll(m);
+        const int i0 = __builtin_amdgcn_readlane(nle, l0) - 1;
+        const int b0 = spl * l0 + i0;
         auto pick4 = [&](const int(&r)[4]) __attribute__((always_inline)) {
             return __builtin_amdgcn_readlane(i0 == 0 ? r[0] : (i0 == 1 ? r[1] : (i0 == 2 ? r[2] : r[3])), l0);
         };
