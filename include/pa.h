@@ -97,9 +97,12 @@ enum {
                                       i.e. max_q_seq_len * head_num / kv_head_num <= 8) */
     PA_FLAG_FORCE_MFMA = 1u << 1,  /* testing: take the MFMA tile path always */
     PA_FLAG_NO_SPLIT = 1u << 2,    /* testing: one worker per (sequence, KV head, row tile); no merge */
-    PA_FLAG_SHARED_KV = 1u << 3    /* one cache for K and V: the V row of a token is the leading
+    PA_FLAG_SHARED_KV = 1u << 3,   /* one cache for K and V: the V row of a token is the leading
                                       head_size_v elements of its K row (requires Dv <= Dk); see
                                       pa_forward's value_cache */
+    PA_FLAG_STATIC_PIECES = 1u << 4 /* measurement: the decode streaming kernel keeps one piece per
+                                       worker (no pieces claimed at run time); results agree with
+                                       the default to the usual tolerance, not bit for bit */
 };
 
 /* Device error word bits (pa_get_device_error). */

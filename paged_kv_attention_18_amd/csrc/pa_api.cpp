@@ -31,6 +31,8 @@ struct Variant {
     int chunk;
     int partitions;  // balanced-mode workers (waves for the VALU kernel, workgroups for MFMA)
     int pieces_per_worker;
+    bool claimed_tail;   // self-planning launches cut a claimed tail (up to pa::kTailRounds rounds)
+    int max_pieces() const { return partitions * (claimed_tail ? 1 + pa::kTailRounds : pieces_per_worker); }
 };
 
 int next_pow2(int x)
@@ -76,6 +78,7 @@ struct pa_handle {
     pa::Workspace ws{};
     int max_partitions = 0;
     size_t max_partial_floats = 0;
+    size_t max_pieces = 0;   // pieces of a pass, at most (split entries and partial slot pairs)
     // timing
     bool timing = false;
     std::vector<hipEvent_t> events;   // 4 per pass
@@ -121,6 +124,10 @@ struct pa_handle {
                 v.partitions = w3 < v.partitions ? w3 : v.partitions;
             }
             v.pieces_per_worker = var == 0 ? 1 : kMaxPiecesPerWorker;
+            // the self-planning streaming kernel may add rounds of claimed
+            // pieces (pa::PieceMap)
+            v.claimed_tail = var == 0 && pa::tile_supported(dk, dv, kSelfPlanVariant) &&
+                             !(cfg.flags & PA_FLAG_STATIC_PIECES);
         }
         if (cfg.num_partitions > 0)
             v.partitions = cfg.num_partitions;
@@ -160,7 +167,8 @@ static pa_status check_config(const pa_config *c)
         return PA_ERR_INVALID_ARG;
     if ((c->flags & PA_FLAG_FORCE_VALU) && (c->flags & PA_FLAG_FORCE_MFMA))
         return PA_ERR_INVALID_ARG;
-    if (c->flags & ~(uint32_t)(PA_FLAG_FORCE_VALU | PA_FLAG_FORCE_MFMA | PA_FLAG_NO_SPLIT | PA_FLAG_SHARED_KV))
+    if (c->flags & ~(uint32_t)(PA_FLAG_FORCE_VALU | PA_FLAG_FORCE_MFMA | PA_FLAG_NO_SPLIT | PA_FLAG_SHARED_KV |
+                               PA_FLAG_STATIC_PIECES))
         return PA_ERR_INVALID_ARG;
     if ((c->flags & PA_FLAG_SHARED_KV) && c->head_size_v > c->head_size_k)
         return PA_ERR_INVALID_ARG;   // V must fit inside the K row
@@ -226,7 +234,7 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
     h->num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
 
     // Largest grid and partial slot over every call this handle may see.
-    size_t max_floats = 0;
+    size_t max_floats = 0, max_pieces = 1, max_slot_floats = 0;   // slot floats: pieces x floats per slot
     int max_p = 8;
     // The variant depends on max_q * G only through thresholds at or below 65
     // rows, so the calls with max_q <= 65 and max_q = cfg->max_q_seq_len
@@ -246,6 +254,10 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
             max_floats = f;
         if (v.partitions > max_p)
             max_p = v.partitions;
+        if ((size_t)v.max_pieces() > max_pieces)
+            max_pieces = (size_t)v.max_pieces();
+        if ((size_t)v.max_pieces() * f > max_slot_floats)
+            max_slot_floats = (size_t)v.max_pieces() * f;
         const int tiles = (int)(((int64_t)q * G + v.rows_per_tile - 1) / v.rows_per_tile);
         if (tiles > max_tiles)
             max_tiles = tiles;
@@ -253,23 +265,23 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
     (void)max_tiles;
     h->max_partitions = max_p;
     h->max_partial_floats = max_floats;
+    h->max_pieces = max_pieces;
 
     const int B = cfg->max_batch;
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
     size_t off = 0;
-    const size_t o_hdr = off; off = align(off + 4 * sizeof(int32_t));
+    const size_t o_hdr = off; off = align(off + 8 * sizeof(int32_t));
     const size_t o_cuq = off; off = align(off + (B + 1) * sizeof(int32_t));
     const size_t o_wsb = off; off = align(off + (B + 1) * sizeof(int32_t));
     const size_t o_ipg = off; off = align(off + B * sizeof(int32_t));
     const size_t o_ql = off; off = align(off + B * sizeof(int32_t));
     const size_t o_kv = off; off = align(off + B * sizeof(int32_t));
-    const size_t max_pieces = (size_t)max_p * kMaxPiecesPerWorker;
     const size_t o_wgb = off; off = align(off + max_pieces * sizeof(int32_t));
     const size_t o_spl = off; off = align(off + max_pieces * 8 * sizeof(int32_t));
     const size_t o_err = off; off = align(off + sizeof(uint32_t));
     const size_t zero_bytes = 16 * (size_t)cfg->kv_head_num * (size_t)(cfg->head_size_k > cfg->head_size_v ? cfg->head_size_k : cfg->head_size_v) * 2;
     const size_t o_zero = off; off = align(off + zero_bytes);
-    const size_t o_part = off; off = align(off + 2 * max_pieces * max_floats * sizeof(float));
+    const size_t o_part = off; off = align(off + 2 * max_slot_floats * sizeof(float));
     h->ws_bytes = off;
     if (hipMalloc(&h->ws_base, h->ws_bytes) != hipSuccess) {
         delete h;
@@ -400,6 +412,7 @@ static pa_status forward_impl(pa_handle *h, const void *query, const void *key_c
     p.pieces = p.no_split ? 0 : p.partitions * v.pieces_per_worker;
     p.partial_stride = (int32_t)partial_floats(v.rows_per_tile, c.head_size_v);
     p.ws = h->ws;
+    p.tail_min = 0;
     // The streaming kernel cuts its own pieces when the lengths fit in a
     // wave's registers: one launch fewer, and no wait on plan data when a
     // worker starts or moves to the next unit.
@@ -408,6 +421,11 @@ static pa_status forward_impl(pa_handle *h, const void *query, const void *key_c
                    pa::tile_supported(c.head_size_k, c.head_size_v, kSelfPlanVariant))
                       ? 1
                       : 0;
+    // self-planning: claimed pieces after the static ones, in rounds that
+    // shrink down to kTailMinChunks chunks (the kernel decides from the
+    // lengths whether the pass is long enough for them)
+    if (p.self_plan && v.claimed_tail)
+        p.tail_min = pa::kTailMinChunks;
 
     const bool timed = h->timing && h->timed < kMaxTimedPasses;
     hipEvent_t *ev = timed ? &h->events[4 * h->timed] : nullptr;

@@ -22,14 +22,18 @@ namespace pa {
 //  persistent workers (workgroups of the MFMA kernel, waves of the VALU
 //  kernel) takes piece w first, then further pieces from a shared counter
 //  (pieces P, P + 1, ...) until none is left, so the workers finish
-//  together even when they stream at different rates.  In no-split mode
+//  together even when they stream at different rates.  The pieces are
+//  either all alike, or (the self-planning streaming kernel, PieceMap) P
+//  static pieces holding about four fifths of the items followed by rounds
+//  of smaller pieces that workers claim as they run out.  In no-split mode
 //  (per = 0) every workgroup is one unit.  A unit whose items lie in more
 //  than one piece is split: each of its pieces leaves an fp32 partial
 //  (acc, m, l) in its slot (2k if the unit is the first of piece k, 2k + 1
 //  if it is the last), and the merge kernel combines them.
 
 struct Workspace {
-    int32_t *hdr;        // [4]: W (total items), per, N (pieces), next piece counter
+    int32_t *hdr;        // [8]: W (total items), per, N (pieces), next piece counter, and
+                         //      the rest of the PieceMap: a, m, P, nr
     int32_t *cu_q;       // [max_batch + 1]: first packed query row of each sequence
     int32_t *wsb;        // [max_batch + 1]: first item of each sequence
     int32_t *ipg;        // [max_batch]: items of each (b, g) (equal for all g of b)
@@ -82,11 +86,26 @@ struct Params {
     // reads the lengths and cuts the pieces as the plan kernel would, and
     // writes the header and the split entry of its own piece.
     int32_t self_plan;
+    // Self-planning launches: smallest piece of the claimed tail in items
+    // (0: one piece per worker, no tail).
+    int32_t tail_min;
     Workspace ws;
 };
 
 // Largest batch a self-planning launch takes (four sequences per lane).
 constexpr int kSelfPlanMaxBatch = 256;
+
+// Claimed pieces per worker share, at most: a launch with a claimed tail
+// has at most (1 + kTailRounds) * workers pieces.
+constexpr int kTailRounds = 8;
+// Smallest claimed piece of the streaming kernel, in chunks: a worker claims
+// its next piece while it computes the current one, at least 4 chunks
+// before its issuing side needs it (the ring is 4 stages deep); and every
+// piece beyond the first of a unit costs a partial write and its merge.
+constexpr int kTailMinChunks = 16;
+// Shares of fewer chunks per worker keep one piece each: balancing short
+// streams gains less than the merge work the extra pieces cost.
+constexpr int kTailMinShare = 20;   // in units of the tail minimum
 
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const Params &p, hipStream_t s);
@@ -563,13 +582,13 @@ __device__ __forceinline__ int seq_items_per_group(const Params &p, int kv, int 
     return ipg;
 }
 
-// Piece k begins at item s = k * pe, inside sequence b (first item wsb,
-// items per KV head ipg, first packed query row t0).  Returns the cursor at
-// s and, when `write` and k > 0, writes split entry k - 1: the unit that
-// boundary k cuts, if s falls strictly inside it and the unit began in
-// piece k - 1 (a unit cut several times is listed once).
-__device__ __forceinline__ Cursor piece_start(const Params &p, int k, int s, int pe, int b, int kv, int ql, int ipg,
-                                              int wsb, int t0, bool write)
+// Piece k begins at item s, inside sequence b (first item wsb, items per KV
+// head ipg, first packed query row t0); piece k - 1 began at item s_prev.
+// Returns the cursor at s and, when `write` and k > 0, writes split entry
+// k - 1: the unit that boundary k cuts, if s falls strictly inside it and
+// the unit began in piece k - 1 (a unit cut several times is listed once).
+__device__ __forceinline__ Cursor piece_start(const Params &p, int k, int s, int s_prev, int b, int kv, int ql,
+                                              int ipg, int wsb, int t0, bool write)
 {
     int local = s - wsb;
     const int gg = local / ipg;
@@ -584,7 +603,7 @@ __device__ __forceinline__ Cursor piece_start(const Params &p, int k, int s, int
     }
     if (write && k > 0) {
         int32_t *d = p.ws.splits + (size_t)(k - 1) * 8;
-        const bool split = s > u0 && s - pe <= u0;
+        const bool split = s > u0 && s_prev <= u0;
         int rows = ql * p.group - t * p.rows_per_tile;
         rows = rows < p.rows_per_tile ? rows : p.rows_per_tile;
         d[0] = split ? b : -1;
@@ -604,6 +623,136 @@ __device__ __forceinline__ Cursor piece_start(const Params &p, int k, int s, int
     cu.ntile = seq_tiles(p, ql);
     cu.item = s;
     return cu;
+}
+
+// ------------------------------------------------------------ piece map
+// Where the pieces of an item range lie; pieces are numbered in item order.
+// Uniform map (m = 0): pieces of `per` items, cut short at W (N = a pieces).
+// Map with a claimed tail (m > 0, the self-planning streaming kernel): the
+// range is cut into P shares of `per` items (the first W - P * per shares
+// hold one item more, in their static piece); a share is its worker's
+// static piece of `a` items followed by nr smaller pieces, of about half the share's remaining
+// tail each, down to m items, the last taking what is left (at least m; at
+// most kTailRounds of them).  Workers take their static piece first, then
+// claim the tail pieces round by round over all shares (the largest first:
+// the guided scheme known as factoring), so fast workers take more; and
+// since every share keeps its own tail, a unit of the range is cut into at
+// most about nr + 1 pieces per share it spans.  The map depends on the
+// lengths alone, like the pieces themselves.
+struct PieceMap {
+    int W, per, a, m, P, nr;
+};
+
+// First item of share w (the first L = W - P * per shares hold per + 1).
+__host__ __device__ __forceinline__ int share_start(const PieceMap &pm, int w)
+{
+    const int L = pm.W - pm.P * pm.per;
+    return w * pm.per + (w < L ? w : L);
+}
+
+// Items of round r's piece in every share's tail (tail = per - a items).
+__host__ __device__ __forceinline__ int tail_piece_size(const PieceMap &pm, int r, int &left)
+{
+    int s = left / 2;
+    s = s > pm.m ? s : pm.m;
+    if (left - s < pm.m || r == kTailRounds - 1)
+        s = left;
+    left -= s;
+    return s;
+}
+
+// Pieces of the map.
+__host__ __device__ __forceinline__ int piece_count(const PieceMap &pm)
+{
+    return pm.m > 0 ? pm.P * (1 + pm.nr) : pm.a;
+}
+
+// The piece a worker starts with, and the piece a claim (0, 1, ...: round
+// by round, share by share) stands for (-1: none left).
+__host__ __device__ __forceinline__ int static_piece(const PieceMap &pm, int w)
+{
+    return pm.m > 0 ? w * (1 + pm.nr) : w;
+}
+
+__host__ __device__ __forceinline__ int claimed_piece(const PieceMap &pm, int c)
+{
+    if (pm.m <= 0 || c < 0 || c >= pm.nr * pm.P)
+        return -1;
+    return (c % pm.P) * (1 + pm.nr) + 1 + c / pm.P;
+}
+
+// Items [s0, s1) of piece k (empty past the last piece).
+__host__ __device__ __forceinline__ void piece_range(const PieceMap &pm, int k, int &s0, int &s1)
+{
+    if (pm.m <= 0) {
+        const int64_t x = (int64_t)k * pm.per, y = x + pm.per;
+        s0 = x < pm.W ? (int)x : pm.W;
+        s1 = y < pm.W ? (int)y : pm.W;
+        return;
+    }
+    if (k < 0 || k >= piece_count(pm)) {
+        s0 = s1 = k < 0 ? 0 : pm.W;
+        return;
+    }
+    const int w = k / (1 + pm.nr), j = k - w * (1 + pm.nr);
+    const int a = pm.a + (share_start(pm, w + 1) - share_start(pm, w) - pm.per);   // static piece
+    s0 = share_start(pm, w);
+    if (j == 0) {
+        s1 = s0 + a;
+        return;
+    }
+    s0 += a;
+    int left = pm.per - pm.a, sz = 0;
+    for (int r = 0; r < j; ++r) {
+        s0 += sz;
+        sz = tail_piece_size(pm, r, left);
+    }
+    s1 = s0 + sz;
+}
+
+// The piece holding item `item` (0 <= item < W).
+__host__ __device__ __forceinline__ int piece_of(const PieceMap &pm, int item)
+{
+    if (pm.m <= 0)
+        return item / pm.per;
+    const int L = pm.W - pm.P * pm.per;
+    const int w = item < L * (pm.per + 1) ? item / (pm.per + 1) : L + (item - L * (pm.per + 1)) / pm.per;
+    int off = item - share_start(pm, w) - pm.a - (w < L ? 1 : 0);
+    if (off < 0)
+        return w * (1 + pm.nr);
+    int left = pm.per - pm.a;
+    for (int r = 0; r < pm.nr; ++r) {
+        const int sz = tail_piece_size(pm, r, left);
+        if (off < sz || r == pm.nr - 1)
+            return w * (1 + pm.nr) + 1 + r;
+        off -= sz;
+    }
+    return w * (1 + pm.nr) + pm.nr;
+}
+
+// The map as written in the workspace header.
+__device__ __forceinline__ PieceMap header_piece_map(const int32_t *hdr)
+{
+    return PieceMap{hdr[0], hdr[1], hdr[4], hdr[5], hdr[6], hdr[7]};
+}
+
+// The self-planning streaming kernel's map of W items: with a claimed tail
+// when the launch asks for one and every share holds at least
+// kTailMinShare * m items (static pieces of 4/5 of a share, so a tail holds
+// at least m), else one uniform piece per worker.
+__host__ __device__ __forceinline__ PieceMap self_piece_map(const Params &p, int W)
+{
+    const int P = p.partitions, m = p.tail_min;
+    if (m > 0 && (int64_t)W >= (int64_t)kTailMinShare * m * P) {
+        PieceMap pm{W, W / P, 0, m, P, 0};
+        pm.a = (int)(((int64_t)4 * pm.per) / 5);
+        int left = pm.per - pm.a;
+        while (left > 0)
+            (void)tail_piece_size(pm, pm.nr++, left);
+        return pm;
+    }
+    const int per = (W + p.pieces - 1) / p.pieces;
+    return PieceMap{W, per > 0 ? per : 1, p.pieces, 0, P, 0};
 }
 
 // Next piece for a worker that finished its current one (one lane calls).

@@ -104,6 +104,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         p.ws.hdr[1] = per > 0 ? per : (p.no_split ? 0 : 1);
         p.ws.hdr[2] = p.no_split ? 0 : p.pieces;
         p.ws.hdr[3] = 0;
+        p.ws.hdr[4] = p.no_split ? 0 : p.pieces;   // all pieces alike: no tail
+        p.ws.hdr[5] = 0;
+        p.ws.hdr[6] = p.partitions;
+        p.ws.hdr[7] = 0;
         if (s_carry_q != p.num_q_tokens)
             s_err |= PA_DEVERR_TOKENS;
     }
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
             const int ql = lds ? s_ql[b] : p.ws.qlen[b];
             const int ipg = lds ? s_ipg[b] : p.ws.ipg[b];
             const int t0 = lds ? s_t0[b] : p.ws.cu_q[b];
-            (void)piece_start(p, k, s, pe, b, kv, ql, ipg, wsb_of(b), t0, true);
+            (void)piece_start(p, k, s, s - pe, b, kv, ql, ipg, wsb_of(b), t0, true);
         }
         // boundaries past the last item
         for (int k = (W + pe - 1) / pe + tid; k < p.pieces; k += kPlanThreads)
@@ -147,6 +151,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         set_error(p.ws.err, s_err);
 }
 
+// Merge workgroups at most; more tasks are taken in turn.
+constexpr long long kMergeMaxGrid = 16384;
+
 // Rows per merge workgroup: enough to give every thread ~4 outputs.
 __host__ __device__ inline int merge_rows_per_wg(int dv)
 {
@@ -154,24 +161,29 @@ __host__ __device__ inline int merge_rows_per_wg(int dv)
     return r < 1 ? 1 : (r > 64 ? 64 : r);
 }
 
-// One workgroup per (split unit, group of rows).  Piece k's partial of a
-// unit is in slot 0 if the unit started at or before the piece, else in slot 1.
+// One workgroup per (split unit, group of rows), the grid striding over the
+// split entries of the pass (their number is known on the device only).
+// Piece k's partial of a unit is in slot 0 if the unit started at or before
+// the piece, else in slot 1: slot 1 only for the first piece of the unit.
+// Workgroup 0 also resets the piece counter for the next pass, which the
+// attention kernel has finished with (the self-planning kernel does not
+// reset it: its workers claim pieces from the moment they start).
 // Each thread owns four consecutive outputs of one row and combines the
 // parts online (running max, rescaled sum and accumulator), reading a part's
-// m, l and its four accumulator values together: the loads of up to KB
+// m, l and its four accumulator values together: the loads of KB = 8
 // parts are issued before any is used, so each batch of parts costs one
 // memory round trip and the row statistics need no pass of their own.
-template <int DT>
-__global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_groups)
+template <int DT, int KB>
+__device__ __forceinline__ void merge_task(const Params &p, const PieceMap &pm, int entry, int rgp)
 {
-    constexpr int KB = 4;
-    const int per = p.ws.hdr[1];
-    const int32_t *d = p.ws.splits + (size_t)(blockIdx.x / row_groups) * 8;
-    const int b = d[0];
-    if (b < 0 || per <= 0)
+    // the entry by scalar loads: the piece arithmetic below runs once per
+    // workgroup on the scalar unit
+    const int32_t *d = p.ws.splits + (size_t)entry * 8;
+    const int b = sload(d, 0);
+    if (b < 0)
         return;
-    const int g = d[1], qt = d[2], us = d[3], ue = d[4], t0 = d[5], rows = d[6];
-    const int rgp = blockIdx.x % row_groups;
+    const int g = sload(d, 1), qt = sload(d, 2), us = sload(d, 3), ue = sload(d, 4), t0 = sload(d, 5),
+              rows = sload(d, 6);
     const int G = p.group;
     const int R = p.rows_per_tile;
     const int DV = p.head_size_v;
@@ -180,11 +192,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_group
     if (r0 >= rows)
         return;
     const int nr = rows - r0 < RPW ? rows - r0 : RPW;
-    const int first = us / per;
-    const int last = (ue - 1) / per;
+    const int first = piece_of(pm, us);
+    const int last = piece_of(pm, ue - 1);
+    int f0, f1;
+    piece_range(pm, first, f0, f1);
+    const int slot_first = 2 * first + (f0 >= us ? 0 : 1);
     auto part_of = [&](int k) -> const float * {
         k = k < last ? k : last;
-        return p.ws.partials + (size_t)(2 * k + (k * per >= us ? 0 : 1)) * p.partial_stride;
+        return p.ws.partials + (size_t)(k == first ? slot_first : 2 * k) * p.partial_stride;
     };
     uint16_t *out = (uint16_t *)p.out;
     // four consecutive outputs per thread and step (DV is a multiple of 4)
@@ -240,6 +255,21 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_group
     }
 }
 
+template <int DT>
+__global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_groups)
+{
+    constexpr int KB = 8;
+    const PieceMap pm{sload(p.ws.hdr, 0), sload(p.ws.hdr, 1), sload(p.ws.hdr, 4),
+                      sload(p.ws.hdr, 5), sload(p.ws.hdr, 6), sload(p.ws.hdr, 7)};
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        p.ws.hdr[3] = 0;
+    if (pm.per <= 0)
+        return;
+    const int nent = piece_count(pm) - 1;   // boundaries between pieces
+    for (int task = blockIdx.x; task < nent * row_groups; task += gridDim.x)
+        merge_task<DT, KB>(p, pm, task / row_groups, task % row_groups);
+}
+
 }  // namespace
 
 hipError_t launch_plan(const Params &p, hipStream_t s)
@@ -252,9 +282,15 @@ hipError_t launch_merge(const Params &p, int dtype, hipStream_t s)
 {
     const int row_groups = (p.rows_per_tile + merge_rows_per_wg(p.head_size_v) - 1) /
                            merge_rows_per_wg(p.head_size_v);
-    const long long grid = (long long)(p.pieces - 1) * row_groups;
+    // the self-planning kernel's claimed tail makes up to kTailRounds rounds
+    // of pieces more; workgroups past the pass's split entries return at once
+    const long long max_pieces = (p.self_plan && p.tail_min > 0) ? (long long)(1 + kTailRounds) * p.partitions
+                                                                 : (long long)p.pieces;
+    long long grid = (max_pieces - 1) * row_groups;
     if (grid <= 0 || p.no_split)
         return hipSuccess;
+    if (grid > kMergeMaxGrid)   // the workgroups stride over the tasks
+        grid = kMergeMaxGrid;
     if (grid > 0x7fffffff)
         return hipErrorInvalidValue;
     if (dtype == 0)

@@ -905,16 +905,25 @@ void tile_kernel(Params p)
 // the stores sit on the other wave's memory counter.  The first chunk of
 // every segment also carries the segment's 16 x Dk Q tile into its stage,
 // and each stage carries the chunk's segment parameters in a small LDS
-// record, so the compute side never waits for a lookup.  A worker keeps one
-// piece: taking further pieces from a shared counter needs the atomic's
-// return, and waiting for it is a wait on every load of the in-order vector
-// memory counter, which drains the ring.  MODE as for the tile kernel.
+// record, so the compute side never waits for a lookup.  MODE as for the
+// tile kernel.
 // SELF: the kernel plans for itself (no plan kernel, at most
 // kSelfPlanMaxBatch sequences): the issuing wave reads and sums the lengths
 // as the plan kernel does, finds its piece, writes the header (worker 0)
-// and its piece's split entry, and keeps the sequences' lengths in LDS, so
-// neither the start nor a move to the next unit waits for plan data in
-// memory.
+// and its piece's split entry, and keeps the sequences' lengths and first
+// items in LDS, so neither the start nor a move to the next unit waits for
+// plan data in memory.  With a claimed tail (PieceMap), a worker goes on
+// from its static piece to pieces it claims from the shared counter.  The
+// computing wave claims: the atomic's return would make the issuing wave
+// wait on its in-order memory counter, behind every KV load in flight,
+// while the computing wave's counter holds only its few stores.  It sends
+// the atomic kClaimAhead chunks before it must know the answer and puts the
+// claimed piece (or -1: none left) into LDS before the barrier after which
+// the issuing wave issues the last chunk of the current piece; the issuing
+// wave then moves straight on to the claimed piece and the ring never
+// drains.  Every stage record carries the chunks left in its piece, and the
+// last chunk of a worker's stream is flagged, so the two waves agree on the
+// number of barriers.
 template <int DT, int DK, int DV, int KT, int S, int MODE, bool SELF>
 __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
 {
@@ -929,7 +938,8 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     constexpr int IPGV = RBV / 64;
     constexpr int LW = NTT * (IPGK + IPGV);       // loads per chunk (plus IPGK for a Q tile)
     constexpr int STK = KT * RBK, STV = KT * RBV, STQ = 16 * RBK;
-    constexpr int MW = 12;                        // ints per stage record
+    constexpr int MW = 13;                        // ints per stage record
+    constexpr int kClaimAhead = 4;                // chunks between a claim and its deadline
     static_assert(DK <= 256 && DV <= 256 && DK % 32 == 0 && DV % 64 == 0 && (KT == 16 || KT == 32), "shape");
     static_assert(S >= 2 && S <= 4 && LW * (S - 2) + IPGK < 64, "ring");
 
@@ -942,8 +952,11 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     // (at most 16 here) of each sequence
     __shared__ int s_skv[SELF ? kSelfPlanMaxBatch : 1], s_st0[SELF ? kSelfPlanMaxBatch : 1];
     __shared__ uint8_t s_sql[SELF ? kSelfPlanMaxBatch : 4];
+    // SELF: first item of each sequence; the piece claimed next
+    __shared__ int s_wsb[SELF ? kSelfPlanMaxBatch : 1];
+    __shared__ int s_claim;
 
-    __shared__ int s_n;   // chunks of the worker's piece
+    __shared__ int s_n, s_nr, s_dyn;   // chunks of the first piece, claimed pieces per share, claimed tail
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15;
     const int lg = lane >> 4;
@@ -1032,10 +1045,12 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     int ipiece = worker;
     Cursor ic{};
     int iend = 0;
+    PieceMap ipm{};   // SELF: the pass's piece map (issuing wave)
     if (ipiece >= p.partitions)
         return;
     if (wave == 0) {
     bool have = true;
+    int nr = 0, dyn = 0;
     if constexpr (SELF) {
         // up to four consecutive sequences per lane: b = spl * lane + i,
         // summed in the lane first and then over the wave (one scan each for
@@ -1077,12 +1092,15 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
                 s_skv[b] = kvr[i];
                 s_st0[b] = t0r[i];
                 s_sql[b] = (uint8_t)qlr[i];
+                s_wsb[b] = wsbr[i];
             }
         }
         const int W = cw;
-        const int per = (W + p.pieces - 1) / p.pieces;
-        const int pe = per > 0 ? per : 1;
-        if (ipiece == 0) {
+        ipm = self_piece_map(p, W);
+        nr = ipm.nr;
+        dyn = ipm.m > 0 ? 1 : 0;
+        ipiece = static_piece(ipm, worker);
+        if (worker == 0) {
             // the header and the error word, as the plan kernel writes them
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1)
@@ -1090,16 +1108,22 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             if (cq != p.num_q_tokens)
                 serr |= PA_DEVERR_TOKENS;
             if (lane == 0) {
+                // (the piece counter, hdr[3], is reset by the merge kernel)
                 p.ws.hdr[0] = W;
-                p.ws.hdr[1] = pe;
-                p.ws.hdr[2] = p.pieces;
-                p.ws.hdr[3] = 0;
+                p.ws.hdr[1] = ipm.per;
+                p.ws.hdr[2] = piece_count(ipm);
+                p.ws.hdr[4] = ipm.a;
+                p.ws.hdr[5] = ipm.m;
+                p.ws.hdr[6] = ipm.P;
+                p.ws.hdr[7] = ipm.nr;
                 if (serr)
                     set_error(p.ws.err, serr);
             }
         }
-        const int s0 = ipiece * pe;
-        have = s0 < W;
+        int s0, s1, sp0, sp1;
+        piece_range(ipm, ipiece, s0, s1);
+        piece_range(ipm, ipiece - 1, sp0, sp1);
+        have = s0 < s1;
         // a boundary past the last item cuts nothing
         if (!have && ipiece > 0 && lane == 0)
             p.ws.splits[(size_t)(ipiece - 1) * 8] = -1;
@@ -1118,15 +1142,19 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
         auto pick4 = [&](const int(&r)[4]) __attribute__((always_inline)) {
             return __builtin_amdgcn_readlane(i0 == 0 ? r[0] : (i0 == 1 ? r[1] : (i0 == 2 ? r[2] : r[3])), l0);
         };
-        ic = piece_start(p, ipiece, s0, pe, b0, pick4(kvr), pick4(qlr), pick4(ipr), pick4(wsbr), pick4(t0r),
+        ic = piece_start(p, ipiece, s0, sp0, b0, pick4(kvr), pick4(qlr), pick4(ipr), pick4(wsbr), pick4(t0r),
                          lane == 0);
-        iend = s0 + pe < W ? s0 + pe : W;
+        iend = s1;
         }
     } else {
         have = wg_range(p, ipiece, ic, iend);
     }
-    if (lane == 0)
+    if (lane == 0) {
         s_n = have ? iend - ic.item : 0;
+        s_nr = nr;
+        s_dyn = dyn;
+        s_claim = -1;
+    }
     }
     // both waves learn the piece's length (0: no work) from wave 0
     wait_lgkm0();
@@ -1134,6 +1162,8 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     const int n = __builtin_amdgcn_readfirstlane(s_n);
     if (n <= 0)
         return;
+    const bool cdyn = SELF && __builtin_amdgcn_readfirstlane(s_dyn) != 0;
+    const int c_nr = __builtin_amdgcn_readfirstlane(s_nr);
     // the first chunk of the next unit (skipping sequences without rows);
     // the caller has already advanced ic.item past the current unit
     auto next_unit = [&]() __attribute__((always_inline)) {
@@ -1181,6 +1211,30 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
         for (int q = 0; q < NTT; ++q) {
             const int blk = div_bs((icf + ic.c) * KT + 16 * q, bs, bsh);
             ibid[q] = sload(ibt, blk < inblk ? blk : inblk - 1);
+        }
+    };
+    // SELF: the sequence holding item s (the last one whose first item is
+    // <= s; lane 0 always qualifies) and the cursor at the start of piece k
+    auto goto_piece = [&](int k) __attribute__((always_inline)) {
+        if constexpr (SELF) {
+            int s0, s1, sp0, sp1;
+            piece_range(ipm, k, s0, s1);
+            piece_range(ipm, k - 1, sp0, sp1);
+            const int spl = (p.batch + 63) >> 6;
+            int nle = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int b = spl * lane + i;
+                nle += (i < spl && b < p.batch && s_wsb[b] <= s0) ? 1 : 0;
+            }
+            const uint64_t m = __ballot(nle > 0);
+            const int l0 = 63 - __builtin_clzll(m);
+            const int b0 = spl * l0 + __builtin_amdgcn_readlane(nle, l0) - 1;
+            const int kv0 = lds_int(s_skv, b0), ql0 = seq_ql(b0);
+            ic = piece_start(p, k, s0, sp0, b0, kv0, ql0, seq_items_per_group(p, kv0, ql0), lds_int(s_wsb, b0),
+                             lds_int(s_st0, b0), lane == 0);
+            iend = s1;
+            ipiece = k;
         }
     };
     int n_issued = 0;
@@ -1240,6 +1294,14 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
                 lds_load16(vbase + voV[m], (lds_u8 *)sV + st * STV + (q * IPGV + m) * 1024);
         }
         const bool seg_end = ic.c + 1 == ic1;
+        // the last chunk of the piece: the piece the computing wave claimed
+        // to follow it is in LDS by now (-1: none, the stream ends here)
+        const bool piece_end = ic.item + 1 == iend;
+        int nxt = -1;
+        if constexpr (SELF) {
+            if (piece_end && cdyn)
+                nxt = __builtin_amdgcn_readfirstlane(*(volatile int *)&s_claim);
+        }
         if (lane == 0) {
             int *md = s_meta + st * MW;
             md[0] = ic.b;
@@ -1254,6 +1316,7 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             md[9] = it0;
             md[10] = irows;
             md[11] = ilo;
+            md[12] = iend - ic.item - 1;   // chunks of the piece after this one
         }
         ++n_issued;
         // advance the issue position by one chunk
@@ -1265,11 +1328,17 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             if (more) {
                 next_unit();
                 more = ic.b < p.batch;
+            } else if (nxt >= 0) {
+                goto_piece(nxt);
+                ifirst = 1;
+                more = true;
             }
             idone = more ? 0 : 1;
             if (!idone)
                 iseg();
         }
+        if (idone && lane == 0)   // the last chunk of the stream: the computing wave stops after it
+            s_meta[st * MW + 4] |= 16;
         if (!idone)
             ifetch();
     };
@@ -1282,14 +1351,15 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     int lo_r = 0, max_lo = 0, lo_tile = 0;
 
     if (wave == 0) {
-        // the issuing wave: n barriers, one per chunk, as the computing wave
+        // the issuing wave: one barrier per chunk of the stream, as the
+        // computing wave (the stream's length is known once it has ended)
         iseg();
         ifetch();
 #pragma unroll
         for (int k = 0; k < S - 1; ++k)
             issue(k);
-        for (int k = 0; k < n; ++k) {
-            wait_ahead<LW, S - 2>(n - 1 - k);   // chunk k (and any earlier Q tile) is in LDS
+        for (int k = 0; k < n_issued; ++k) {
+            wait_ahead<LW, S - 2>(n_issued - 1 - k);   // chunk k (and any earlier Q tile) is in LDS
             wait_lgkm0();                       // and its stage record
             __builtin_amdgcn_s_barrier();       // wave 1 has finished chunk k - 1 ...
             issue((k + S - 1) % S);             // ... whose stage this load fills
@@ -1299,15 +1369,29 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
         return;
     }
 
-    for (int k = 0; k < n; ++k) {
+    // claim state: the piece whose successor is being claimed, and 0 (not
+    // yet), 1 (atomic sent), 2 (answer in LDS)
+    int cpiece = -1, cstate = 0, cval = 0;
+    for (int k = 0;; ++k) {
         const int st = k % S;
         wait_lgkm0();                  // this wave's reads of chunk k - 1 are done
         __builtin_amdgcn_s_barrier();  // chunk k has landed
-        int md[12];
+        int md[MW];
 #pragma unroll
-        for (int i = 0; i < 12; ++i)
+        for (int i = 0; i < MW; ++i)
             md[i] = __builtin_amdgcn_readfirstlane(s_meta[st * MW + i]);
         const int b = md[0], g = md[1], qt = md[2], c = md[3], fl = md[4];
+        if (cdyn) {
+            if (md[5] != cpiece) {
+                cpiece = md[5];
+                cstate = 0;
+            }
+            if (cstate == 0 && md[12] <= S + kClaimAhead) {
+                if (lane == 0)
+                    cval = __hip_atomic_fetch_add(p.ws.hdr + 3, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                cstate = 1;
+            }
+        }
         const lds_u8 *kb = (const lds_u8 *)sK + st * STK;
         const lds_u8 *vb = (const lds_u8 *)sV + st * STV;
         if (fl & 1) {
@@ -1471,6 +1555,14 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             }
         }
 
+        if (cdyn && cstate == 1 && md[12] <= S) {
+            // the deadline: the issuing wave reads the answer after the next
+            // barrier, when it issues the piece's last chunk
+            const int nx = claimed_piece(PieceMap{0, 0, 0, 1, p.partitions, c_nr}, __builtin_amdgcn_readlane(cval, 0));
+            if (lane == 0)
+                s_claim = nx;
+            cstate = 2;
+        }
         if (fl & 2) {
             // last chunk of the segment: output or partial
             const bool whole = fl & 4;
@@ -1509,6 +1601,8 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
                 }
             }
         }
+        if (fl & 16)   // the last chunk of the stream
+            break;
     }
     if (err)
         set_error(p.ws.err, err);

@@ -516,10 +516,14 @@ def test_hip_graph_replays_match_eager():
     gives the eager result bit for bit (decode with split units, and a
     causal splitfuse mix on the matrix cores)."""
     log("graph replay")
-    for p_cpu in (synth.custom([3000, 100, 2049, 700], 32, 8, 128, 128, 128, "bf16", seed=27),
-                  synth.custom([600, 90], 8, 2, 128, 128, 64, "f16", "causal", q_seq_lens=[130, 6], seed=28)):
+    tail = synth.custom(np.random.default_rng(29).integers(1000, 4000, size=24).tolist(), 32, 8, 128, 128, 128,
+                        "bf16", seed=29)
+    for p_cpu, parts in ((synth.custom([3000, 100, 2049, 700], 32, 8, 128, 128, 128, "bf16", seed=27), 0),
+                         (synth.custom([600, 90], 8, 2, 128, 128, 64, "f16", "causal", q_seq_lens=[130, 6],
+                                       seed=28), 0),
+                         (tail, 16)):   # the streaming kernel's claimed tail (counter reset by the merge)
         p = to_device(p_cpu)
-        att = binding.for_problem(p)
+        att = binding.for_problem(p, num_partitions=parts)
         T, H, Dv = p.num_q_tokens, p.workload.head_num, p.workload.head_size_v
         ref_o, ref_l = binding.run_problem(att, p, return_lse=True)
         ref_o, ref_l = ref_o.clone(), ref_l.clone()
@@ -579,6 +583,65 @@ def test_decode_batch_sizes_around_self_planning(batch):
     lens = rng.integers(1, 300, size=batch).tolist()
     p = synth.custom(lens, 8, 2, 64, 64, 16, "f16", seed=batch)
     check_full(p, what=f"batch {batch}")
+
+
+# The self-planning streaming kernel's claimed tail: each worker streams a
+# static piece of about four fifths of its share, then claims further, smaller
+# pieces from a counter while it computes, so fast workers take more.  Few
+# workers make the tail appear at sizes the oracle finishes quickly (it needs
+# at least 20 * 16 chunks per worker); the map of pieces depends on the
+# lengths alone, so results are the same whichever worker ran which piece.
+TAIL_CASES = [
+    # (batch, length range, H, Hkv, D, bs, dtype, workers)
+    (48, (200, 3000), 32, 8, 128, 128, "bf16", 16),
+    (100, (1, 1800), 16, 2, 64, 16, "f16", 8),
+    (256, (1, 2000), 32, 8, 128, 64, "f16", 48),
+    (7, (3000, 9000), 64, 8, 128, 128, "bf16", 8),
+]
+
+
+@pytest.mark.parametrize("case", TAIL_CASES, ids=lambda c: f"B{c[0]}_G{c[2]//c[3]}_D{c[4]}_P{c[7]}")
+def test_claimed_tail_parity(case):
+    B, (lo, hi), H, Hkv, D, bs, dt, P = case
+    log(f"claimed tail {case}")
+    lens = np.random.default_rng(B + P).integers(lo, hi, size=B).tolist()
+    p = synth.custom(lens, H, Hkv, D, D, bs, dt, seed=40 + P)
+    items = sum(-(-k // 16) for k in lens) * Hkv
+    assert items >= 20 * 16 * P   # long enough for a tail
+    check_full(p, num_partitions=P, what=f"tail {case}")
+    check_full(p, num_partitions=P, flags=F.PA_FLAG_STATIC_PIECES, what=f"static pieces {case}")
+
+
+def test_claimed_tail_repeatable_and_reset_between_calls():
+    """Back-to-back calls on one handle (the piece counter is reset after
+    every pass): the same lengths give bit-identical results, a different
+    batch in between gives its own oracle answer, and a permutation of the
+    physical blocks changes nothing."""
+    log("claimed tail: repeats")
+    rng = np.random.default_rng(77)
+    la, lb = rng.integers(500, 4000, size=40).tolist(), rng.integers(100, 2500, size=64).tolist()
+    nb = int(1.25 * max(sum(-(-k // 128) for k in la), sum(-(-k // 128) for k in lb)))
+    pa_cpu = synth.custom(la, 32, 8, 128, 128, 128, "bf16", seed=78, num_blocks=nb, max_blocks=32)
+    pb_cpu = synth.custom(lb, 32, 8, 128, 128, 128, "bf16", seed=79, num_blocks=nb, max_blocks=32)
+    pa, pb = to_device(pa_cpu), to_device(pb_cpu)
+    att = binding.for_problem(pb, num_partitions=16)
+    first = binding.run_problem(att, pa).clone()
+    ob = binding.run_problem(att, pb).clone()
+    again = binding.run_problem(att, pa).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+    assert_close(first.double().cpu().numpy(), oracle_full(pa_cpu)[0], "bf16", "tail call 1")
+    assert_close(ob.double().cpu().numpy(), oracle_full(pb_cpu)[0], "bf16", "tail call 2")
+    perm = np.random.default_rng(5).permutation(pa_cpu.num_blocks)
+    inv = torch.from_numpy(np.argsort(perm).astype(np.int64))
+    p2 = synth.Problem(**{**pa_cpu.__dict__})
+    p2.key_cache = pa_cpu.key_cache[inv].clone()
+    p2.value_cache = pa_cpu.value_cache[inv].clone()
+    p2.block_tables_np = perm[pa_cpu.block_tables_np].astype(np.int32)
+    permuted = binding.run_problem(att, to_device(p2)).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), permuted.view(torch.int16))
+    assert att.device_error() == 0
 
 
 def test_stream_sequences_without_rows():
