@@ -64,8 +64,10 @@ int kernel_mode(int mask)
 // Sparse lists: every 64-row tile must hold the rows of one query token.
 constexpr int kSparseTileRows = 64;
 
-// Kernel variant of the streaming kernel that plans for itself.
+// Kernel variants of the streaming kernel that plan for themselves: one
+// static piece per worker, and the same with a claimed tail of pieces.
 constexpr int kSelfPlanVariant = 3;
+constexpr int kSelfPlanTailVariant = 4;
 
 }  // namespace
 
@@ -119,14 +121,16 @@ struct pa_handle {
             v.chunk = pa::tile_chunk(dk, dv, var, sh, mode);
             v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var, sh, mode);
             if (var == 0 && pa::tile_supported(dk, dv, kSelfPlanVariant)) {
-                // the self-planning twin of the streaming kernel runs the same grid
-                const int w3 = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, kSelfPlanVariant, sh, mode);
-                v.partitions = w3 < v.partitions ? w3 : v.partitions;
+                // the self-planning twins of the streaming kernel run the same grid
+                for (int sv : {kSelfPlanVariant, kSelfPlanTailVariant}) {
+                    const int w3 = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, sv, sh, mode);
+                    v.partitions = w3 < v.partitions ? w3 : v.partitions;
+                }
             }
             v.pieces_per_worker = var == 0 ? 1 : kMaxPiecesPerWorker;
             // the self-planning streaming kernel may add rounds of claimed
             // pieces (pa::PieceMap)
-            v.claimed_tail = var == 0 && pa::tile_supported(dk, dv, kSelfPlanVariant) &&
+            v.claimed_tail = var == 0 && pa::tile_supported(dk, dv, kSelfPlanTailVariant) &&
                              !(cfg.flags & PA_FLAG_STATIC_PIECES);
         }
         if (cfg.num_partitions > 0)
@@ -422,10 +426,15 @@ static pa_status forward_impl(pa_handle *h, const void *query, const void *key_c
                       ? 1
                       : 0;
     // self-planning: claimed pieces after the static ones, in rounds that
-    // shrink down to kTailMinChunks chunks (the kernel decides from the
-    // lengths whether the pass is long enough for them)
-    if (p.self_plan && v.claimed_tail)
-        p.tail_min = pa::kTailMinChunks;
+    // shrink down to kTailMinChunks chunks, where the block tables can hold
+    // a pass long enough for them (the kernel decides from the lengths);
+    // shorter passes take the kernel without the claiming code
+    if (p.self_plan && v.claimed_tail) {
+        const int64_t cap = (int64_t)c.max_num_blocks_per_seq * c.block_size;
+        const int64_t w_max = (int64_t)batch * c.kv_head_num * ((cap + v.chunk - 1) / v.chunk);
+        if (w_max >= (int64_t)pa::kTailMinShare * pa::kTailMinChunks * p.partitions)
+            p.tail_min = pa::kTailMinChunks;
+    }
 
     const bool timed = h->timing && h->timed < kMaxTimedPasses;
     hipEvent_t *ev = timed ? &h->events[4 * h->timed] : nullptr;
@@ -436,7 +445,10 @@ static pa_status forward_impl(pa_handle *h, const void *query, const void *key_c
     if (timed && hipEventRecord(ev[1], s) != hipSuccess)
         return PA_ERR_HIP;
     hipError_t e = v.path == 0 ? pa::launch_decode(p, c.dtype, v.rows_pad, s)
-                               : pa::launch_tile(p, c.dtype, p.self_plan ? kSelfPlanVariant : v.tile_variant, s);
+                               : pa::launch_tile(p, c.dtype,
+                                                 p.self_plan ? (p.tail_min > 0 ? kSelfPlanTailVariant : kSelfPlanVariant)
+                                                             : v.tile_variant,
+                                                 s);
     if (e != hipSuccess)
         return PA_ERR_HIP;
     if (timed && hipEventRecord(ev[2], s) != hipSuccess)

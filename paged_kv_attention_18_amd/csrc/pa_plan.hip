@@ -151,9 +151,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         set_error(p.ws.err, s_err);
 }
 
-// Merge workgroups at most; more tasks are taken in turn.
-constexpr long long kMergeMaxGrid = 16384;
-
 // Rows per merge workgroup: enough to give every thread ~4 outputs.
 __host__ __device__ inline int merge_rows_per_wg(int dv)
 {
@@ -161,8 +158,8 @@ __host__ __device__ inline int merge_rows_per_wg(int dv)
     return r < 1 ? 1 : (r > 64 ? 64 : r);
 }
 
-// One workgroup per (split unit, group of rows), the grid striding over the
-// split entries of the pass (their number is known on the device only).
+// One workgroup per (split entry, group of rows), for as many entries as a
+// pass can have (their number is known on the device only).
 // Piece k's partial of a unit is in slot 0 if the unit started at or before
 // the piece, else in slot 1: slot 1 only for the first piece of the unit.
 // Workgroup 0 also resets the piece counter for the next pass, which the
@@ -170,20 +167,43 @@ __host__ __device__ inline int merge_rows_per_wg(int dv)
 // reset it: its workers claim pieces from the moment they start).
 // Each thread owns four consecutive outputs of one row and combines the
 // parts online (running max, rescaled sum and accumulator), reading a part's
-// m, l and its four accumulator values together: the loads of KB = 8
+// m, l and its four accumulator values together: the loads of KB = 4
 // parts are issued before any is used, so each batch of parts costs one
 // memory round trip and the row statistics need no pass of their own.
-template <int DT, int KB>
-__device__ __forceinline__ void merge_task(const Params &p, const PieceMap &pm, int entry, int rgp)
+// TAIL: the pass may have a claimed tail (PieceMap); else its pieces are
+// all alike and every entry of the grid belongs to the pass.
+template <int DT, bool TAIL>
+__device__ __forceinline__ void merge_body(const Params &p, int row_groups)
 {
-    // the entry by scalar loads: the piece arithmetic below runs once per
-    // workgroup on the scalar unit
+    constexpr int KB = 4;
+    const int entry = blockIdx.x / row_groups;
     const int32_t *d = p.ws.splits + (size_t)entry * 8;
-    const int b = sload(d, 0);
-    if (b < 0)
-        return;
-    const int g = sload(d, 1), qt = sload(d, 2), us = sload(d, 3), ue = sload(d, 4), t0 = sload(d, 5),
-              rows = sload(d, 6);
+    int first, last, slot_first;
+    int us, ue;
+    if constexpr (TAIL) {
+        const PieceMap pm = header_piece_map(p.ws.hdr);
+        // entries past the pass's last boundary are left over from other passes
+        if (d[0] < 0 || pm.per <= 0 || entry >= piece_count(pm) - 1)
+            return;
+        us = d[3];
+        ue = d[4];
+        first = piece_of(pm, us);
+        last = piece_of(pm, ue - 1);
+        int f0, f1;
+        piece_range(pm, first, f0, f1);
+        slot_first = 2 * first + (f0 >= us ? 0 : 1);
+    } else {
+        const int per = p.ws.hdr[1];
+        if (d[0] < 0 || per <= 0)
+            return;
+        us = d[3];
+        ue = d[4];
+        first = us / per;
+        last = (ue - 1) / per;
+        slot_first = 2 * first + (first * per >= us ? 0 : 1);
+    }
+    const int g = d[1], qt = d[2], t0 = d[5], rows = d[6];
+    const int rgp = blockIdx.x % row_groups;
     const int G = p.group;
     const int R = p.rows_per_tile;
     const int DV = p.head_size_v;
@@ -192,11 +212,6 @@ __device__ __forceinline__ void merge_task(const Params &p, const PieceMap &pm, 
     if (r0 >= rows)
         return;
     const int nr = rows - r0 < RPW ? rows - r0 : RPW;
-    const int first = piece_of(pm, us);
-    const int last = piece_of(pm, ue - 1);
-    int f0, f1;
-    piece_range(pm, first, f0, f1);
-    const int slot_first = 2 * first + (f0 >= us ? 0 : 1);
     auto part_of = [&](int k) -> const float * {
         k = k < last ? k : last;
         return p.ws.partials + (size_t)(k == first ? slot_first : 2 * k) * p.partial_stride;
@@ -255,19 +270,14 @@ __device__ __forceinline__ void merge_task(const Params &p, const PieceMap &pm, 
     }
 }
 
-template <int DT>
+template <int DT, bool TAIL>
 __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_groups)
 {
-    constexpr int KB = 8;
-    const PieceMap pm{sload(p.ws.hdr, 0), sload(p.ws.hdr, 1), sload(p.ws.hdr, 4),
-                      sload(p.ws.hdr, 5), sload(p.ws.hdr, 6), sload(p.ws.hdr, 7)};
+    merge_body<DT, TAIL>(p, row_groups);
+    // after every load of the header (a store ahead of them would keep them
+    // off the scalar cache)
     if (blockIdx.x == 0 && threadIdx.x == 0)
         p.ws.hdr[3] = 0;
-    if (pm.per <= 0)
-        return;
-    const int nent = piece_count(pm) - 1;   // boundaries between pieces
-    for (int task = blockIdx.x; task < nent * row_groups; task += gridDim.x)
-        merge_task<DT, KB>(p, pm, task / row_groups, task % row_groups);
 }
 
 }  // namespace
@@ -289,14 +299,12 @@ hipError_t launch_merge(const Params &p, int dtype, hipStream_t s)
     long long grid = (max_pieces - 1) * row_groups;
     if (grid <= 0 || p.no_split)
         return hipSuccess;
-    if (grid > kMergeMaxGrid)   // the workgroups stride over the tasks
-        grid = kMergeMaxGrid;
     if (grid > 0x7fffffff)
         return hipErrorInvalidValue;
-    if (dtype == 0)
-        hipLaunchKernelGGL(merge_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, row_groups);
-    else
-        hipLaunchKernelGGL(merge_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, row_groups);
+    const bool tail = p.self_plan && p.tail_min > 0;
+    void (*k)(Params, int) = dtype == 0 ? (tail ? merge_kernel<0, true> : merge_kernel<0, false>)
+                                        : (tail ? merge_kernel<1, true> : merge_kernel<1, false>);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, p, row_groups);
     return hipGetLastError();
 }
 

@@ -924,9 +924,10 @@ void tile_kernel(Params p)
 // drains.  Every stage record carries the chunks left in its piece, and the
 // last chunk of a worker's stream is flagged, so the two waves agree on the
 // number of barriers.
-template <int DT, int DK, int DV, int KT, int S, int MODE, bool SELF>
+template <int DT, int DK, int DV, int KT, int S, int MODE, bool SELF, bool TAIL>
 __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
 {
+    static_assert(SELF || !TAIL, "a claimed tail needs the kernel's own plan");
     constexpr bool BAND = MODE == MODE_BAND, TMASK = MODE == MODE_TENSOR;
     constexpr int SDW = slab_row_dwords<KT>();
     constexpr int SLB = TMASK ? slab_bytes<16, KT>() : 0;   // bytes of a mask slab stage
@@ -938,7 +939,7 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     constexpr int IPGV = RBV / 64;
     constexpr int LW = NTT * (IPGK + IPGV);       // loads per chunk (plus IPGK for a Q tile)
     constexpr int STK = KT * RBK, STV = KT * RBV, STQ = 16 * RBK;
-    constexpr int MW = 13;                        // ints per stage record
+    constexpr int MW = TAIL ? 13 : 12;            // ints per stage record
     constexpr int kClaimAhead = 4;                // chunks between a claim and its deadline
     static_assert(DK <= 256 && DV <= 256 && DK % 32 == 0 && DV % 64 == 0 && (KT == 16 || KT == 32), "shape");
     static_assert(S >= 2 && S <= 4 && LW * (S - 2) + IPGK < 64, "ring");
@@ -952,11 +953,13 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     // (at most 16 here) of each sequence
     __shared__ int s_skv[SELF ? kSelfPlanMaxBatch : 1], s_st0[SELF ? kSelfPlanMaxBatch : 1];
     __shared__ uint8_t s_sql[SELF ? kSelfPlanMaxBatch : 4];
-    // SELF: first item of each sequence; the piece claimed next
-    __shared__ int s_wsb[SELF ? kSelfPlanMaxBatch : 1];
-    __shared__ int s_claim;
+    // SELF: first item of each sequence; the piece claimed next (index, or
+    // -1: none; then its cursor and end item)
+    __shared__ int s_wsb[TAIL ? kSelfPlanMaxBatch : 1];
+    __shared__ int s_claim[TAIL ? 9 : 1];
 
-    __shared__ int s_n, s_nr, s_dyn;   // chunks of the first piece, claimed pieces per share, claimed tail
+    __shared__ int s_n, s_dyn;   // chunks of the first piece, claimed tail
+    __shared__ PieceMap s_pm;    // TAIL: the pass's piece map
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15;
     const int lg = lane >> 4;
@@ -1045,12 +1048,11 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     int ipiece = worker;
     Cursor ic{};
     int iend = 0;
-    PieceMap ipm{};   // SELF: the pass's piece map (issuing wave)
     if (ipiece >= p.partitions)
         return;
     if (wave == 0) {
     bool have = true;
-    int nr = 0, dyn = 0;
+    int dyn = 0;
     if constexpr (SELF) {
         // up to four consecutive sequences per lane: b = spl * lane + i,
         // summed in the lane first and then over the wave (one scan each for
@@ -1092,12 +1094,14 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
                 s_skv[b] = kvr[i];
                 s_st0[b] = t0r[i];
                 s_sql[b] = (uint8_t)qlr[i];
-                s_wsb[b] = wsbr[i];
+                if constexpr (TAIL)
+                    s_wsb[b] = wsbr[i];
             }
         }
         const int W = cw;
-        ipm = self_piece_map(p, W);
-        nr = ipm.nr;
+        const PieceMap ipm = self_piece_map(p, W);
+        if (TAIL && lane == 0)
+            s_pm = ipm;
         dyn = ipm.m > 0 ? 1 : 0;
         ipiece = static_piece(ipm, worker);
         if (worker == 0) {
@@ -1151,9 +1155,8 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     }
     if (lane == 0) {
         s_n = have ? iend - ic.item : 0;
-        s_nr = nr;
         s_dyn = dyn;
-        s_claim = -1;
+        s_claim[0] = -1;
     }
     }
     // both waves learn the piece's length (0: no work) from wave 0
@@ -1162,8 +1165,7 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     const int n = __builtin_amdgcn_readfirstlane(s_n);
     if (n <= 0)
         return;
-    const bool cdyn = SELF && __builtin_amdgcn_readfirstlane(s_dyn) != 0;
-    const int c_nr = __builtin_amdgcn_readfirstlane(s_nr);
+    const bool cdyn = TAIL && __builtin_amdgcn_readfirstlane(s_dyn) != 0;
     // the first chunk of the next unit (skipping sequences without rows);
     // the caller has already advanced ic.item past the current unit
     auto next_unit = [&]() __attribute__((always_inline)) {
@@ -1213,13 +1215,33 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             ibid[q] = sload(ibt, blk < inblk ? blk : inblk - 1);
         }
     };
-    // SELF: the sequence holding item s (the last one whose first item is
-    // <= s; lane 0 always qualifies) and the cursor at the start of piece k
+    // SELF: the cursor at the start of piece k and its end, as the computing
+    // wave resolved them (see resolve_piece)
     auto goto_piece = [&](int k) __attribute__((always_inline)) {
-        if constexpr (SELF) {
+        if constexpr (TAIL) {
+            ic.b = lds_int(s_claim, 1);
+            ic.g = lds_int(s_claim, 2);
+            ic.qt = lds_int(s_claim, 3);
+            ic.c = lds_int(s_claim, 4);
+            ic.nch = lds_int(s_claim, 5);
+            ic.ntile = lds_int(s_claim, 6);
+            ic.item = lds_int(s_claim, 7);
+            iend = lds_int(s_claim, 8);
+            ipiece = k;
+        }
+    };
+    // SELF (computing wave): the claimed piece k, resolved for the issuing
+    // wave -- the sequence holding its first item (the last one whose first
+    // item is <= it; lane 0 always qualifies), the cursor there, and the
+    // piece's split entry (entry k - 1) -- so that the issuing wave's loop
+    // carries none of this arithmetic
+    auto resolve_piece = [&](int k) __attribute__((always_inline)) {
+        if constexpr (TAIL) {
+            const PieceMap pm{lds_int(&s_pm.W, 0), lds_int(&s_pm.per, 0), lds_int(&s_pm.a, 0),
+                              lds_int(&s_pm.m, 0), lds_int(&s_pm.P, 0), lds_int(&s_pm.nr, 0)};
             int s0, s1, sp0, sp1;
-            piece_range(ipm, k, s0, s1);
-            piece_range(ipm, k - 1, sp0, sp1);
+            piece_range(pm, k, s0, s1);
+            piece_range(pm, k - 1, sp0, sp1);
             const int spl = (p.batch + 63) >> 6;
             int nle = 0;
 #pragma unroll
@@ -1231,10 +1253,18 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             const int l0 = 63 - __builtin_clzll(m);
             const int b0 = spl * l0 + __builtin_amdgcn_readlane(nle, l0) - 1;
             const int kv0 = lds_int(s_skv, b0), ql0 = seq_ql(b0);
-            ic = piece_start(p, k, s0, sp0, b0, kv0, ql0, seq_items_per_group(p, kv0, ql0), lds_int(s_wsb, b0),
-                             lds_int(s_st0, b0), lane == 0);
-            iend = s1;
-            ipiece = k;
+            const Cursor cu = piece_start(p, k, s0, sp0, b0, kv0, ql0, seq_items_per_group(p, kv0, ql0),
+                                          lds_int(s_wsb, b0), lds_int(s_st0, b0), lane == 0);
+            if (lane == 0) {
+                s_claim[1] = cu.b;
+                s_claim[2] = cu.g;
+                s_claim[3] = cu.qt;
+                s_claim[4] = cu.c;
+                s_claim[5] = cu.nch;
+                s_claim[6] = cu.ntile;
+                s_claim[7] = cu.item;
+                s_claim[8] = s1;
+            }
         }
     };
     int n_issued = 0;
@@ -1298,9 +1328,9 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
         // to follow it is in LDS by now (-1: none, the stream ends here)
         const bool piece_end = ic.item + 1 == iend;
         int nxt = -1;
-        if constexpr (SELF) {
+        if constexpr (TAIL) {
             if (piece_end && cdyn)
-                nxt = __builtin_amdgcn_readfirstlane(*(volatile int *)&s_claim);
+                nxt = __builtin_amdgcn_readfirstlane(*(volatile int *)&s_claim[0]);
         }
         if (lane == 0) {
             int *md = s_meta + st * MW;
@@ -1316,7 +1346,8 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             md[9] = it0;
             md[10] = irows;
             md[11] = ilo;
-            md[12] = iend - ic.item - 1;   // chunks of the piece after this one
+            if constexpr (TAIL)   // chunks of the piece after this one (no claims: many)
+                md[12] = cdyn ? iend - ic.item - 1 : 0x7fffffff;
         }
         ++n_issued;
         // advance the issue position by one chunk
@@ -1328,7 +1359,7 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             if (more) {
                 next_unit();
                 more = ic.b < p.batch;
-            } else if (nxt >= 0) {
+            } else if (TAIL && nxt >= 0) {
                 goto_piece(nxt);
                 ifirst = 1;
                 more = true;
@@ -1337,7 +1368,7 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             if (!idone)
                 iseg();
         }
-        if (idone && lane == 0)   // the last chunk of the stream: the computing wave stops after it
+        if (TAIL && idone && lane == 0)   // the last chunk of the stream: the computing wave stops after it
             s_meta[st * MW + 4] |= 16;
         if (!idone)
             ifetch();
@@ -1347,7 +1378,7 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     u32x4 qb[KS];
     f32x4 oacc[ND];
     float m_run = -INFINITY, lsum = 0.f;
-    int lim = 0, min_lim = 0, nvis = 0, rows = 0, t0 = 0, kv = 0, ql = 0;
+    int lim = 0, min_lim = 0, nvis = 0, seg_prefix = 0;
     int lo_r = 0, max_lo = 0, lo_tile = 0;
 
     if (wave == 0) {
@@ -1358,8 +1389,8 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
 #pragma unroll
         for (int k = 0; k < S - 1; ++k)
             issue(k);
-        for (int k = 0; k < n_issued; ++k) {
-            wait_ahead<LW, S - 2>(n_issued - 1 - k);   // chunk k (and any earlier Q tile) is in LDS
+        for (int k = 0; k < (TAIL ? n_issued : n); ++k) {
+            wait_ahead<LW, S - 2>((TAIL ? n_issued : n) - 1 - k);   // chunk k (and any earlier Q tile) is in LDS
             wait_lgkm0();                       // and its stage record
             __builtin_amdgcn_s_barrier();       // wave 1 has finished chunk k - 1 ...
             issue((k + S - 1) % S);             // ... whose stage this load fills
@@ -1369,24 +1400,25 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
         return;
     }
 
-    // claim state: the piece whose successor is being claimed, and 0 (not
-    // yet), 1 (atomic sent), 2 (answer in LDS)
-    int cpiece = -1, cstate = 0, cval = 0;
-    for (int k = 0;; ++k) {
+    // claim state for the successor of the current piece: 0 (not yet), 1
+    // (atomic sent), 2 (answer in LDS)
+    int cstate = 0, cval = 0;
+    for (int k = 0; TAIL || k < n; ++k) {
         const int st = k % S;
         wait_lgkm0();                  // this wave's reads of chunk k - 1 are done
         __builtin_amdgcn_s_barrier();  // chunk k has landed
+        // the record: what every chunk needs (the segment's lengths are
+        // read at its first chunk only)
         int md[MW];
 #pragma unroll
-        for (int i = 0; i < MW; ++i)
+        for (int i = 0; i < 6; ++i)
             md[i] = __builtin_amdgcn_readfirstlane(s_meta[st * MW + i]);
-        const int b = md[0], g = md[1], qt = md[2], c = md[3], fl = md[4];
-        if (cdyn) {
-            if (md[5] != cpiece) {
-                cpiece = md[5];
+        const int g = md[1], qt = md[2], c = md[3], fl = md[4];
+        if constexpr (TAIL) {
+            md[12] = __builtin_amdgcn_readfirstlane(s_meta[st * MW + 12]);
+            if ((fl & 9) == 9)   // the first chunk of a piece
                 cstate = 0;
-            }
-            if (cstate == 0 && md[12] <= S + kClaimAhead) {
+            if (cstate == 0 && md[12] <= S + kClaimAhead) {   // (never without claims)
                 if (lane == 0)
                     cval = __hip_atomic_fetch_add(p.ws.hdr + 3, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
                 cstate = 1;
@@ -1396,11 +1428,11 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
         const lds_u8 *vb = (const lds_u8 *)sV + st * STV;
         if (fl & 1) {
             // first chunk of a segment: its Q tile and row limits
+#pragma unroll
+            for (int i = 6; i < 12; ++i)
+                md[i] = __builtin_amdgcn_readfirstlane(s_meta[st * MW + i]);
             nvis = md[6];
-            kv = md[7];
-            ql = md[8];
-            t0 = md[9];
-            rows = md[10];
+            const int kv = md[7], ql = md[8], rows = md[10];
             const lds_u8 *qs = (const lds_u8 *)sQ + st * STQ;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -1410,6 +1442,7 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             }
             lo_tile = md[11];
             const int prefix = seq_prefix(kv, ql);
+            seg_prefix = prefix;
             const int rg = qt * 16 + lr;
             lim = row_hi_t<BAND>(p, kv, prefix, rg / G);
             lo_r = row_lo_t<BAND>(p, prefix, rg / G);
@@ -1439,7 +1472,7 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
         if constexpr (TMASK) {
             // scaled log2-domain scores plus the matrix; the causal rule
             // outside it
-            const int c0m = jb - seq_prefix(kv, ql);
+            const int c0m = jb - seg_prefix;
 #pragma unroll
             for (int n = 0; n < NTT; ++n)
                 sacc[n] *= scq;
@@ -1555,18 +1588,24 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             }
         }
 
-        if (cdyn && cstate == 1 && md[12] <= S) {
+        if (TAIL && cstate == 1 && md[12] <= S) {
             // the deadline: the issuing wave reads the answer after the next
             // barrier, when it issues the piece's last chunk
-            const int nx = claimed_piece(PieceMap{0, 0, 0, 1, p.partitions, c_nr}, __builtin_amdgcn_readlane(cval, 0));
+            const int nx = claimed_piece(PieceMap{0, 0, 0, 1, p.partitions, lds_int(&s_pm.nr, 0)},
+                                         __builtin_amdgcn_readlane(cval, 0));
+            if (nx >= 0)
+                resolve_piece(nx);
             if (lane == 0)
-                s_claim = nx;
+                s_claim[0] = nx;
             cstate = 2;
         }
         if (fl & 2) {
-            // last chunk of the segment: output or partial
+            // last chunk of the segment: output or partial (its first
+            // query row and row count are in this chunk's record too)
             const bool whole = fl & 4;
             const int piece = md[5];
+            const int t0 = __builtin_amdgcn_readfirstlane(s_meta[st * MW + 9]);
+            const int rows = __builtin_amdgcn_readfirstlane(s_meta[st * MW + 10]);
             float *part = p.ws.partials + (size_t)(2 * piece + ((fl & 8) ? 0 : 1)) * p.partial_stride;
             const float L = xor_sum<32>(xor_sum<16>(lsum));
             const float Ms = m_run * sc;   // log2 domain
@@ -1601,7 +1640,7 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
                 }
             }
         }
-        if (fl & 16)   // the last chunk of the stream
+        if (TAIL && (fl & 16))   // the last chunk of the stream
             break;
     }
     if (err)
@@ -1648,11 +1687,15 @@ const void *kernel_for(int variant, bool shared, TileShape *t)
         } else {
             if (variant == 0) {   // one wave per workgroup, streaming across units
                 *t = TileShape{1, 16, 1, 1, 4, 128};
-                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, false>;
+                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, false, false>;
             }
             if (variant == 3) {   // the same, planning for itself
                 *t = TileShape{1, 16, 1, 1, 4, 128};
-                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, true>;
+                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, true, false>;
+            }
+            if (variant == 4) {   // the same, with a claimed tail of pieces
+                *t = TileShape{1, 16, 1, 1, 4, 128};
+                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, true, true>;
             }
             if constexpr (MODE == MODE_TENSOR) {
                 if (variant == 1)
