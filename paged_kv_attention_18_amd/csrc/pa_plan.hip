@@ -167,15 +167,15 @@ __host__ __device__ inline int merge_rows_per_wg(int dv)
 // reset it: its workers claim pieces from the moment they start).
 // Each thread owns four consecutive outputs of one row and combines the
 // parts online (running max, rescaled sum and accumulator), reading a part's
-// m, l and its four accumulator values together: the loads of KB = 4
-// parts are issued before any is used, so each batch of parts costs one
+// m, l and its four accumulator values together: the loads of KB parts
+// (4, or 8 with a claimed tail) are issued before any is used, so each batch of parts costs one
 // memory round trip and the row statistics need no pass of their own.
 // TAIL: the pass may have a claimed tail (PieceMap); else its pieces are
 // all alike and every entry of the grid belongs to the pass.
 template <int DT, bool TAIL>
 __device__ __forceinline__ void merge_body(const Params &p, int row_groups)
 {
-    constexpr int KB = 4;
+    constexpr int KB = TAIL ? 8 : 4;   // a claimed tail cuts units into more parts
     const int entry = blockIdx.x / row_groups;
     const int32_t *d = p.ws.splits + (size_t)entry * 8;
     int first, last, slot_first;
