@@ -612,6 +612,34 @@ def test_claimed_tail_parity(case):
     check_full(p, num_partitions=P, flags=F.PA_FLAG_STATIC_PIECES, what=f"static pieces {case}")
 
 
+# The claimed tail in the other modes of the streaming kernel (each mode is
+# its own kernel instance): causal rows of a few query tokens, the band
+# mask, the shared mask matrix, and one cache for K and V.
+TAIL_MODE_CASES = [
+    # (name, batch, length range, q range, H, Hkv, Dk, Dv, bs, dtype, mask, window, shared, workers)
+    ("causal", 40, (300, 4000), (1, 4), 32, 8, 128, 128, 128, "f16", "causal", (0, 0), False, 16),
+    ("band", 96, (500, 6000), None, 16, 8, 64, 64, 16, "bf16", "band", (127, 0), False, 8),
+    ("tensor", 32, (300, 3000), (1, 2), 16, 4, 128, 128, 64, "f16", "tensor", (0, 0), False, 8),
+    ("shared", 48, (200, 3000), None, 32, 8, 128, 128, 128, "bf16", "none", (0, 0), True, 16),
+]
+
+
+@pytest.mark.parametrize("case", TAIL_MODE_CASES, ids=lambda c: c[0])
+def test_claimed_tail_mask_modes(case):
+    name, B, (lo, hi), qr, H, Hkv, Dk, Dv, bs, dt, mask, win, shared, P = case
+    log(f"claimed tail, {name}")
+    rng = np.random.default_rng(B * 7 + P)
+    lens = rng.integers(lo, hi, size=B).tolist()
+    ql = None if qr is None else rng.integers(qr[0], qr[1] + 1, size=B).tolist()
+    p = synth.custom(lens, H, Hkv, Dk, Dv, bs, dt, mask, q_seq_lens=ql, seed=70 + B, shared_kv=shared,
+                     window=win)
+    if mask == "tensor":
+        p.mask_tensor = synth.random_mask_tensor(71)
+    assert binding.for_problem(to_device(p), num_partitions=P).describe()["path"] == "stream"
+    check_full(p, num_partitions=P, what=f"tail {name}")
+    check_full(p, num_partitions=P, flags=F.PA_FLAG_STATIC_PIECES, what=f"static pieces {name}")
+
+
 def test_claimed_tail_repeatable_and_reset_between_calls():
     """Back-to-back calls on one handle (the piece counter is reset after
     every pass): the same lengths give bit-identical results, a different
