@@ -527,19 +527,28 @@ void tile_kernel(Params p)
                 const size_t trow = (size_t)bid[q] * bs + mod_bs(j0, bs, bsh);
                 const char *kbase = (vis && inb) ? kgh + trow * rsk : zg;
                 const char *vbase = (vis && inb) ? vgh + trow * rsv : zg;
+                // (the empty asm hides each 32-bit offset from loop-invariant
+                // hoisting: otherwise the 64-bit forms of all of a chunk's
+                // offsets stay live across the chunk loop, and where the
+                // registers run out one is spilled and reloaded behind the
+                // next chunk's first load, which then waits for that load)
 #pragma unroll
                 for (int m = 0; m < MK; ++m) {
                     const int i = wave + NW * m;
                     lds_u8 *dst = (!PAD || i < IPGK) ? kb + (q * IPGK + i) * 1024 : (lds_u8 *)sJunk;
                     const char *src = (!PAD || i < IPGK) ? kbase : zg;
-                    lds_load16(src + voK[m], dst);
+                    uint32_t off = voK[m];
+                    asm volatile("" : "+v"(off));
+                    lds_load16(src + off, dst);
                 }
 #pragma unroll
                 for (int m = 0; m < MV; ++m) {
                     const int i = wave + NW * m;
                     lds_u8 *dst = (!PAD || i < IPGV) ? vb + (q * IPGV + i) * 1024 : (lds_u8 *)sJunk;
                     const char *src = (!PAD || i < IPGV) ? vbase : zg;
-                    lds_load16(src + voV[m], dst);
+                    uint32_t off = voV[m];
+                    asm volatile("" : "+v"(off));
+                    lds_load16(src + off, dst);
                 }
             }
         };
