@@ -18,9 +18,12 @@ constexpr int kMaxTimedPasses = 1024;
 // Pieces of the item range per worker in balanced mode.  With more pieces
 // than workers, workers that finish early take the remaining pieces, which
 // evens out end times; it pays where a chunk is long (many rows on the
-// matrix cores).  The decode kernels keep one piece per worker: taking a
-// piece means waiting for an atomic's return, and that wait drains their
-// load pipelines (one in-order vector memory counter per wave).
+// matrix cores).  The decode streaming kernel keeps one static piece per
+// worker (the plan kernel's pieces), or, planning for itself on a long
+// pass, adds the claimed tail of pa::PieceMap (variant 4): there the
+// computing wave claims, since waiting for an atomic's return on the
+// issuing wave would drain its load pipeline (one in-order vector memory
+// counter per wave).
 constexpr int kMaxPiecesPerWorker = 2;
 
 struct Variant {
