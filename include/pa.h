@@ -49,11 +49,16 @@
  * token gets out = 0 and lse = -inf.
  *
  * Ownership: every tensor argument of pa_forward is a device pointer owned by
- * the caller.  The handle owns its workspace (work plan, split partials, an
- * error word), allocated once by pa_create and freed by pa_destroy.
- * pa_forward allocates nothing, does not synchronise, and enqueues all of its
- * work on the given stream, so it may be captured in a HIP graph.  One handle
- * must not be used by two streams at once (the workspace is shared).
+ * the caller.  The handle owns its workspace (work plan, split partials, a
+ * piece counter, an error word), allocated once by pa_create and freed by
+ * pa_destroy; it is sized for the largest pass the configuration allows,
+ * including, for decode shapes whose passes may be long, the pieces the
+ * streaming kernel claims at run time (up to 9 per worker; none with
+ * PA_FLAG_STATIC_PIECES).  pa_forward allocates nothing, does not
+ * synchronise, and enqueues all of its work on the given stream, so it may be
+ * captured in a HIP graph; every pass leaves the piece counter reset for the
+ * next one.  One handle must not be used by two streams at once (the
+ * workspace is shared).
  *
  * Errors: functions return a pa_status synchronously.  Argument and shape
  * errors are reported before any device work is queued.  Problems that can
