@@ -290,8 +290,11 @@ hipError_t launch_plan(const Params &p, hipStream_t s)
 
 hipError_t launch_merge(const Params &p, int dtype, hipStream_t s)
 {
-    const int row_groups = (p.rows_per_tile + merge_rows_per_wg(p.head_size_v) - 1) /
-                           merge_rows_per_wg(p.head_size_v);
+    // row groups of the largest unit this pass can have (a decode unit has
+    // only its query heads' rows, fewer than the tile's)
+    const long long max_rows = (long long)p.max_q * p.group;
+    const int rows = max_rows < p.rows_per_tile ? (int)max_rows : p.rows_per_tile;
+    const int row_groups = (rows + merge_rows_per_wg(p.head_size_v) - 1) / merge_rows_per_wg(p.head_size_v);
     // the self-planning kernel's claimed tail makes up to kTailRounds rounds
     // of pieces more; workgroups past the pass's split entries return at once
     const long long max_pieces = (p.self_plan && p.tail_min > 0) ? (long long)(1 + kTailRounds) * p.partitions
