@@ -412,6 +412,10 @@ static pa_status forward_impl(pa_handle *h, const void *query, const void *key_c
     p.scale_log2 = c.scale * 1.4426950408889634f;
     p.rows_per_tile = v.rows_per_tile;
     p.chunk = v.chunk;
+    auto log2_or_none = [](int x) { return (x > 0 && (x & (x - 1)) == 0) ? __builtin_ctz((unsigned)x) : -1; };
+    p.chunk_shift = log2_or_none(v.chunk);
+    p.group_shift = log2_or_none(G);
+    p.tile_shift = log2_or_none(v.rows_per_tile);
     p.max_tiles = (max_q_seq_len * G + v.rows_per_tile - 1) / v.rows_per_tile;
     p.no_split = (c.flags & PA_FLAG_NO_SPLIT) ? 1 : 0;
     p.partitions = p.no_split ? batch * c.kv_head_num * p.max_tiles

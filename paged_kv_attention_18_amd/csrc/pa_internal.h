@@ -72,6 +72,8 @@ struct Params {
     float scale_log2;                  // scale * log2(e)
     int32_t rows_per_tile;             // R
     int32_t chunk;                     // CT
+    // log2 of CT, of the group and of R where they are powers of 2, else -1
+    int32_t chunk_shift, group_shift, tile_shift;
     int32_t partitions;                // P: workers in the grid (no-split mode: units)
     int32_t pieces;                    // N: pieces of the item range (balanced mode)
     int32_t no_split;
@@ -198,9 +200,21 @@ __device__ __forceinline__ int seq_prefix(int kv, int qlen)
 
 // Tokens up to which some row of rows [.., r1] of (b, g) looks (exclusive):
 // the limit of row r1, the largest.
+// Quotients the planner takes many times per piece, as shifts where the
+// divisor is a power of 2 (x >= 0 there; the divisions otherwise).
+__device__ __forceinline__ int div_group(const Params &p, int x)
+{
+    return (p.group_shift >= 0 && x >= 0) ? x >> p.group_shift : x / p.group;
+}
+
+__device__ __forceinline__ int div_chunk(const Params &p, int x)
+{
+    return (p.chunk_shift >= 0 && x >= 0) ? x >> p.chunk_shift : x / p.chunk;
+}
+
 __device__ __forceinline__ int tile_nvis(const Params &p, int kv, int qlen, int r1)
 {
-    return row_hi(p, kv, seq_prefix(kv, qlen), r1 / p.group);
+    return row_hi(p, kv, seq_prefix(kv, qlen), div_group(p, r1));
 }
 
 // The row tile qt of (b, g) covers chunks [first, first + count) of its
@@ -208,18 +222,18 @@ __device__ __forceinline__ int tile_nvis(const Params &p, int kv, int qlen, int 
 // row (0 unless banded) to the one holding the last token its last row sees.
 __device__ __forceinline__ int unit_first_chunk(const Params &p, int kv, int qlen, int qt)
 {
-    return row_lo(p, seq_prefix(kv, qlen), (qt * p.rows_per_tile) / p.group) / p.chunk;
+    return div_chunk(p, row_lo(p, seq_prefix(kv, qlen), div_group(p, qt * p.rows_per_tile)));
 }
 
 __device__ __forceinline__ int unit_chunks(const Params &p, int kv, int qlen, int qt)
 {
     if (p.sparse)   // the entries of the query token's list
-        return (p.topk + p.chunk - 1) / p.chunk;
+        return div_chunk(p, p.topk + p.chunk - 1);
     const int rows = qlen * p.group;
     int r1 = (qt + 1) * p.rows_per_tile;
     r1 = (r1 < rows ? r1 : rows) - 1;
     const int n = tile_nvis(p, kv, qlen, r1);
-    const int c = (n + p.chunk - 1) / p.chunk - unit_first_chunk(p, kv, qlen, qt);
+    const int c = div_chunk(p, n + p.chunk - 1) - unit_first_chunk(p, kv, qlen, qt);
     return c > 1 ? c : 1;
 }
 
@@ -438,7 +452,8 @@ struct Cursor {
 
 __device__ __forceinline__ int seq_tiles(const Params &p, int qlen)
 {
-    return (qlen * p.group + p.rows_per_tile - 1) / p.rows_per_tile;
+    const int x = qlen * p.group + p.rows_per_tile - 1;
+    return (p.tile_shift >= 0 && x >= 0) ? x >> p.tile_shift : x / p.rows_per_tile;
 }
 
 // Position the cursor at item `item`, which lies in sequence b.
