@@ -4,11 +4,13 @@
 // SparseAttnSharedkvMetadata README describes (function section: a list of
 // start/end points -- batch, head, Q block, K block -- for every core,
 // consumed by the attention operator, and reduction tasks for split rows).
-// Here it runs on the GPU in one workgroup and reads only the lengths: it
-// sanitises them, numbers the (sequence, KV head, row tile, KV chunk) items,
-// cuts them into N equal pieces, lists the units that a piece boundary cuts
-// (the reduction tasks) and resets the counter the attention kernels use to
-// hand out pieces.  The pieces depend on the lengths alone, so the partial
+// Here it runs on the GPU and reads only the lengths: it sanitises them,
+// numbers the (sequence, KV head, row tile, KV chunk) items, cuts them into
+// N equal pieces, lists the units that a piece boundary cuts (the reduction
+// tasks) and resets the counter the attention kernels use to hand out
+// pieces.  Every workgroup numbers the items (a scan over the batch); each
+// then places kPlanPieces of the pieces, and workgroup 0 alone writes the
+// per-sequence arrays, the header and the error bits.  The pieces depend on the lengths alone, so the partial
 // sums that make up an output row, and the order they are merged in, do not
 // depend on which workgroup ran which piece.
 //
@@ -26,6 +28,9 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanLdsB = 2048;   // sequences kept in LDS for the piece phase
+// pieces per workgroup: placing a piece walks its sequence's row tiles on
+// one thread, so one wave of pieces per workgroup keeps each CU's walk short
+constexpr int kPlanPieces = 64;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
 {
@@ -37,6 +42,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
     __shared__ uint32_t s_err;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
+    const bool lead = blockIdx.x == 0;
     if (tid == 0) {
         s_carry_q = 0;
         s_carry_w = 0;
@@ -54,9 +60,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
             err = sanitize_seq(p, cap, kv, ql);
             ipg = seq_items_per_group(p, kv, ql);
             items = ipg * p.kv_head_num;
-            p.ws.qlen[b] = ql;
-            p.ws.kvlen[b] = kv;
-            p.ws.ipg[b] = ipg;
+            if (lead) {
+                p.ws.qlen[b] = ql;
+                p.ws.kvlen[b] = kv;
+                p.ws.ipg[b] = ipg;
+            }
         }
         if (err)
             atomicOr(&s_err, err);
@@ -83,8 +91,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         const int t0 = s_wq[wv] + iq - ql;
         const int wsb = s_ww[wv] + iw - items;
         if (b < p.batch) {
-            p.ws.cu_q[b] = t0;
-            p.ws.wsb[b] = wsb;
+            if (lead) {
+                p.ws.cu_q[b] = t0;
+                p.ws.wsb[b] = wsb;
+            }
             if (b < kPlanLdsB) {
                 s_wsb[b] = wsb;
                 s_kv[b] = kv;
@@ -97,7 +107,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
     }
     const int W = s_carry_w;
     const int per = p.no_split ? 0 : (W + p.pieces - 1) / p.pieces;
-    if (tid == 0) {
+    if (lead && tid == 0) {
         p.ws.cu_q[p.batch] = s_carry_q;
         p.ws.wsb[p.batch] = W;
         p.ws.hdr[0] = W;
@@ -117,12 +127,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         if (tid == 0 && lds)
             s_wsb[p.batch] = W;
         __syncthreads();
+        // Past kPlanLdsB sequences the piece phase reads the per-sequence
+        // arrays back from memory, where only workgroup 0's writes are
+        // ready for it: then workgroup 0 places every piece.
+        const bool spread = lds && gridDim.x > 1;
+        if (!spread && !lead)
+            return;
+        const int k0 = spread ? blockIdx.x * kPlanPieces : 0;
+        const int k1 = spread ? min(k0 + kPlanPieces, p.pieces) : p.pieces;
         auto wsb_of = [&](int b) { return lds ? s_wsb[b] : p.ws.wsb[b]; };
         // Piece k starts at item k * pe, in the last sequence b with
         // wsb[b] <= k * pe.  Its split entry (entry k - 1) records the unit
         // that boundary k cuts, if it falls strictly inside one.
         const int nk = (W + pe - 1) / pe < p.pieces ? (W + pe - 1) / pe : p.pieces;
-        for (int k = tid; k < nk; k += kPlanThreads) {
+        for (int k = k0 + tid; k < k1 && k < nk; k += kPlanThreads) {
             const int s = k * pe;
             int lo = 0, hi = p.batch - 1;
             while (lo < hi) {
@@ -143,11 +161,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
             (void)piece_start(p, k, s, s - pe, b, kv, ql, ipg, wsb_of(b), t0, true);
         }
         // boundaries past the last item
-        for (int k = (W + pe - 1) / pe + tid; k < p.pieces; k += kPlanThreads)
+        for (int k = max((W + pe - 1) / pe, k0) + tid; k < k1; k += kPlanThreads)
             if (k > 0)
                 p.ws.splits[(size_t)(k - 1) * 8] = -1;
     }
-    if (tid == 0 && s_err)
+    if (lead && tid == 0 && s_err)
         set_error(p.ws.err, s_err);
 }
 
@@ -284,7 +302,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_group
 
 hipError_t launch_plan(const Params &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p);
+    // one workgroup when the piece phase cannot keep the sequences in LDS
+    const int wgs = (p.no_split || p.batch > kPlanLdsB) ? 1 : (p.pieces + kPlanPieces - 1) / kPlanPieces;
+    hipLaunchKernelGGL(plan_kernel, dim3(wgs > 0 ? wgs : 1), dim3(kPlanThreads), 0, s, p);
     return hipGetLastError();
 }
 
