@@ -602,19 +602,37 @@ __device__ __forceinline__ int seq_items_per_group(const Params &p, int kv, int 
 // Returns the cursor at s and, when `write` and k > 0, writes split entry
 // k - 1: the unit that boundary k cuts, if s falls strictly inside it and
 // the unit began in piece k - 1 (a unit cut several times is listed once).
+// With `tp` (the sequence's items per KV head before each of its row tiles,
+// tp[0] = 0) the row tile is found by bisection, else by walking the tiles.
 __device__ __forceinline__ Cursor piece_start(const Params &p, int k, int s, int s_prev, int b, int kv, int ql,
-                                              int ipg, int wsb, int t0, bool write)
+                                              int ipg, int wsb, int t0, bool write, const int *tp = nullptr)
 {
     int local = s - wsb;
     const int gg = local / ipg;
     local -= gg * ipg;
     int u0 = wsb + gg * ipg;
-    int t = 0, n = unit_chunks(p, kv, ql, 0);
-    while (local >= n) {
-        local -= n;
-        u0 += n;
-        ++t;
+    int t = 0, n;
+    if (tp) {
+        // every tile has at least one chunk: tp rises strictly
+        int hi = seq_tiles(p, ql) - 1;
+        while (t < hi) {
+            const int mid = (t + hi + 1) >> 1;
+            if (tp[mid] <= local)
+                t = mid;
+            else
+                hi = mid - 1;
+        }
+        local -= tp[t];
+        u0 += tp[t];
         n = unit_chunks(p, kv, ql, t);
+    } else {
+        n = unit_chunks(p, kv, ql, 0);
+        while (local >= n) {
+            local -= n;
+            u0 += n;
+            ++t;
+            n = unit_chunks(p, kv, ql, t);
+        }
     }
     if (write && k > 0) {
         int32_t *d = p.ws.splits + (size_t)(k - 1) * 8;

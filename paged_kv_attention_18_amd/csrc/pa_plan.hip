@@ -31,20 +31,27 @@ constexpr int kPlanLdsB = 2048;   // sequences kept in LDS for the piece phase
 // pieces per workgroup: placing a piece walks its sequence's row tiles on
 // one thread, so one wave of pieces per workgroup keeps each CU's walk short
 constexpr int kPlanPieces = 64;
+// row tiles whose leading item counts are kept in LDS, so that placing a
+// piece bisects its sequence's tiles instead of walking them
+constexpr int kPlanLdsT = 8192;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
 {
     constexpr int NWV = kPlanThreads / 64;
-    __shared__ int s_wq[NWV], s_ww[NWV];
+    __shared__ int s_wq[NWV], s_wt[NWV], s_ww[NWV];
     // per-sequence data for the piece phase (global arrays past kPlanLdsB)
     __shared__ int s_wsb[kPlanLdsB + 1], s_kv[kPlanLdsB], s_ql[kPlanLdsB], s_ipg[kPlanLdsB], s_t0[kPlanLdsB];
-    __shared__ int s_carry_q, s_carry_w;
+    // each sequence's first row tile in s_tp, and per row tile the items per
+    // KV head of its sequence before it
+    __shared__ int s_toff[kPlanLdsB], s_tp[kPlanLdsT];
+    __shared__ int s_carry_q, s_carry_t, s_carry_w;
     __shared__ uint32_t s_err;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const bool lead = blockIdx.x == 0;
     if (tid == 0) {
         s_carry_q = 0;
+        s_carry_t = 0;
         s_carry_w = 0;
         s_err = 0;
     }
@@ -52,43 +59,65 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
     const int cap = seq_cap(p);
     for (int base = 0; base < p.batch; base += kPlanThreads) {
         const int b = base + tid;
-        int ql = 0, kv = 0, ipg = 0, items = 0;
+        int ql = 0, kv = 0, nt = 0;
         uint32_t err = 0;
         if (b < p.batch) {
             kv = p.context_lens[b];
             ql = p.q_seq_lens ? p.q_seq_lens[b] : 1;
             err = sanitize_seq(p, cap, kv, ql);
-            ipg = seq_items_per_group(p, kv, ql);
-            items = ipg * p.kv_head_num;
-            if (lead) {
-                p.ws.qlen[b] = ql;
-                p.ws.kvlen[b] = kv;
-                p.ws.ipg[b] = ipg;
-            }
+            nt = seq_tiles(p, ql);
         }
         if (err)
             atomicOr(&s_err, err);
-        // exclusive prefix sums of ql and items: wave scans, then the wave totals
-        const int iq = wave_scan(ql, lane), iw = wave_scan(items, lane);
+        // exclusive prefix sums (wave scans, then the wave totals) of the
+        // query tokens and row tiles, then of the items
+        const int iq = wave_scan(ql, lane), it = wave_scan(nt, lane);
         if (lane == 63) {
             s_wq[wv] = iq;
-            s_ww[wv] = iw;
+            s_wt[wv] = it;
         }
         __syncthreads();
         if (tid == 0) {
-            int aq = s_carry_q, aw = s_carry_w;
+            int aq = s_carry_q, at = s_carry_t;
             for (int w = 0; w < NWV; ++w) {
-                const int tq = s_wq[w], tw = s_ww[w];
+                const int tq = s_wq[w], tt = s_wt[w];
                 s_wq[w] = aq;
-                s_ww[w] = aw;
+                s_wt[w] = at;
                 aq += tq;
-                aw += tw;
+                at += tt;
             }
             s_carry_q = aq;
-            s_carry_w = aw;
+            s_carry_t = at;
         }
         __syncthreads();
         const int t0 = s_wq[wv] + iq - ql;
+        const int toff = s_wt[wv] + it - nt;
+        int ipg = 0;
+        for (int qt = 0; qt < nt; ++qt) {
+            if (toff + qt < kPlanLdsT)
+                s_tp[toff + qt] = ipg;
+            ipg += unit_chunks(p, kv, ql, qt);
+        }
+        const int items = ipg * p.kv_head_num;
+        if (lead && b < p.batch) {
+            p.ws.qlen[b] = ql;
+            p.ws.kvlen[b] = kv;
+            p.ws.ipg[b] = ipg;
+        }
+        const int iw = wave_scan(items, lane);
+        if (lane == 63)
+            s_ww[wv] = iw;
+        __syncthreads();
+        if (tid == 0) {
+            int aw = s_carry_w;
+            for (int w = 0; w < NWV; ++w) {
+                const int tw = s_ww[w];
+                s_ww[w] = aw;
+                aw += tw;
+            }
+            s_carry_w = aw;
+        }
+        __syncthreads();
         const int wsb = s_ww[wv] + iw - items;
         if (b < p.batch) {
             if (lead) {
@@ -101,6 +130,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
                 s_ql[b] = ql;
                 s_ipg[b] = ipg;
                 s_t0[b] = t0;
+                s_toff[b] = toff;
             }
         }
         __syncthreads();
@@ -136,6 +166,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         const int k0 = spread ? blockIdx.x * kPlanPieces : 0;
         const int k1 = spread ? min(k0 + kPlanPieces, p.pieces) : p.pieces;
         auto wsb_of = [&](int b) { return lds ? s_wsb[b] : p.ws.wsb[b]; };
+        const bool table = lds && s_carry_t <= kPlanLdsT;
         // Piece k starts at item k * pe, in the last sequence b with
         // wsb[b] <= k * pe.  Its split entry (entry k - 1) records the unit
         // that boundary k cuts, if it falls strictly inside one.
@@ -158,7 +189,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
             const int ql = lds ? s_ql[b] : p.ws.qlen[b];
             const int ipg = lds ? s_ipg[b] : p.ws.ipg[b];
             const int t0 = lds ? s_t0[b] : p.ws.cu_q[b];
-            (void)piece_start(p, k, s, s - pe, b, kv, ql, ipg, wsb_of(b), t0, true);
+            (void)piece_start(p, k, s, s - pe, b, kv, ql, ipg, wsb_of(b), t0, true, table ? s_tp + s_toff[b] : nullptr);
         }
         // boundaries past the last item
         for (int k = max((W + pe - 1) / pe, k0) + tid; k < k1; k += kPlanThreads)
