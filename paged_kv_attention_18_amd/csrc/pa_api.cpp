@@ -2,6 +2,7 @@
 // checks, kernel selection, workspace, launches and timing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -71,6 +72,8 @@ constexpr int kSparseTileRows = 64;
 // static piece per worker, and the same with a claimed tail of pieces.
 constexpr int kSelfPlanVariant = 3;
 constexpr int kSelfPlanTailVariant = 4;
+// band units of at most this many KV chunks run whole (no split, no merge)
+constexpr int kBandWholeUnitChunks = 8;
 
 }  // namespace
 
@@ -418,6 +421,22 @@ static pa_status forward_impl(pa_handle *h, const void *query, const void *key_c
     p.tile_shift = log2_or_none(v.rows_per_tile);
     p.max_tiles = (max_q_seq_len * G + v.rows_per_tile - 1) / v.rows_per_tile;
     p.no_split = (c.flags & PA_FLAG_NO_SPLIT) ? 1 : 0;
+    // A band unit's keys lie within its query tokens plus the window.  When
+    // that is a few chunks and there are no more units than workers (so
+    // that pieces would cut nearly every unit), the fp32 partials and the
+    // merge cost more than the parallelism they buy: each unit then runs
+    // whole on one workgroup.  With more units, pieces that stream through
+    // several units stay faster; the streaming kernel always keeps its
+    // pieces.
+    if (!p.no_split && c.mask == PA_MASK_BAND && v.path == 1 &&
+        !pa::tile_streaming(c.head_size_k, c.head_size_v, v.tile_variant)) {
+        const int64_t rows = std::min<int64_t>((int64_t)max_q_seq_len * G, v.rows_per_tile);
+        const int64_t keys = (rows + G - 1) / G + 1 + (int64_t)c.window_left + c.window_right;
+        const int64_t units = (int64_t)batch * c.kv_head_num * p.max_tiles;
+        if ((keys + v.chunk - 1) / v.chunk + 1 <= kBandWholeUnitChunks &&
+            units <= std::min(v.partitions, h->max_partitions))
+            p.no_split = 1;
+    }
     p.partitions = p.no_split ? batch * c.kv_head_num * p.max_tiles
                               : (v.partitions < h->max_partitions ? v.partitions : h->max_partitions);
     p.pieces = p.no_split ? 0 : p.partitions * v.pieces_per_worker;

@@ -233,6 +233,7 @@ BAND_CASES = [
     ([900, 300], 32, 8, 128, 128, 128, "f16", [512, 8], (127, 0), False),     # long chunk, most blocks skipped
     ([1500, 77, 640], 64, 1, 576, 512, 128, "bf16", None, (127, 0), True),    # the pages' shape: 64 heads, 1 KV head
     ([300, 70], 16, 1, 576, 512, 64, "f16", [5, 2], (40, 2), False),
+    ([2500, 900], 16, 2, 128, 128, 64, "f16", [64, 3], (700, 0), False),    # window of many chunks: split units
 ]
 
 
