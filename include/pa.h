@@ -101,7 +101,11 @@ enum {
     PA_FLAG_FORCE_VALU = 1u << 0,  /* testing: require the VALU decode path (at most 8 rows per unit,
                                       i.e. max_q_seq_len * head_num / kv_head_num <= 8) */
     PA_FLAG_FORCE_MFMA = 1u << 1,  /* testing: take the MFMA tile path always */
-    PA_FLAG_NO_SPLIT = 1u << 2,    /* testing: one worker per (sequence, KV head, row tile); no merge */
+    PA_FLAG_NO_SPLIT = 1u << 2,    /* testing: one worker per (sequence, KV head, row tile); no merge.
+                                      Without the flag the library takes this path by itself for a
+                                      band mask whose units reach at most 8 KV chunks when there are
+                                      no more units than workers (pa_describe's partitions is then
+                                      the split count it would otherwise use) */
     PA_FLAG_SHARED_KV = 1u << 3,   /* one cache for K and V: the V row of a token is the leading
                                       head_size_v elements of its K row (requires Dv <= Dk); see
                                       pa_forward's value_cache */
