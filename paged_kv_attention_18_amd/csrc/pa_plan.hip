@@ -200,10 +200,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         set_error(p.ws.err, s_err);
 }
 
-// Rows per merge workgroup: enough to give every thread ~4 outputs.
+// Rows per merge workgroup: enough to give every thread ~4 outputs, or ~16
+// for narrow rows (Dv <= 128), where a workgroup's dependent reads of the
+// header and its split entry cost more than its few outputs.
 __host__ __device__ inline int merge_rows_per_wg(int dv)
 {
-    const int r = (4 * kThreads) / dv;
+    const int r = ((dv <= 128 ? 16 : 4) * kThreads) / dv;
     return r < 1 ? 1 : (r > 64 ? 64 : r);
 }
 
