@@ -2,16 +2,21 @@
 """Throughput of the paged-attention forward pass on one MI355X.
 
 One step is one full forward pass (plan + attention + merge) over one batch of
-the named synthetic workload (default: GQA decode, batch 64, 32 query / 8 KV
-heads, head size 128, block size 128, context lengths uniform in
-[512, 4096], bf16).  Inputs are resident in HBM before timing starts; the
-timed steps rotate over several copies of the KV cache so no step finds the
-previous step's KV bytes in the caches.
+the named synthetic workload.  The default is the largest decode workload,
+the long-context skewed decode: batch 256, 64 query / 8 KV heads, head size
+128, block size 128, fp16, context lengths log-uniform in [256, 32768] with
+four sequences at 32768.  Inputs are resident in HBM before timing starts;
+the timed steps rotate over several copies of the KV cache so no step finds
+the previous step's KV bytes in the caches.
 
-Prints one JSON line: tokens/s (query tokens per second), the attention
-kernel's achieved HBM bandwidth on the KV bytes the method must read (each
-visible (sequence, KV head, token) row of K and V once) against the 8 TB/s
-peak, and the oracle's own throughput on the host cores for context.
+Prints one JSON line: tokens/s (query tokens per second), the step time's
+p10 / p50 / p90, the attention kernel's achieved HBM bandwidth on the KV
+bytes the method must read (each visible (sequence, KV head, token) row of K
+and V once) against the 8 TB/s peak and against a measured streaming-read
+ceiling of this device, the oracle's own throughput on the host cores, and
+(unless --no-table) the same figures for the five named configurations:
+tiny decode as latency, GQA decode, skewed long decode, splitfuse with the
+causal mask (matrix-core roofline) and MLA decode.
 """
 from __future__ import annotations
 
@@ -163,13 +168,186 @@ def cpu_baseline(p, target_s, threads):
                       f"{int(kv[seqs].sum())} KV tokens), fp64, {reps} run(s) in {dt:.1f} s wall"}
 
 
+TABLE = ("tiny_decode", "gqa_decode", "skewed_long_decode", "splitfuse_causal", "mla_decode")
+
+
+def pct(xs):
+    import numpy as np
+
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean())}
+
+
+def read_peak(dev, nbytes=2 << 30, reps=10):
+    """The device's streaming-read rate: a plain kernel reading one large
+    buffer in contiguous per-workgroup shares (the library's read probe),
+    timed with events on the stream it runs on.  Best and median of reps."""
+    import torch
+
+    from paged_kv_attention_18_amd import binding
+
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(7)
+    wgs = 2048
+    sink = torch.empty(wgs, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for _ in range(3):
+        binding.pa_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), wgs, sp)
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        binding.pa_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), wgs, sp)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del buf, sink
+    torch.cuda.empty_cache()
+    times.sort()
+    return {"gbps_best": nbytes / (times[0] * 1e-3) / 1e9, "gbps_median": nbytes / (times[len(times) // 2] * 1e-3) / 1e9,
+            "bytes": nbytes, "reps": reps,
+            "method": f"pa_read_probe: {wgs} workgroups x 256 threads, contiguous shares, 8 x 16-byte loads in flight per thread"}
+
+
+def measure(w, dev, steps, warmup, flags=0, partitions=0, graph=False, copies=0, peak=None):
+    """Times `steps` forward passes of workload w (after `warmup`): the whole
+    pass without per-kernel events (throughput), each pass on its own
+    (percentiles), and each kernel with the library's HIP events (roofline)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_attention_18_amd import binding, synth
+
+    p = synth.generate(w, device=dev)
+    vc_numel = 0 if p.value_cache is None else p.value_cache.numel()
+    cache_bytes = (p.key_cache.numel() + vc_numel) * p.key_cache.element_size()
+    copies = copies or max(3, math.ceil((1.5 * (1 << 30)) / cache_bytes))
+    kcs = [p.key_cache] + [p.key_cache.clone() for _ in range(copies - 1)]
+    # shared K/V: no value cache (V is read from the K rows)
+    vcs = [None] * copies if p.value_cache is None else [p.value_cache] + [p.value_cache.clone() for _ in range(copies - 1)]
+    att = binding.for_problem(p, flags=flags, num_partitions=partitions)
+    desc = att.describe()
+    out = torch.empty(p.num_q_tokens, w.head_num, w.head_size_v, dtype=p.query.dtype, device=dev)
+    ql_max = max(1, p.max_q_seq_len)
+
+    def step(k):
+        att.forward(p.query, kcs[k % copies], vcs[k % copies], p.block_tables, p.context_lens,
+                    p.q_seq_lens, max_q_seq_len=ql_max, out=out, topk_indices=p.topk_idx)
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    if att.device_error() != 0:
+        raise RuntimeError("device error flag set during warm-up")
+
+    stream = torch.cuda.current_stream()
+    run = step
+    if graph:
+        # one captured forward pass per KV copy, replayed in the same rotation
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for k in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(k)
+                graphs.append(g)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        run = lambda k: graphs[k % copies].replay()
+        for k in range(warmup):
+            run(k)
+        torch.cuda.synchronize()
+
+    # (1) whole-pass throughput: events only around the K steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(steps):
+        run(k)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    # (2) the same steps with an event between consecutive passes (percentiles)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for k in range(steps):
+        run(k)
+        evs[k + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = [evs[k].elapsed_time(evs[k + 1]) for k in range(steps)]
+    # (3) eager passes with HIP events around each kernel, recorded by the
+    #     library on the stream its kernels run on
+    binding.pa_set_timing(att.handle, 1)
+    for k in range(steps):
+        step(k)
+    torch.cuda.synchronize()
+    kms, passes, planned, per_pass = binding.pa_read_timing(att.handle, per_pass_cap=steps)
+    binding.pa_set_timing(att.handle, 0)
+    assert passes == steps
+    if att.device_error() != 0:
+        raise RuntimeError("device error flag set during the timed steps")
+
+    ms_per_step = total_ms / steps
+    kv_bytes = synth.kv_bytes(p)
+    attn = [r[1] for r in per_pass]
+    attn_ms = kms[1] / passes
+    kernel = {"valu": "decode_kernel", "mfma": "tile_kernel", "stream": "stream_kernel"}[desc["path"]]
+    traffic = measured_traffic(w.name, kernel)
+    flops = attention_flops(p)
+    hbm_gbps = kv_bytes / (attn_ms * 1e-3) / 1e9
+    if flops / kv_bytes > RIDGE:
+        # compute-bound (long splitfuse chunks): matrix-core roofline
+        achieved = flops / (attn_ms * 1e-3) / 1e12
+        roofline = {"kernel": kernel, "bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS, "traffic": traffic,
+                    "flops_per_launch": flops, "hbm_gbps_on_kv_bytes": hbm_gbps}
+    else:
+        roofline = {"kernel": kernel, "bound": "hbm", "achieved": hbm_gbps, "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": hbm_gbps / HBM_PEAK_GBPS, "traffic": traffic,
+                    "kv_bytes_per_launch": kv_bytes}
+        if peak:
+            roofline["measured_read_peak"] = peak
+            roofline["frac_of_measured_read_peak"] = hbm_gbps / peak
+    res = {
+        "p": p, "desc": desc, "copies": copies, "ms_per_step": ms_per_step, "step_ms": pct(step_ms),
+        "attention_ms": pct(attn), "kv_bytes": kv_bytes, "flops": flops, "roofline": roofline,
+        "kernels_ms": {"plan": kms[0] / planned if planned else None, "attention": attn_ms,
+                       "merge": kms[2] / passes},
+    }
+    del kcs, vcs, out, att
+    return res
+
+
+def table_row(w, r):
+    p = r["p"]
+    row = {"workload": w.name, "batch": p.batch, "query_tokens": p.num_q_tokens, "kv_tokens": p.kv_tokens(),
+           "kv_bytes": r["kv_bytes"], "path": r["desc"]["path"], "step_ms": r["step_ms"],
+           "attention_ms": r["attention_ms"], "kernels_ms": r["kernels_ms"]}
+    if w.name == "tiny_decode":
+        # parity-sized: reported as latency
+        row["latency_us"] = {k: v * 1e3 for k, v in r["step_ms"].items()}
+        return row
+    row["tokens_per_s"] = p.num_q_tokens / (r["ms_per_step"] * 1e-3)
+    rf = r["roofline"]
+    row["roofline"] = {k: rf[k] for k in ("bound", "achieved", "unit", "frac") if k in rf}
+    if "frac_of_measured_read_peak" in rf:
+        row["roofline"]["frac_of_measured_read_peak"] = rf["frac_of_measured_read_peak"]
+    if rf["bound"] == "mfma":
+        row["roofline"]["hbm_gbps_on_kv_bytes"] = rf["hbm_gbps_on_kv_bytes"]
+    return row
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa_decode",
-                    help="tiny_decode | gqa_decode | skewed_long_decode | splitfuse_causal | mla_decode")
+    ap.add_argument("--workload", default="skewed_long_decode",
+                    help="tiny_decode | gqa_decode | skewed_long_decode | splitfuse_causal | mla_decode | ...")
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies to rotate over (0 = auto)")
     ap.add_argument("--flags", type=int, default=0, help="pa_config.flags (PA_FLAG_* bits; 0 = automatic)")
     ap.add_argument("--partitions", type=int, default=0, help="pa_config.num_partitions (0 = automatic)")
@@ -177,6 +355,8 @@ def main():
                     help="replay the forward pass from HIP graphs (one per KV copy) for the throughput figure")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size, in seconds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-table", action="store_true", help="time the named workload only")
+    ap.add_argument("--table-steps", type=int, default=20, help="timed steps per workload of the table")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -186,10 +366,9 @@ def main():
               "(the attention has no cross-GPU path here)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from paged_kv_attention_18_amd import binding, synth
+    from paged_kv_attention_18_amd import synth
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
@@ -205,97 +384,23 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
         return
 
+    peak = read_peak(dev)
+    print(f"# measured streaming read: {peak['gbps_best']:.0f} GB/s best, {peak['gbps_median']:.0f} median",
+          file=sys.stderr, flush=True)
     w = synth.WORKLOADS[int(args.workload)] if args.workload.isdigit() else synth.by_name(args.workload)
-    p = synth.generate(w, device=dev)
-    vc_numel = 0 if p.value_cache is None else p.value_cache.numel()
-    cache_bytes = (p.key_cache.numel() + vc_numel) * p.key_cache.element_size()
-    copies = args.copies or max(3, math.ceil((1.5 * (1 << 30)) / cache_bytes))
-    kcs = [p.key_cache] + [p.key_cache.clone() for _ in range(copies - 1)]
-    # shared K/V: no value cache (V is read from the K rows)
-    vcs = [None] * copies if p.value_cache is None else [p.value_cache] + [p.value_cache.clone() for _ in range(copies - 1)]
-    att = binding.for_problem(p, flags=args.flags, num_partitions=args.partitions)
-    desc = att.describe()
-    out = torch.empty(p.num_q_tokens, w.head_num, w.head_size_v, dtype=p.query.dtype, device=dev)
-    ql_max = max(1, p.max_q_seq_len)
-
-    def step(k):
-        att.forward(p.query, kcs[k % copies], vcs[k % copies], p.block_tables, p.context_lens,
-                    p.q_seq_lens, max_q_seq_len=ql_max, out=out, topk_indices=p.topk_idx)
-
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    if att.device_error() != 0:
-        raise RuntimeError("device error flag set during warm-up")
-
-    stream = torch.cuda.current_stream()
-    run = step
-    if args.graph:
-        # one captured forward pass per KV copy, replayed in the same rotation
-        graphs = []
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for k in range(copies):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    step(k)
-                graphs.append(g)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        run = lambda k: graphs[k % copies].replay()
-        for k in range(args.warmup):
-            run(k)
-        torch.cuda.synchronize()
-
-    def timed(n):
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for k in range(n):
-            run(k)
-        stop.record(stream)
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop)
-
-    # (1) whole-pass throughput, no per-kernel events in the stream
-    total_ms = timed(args.steps)
-    # (2) the same steps again with HIP events around each kernel of the pass
-    #     (eager launches: events are recorded on the stream the kernels use)
-    binding.pa_set_timing(att.handle, 1)
-    run = step
-    timed_ms = timed(args.steps)
-    kms, passes = binding.pa_read_timing(att.handle)
-    binding.pa_set_timing(att.handle, 0)
-    assert passes == args.steps
-
-    ms_per_step = total_ms / args.steps
+    r = measure(w, dev, args.steps, args.warmup, args.flags, args.partitions, args.graph, args.copies,
+                peak["gbps_best"])
+    print(f"# {w.name}: {r['ms_per_step'] * 1e3:.1f} us per step", file=sys.stderr, flush=True)
+    p = r["p"]
     tokens = p.num_q_tokens
-    kv_bytes = synth.kv_bytes(p)
-    attn_ms = kms[1] / passes
-    kernel = {"valu": "decode_kernel", "mfma": "tile_kernel", "stream": "stream_kernel"}[desc["path"]]
-    traffic = measured_traffic(w.name, kernel)
-    flops = attention_flops(p)
-    if flops / kv_bytes > RIDGE:
-        # compute-bound (long splitfuse chunks): matrix-core roofline
-        achieved = flops / (attn_ms * 1e-3) / 1e12
-        roofline = {"kernel": kernel, "bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS, "traffic": traffic,
-                    "flops_per_launch": flops, "hbm_gbps_on_kv_bytes": kv_bytes / (attn_ms * 1e-3) / 1e9}
-    else:
-        achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
-        roofline = {"kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                    "kv_bytes_per_launch": kv_bytes}
-
     result = {
         "metric": METRIC,
-        "value": tokens / (ms_per_step * 1e-3),
+        "value": tokens / (r["ms_per_step"] * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -304,17 +409,32 @@ def main():
         "config": {
             "workload": w.name, "batch": p.batch, "head_num": w.head_num, "kv_head_num": w.kv_head_num,
             "head_size_k": w.head_size_k, "head_size_v": w.head_size_v, "block_size": w.block_size,
-            "mask": w.mask, "shared_kv": w.shared_kv, "query_tokens": tokens, "kv_tokens": p.kv_tokens(), "kv_bytes": kv_bytes,
-            "seed": w.seed, "kv_cache_copies": copies, "path": desc["path"],
-            "partitions": desc["partitions"], "flags": args.flags, "parallelism": "none (1 GPU)",
+            "mask": w.mask, "shared_kv": w.shared_kv, "query_tokens": tokens, "kv_tokens": p.kv_tokens(),
+            "kv_bytes": r["kv_bytes"], "seed": w.seed, "kv_cache_copies": r["copies"], "path": r["desc"]["path"],
+            "partitions": r["desc"]["partitions"], "flags": args.flags, "parallelism": "none (1 GPU)",
         },
-        "pass_hbm_gbps": kv_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_ms": r["step_ms"],
+        "pass_hbm_gbps": r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
         "launch": "hip graph replay" if args.graph else "eager",
-        "ms_per_step_with_kernel_events": timed_ms / args.steps,
-        "kernels_ms": {"plan": kms[0] / passes, "attention": attn_ms, "merge": kms[2] / passes},
-        "roofline": roofline,
+        "kernels_ms": r["kernels_ms"],
+        "attention_ms": r["attention_ms"],
+        "read_peak": peak,
+        "roofline": r["roofline"],
         "cpu_baseline": None,
+        "configs": None,
     }
+    headline = r
+    if not args.no_table:
+        rows = []
+        for name in TABLE:
+            wt = synth.by_name(name)
+            rt = headline if name == w.name else measure(wt, dev, args.table_steps, 3, peak=peak["gbps_best"])
+            rows.append(table_row(wt, rt))
+            print(f"# table {name}: {rt['step_ms']['p50'] * 1e3:.1f} us p50", file=sys.stderr, flush=True)
+            if rt is not headline:
+                del rt
+                torch.cuda.empty_cache()
+        result["configs"] = rows
     if not args.no_cpu_baseline:
         threads = min(CPU_SHARE, len(os.sched_getaffinity(0)))
         result["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds, threads)

@@ -237,11 +237,29 @@ pa_status pa_get_device_error(pa_handle *h, uint32_t *code, int32_t clear);
  * events on its stream around each of its kernels (plan, attention, merge).
  * pa_read_timing synchronises, adds up the elapsed times of all recorded
  * passes since the last read into ms[3] (plan, attention, merge) and the
- * number of passes into *count, and resets the totals.  At most 1024 passes
- * are kept between reads; later ones are not timed.
+ * number of passes into *count, and resets the totals.  A pass whose
+ * attention kernel planned for itself launches no plan kernel: ms[0] sums
+ * the passes that launched one, and *plan_launches (if not NULL) receives
+ * their number.  If per_pass_cap > 0, per_pass_ms (host, 3 * per_pass_cap
+ * doubles) receives (plan, attention, merge) of each of the first
+ * per_pass_cap passes, plan = -1 for a pass without a plan kernel.  At most
+ * 1024 passes are kept between reads; later ones are not timed.
  */
 pa_status pa_set_timing(pa_handle *h, int32_t enable);
-pa_status pa_read_timing(pa_handle *h, double ms[3], int32_t *count);
+pa_status pa_read_timing(pa_handle *h, double ms[3], int32_t *count, int32_t *plan_launches, double *per_pass_ms,
+                         int32_t per_pass_cap);
+
+/*
+ * Measurement support, not part of the forward pass: a plain streaming read
+ * of `bytes` (> 0, a multiple of 16) at the device address src, enqueued on
+ * `stream`.  Each of `workgroups` workgroups reads one contiguous share with
+ * 16-byte loads and writes one word of sink (device, uint32 [workgroups]).
+ * The rate it reaches is the device's read ceiling for whole-buffer
+ * streaming, which the attention kernels' HBM bandwidth is set beside.
+ * PA_ERR_INVALID_ARG for a NULL pointer or a bad size; PA_ERR_HIP if the
+ * launch fails.
+ */
+pa_status pa_read_probe(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups, void *stream);
 
 /*
  * What pa_create chose, for logging and tests: *path is 0 for the VALU decode

@@ -56,10 +56,17 @@ def load(path=None):
 
 
 def default_threads():
+    """The host threads to use: the CPUs this process may run on, at most the
+    share named by OMP_NUM_THREADS (16 when unset)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "16"))
+    except ValueError:
+        share = 16
+    return max(1, min(n, share if share > 0 else 16))
 
 
 class Inputs:

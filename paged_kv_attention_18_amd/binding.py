@@ -25,7 +25,7 @@ PA_FLAG_FORCE_VALU, PA_FLAG_FORCE_MFMA, PA_FLAG_NO_SPLIT, PA_FLAG_SHARED_KV, PA_
 PA_DEVERR_BLOCK_ID, PA_DEVERR_TABLE_SHORT, PA_DEVERR_QLEN, PA_DEVERR_TOKENS, PA_DEVERR_CTX = 1, 2, 4, 8, 16
 
 EXPORTS = ("pa_create", "pa_forward", "pa_forward_sparse", "pa_destroy", "pa_status_string",
-           "pa_get_device_error", "pa_set_timing", "pa_read_timing", "pa_describe")
+           "pa_get_device_error", "pa_set_timing", "pa_read_timing", "pa_describe", "pa_read_probe")
 
 
 class pa_config(ctypes.Structure):
@@ -86,8 +86,11 @@ def load_library(path=LIB_PATH):
         lib.pa_get_device_error.restype = ctypes.c_int
         lib.pa_set_timing.argtypes = [P, i32]
         lib.pa_set_timing.restype = ctypes.c_int
-        lib.pa_read_timing.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+        lib.pa_read_timing.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                       ctypes.POINTER(ctypes.c_double), i32]
         lib.pa_read_timing.restype = ctypes.c_int
+        lib.pa_read_probe.argtypes = [P, ctypes.c_int64, P, i32, P]
+        lib.pa_read_probe.restype = ctypes.c_int
         lib.pa_describe.argtypes = [P, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                     ctypes.POINTER(i32), ctypes.POINTER(i32)]
         lib.pa_describe.restype = ctypes.c_int
@@ -153,12 +156,23 @@ def pa_set_timing(handle, enable):
     _check(load_library().pa_set_timing(handle, int(enable)), "pa_set_timing")
 
 
-def pa_read_timing(handle):
-    """Returns ([plan_ms, attention_ms, merge_ms] summed, passes)."""
+def pa_read_timing(handle, per_pass_cap=0):
+    """Returns ([plan_ms, attention_ms, merge_ms] summed, passes, passes that
+    launched the plan kernel, per-pass [plan, attention, merge] ms lists --
+    plan -1 where no plan kernel ran -- for the first per_pass_cap passes)."""
     ms = (ctypes.c_double * 3)()
-    n = ctypes.c_int32()
-    _check(load_library().pa_read_timing(handle, ms, ctypes.byref(n)), "pa_read_timing")
-    return [ms[0], ms[1], ms[2]], n.value
+    n, planned = ctypes.c_int32(), ctypes.c_int32()
+    cap = max(0, int(per_pass_cap))
+    per = (ctypes.c_double * (3 * max(1, cap)))()
+    _check(load_library().pa_read_timing(handle, ms, ctypes.byref(n), ctypes.byref(planned), per if cap else None,
+                                         cap), "pa_read_timing")
+    rows = [[per[3 * k], per[3 * k + 1], per[3 * k + 2]] for k in range(min(cap, n.value))]
+    return [ms[0], ms[1], ms[2]], n.value, planned.value, rows
+
+
+def pa_read_probe(src, nbytes, sink, workgroups, stream):
+    """Pointer-level call of the streaming-read probe (device addresses)."""
+    _check(load_library().pa_read_probe(src, int(nbytes), sink, int(workgroups), stream or None), "pa_read_probe")
 
 
 def pa_describe(handle, max_q_seq_len):

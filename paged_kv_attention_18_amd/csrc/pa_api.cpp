@@ -90,6 +90,7 @@ struct pa_handle {
     // timing
     bool timing = false;
     std::vector<hipEvent_t> events;   // 4 per pass
+    std::vector<char> planned;        // per timed pass: the plan kernel was launched
     int timed = 0;
 
     Variant choose(int max_q) const
@@ -350,11 +351,15 @@ pa_status pa_describe(const pa_handle *h, int32_t max_q_seq_len, int32_t *path, 
     return PA_OK;
 }
 
-static pa_status forward_impl(pa_handle *h, const void *query, const void *key_cache, const void *value_cache,
+// Checks the arguments of one pass and fills its launch parameters (all but
+// the workspace pointers).  *empty: nothing to launch (no sequence or no
+// query token).
+static pa_status setup_params(const pa_handle *h, const void *query, const void *key_cache, const void *value_cache,
                               const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_seq_lens,
                               const int32_t *topk_indices, int32_t batch, int32_t num_q_tokens, int32_t max_q_seq_len,
-                              void *out, float *lse, void *stream)
+                              void *out, float *lse, pa::Params &p, Variant &v, bool *empty)
 {
+    *empty = true;
     if (!h || !query || !key_cache || !block_tables || !context_lens || !out)
         return PA_ERR_INVALID_ARG;
     const pa_config &c = h->cfg;
@@ -375,11 +380,11 @@ static pa_status forward_impl(pa_handle *h, const void *query, const void *key_c
         return PA_ERR_INVALID_ARG;
     if (batch == 0 || num_q_tokens == 0)
         return PA_OK;
-    hipStream_t s = (hipStream_t)stream;
-    const Variant v = h->choose(max_q_seq_len);
+    *empty = false;
+    v = h->choose(max_q_seq_len);
     const int G = c.head_num / c.kv_head_num;
 
-    pa::Params p{};
+    p = pa::Params{};
     p.query = query;
     p.key_cache = key_cache;
     p.value_cache = shared ? key_cache : value_cache;
@@ -441,7 +446,6 @@ static pa_status forward_impl(pa_handle *h, const void *query, const void *key_c
                               : (v.partitions < h->max_partitions ? v.partitions : h->max_partitions);
     p.pieces = p.no_split ? 0 : p.partitions * v.pieces_per_worker;
     p.partial_stride = (int32_t)partial_floats(v.rows_per_tile, c.head_size_v);
-    p.ws = h->ws;
     p.tail_min = 0;
     // The streaming kernel cuts its own pieces when the lengths fit in a
     // wave's registers: one launch fewer, and no wait on plan data when a
@@ -461,7 +465,21 @@ static pa_status forward_impl(pa_handle *h, const void *query, const void *key_c
         if (w_max >= (int64_t)pa::kTailMinShare * pa::kTailMinChunks * p.partitions)
             p.tail_min = pa::kTailMinChunks;
     }
+    return PA_OK;
+}
 
+// Pieces a pass cuts (split entries and partial slot pairs it may use).
+static int64_t pass_pieces(const pa::Params &p)
+{
+    if (p.no_split)
+        return 0;
+    return (p.self_plan && p.tail_min > 0) ? (int64_t)(1 + pa::kTailRounds) * p.partitions : (int64_t)p.pieces;
+}
+
+// Enqueues the kernels of one pass whose parameters (workspace included) are set.
+static pa_status launch_pass(pa_handle *h, const pa::Params &p, const Variant &v, hipStream_t s)
+{
+    const pa_config &c = h->cfg;
     const bool timed = h->timing && h->timed < kMaxTimedPasses;
     hipEvent_t *ev = timed ? &h->events[4 * h->timed] : nullptr;
     if (timed && hipEventRecord(ev[0], s) != hipSuccess)
@@ -484,9 +502,26 @@ static pa_status forward_impl(pa_handle *h, const void *query, const void *key_c
     if (timed) {
         if (hipEventRecord(ev[3], s) != hipSuccess)
             return PA_ERR_HIP;
+        h->planned[h->timed] = p.self_plan ? 0 : 1;
         ++h->timed;
     }
     return PA_OK;
+}
+
+static pa_status forward_impl(pa_handle *h, const void *query, const void *key_cache, const void *value_cache,
+                              const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_seq_lens,
+                              const int32_t *topk_indices, int32_t batch, int32_t num_q_tokens, int32_t max_q_seq_len,
+                              void *out, float *lse, void *stream)
+{
+    pa::Params p;
+    Variant v;
+    bool empty = true;
+    const pa_status st = setup_params(h, query, key_cache, value_cache, block_tables, context_lens, q_seq_lens,
+                                      topk_indices, batch, num_q_tokens, max_q_seq_len, out, lse, p, v, &empty);
+    if (st != PA_OK || empty)
+        return st;
+    p.ws = h->ws;
+    return launch_pass(h, p, v, (hipStream_t)stream);
 }
 
 pa_status pa_forward(pa_handle *h, const void *query, const void *key_cache, const void *value_cache,
@@ -530,6 +565,7 @@ pa_status pa_set_timing(pa_handle *h, int32_t enable)
         return PA_ERR_INVALID_ARG;
     if (enable && h->events.empty()) {
         h->events.resize(4 * kMaxTimedPasses);
+        h->planned.assign(kMaxTimedPasses, 0);
         for (auto &e : h->events)
             if (hipEventCreate(&e) != hipSuccess)
                 return PA_ERR_HIP;
@@ -539,12 +575,14 @@ pa_status pa_set_timing(pa_handle *h, int32_t enable)
     return PA_OK;
 }
 
-pa_status pa_read_timing(pa_handle *h, double ms[3], int32_t *count)
+pa_status pa_read_timing(pa_handle *h, double ms[3], int32_t *count, int32_t *plan_launches, double *per_pass_ms,
+                         int32_t per_pass_cap)
 {
-    if (!h || !ms || !count)
+    if (!h || !ms || !count || per_pass_cap < 0 || (per_pass_cap > 0 && !per_pass_ms))
         return PA_ERR_INVALID_ARG;
     ms[0] = ms[1] = ms[2] = 0.0;
     *count = h->timed;
+    int planned = 0;
     if (h->timed > 0) {
         if (hipEventSynchronize(h->events[4 * h->timed - 1]) != hipSuccess)
             return PA_ERR_HIP;
@@ -553,12 +591,29 @@ pa_status pa_read_timing(pa_handle *h, double ms[3], int32_t *count)
                 float t = 0.f;
                 if (hipEventElapsedTime(&t, h->events[4 * k + j], h->events[4 * k + j + 1]) != hipSuccess)
                     return PA_ERR_HIP;
-                ms[j] += t;
+                // passes whose kernel planned for itself launched no plan kernel
+                const bool none = j == 0 && !h->planned[k];
+                if (!none)
+                    ms[j] += t;
+                if (k < per_pass_cap)
+                    per_pass_ms[3 * k + j] = none ? -1.0 : (double)t;
             }
+            planned += h->planned[k] ? 1 : 0;
         }
     }
+    if (plan_launches)
+        *plan_launches = planned;
     h->timed = 0;
     return PA_OK;
+}
+
+pa_status pa_read_probe(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups, void *stream)
+{
+    if (!src || !sink || bytes <= 0 || bytes % 16 != 0 || workgroups <= 0)
+        return PA_ERR_INVALID_ARG;
+    return pa::launch_read_probe(src, (long long)bytes, sink, workgroups, (hipStream_t)stream) == hipSuccess
+               ? PA_OK
+               : PA_ERR_HIP;
 }
 
 }  // extern "C"

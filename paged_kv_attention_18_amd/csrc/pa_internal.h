@@ -115,6 +115,9 @@ hipError_t launch_merge(const Params &p, int dtype, hipStream_t s);
 // Returns hipErrorInvalidValue when no kernel exists for the shape.
 hipError_t launch_decode(const Params &p, int dtype, int rows_pad, hipStream_t s);
 hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s);
+// Measurement: a plain streaming read of `bytes` (a multiple of 16) by `workgroups`
+// workgroups, one word per workgroup written to sink.
+hipError_t launch_read_probe(const void *src, long long bytes, uint32_t *sink, int workgroups, hipStream_t s);
 // Shapes and occupancy used by the host to pick kernels and size the grid.
 bool decode_supported(int dk, int dv);
 // MFMA tile kernel variants: 0 for units of at most 16 rows, 1 for up to

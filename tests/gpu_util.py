@@ -68,13 +68,3 @@ def assert_lse_close(gpu_l, ref_l, what=""):
     worst = float(d.max()) if d.size else 0.0
     assert worst <= LSE_TOL, f"{what}: lse err {worst:.3e}"
     return worst
-
-
-def sample_rows(p: synth.Problem, n, seed=0):
-    """n (token, head) rows spread over the batch, incl. first/last tokens."""
-    rng = np.random.default_rng(seed)
-    T, H = p.num_q_tokens, p.workload.head_num
-    toks = np.concatenate([[0, T - 1], rng.integers(0, T, size=max(0, n - 2))]).astype(np.int32)
-    heads = rng.integers(0, H, size=len(toks)).astype(np.int32)
-    heads[0], heads[1] = 0, H - 1
-    return toks, heads

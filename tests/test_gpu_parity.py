@@ -2,7 +2,8 @@
 
 Small problems are compared element by element; they span several chunks,
 several row tiles and ragged tails.  The named workloads are compared at
-full size on sampled rows, with the launch configuration the benchmark uses.
+full size on every output row, element by element, with the launch
+configuration the benchmark uses.
 Probes check gathering, masking and poison handling bit for bit."""
 import math
 
@@ -13,8 +14,7 @@ import torch
 from oracle import pa_ref
 from paged_kv_attention_18_amd import binding, synth
 
-from gpu_util import (assert_close, assert_lse_close, log, oracle_full, run_hip, sample_rows,
-                      to_device)
+from gpu_util import assert_close, assert_lse_close, log, oracle_full, run_hip, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -120,12 +120,23 @@ def test_causal_small_rows():
     log("causal small rows")
     p = synth.custom([50, 9, 200], 8, 4, 128, 128, 16, "bf16", "causal", q_seq_lens=[7, 3, 5], seed=12)
     check_full(p, what="causal small rows")
-    # The VALU kernel's causal mode is switched off (a GPU memory fault was
-    # seen once in this case, cause not found): the handle is refused.
+    # The VALU kernel's causal mode is switched off: the handle is refused.
     p = synth.custom([50, 9, 200], 8, 4, 128, 128, 16, "bf16", "causal", q_seq_lens=[4, 3, 1], seed=12)
     with pytest.raises(binding.PaError) as e:
         binding.for_problem(to_device(p), flags=F.PA_FLAG_FORCE_VALU)
     assert e.value.status == binding.PA_ERR_UNSUPPORTED
+
+
+VALU_CAUSAL_FAULT = ("one GPU run of this case on the VALU kernel's causal mode ended in a GPU memory "
+                     "fault; its cause has not been shown, so the mode is refused and the case stays off the GPU")
+
+
+@pytest.mark.skip(reason=VALU_CAUSAL_FAULT)
+def test_causal_small_rows_valu():
+    # kv [50, 9, 200], q [4, 3, 1], H 8 / Hkv 4 (G 2, 8 rows), D 128, bs 16, bf16
+    log("causal small rows valu")
+    p = synth.custom([50, 9, 200], 8, 4, 128, 128, 16, "bf16", "causal", q_seq_lens=[4, 3, 1], seed=12)
+    check_full(p, flags=F.PA_FLAG_FORCE_VALU, what="causal valu")
 
 
 def test_no_mask_multi_token():
@@ -723,25 +734,25 @@ def test_describe_paths():
 
 
 # ----------------------------------------------------- the named workloads
-def full_size_sampled(n, rows, seed=0):
+def full_size_all_rows(n):
+    """A named workload at full size, in the benchmark's launch configuration,
+    compared with the oracle on every output row, element by element."""
     w = synth.WORKLOADS[n]
     log(f"workload {w.name}: generating on the GPU")
     p = synth.generate(w, device="cuda")
     o, l, att = run_hip(p)
     assert att.device_error() == 0
-    log(f"workload {w.name}: oracle on {rows} rows ({att.describe()})")
-    toks, heads = sample_rows(p, rows, seed)
-    inp = pa_ref.Inputs.from_problem(p)
-    ro, rl = pa_ref.rows(inp, toks, heads)
-    e = assert_close(o[toks, heads], ro, w.dtype, w.name)
-    assert_lse_close(l[toks, heads], rl, w.name)
+    log(f"workload {w.name}: oracle on all {p.num_q_tokens} x {w.head_num} rows ({att.describe()})")
+    ro, rl = pa_ref.forward(pa_ref.Inputs.from_problem(p))
+    e = assert_close(o, ro, w.dtype, w.name)
+    assert_lse_close(l, rl, w.name)
     # properties that hold at any size: finite everywhere, |o| <= max |V|
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
     vsrc = p.key_cache[..., :w.head_size_v] if w.shared_kv else p.value_cache
     vmax = float(vsrc.abs().max())
     assert np.abs(o).max() <= vmax * (1 + 1e-2)
-    log(f"workload {w.name}: max err {e:.2e}")
-    return p, o, l
+    log(f"workload {w.name}: max err {e:.2e} over {o.size} outputs")
+    return p, o, l, ro, rl
 
 
 def test_workload_tiny_decode_full():
@@ -750,58 +761,54 @@ def test_workload_tiny_decode_full():
     check_full(p, what=w.name)
 
 
-def test_workload_gqa_decode_sampled():
-    full_size_sampled(2, 256)
+def test_workload_gqa_decode_full():
+    full_size_all_rows(2)
 
 
-def test_workload_skewed_long_decode_sampled():
-    p, o, l = full_size_sampled(3, 128, seed=1)
-    # the longest sequences (32768 tokens) are sampled explicitly
-    long_b = np.flatnonzero(p.context_lens_np == 32768)[:2]
-    inp = pa_ref.Inputs.from_problem(p)
-    toks = np.repeat(long_b, 2).astype(np.int32)
-    heads = np.array([0, 63] * len(long_b), np.int32)
-    ro, rl = pa_ref.rows(inp, toks, heads)
-    assert_close(o[toks, heads], ro, "f16", "skewed long rows")
+def test_workload_skewed_long_decode_full():
+    p, o, l, ro, rl = full_size_all_rows(3)
+    # the longest sequences (32768 tokens), every head, once more on their own
+    long_b = np.flatnonzero(p.context_lens_np == 32768)
+    assert len(long_b) == 4
+    assert_close(o[long_b], ro[long_b], "f16", "skewed 32768-token rows")
+    assert_lse_close(l[long_b], rl[long_b], "skewed 32768-token rows")
 
 
-def test_workload_splitfuse_causal_sampled():
-    p, o, l = full_size_sampled(4, 192, seed=2)
-    # rows at chunk starts and ends of the prefill sequences
+def test_workload_splitfuse_causal_full():
+    p, o, l, ro, rl = full_size_all_rows(4)
+    # rows at the starts and ends of the prefill chunks (the causal diagonal
+    # at the first and last query token), on their own
     cu = np.concatenate([[0], np.cumsum(p.q_seq_lens_np)])
-    big = np.flatnonzero(p.q_seq_lens_np == 512)[:3]
-    toks = np.concatenate([[cu[b], cu[b] + 1, cu[b + 1] - 1] for b in big]).astype(np.int32)
-    heads = (np.arange(len(toks)) * 7 % 32).astype(np.int32)
-    ro, rl = pa_ref.rows(pa_ref.Inputs.from_problem(p), toks, heads)
-    assert_close(o[toks, heads], ro, "f16", "splitfuse chunk edges")
+    big = np.flatnonzero(p.q_seq_lens_np == 512)
+    toks = np.concatenate([[cu[b], cu[b] + 1, cu[b + 1] - 1] for b in big]).astype(np.int64)
+    assert_close(o[toks], ro[toks], "f16", "splitfuse chunk edges")
+    assert_lse_close(l[toks], rl[toks], "splitfuse chunk edges")
 
 
-def test_workload_mla_decode_sampled():
-    full_size_sampled(5, 128, seed=3)
+def test_workload_mla_decode_full():
+    full_size_all_rows(5)
 
 
-def test_workload_mla_shared_kv_decode_sampled():
-    full_size_sampled(6, 128, seed=4)
+def test_workload_mla_shared_kv_decode_full():
+    full_size_all_rows(6)
 
 
-def test_workload_band_shared_kv_decode_sampled():
-    full_size_sampled(7, 256, seed=5)
+def test_workload_band_shared_kv_decode_full():
+    full_size_all_rows(7)
 
 
-def test_workload_splitfuse_tensor_mask_sampled():
-    full_size_sampled(9, 192, seed=7)
+def test_workload_splitfuse_tensor_mask_full():
+    full_size_all_rows(9)
 
 
-def test_workload_sparse_topk_decode_sampled():
-    full_size_sampled(10, 128, seed=8)
+def test_workload_sparse_topk_decode_full():
+    full_size_all_rows(10)
 
 
-def test_workload_splitfuse_band_sampled():
-    p, o, l = full_size_sampled(8, 256, seed=6)
-    # rows at the starts and ends of the prefill chunks
+def test_workload_splitfuse_band_full():
+    p, o, l, ro, rl = full_size_all_rows(8)
+    # rows at the starts and ends of the prefill chunks, on their own
     cu = np.concatenate([[0], np.cumsum(p.q_seq_lens_np)])
-    big = np.flatnonzero(p.q_seq_lens_np == 512)[:3]
-    toks = np.concatenate([[cu[b], cu[b] + 1, cu[b] + 200, cu[b + 1] - 1] for b in big]).astype(np.int32)
-    heads = (np.arange(len(toks)) * 5 % 32).astype(np.int32)
-    ro, rl = pa_ref.rows(pa_ref.Inputs.from_problem(p), toks, heads)
-    assert_close(o[toks, heads], ro, "f16", "splitfuse band chunk rows")
+    big = np.flatnonzero(p.q_seq_lens_np == 512)
+    toks = np.concatenate([[cu[b], cu[b] + 1, cu[b] + 200, cu[b + 1] - 1] for b in big]).astype(np.int64)
+    assert_close(o[toks], ro[toks], "f16", "splitfuse band chunk rows")
