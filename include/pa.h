@@ -82,7 +82,8 @@ typedef enum {
     PA_ERR_INVALID_ARG = 1,   /* NULL pointer, bad size, shape outside the documented limits */
     PA_ERR_UNSUPPORTED = 2,   /* valid by the operator's rules but not built here (see pa_create) */
     PA_ERR_HIP = 3,           /* a HIP runtime call failed */
-    PA_ERR_OOM = 4            /* workspace allocation failed */
+    PA_ERR_OOM = 4,           /* workspace allocation failed */
+    PA_ERR_SCRATCH = 5        /* pa_forward_noalloc: the pass needs more workspace than its static array */
 } pa_status;
 
 typedef enum { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
@@ -218,6 +219,41 @@ pa_status pa_forward_sparse(pa_handle *h, const void *query, const void *key_cac
                             const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_seq_lens,
                             const int32_t *topk_indices, int32_t batch, int32_t num_q_tokens, int32_t max_q_seq_len,
                             void *out, float *lse, void *stream);
+
+/* Bytes of the static device array that holds pa_forward_noalloc's workspace on each GPU. */
+#define PA_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: pa_forward
+ * without a handle.  cfg is checked as pa_create checks it (same statuses,
+ * before any HIP call); the other arguments are pa_forward's.  The pass runs
+ * the kernels, pieces and merge order that pa_forward runs on a handle
+ * created from cfg, so the outputs agree bit for bit.  Sparse-list
+ * configurations are refused (PA_ERR_INVALID_ARG), as pa_forward refuses
+ * them.
+ *
+ * The workspace (plan arrays, split entries, fp32 partials, piece counter,
+ * error word, zero page) is laid out for this pass in a static device array
+ * of PA_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends; nothing is allocated or freed.  The first call on a
+ * device looks up that device's array and properties; later calls do no
+ * set-up.  Each call clears the piece counter, the error word and the zero
+ * page with a small fill kernel on `stream` (no memset), then enqueues the
+ * pass; it does not synchronise.  PA_ERR_SCRATCH: the pass needs more than
+ * the array holds (the partials grow with the partitions, the rows per tile
+ * and Dv, the plan arrays with the batch); a smaller cfg.num_partitions or
+ * PA_FLAG_STATIC_PIECES (no claimed tail) makes the pass smaller.  Device-data
+ * errors are clamped as in pa_forward; the error word is not reported.
+ *
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents: calls that overlap in time on the same GPU (two streams,
+ * or two host threads) race on it, and the caller must order them.
+ */
+pa_status pa_forward_noalloc(const pa_config *cfg, const void *query, const void *key_cache,
+                             const void *value_cache, const int32_t *block_tables, const int32_t *context_lens,
+                             const int32_t *q_seq_lens, int32_t batch, int32_t num_q_tokens, int32_t max_q_seq_len,
+                             void *out, float *lse, void *stream);
 
 /* Frees the workspace and the handle (synchronises the device first).  NULL is a no-op. */
 pa_status pa_destroy(pa_handle *h);

@@ -18,14 +18,16 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpa.so")
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_OOM = range(5)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_OOM, PA_ERR_SCRATCH = range(6)
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 PA_F16, PA_BF16 = 0, 1
 PA_MASK_NONE, PA_MASK_CAUSAL, PA_MASK_BAND, PA_MASK_TENSOR, PA_MASK_SPARSE = 0, 1, 2, 3, 4
 PA_FLAG_FORCE_VALU, PA_FLAG_FORCE_MFMA, PA_FLAG_NO_SPLIT, PA_FLAG_SHARED_KV, PA_FLAG_STATIC_PIECES = 1, 2, 4, 8, 16
 PA_DEVERR_BLOCK_ID, PA_DEVERR_TABLE_SHORT, PA_DEVERR_QLEN, PA_DEVERR_TOKENS, PA_DEVERR_CTX = 1, 2, 4, 8, 16
 
 EXPORTS = ("pa_create", "pa_forward", "pa_forward_sparse", "pa_destroy", "pa_status_string",
-           "pa_get_device_error", "pa_set_timing", "pa_read_timing", "pa_describe", "pa_read_probe")
+           "pa_get_device_error", "pa_set_timing", "pa_read_timing", "pa_describe", "pa_read_probe",
+           "pa_forward_noalloc")
 
 
 class pa_config(ctypes.Structure):
@@ -78,6 +80,8 @@ def load_library(path=LIB_PATH):
         lib.pa_forward.restype = ctypes.c_int
         lib.pa_forward_sparse.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, P, P, P]
         lib.pa_forward_sparse.restype = ctypes.c_int
+        lib.pa_forward_noalloc.argtypes = [ctypes.POINTER(pa_config), P, P, P, P, P, P, i32, i32, i32, P, P, P]
+        lib.pa_forward_noalloc.restype = ctypes.c_int
         lib.pa_destroy.argtypes = [P]
         lib.pa_destroy.restype = ctypes.c_int
         lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -135,6 +139,17 @@ def pa_forward_sparse(handle, query, key_cache, value_cache, block_tables, conte
     _check(lib.pa_forward_sparse(handle, query, key_cache, value_cache, block_tables, context_lens,
                                  q_seq_lens or None, topk_indices, batch, num_q_tokens, max_q_seq_len, out,
                                  lse or None, stream or None), "pa_forward_sparse")
+
+
+def pa_forward_noalloc(cfg: pa_config, query, key_cache, value_cache, block_tables, context_lens, q_seq_lens,
+                       batch, num_q_tokens, max_q_seq_len, out, lse, stream):
+    """Pointer-level call of the allocation-free pass (no handle; device
+    addresses or 0).  Returns the status instead of raising, so callers can
+    tell PA_ERR_SCRATCH apart."""
+    lib = load_library()
+    return lib.pa_forward_noalloc(ctypes.byref(cfg), query, key_cache, value_cache, block_tables, context_lens,
+                                  q_seq_lens or None, batch, num_q_tokens, max_q_seq_len, out, lse or None,
+                                  stream or None)
 
 
 def pa_destroy(handle):

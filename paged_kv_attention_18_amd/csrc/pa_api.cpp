@@ -156,6 +156,7 @@ const char *pa_status_string(pa_status s)
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_OOM: return "out of device memory";
+    case PA_ERR_SCRATCH: return "the pass needs more workspace than pa_forward_noalloc's static device array";
     }
     return "unknown status";
 }
@@ -617,3 +618,84 @@ pa_status pa_read_probe(const void *src, int64_t bytes, uint32_t *sink, int32_t 
 }
 
 }  // extern "C"
+
+namespace pa {
+
+pa_status validate_config(const pa_config *cfg)
+{
+    return check_config(cfg);
+}
+
+pa_status forward_in_buffer(const pa_config *cfg, int num_cus, void *base, size_t capacity, const void *query,
+                            const void *key_cache, const void *value_cache, const int32_t *block_tables,
+                            const int32_t *context_lens, const int32_t *q_seq_lens, int32_t batch,
+                            int32_t num_q_tokens, int32_t max_q_seq_len, void *out, float *lse, void *stream)
+{
+    const pa_status cst = check_config(cfg);
+    if (cst != PA_OK)
+        return cst;
+    if (!base || max_q_seq_len < 1 || max_q_seq_len > cfg->max_q_seq_len)
+        return PA_ERR_INVALID_ARG;
+    // a handle on the stack: the configuration and the grid bound pa_create
+    // would give this call (its partitions), no workspace, no events
+    pa_handle h;
+    h.cfg = *cfg;
+    h.num_cus = num_cus > 0 ? num_cus : 256;
+    h.max_partitions = h.choose(max_q_seq_len).partitions;
+    Params p;
+    Variant v;
+    bool empty = true;
+    const pa_status st = setup_params(&h, query, key_cache, value_cache, block_tables, context_lens, q_seq_lens,
+                                      nullptr, batch, num_q_tokens, max_q_seq_len, out, lse, p, v, &empty);
+    if (st != PA_OK || empty)
+        return st;
+    // Layout for this pass only: the words that must start at zero (header
+    // with the piece counter, error word, zero page) first, then the plan
+    // arrays of `batch` sequences, the split entries and the partial slot
+    // pairs of the pass's pieces.
+    const size_t N = (size_t)pass_pieces(p);
+    const size_t ent = N > 0 ? N : 1;
+    const size_t B = (size_t)batch;
+    const size_t zero_bytes = 16 * (size_t)cfg->kv_head_num *
+                              (size_t)(cfg->head_size_k > cfg->head_size_v ? cfg->head_size_k : cfg->head_size_v) * 2;
+    size_t off = 0;
+    auto take = [&off](size_t bytes) {
+        const size_t o = off;
+        off = (off + bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    const size_t o_hdr = take(8 * sizeof(int32_t));
+    const size_t o_err = take(sizeof(uint32_t));
+    const size_t o_zero = take(zero_bytes);
+    const size_t cleared = off;
+    const size_t o_cuq = take((B + 1) * sizeof(int32_t));
+    const size_t o_wsb = take((B + 1) * sizeof(int32_t));
+    const size_t o_ipg = take(B * sizeof(int32_t));
+    const size_t o_ql = take(B * sizeof(int32_t));
+    const size_t o_kv = take(B * sizeof(int32_t));
+    const size_t o_wgb = take(ent * sizeof(int32_t));
+    const size_t o_spl = take(ent * 8 * sizeof(int32_t));
+    const size_t o_part = take(2 * N * (size_t)p.partial_stride * sizeof(float));
+    if (off > capacity)
+        return PA_ERR_SCRATCH;
+    char *b = (char *)base;
+    p.ws.hdr = (int32_t *)(b + o_hdr);
+    p.ws.err = (uint32_t *)(b + o_err);
+    p.ws.zeros = b + o_zero;
+    p.ws.cu_q = (int32_t *)(b + o_cuq);
+    p.ws.wsb = (int32_t *)(b + o_wsb);
+    p.ws.ipg = (int32_t *)(b + o_ipg);
+    p.ws.qlen = (int32_t *)(b + o_ql);
+    p.ws.kvlen = (int32_t *)(b + o_kv);
+    p.ws.wg_b = (int32_t *)(b + o_wgb);
+    p.ws.splits = (int32_t *)(b + o_spl);
+    p.ws.partials = (float *)(b + o_part);
+    // earlier calls leave other contents here: clear what must start at
+    // zero with a fill kernel (no memset node if the caller captures a graph)
+    const hipStream_t s = (hipStream_t)stream;
+    if (launch_zero_words((uint32_t *)b, (long long)(cleared / sizeof(uint32_t)), s) != hipSuccess)
+        return PA_ERR_HIP;
+    return launch_pass(&h, p, v, s);
+}
+
+}  // namespace pa

@@ -115,6 +115,18 @@ hipError_t launch_merge(const Params &p, int dtype, hipStream_t s);
 // Returns hipErrorInvalidValue when no kernel exists for the shape.
 hipError_t launch_decode(const Params &p, int dtype, int rows_pad, hipStream_t s);
 hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s);
+// Allocation-free passes (pa_forward_noalloc).  validate_config applies
+// pa_create's checks.  forward_in_buffer runs one pass of pa_forward for cfg
+// without a handle: it lays the pass's workspace out in `base` (device
+// memory of `capacity` bytes), clears the words that must start at zero with
+// launch_zero_words on the stream, and enqueues the pass; PA_ERR_SCRATCH when
+// the pass needs more than `capacity` bytes.  Nothing is allocated.
+pa_status validate_config(const pa_config *cfg);
+pa_status forward_in_buffer(const pa_config *cfg, int num_cus, void *base, size_t capacity, const void *query,
+                            const void *key_cache, const void *value_cache, const int32_t *block_tables,
+                            const int32_t *context_lens, const int32_t *q_seq_lens, int32_t batch,
+                            int32_t num_q_tokens, int32_t max_q_seq_len, void *out, float *lse, void *stream);
+hipError_t launch_zero_words(uint32_t *p, long long n, hipStream_t s);
 // Measurement: a plain streaming read of `bytes` (a multiple of 16) by `workgroups`
 // workgroups, one word per workgroup written to sink.
 hipError_t launch_read_probe(const void *src, long long bytes, uint32_t *sink, int workgroups, hipStream_t s);
