@@ -160,7 +160,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
     const uint16_t *__restrict__ vg = (const uint16_t *)p.value_cache;
     uint16_t *__restrict__ og = (uint16_t *)p.out;
     const int G = p.group;
-    const int H = p.head_num;
     const int bs = p.block_size;
     const int bsh = p.bs_shift;
     const size_t row_stride = (size_t)p.kv_head_num * D;
@@ -196,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
         for (int r = 0; r < RP; ++r) {
             const int t = t0 + r / G;
             if (r < rows && t < p.num_q_tokens) {
-                const uint16_t *src = qg + ((size_t)t * H + g * G + r % G) * D;
+                const uint16_t *src = qg + head_row(p, t, g, r) * D;
                 const u32x4 a = *(const u32x4 *)(src + d0), c = *(const u32x4 *)(src + d1);
                 qr[r][0] = a.x; qr[r][1] = a.y; qr[r][2] = a.z; qr[r][3] = a.w;
                 qr[r][4] = c.x; qr[r][5] = c.y; qr[r][6] = c.z; qr[r][7] = c.w;
@@ -236,8 +235,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
         int okA = 0, okB = 0;   // bit t: token t of the buffered chunk is visible and readable
 #define PA_FETCH_BIDS(c_)                                                         \
         _Pragma("unroll") for (int t = 0; t < TL; ++t) {                          \
-            const int blk = div_bs((c_) * CT + t * NG + grp, bs, bsh);            \
-            bid[t] = bt[blk < nblk ? blk : nblk - 1];                             \
+            bid[t] = bt[bt_column((c_) * CT + t * NG + grp, bs, bsh, nblk)];      \
         }
 #define PA_LOAD_CHUNK(kregs_, vregs_, okm_, c_)                                   \
         okm_ = 0;                                                                 \
@@ -247,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
             const bool ok = j < nvis && inb;                                      \
             err |= (j < nvis && !inb) ? (uint32_t)PA_DEVERR_BLOCK_ID : 0u;        \
             okm_ |= ok ? (1 << t) : 0;                                            \
-            const size_t off = ok ? ((size_t)bid[t] * bs + mod_bs(j, bs, bsh)) * row_stride + head_off : 0; \
+            const size_t off = kv_row_elem(ok, bid[t], j, bs, bsh, row_stride, head_off); \
             kregs_[t][0] = *(const u32x4 *)(kg + off + d0);                       \
             kregs_[t][1] = *(const u32x4 *)(kg + off + d1);                       \
             vregs_[t][0] = *(const u32x4 *)(vg + off + d0);                       \
@@ -393,7 +391,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
         slot_treduce<NQ, 32, L>(flat, lane);
         // lane holds quantities q = (NQ / NG) * grp + k: row q / 16, element q % 16
         constexpr int PER = NQ / NG;
-        const int unit = (b * p.kv_head_num + g) * p.max_tiles;
         // row statistics of row r (wave-uniform values, lane-dependent r)
         auto row_stat = [&](int r, float &Mr, float &Lr) __attribute__((always_inline)) {
             Mr = m_all[0];
@@ -415,8 +412,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
                     float Mr, Lr;
                     row_stat(r, Mr, Lr);
                     const float inv = Lr > 0.f ? 1.f / Lr : 0.f;
-                    const int col = e < 8 ? d0 + e : d1 + e - 8;
-                    uint16_t *dst = og + ((size_t)t * H + g * G + r % G) * D + col;
+                    const int col = lane_col(e, d0, d1);
+                    uint16_t *dst = og + head_row(p, t, g, r) * D + col;
                     if constexpr (W == 8) {
                         uint4 o;
                         o.x = (uint32_t)to_bits<DT>(flat[k0] * inv) | ((uint32_t)to_bits<DT>(flat[k0 + 1] * inv) << 16);
@@ -430,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
                             dst[k] = to_bits<DT>(flat[k0 + k] * inv);
                     }
                     if (e == 0 && kq == 0 && p.lse)
-                        p.lse[(size_t)t * H + g * G + r % G] =
+                        p.lse[head_row(p, t, g, r)] =
                             Lr > 0.f ? (Mr + log2f(Lr)) * 0.69314718055994531f : -INFINITY;
                 }
             }
@@ -441,8 +438,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p)
             for (int k = 0; k < PER; ++k) {
                 const int q = PER * grp + k;
                 const int r = q / 16, e = q % 16;
-                const int col = e < 8 ? d0 + e : d1 + e - 8;
-                part[r * D + col] = flat[k];
+                part[r * D + lane_col(e, d0, d1)] = flat[k];
             }
             if (lane < RP) {
                 float Mr, Lr;

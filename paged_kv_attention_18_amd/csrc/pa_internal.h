@@ -172,7 +172,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // position prefix + i, prefix = max(0, kv - qlen)): j in [row_lo, row_hi).
 // No mask: [0, kv); causal: j <= prefix + i; band: prefix + i - win_left <=
 // j <= prefix + i + win_right (win_right = 0 in causal mode).
-__device__ __forceinline__ int row_hi(const Params &p, int kv, int prefix, int i)
+__host__ __device__ __forceinline__ int row_hi(const Params &p, int kv, int prefix, int i)
 {
     if (!p.causal)
         return kv;
@@ -180,7 +180,7 @@ __device__ __forceinline__ int row_hi(const Params &p, int kv, int prefix, int i
     return lim < kv ? lim : kv;
 }
 
-__device__ __forceinline__ int row_lo(const Params &p, int prefix, int i)
+__host__ __device__ __forceinline__ int row_lo(const Params &p, int prefix, int i)
 {
     if (!p.band)
         return 0;
@@ -191,7 +191,7 @@ __device__ __forceinline__ int row_lo(const Params &p, int prefix, int i)
 // The same with the mask kind fixed at compile time (BAND false: no lower
 // bound, and the upper one of the causal mask).
 template <bool BAND>
-__device__ __forceinline__ int row_hi_t(const Params &p, int kv, int prefix, int i)
+__host__ __device__ __forceinline__ int row_hi_t(const Params &p, int kv, int prefix, int i)
 {
     if (!p.causal)
         return kv;
@@ -200,7 +200,7 @@ __device__ __forceinline__ int row_hi_t(const Params &p, int kv, int prefix, int
 }
 
 template <bool BAND>
-__device__ __forceinline__ int row_lo_t(const Params &p, int prefix, int i)
+__host__ __device__ __forceinline__ int row_lo_t(const Params &p, int prefix, int i)
 {
     if constexpr (!BAND)
         return 0;
@@ -208,7 +208,7 @@ __device__ __forceinline__ int row_lo_t(const Params &p, int prefix, int i)
     return lo > 0 ? lo : 0;
 }
 
-__device__ __forceinline__ int seq_prefix(int kv, int qlen)
+__host__ __device__ __forceinline__ int seq_prefix(int kv, int qlen)
 {
     return kv - qlen > 0 ? kv - qlen : 0;
 }
@@ -217,17 +217,17 @@ __device__ __forceinline__ int seq_prefix(int kv, int qlen)
 // the limit of row r1, the largest.
 // Quotients the planner takes many times per piece, as shifts where the
 // divisor is a power of 2 (x >= 0 there; the divisions otherwise).
-__device__ __forceinline__ int div_group(const Params &p, int x)
+__host__ __device__ __forceinline__ int div_group(const Params &p, int x)
 {
     return (p.group_shift >= 0 && x >= 0) ? x >> p.group_shift : x / p.group;
 }
 
-__device__ __forceinline__ int div_chunk(const Params &p, int x)
+__host__ __device__ __forceinline__ int div_chunk(const Params &p, int x)
 {
     return (p.chunk_shift >= 0 && x >= 0) ? x >> p.chunk_shift : x / p.chunk;
 }
 
-__device__ __forceinline__ int tile_nvis(const Params &p, int kv, int qlen, int r1)
+__host__ __device__ __forceinline__ int tile_nvis(const Params &p, int kv, int qlen, int r1)
 {
     return row_hi(p, kv, seq_prefix(kv, qlen), div_group(p, r1));
 }
@@ -235,12 +235,12 @@ __device__ __forceinline__ int tile_nvis(const Params &p, int kv, int qlen, int 
 // The row tile qt of (b, g) covers chunks [first, first + count) of its
 // sequence: from the chunk holding the lowest visible token of its first
 // row (0 unless banded) to the one holding the last token its last row sees.
-__device__ __forceinline__ int unit_first_chunk(const Params &p, int kv, int qlen, int qt)
+__host__ __device__ __forceinline__ int unit_first_chunk(const Params &p, int kv, int qlen, int qt)
 {
     return div_chunk(p, row_lo(p, seq_prefix(kv, qlen), div_group(p, qt * p.rows_per_tile)));
 }
 
-__device__ __forceinline__ int unit_chunks(const Params &p, int kv, int qlen, int qt)
+__host__ __device__ __forceinline__ int unit_chunks(const Params &p, int kv, int qlen, int qt)
 {
     if (p.sparse)   // the entries of the query token's list
         return div_chunk(p, p.topk + p.chunk - 1);
@@ -301,14 +301,47 @@ __device__ __forceinline__ float hi_f32(uint32_t w)
         return __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
-__device__ __forceinline__ int div_bs(int j, int bs, int shift)
+__host__ __device__ __forceinline__ int div_bs(int j, int bs, int shift)
 {
     return shift >= 0 ? (j >> shift) : (j / bs);
 }
 
-__device__ __forceinline__ int mod_bs(int j, int bs, int shift)
+__host__ __device__ __forceinline__ int mod_bs(int j, int bs, int shift)
 {
     return shift >= 0 ? (j & (bs - 1)) : (j % bs);
+}
+
+// Addressing of the VALU decode kernel, shared with a host check of its
+// bounds.  Row r of unit (b, g) is query head g * G + r % G of packed token
+// t = t0 + r / G; head_row is its row index in the [T, H] query, output and
+// lse layouts.
+__host__ __device__ __forceinline__ size_t head_row(const Params &p, int t, int g, int r)
+{
+    return (size_t)t * p.head_num + (size_t)g * p.group + (size_t)(r % p.group);
+}
+
+// Block-table column read for token j, clamped to the nblk blocks the unit's
+// rows see (always a valid column, whatever j).
+__host__ __device__ __forceinline__ int bt_column(int j, int bs, int bsh, int nblk)
+{
+    const int blk = div_bs(j, bs, bsh);
+    return blk < nblk ? blk : nblk - 1;
+}
+
+// Element offset of token j's row of the KV head at head_off in a
+// [num_blocks, bs, Hkv, D] cache (row_stride = Hkv * D); 0 (block 0, slot 0)
+// for a token that is not loaded (not visible, or a bad block id).
+__host__ __device__ __forceinline__ size_t kv_row_elem(bool ok, int bid, int j, int bs, int bsh, size_t row_stride,
+                                                       size_t head_off)
+{
+    return ok ? ((size_t)bid * bs + mod_bs(j, bs, bsh)) * row_stride + head_off : 0;
+}
+
+// Output column of accumulator element e (< 16) of a lane whose two 8-element
+// pieces start at d0 and d1.
+__host__ __device__ __forceinline__ int lane_col(int e, int d0, int d1)
+{
+    return e < 8 ? d0 + e : d1 + e - 8;
 }
 
 // Cross-lane moves.  pair_swap<D>: the value of the partner lane in the
@@ -436,7 +469,7 @@ __device__ __forceinline__ float group_sum(float v)
 
 // Workgroup index with consecutive logical indices on the same XCD: the
 // dispatcher deals workgroups round-robin over the 8 XCDs.
-__device__ __forceinline__ int xcd_logical_index(int bid, int nwg)
+__host__ __device__ __forceinline__ int xcd_logical_index(int bid, int nwg)
 {
     if (nwg % 8 != 0)
         return bid;
@@ -450,12 +483,16 @@ __device__ __forceinline__ int xcd_logical_index(int bid, int nwg)
 // flight, so waiting for them never waits for those.
 typedef __attribute__((address_space(4))) const int32_t c_i32;
 
-__device__ __forceinline__ int sload(const int32_t *ptr, size_t i)
+__host__ __device__ __forceinline__ int sload(const int32_t *ptr, size_t i)
 {
+#if defined(__HIP_DEVICE_COMPILE__)
     const uint64_t a = (uint64_t)(uintptr_t)(ptr + i);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     return *(const c_i32 *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+#else
+    return ptr[i];   // host builds of the planning code (bounds checks)
+#endif
 }
 
 struct Cursor {
@@ -465,14 +502,14 @@ struct Cursor {
     int item;            // global index of (unit, c)
 };
 
-__device__ __forceinline__ int seq_tiles(const Params &p, int qlen)
+__host__ __device__ __forceinline__ int seq_tiles(const Params &p, int qlen)
 {
     const int x = qlen * p.group + p.rows_per_tile - 1;
     return (p.tile_shift >= 0 && x >= 0) ? x >> p.tile_shift : x / p.rows_per_tile;
 }
 
 // Position the cursor at item `item`, which lies in sequence b.
-__device__ __forceinline__ void cursor_seek(const Params &p, Cursor &cu, int b, int item)
+__host__ __device__ __forceinline__ void cursor_seek(const Params &p, Cursor &cu, int b, int item)
 {
     const int kv = sload(p.ws.kvlen, b);
     const int ql = sload(p.ws.qlen, b);
@@ -497,7 +534,7 @@ __device__ __forceinline__ void cursor_seek(const Params &p, Cursor &cu, int b, 
 
 // Move to the first chunk of the next unit (skipping sequences without
 // rows); the caller has already advanced cu.item past the current unit.
-__device__ __forceinline__ void cursor_next_unit(const Params &p, Cursor &cu)
+__host__ __device__ __forceinline__ void cursor_next_unit(const Params &p, Cursor &cu)
 {
     cu.c = 0;
     if (++cu.qt >= cu.ntile) {
@@ -517,7 +554,7 @@ __device__ __forceinline__ void cursor_next_unit(const Params &p, Cursor &cu)
 
 // The item range of piece w (balanced mode) or of the unit of workgroup w
 // (no-split mode); returns false if it has none.
-__device__ __forceinline__ bool wg_range(const Params &p, int w, Cursor &cu, int &end)
+__host__ __device__ __forceinline__ bool wg_range(const Params &p, int w, Cursor &cu, int &end)
 {
     const int W = sload(p.ws.hdr, 0);
     const int per = sload(p.ws.hdr, 1);
@@ -570,7 +607,7 @@ __device__ __forceinline__ int wave_scan(int v, int lane)
 }
 
 // Longest context the block table can address.
-__device__ __forceinline__ int seq_cap(const Params &p)
+__host__ __device__ __forceinline__ int seq_cap(const Params &p)
 {
     const int64_t cap64 = (int64_t)p.max_blocks * p.block_size;
     return cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
@@ -578,7 +615,7 @@ __device__ __forceinline__ int seq_cap(const Params &p)
 
 // Clamps one sequence's lengths into range; returns the error bits of what
 // was out of range.
-__device__ __forceinline__ uint32_t sanitize_seq(const Params &p, int cap, int &kv, int &ql)
+__host__ __device__ __forceinline__ uint32_t sanitize_seq(const Params &p, int cap, int &kv, int &ql)
 {
     uint32_t err = 0;
     if (kv < 0) {
@@ -603,7 +640,7 @@ __device__ __forceinline__ uint32_t sanitize_seq(const Params &p, int cap, int &
 }
 
 // Items of one (sequence, KV head): the chunks of all its row tiles.
-__device__ __forceinline__ int seq_items_per_group(const Params &p, int kv, int ql)
+__host__ __device__ __forceinline__ int seq_items_per_group(const Params &p, int kv, int ql)
 {
     const int ntile = seq_tiles(p, ql);
     int ipg = 0;
@@ -619,7 +656,7 @@ __device__ __forceinline__ int seq_items_per_group(const Params &p, int kv, int 
 // the unit began in piece k - 1 (a unit cut several times is listed once).
 // With `tp` (the sequence's items per KV head before each of its row tiles,
 // tp[0] = 0) the row tile is found by bisection, else by walking the tiles.
-__device__ __forceinline__ Cursor piece_start(const Params &p, int k, int s, int s_prev, int b, int kv, int ql,
+__host__ __device__ __forceinline__ Cursor piece_start(const Params &p, int k, int s, int s_prev, int b, int kv, int ql,
                                               int ipg, int wsb, int t0, bool write, const int *tp = nullptr)
 {
     int local = s - wsb;

@@ -158,3 +158,23 @@ def test_piece_map_host_invariants(tmp_path):
                    check=True, capture_output=True, text=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
+
+
+def test_valu_decode_addresses_in_bounds_host(tmp_path):
+    """The VALU decode kernel's addressing and the planning it runs on,
+    compiled for the host from the library's own header: for the causal case
+    whose GPU run once faulted and a seeded sweep (causal and unmasked,
+    malformed lengths and block ids included), every query, cache, table,
+    output, lse and partial access of every lane stays inside its buffer
+    (tests/decode_addr_host.cpp)."""
+    hipcc = "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not installed")
+    src = os.path.join(ROOT, "tests", "decode_addr_host.cpp")
+    exe = str(tmp_path / "decode_addr_host")
+    csrc = os.path.join(ROOT, "paged_kv_attention_18_amd", "csrc")
+    subprocess.run([hipcc, "-x", "hip", "--offload-arch=gfx950", "-O2", "-std=c++17",
+                    "-I", os.path.join(ROOT, "include"), "-I", csrc, src, "-o", exe],
+                   check=True, capture_output=True, text=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
