@@ -273,18 +273,13 @@ void tile_kernel(Params p)
     static_assert(LW * (S - 2) < 64, "vmcnt range");
     static_assert(!SH || DV <= DK, "V inside the K row");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t sK0[KT * RBK];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV0[VTB];
-    __shared__ __attribute__((aligned(1024))) uint8_t sK1[KT * RBK];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV1[VTB];
-    __shared__ __attribute__((aligned(1024))) uint8_t sK2[S > 2 ? KT * RBK : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV2[S > 2 ? VTB : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t sK3[S > 3 ? KT * RBK : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV3[S > 3 ? VTB : 16];
-    __shared__ __attribute__((aligned(256))) uint8_t sM0[SLB];
-    __shared__ __attribute__((aligned(256))) uint8_t sM1[SLB];
-    __shared__ __attribute__((aligned(256))) uint8_t sM2[S > 2 ? SLB : 16];
-    __shared__ __attribute__((aligned(256))) uint8_t sM3[S > 3 ? SLB : 16];
+    // the S stages of the ring, each a K tile, a V tile (none with one K/V
+    // cache) and a mask slab (tensor mask only)
+    constexpr int VSB = SH ? 0 : VTB;
+    constexpr int MSB = TMASK ? SLB : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t sK[S * KT * RBK];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV[SH ? 16 : S * VSB];
+    __shared__ __attribute__((aligned(256))) uint8_t sM[TMASK ? S * MSB : 16];
     // destination of the padding loads that keep every wave's count at LW
     __shared__ __attribute__((aligned(1024))) uint8_t sJunk[PAD ? 1024 : 16];
     // sparse: the cache row of every list entry of the segment (-1: skipped)
@@ -457,6 +452,8 @@ void tile_kernel(Params p)
         const int32_t *lst = SPARSE ? p.topk_idx + ((size_t)(t0 + itok) * p.kv_head_num + g) * p.topk : nullptr;
         int srow = 0;
         uint32_t sbits = 0;
+        // sparse: the visible-entry bits of the chunks issued and not yet
+        // computed, oldest first
         uint32_t smask[S];
         auto fetch_bids = [&](int c) __attribute__((always_inline)) {
             if constexpr (SPARSE) {
@@ -553,9 +550,13 @@ void tile_kernel(Params p)
             }
         };
 
-        // one chunk from (kb, vb): S^T, mask, online softmax, PV
-        auto compute = [&](const lds_u8 *kb, const lds_u8 *vb, const lds_u8 *mb_, int c, uint32_t vbits)
+        // one chunk from (kb, vb): S^T, mask, online softmax, PV.  NM: the
+        // chunk needs the per-element mask (it reaches past the visible range
+        // of some row of the tile); the other chunks take an instance
+        // without any mask or tail code.
+        auto compute = [&](auto nm, const lds_u8 *kb, const lds_u8 *vb, const lds_u8 *mb_, int c, uint32_t vbits)
                            __attribute__((always_inline)) {
+            constexpr bool NM = decltype(nm)::value;
             if (!wave_active)
                 return;
             const int jb = c * KT;
@@ -607,7 +608,6 @@ void tile_kernel(Params p)
                     }
                 }
             }
-            const bool need_mask = SPARSE || jb + KT > min_lim || (BAND && jb < max_lo);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 float mx = -INFINITY;
@@ -615,7 +615,7 @@ void tile_kernel(Params p)
                 for (int n = 0; n < NTT; ++n) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        if (need_mask) {
+                        if constexpr (NM) {
                             const int j = jb + 16 * n + 4 * lg + r;
                             const bool vis = SPARSE ? ((vbits >> (16 * n + 4 * lg + r)) & 1u) != 0
                                                     : (j < lim[mb] && (!BAND || j >= lo_r[mb]));
@@ -655,7 +655,9 @@ void tile_kernel(Params p)
             }
             // V rows of tokens outside [lo_tile, nvis) may be stale or
             // unwritten cache slots: zero their operand halves (P is 0 there).
-            const bool tail = SPARSE || jb + KT > nvis || (BAND && jb < lo_tile);
+            // (Such a chunk always takes the masked instance: nvis and lo_tile
+            // bound the visible range of every row.)
+            const bool tail = NM && (SPARSE || jb + KT > nvis || (BAND && jb < lo_tile));
             auto tok_ok = [&](int t) __attribute__((always_inline)) {
                 if constexpr (SPARSE)
                     return ((vbits >> (t - jb)) & 1u) != 0;
@@ -725,50 +727,35 @@ void tile_kernel(Params p)
             }
         };
 
-        auto kbuf = [&](auto st) __attribute__((always_inline)) -> lds_u8 * {
-            if constexpr (decltype(st)::value == 0)
-                return (lds_u8 *)sK0;
-            else if constexpr (decltype(st)::value == 1)
-                return (lds_u8 *)sK1;
-            else if constexpr (decltype(st)::value == 2)
-                return (lds_u8 *)sK2;
-            else
-                return (lds_u8 *)sK3;
+        auto kbuf = [&](int st) __attribute__((always_inline)) -> lds_u8 * {
+            return (lds_u8 *)sK + st * (KT * RBK);
         };
-        auto mbuf = [&](auto st) __attribute__((always_inline)) -> lds_u8 * {
-            if constexpr (decltype(st)::value == 0)
-                return (lds_u8 *)sM0;
-            else if constexpr (decltype(st)::value == 1)
-                return (lds_u8 *)sM1;
-            else if constexpr (decltype(st)::value == 2)
-                return (lds_u8 *)sM2;
-            else
-                return (lds_u8 *)sM3;
-        };
-        auto vbuf = [&](auto st) __attribute__((always_inline)) -> lds_u8 * {
+        auto vbuf = [&](int st) __attribute__((always_inline)) -> lds_u8 * {
             if constexpr (SH)
                 return kbuf(st);
-            else if constexpr (decltype(st)::value == 0)
-                return (lds_u8 *)sV0;
-            else if constexpr (decltype(st)::value == 1)
-                return (lds_u8 *)sV1;
-            else if constexpr (decltype(st)::value == 2)
-                return (lds_u8 *)sV2;
             else
-                return (lds_u8 *)sV3;
+                return (lds_u8 *)sV + st * VSB;
         };
-        // one pipeline step: chunk c sits in stage st
-        auto step = [&](auto st, int c) __attribute__((always_inline)) {
-            constexpr int ST = decltype(st)::value;
-            constexpr int NX = (ST + S - 1) % S;   // stage of chunk c + S - 1
+        auto mbuf = [&](int st) __attribute__((always_inline)) -> lds_u8 * {
+            return (lds_u8 *)sM + st * MSB;
+        };
+        // one pipeline step: chunk c sits in stage st (NM: the chunk takes
+        // the masked instance of compute)
+        auto step = [&](auto nm, int st, int c) __attribute__((always_inline)) {
+            const int nx = st == 0 ? S - 1 : st - 1;   // stage of chunk c + S - 1
             wait_ahead<LW, S - 2>(c1 - 1 - c);     // this wave's loads of chunk c are in LDS
-            __builtin_amdgcn_s_barrier();          // ... and every wave's; stage NX is free
+            __builtin_amdgcn_s_barrier();          // ... and every wave's; stage nx is free
             if (c + S - 1 < c1) {
-                issue(c + S - 1, kbuf(std::integral_constant<int, NX>{}), vbuf(std::integral_constant<int, NX>{}),
-                      mbuf(std::integral_constant<int, NX>{}));
-                smask[NX] = sbits;
+                issue(c + S - 1, kbuf(nx), vbuf(nx), mbuf(nx));
+                if constexpr (SPARSE)
+                    smask[S - 1] = sbits;
             }
-            compute(kbuf(st), vbuf(st), mbuf(st), c, smask[ST]);
+            compute(nm, kbuf(st), vbuf(st), mbuf(st), c, smask[0]);
+            if constexpr (SPARSE) {
+#pragma unroll
+                for (int i = 0; i + 1 < S; ++i)
+                    smask[i] = smask[i + 1];
+            }
             if (c + S < c1)
                 fetch_bids(c + S);                 // scalar loads land during the next wait
         };
@@ -799,43 +786,39 @@ void tile_kernel(Params p)
             __syncthreads();
         }
         fetch_bids(c0);
-        issue(c0, kbuf(std::integral_constant<int, 0>{}), vbuf(std::integral_constant<int, 0>{}),
-              mbuf(std::integral_constant<int, 0>{}));
+        issue(c0, kbuf(0), vbuf(0), mbuf(0));
         smask[0] = sbits;
-        if constexpr (S > 2) {
-            if (c0 + 1 < c1) {
-                fetch_bids(c0 + 1);
-                issue(c0 + 1, kbuf(std::integral_constant<int, 1>{}), vbuf(std::integral_constant<int, 1>{}),
-                      mbuf(std::integral_constant<int, 1>{}));
-                smask[1] = sbits;
-            }
-        }
-        if constexpr (S > 3) {
-            if (c0 + 2 < c1) {
-                fetch_bids(c0 + 2);
-                issue(c0 + 2, kbuf(std::integral_constant<int, 2>{}), vbuf(std::integral_constant<int, 2>{}),
-                      mbuf(std::integral_constant<int, 2>{}));
-                smask[2] = sbits;
+#pragma unroll
+        for (int i = 1; i + 1 < S; ++i) {
+            if (c0 + i < c1) {
+                fetch_bids(c0 + i);
+                issue(c0 + i, kbuf(i), vbuf(i), mbuf(i));
+                smask[i] = sbits;
             }
         }
         if (c0 + S - 1 < c1)
             fetch_bids(c0 + S - 1);
-        for (int c = c0; c < c1; c += S) {
-            step(std::integral_constant<int, 0>{}, c);
-            if (c + 1 >= c1)
-                break;
-            step(std::integral_constant<int, 1>{}, c + 1);
-            if constexpr (S > 2) {
-                if (c + 2 >= c1)
-                    break;
-                step(std::integral_constant<int, 2>{}, c + 2);
-            }
-            if constexpr (S > 3) {
-                if (c + 3 >= c1)
-                    break;
-                step(std::integral_constant<int, 3>{}, c + 3);
-            }
+        // A chunk needs the per-element mask where it reaches past the
+        // visible range of the tile's first row (c KT + KT > min_lim: the
+        // causal diagonal and the tail of the context) or, with the band
+        // mask, before the start of its last row's window (c KT < max_lo).
+        // Those chunks are a leading and a trailing run of the segment; the
+        // chunks between take the unmasked instance.  Three loops, each with
+        // one instance of compute, keep the register pressure of one.
+        int cu0 = c0, cu1 = c0;   // the unmasked run [cu0, cu1)
+        if constexpr (!SPARSE) {
+            cu0 = BAND ? (max_lo + KT - 1) / KT : c0;
+            cu0 = cu0 < c0 ? c0 : (cu0 > c1 ? c1 : cu0);
+            cu1 = min_lim > 0 ? min_lim / KT : 0;
+            cu1 = cu1 < cu0 ? cu0 : (cu1 > c1 ? c1 : cu1);
         }
+        int c = c0, st = 0;
+        for (; c < cu0; ++c, st = st + 1 == S ? 0 : st + 1)
+            step(std::true_type{}, st, c);
+        for (; c < cu1; ++c, st = st + 1 == S ? 0 : st + 1)
+            step(std::false_type{}, st, c);
+        for (; c < c1; ++c, st = st + 1 == S ? 0 : st + 1)
+            step(std::true_type{}, st, c);
 
         // -------------------------------------------------------- finalise
         if (wave_active) {
