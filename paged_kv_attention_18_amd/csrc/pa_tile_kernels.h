@@ -272,6 +272,8 @@ void tile_kernel(Params p)
     static_assert(NW % CS == 0 && ND % 4 == 0 && S >= 2 && S <= 4, "split");
     static_assert(LW * (S - 2) < 64, "vmcnt range");
     static_assert(!SH || DV <= DK, "V inside the K row");
+    // explicit interleave of operand reads and MFMAs (128-row tiles)
+    constexpr bool SCHED = MB == 2;
 
     // the S stages of the ring, each a K tile, a V tile (none with one K/V
     // cache) and a mask slab (tensor mask only)
@@ -566,14 +568,38 @@ void tile_kernel(Params p)
 #pragma unroll
                 for (int n = 0; n < NTT; ++n)
                     sacc[mb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (SCHED) {
+                // the K fragments of slice ks + 1 are read while slice ks is
+                // multiplied (the scheduler, left alone, waits for each read)
+                u32x4 ka[2][NTT];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+                for (int n = 0; n < NTT; ++n)
+                    ka[0][n] = *(const lds_u32x4 *)(kb + koE + 16 * n * RBK);
 #pragma unroll
-                for (int n = 0; n < NTT; ++n) {
-                    const u32x4 a = *(const lds_u32x4 *)(kb + ((ks & 1) ? koO : koE) + 16 * n * RBK + 64 * ks);
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (ks + 1 < KS) {
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        sacc[mb][n] = Mfma<DT>::run(a, qb[mb][ks], sacc[mb][n]);
+                        for (int n = 0; n < NTT; ++n)
+                            ka[(ks + 1) & 1][n] =
+                                *(const lds_u32x4 *)(kb + (((ks + 1) & 1) ? koO : koE) + 16 * n * RBK + 64 * (ks + 1));
+                    }
+#pragma unroll
+                    for (int n = 0; n < NTT; ++n)
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            sacc[mb][n] = Mfma<DT>::run(ka[ks & 1][n], qb[mb][ks], sacc[mb][n]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                    for (int n = 0; n < NTT; ++n) {
+                        const u32x4 a = *(const lds_u32x4 *)(kb + ((ks & 1) ? koO : koE) + 16 * n * RBK + 64 * ks);
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            sacc[mb][n] = Mfma<DT>::run(a, qb[mb][ks], sacc[mb][n]);
+                    }
                 }
             }
             if constexpr (TMASK) {
@@ -708,20 +734,50 @@ void tile_kernel(Params p)
                                 vm[2 * h + e] = (tok_ok(tb + 16 * h + 2 * e) ? 0xffffu : 0u) |
                                                 (tok_ok(tb + 16 * h + 2 * e + 1) ? 0xffff0000u : 0u);
                     }
-#pragma unroll
-                    for (int nd = 0; nd < ND; ++nd) {
+                    auto vread = [&](int nd) __attribute__((always_inline)) -> u32x4 {
                         const int off = 32 * kk * RBVL + 32 * NVO * (nd / NVO);
                         const v4i16 b0 =
                             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + off));
                         const v4i16 b1 =
                             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + off + 16 * RBVL));
                         const uint2 lo = __builtin_bit_cast(uint2, b0), hi = __builtin_bit_cast(uint2, b1);
-                        u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
-                        if (tail)
-                            bv &= vm;
+                        return u32x4{lo.x, lo.y, hi.x, hi.y};
+                    };
+                    if constexpr (SCHED && ND % 4 == 0) {
+                        // the V fragments of 4 column tiles are read while the
+                        // previous 4 are multiplied
+                        u32x4 vf[2][4];
 #pragma unroll
-                        for (int mb = 0; mb < MB; ++mb)
-                            oacc[mb][nd] = Mfma<DT>::run(pa[mb], bv, oacc[mb][nd]);
+                        for (int i = 0; i < 4; ++i)
+                            vf[0][i] = vread(i);
+#pragma unroll
+                        for (int q = 0; q < ND / 4; ++q) {
+                            if (q + 1 < ND / 4) {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    vf[(q + 1) & 1][i] = vread(4 * (q + 1) + i);
+                            }
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                u32x4 bv = vf[q & 1][i];
+                                if (tail)
+                                    bv &= vm;
+#pragma unroll
+                                for (int mb = 0; mb < MB; ++mb)
+                                    oacc[mb][4 * q + i] = Mfma<DT>::run(pa[mb], bv, oacc[mb][4 * q + i]);
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    } else {
+#pragma unroll
+                        for (int nd = 0; nd < ND; ++nd) {
+                            u32x4 bv = vread(nd);
+                            if (tail)
+                                bv &= vm;
+#pragma unroll
+                            for (int mb = 0; mb < MB; ++mb)
+                                oacc[mb][nd] = Mfma<DT>::run(pa[mb], bv, oacc[mb][nd]);
+                        }
                     }
                 }
             }
