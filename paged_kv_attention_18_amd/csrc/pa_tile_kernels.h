@@ -442,9 +442,13 @@ void tile_kernel(Params p)
             lsum[mb] = 0.f;
         }
 
-        // Block id of each 16-token group of a chunk (clamped table index;
-        // range-checked when used).
-        int bid[NTT];
+        // Block id and slot of each 16-token group of the chunk fetched last
+        // (clamped table index; the id is range-checked when used).  Chunks
+        // are fetched in order, so the block and slot of the next fetch
+        // (f_blk, f_slot) advance by additions; a 16-token group never
+        // crosses a block (block_size % 16 == 0).
+        int bid[NTT], bslot[NTT];
+        int f_blk = 0, f_slot = 0;
         // sparse: the tile's query token, its list, the tokens it may see
         // (c < lim_c), and for the fetched chunk the cache row of entry t in
         // lane t (srow) and the entries that select a visible token (sbits)
@@ -464,11 +468,21 @@ void tile_kernel(Params p)
                 sbits = (uint32_t)__ballot(rv >= 0);
                 srow = rv >= 0 ? rv : 0;
             } else {
+                (void)c;
+                // (wave-uniform: read once into scalar registers)
+                int blk = __builtin_amdgcn_readfirstlane(f_blk), slot = __builtin_amdgcn_readfirstlane(f_slot);
 #pragma unroll
                 for (int q = 0; q < NTT; ++q) {
-                    const int blk = div_bs(c * KT + 16 * q, bs, bsh);
                     bid[q] = sload(bt, blk < nblk ? blk : nblk - 1);
+                    bslot[q] = slot;
+                    slot += 16;
+                    if (slot == bs) {
+                        slot = 0;
+                        ++blk;
+                    }
                 }
+                f_blk = blk;
+                f_slot = slot;
             }
         };
         // Issue the LDS loads of chunk c: exactly LW instructions per wave.
@@ -523,7 +537,7 @@ void tile_kernel(Params p)
                 const bool vis = j0 < nvis && (!BAND || j0 + 16 > lo_tile);
                 const bool inb = (unsigned)bid[q] < nb32;
                 err |= (vis && !inb) ? (uint32_t)PA_DEVERR_BLOCK_ID : 0u;
-                const size_t trow = (size_t)bid[q] * bs + mod_bs(j0, bs, bsh);
+                const size_t trow = (size_t)(uint32_t)bid[q] * (uint32_t)bs + (uint32_t)bslot[q];
                 const char *kbase = (vis && inb) ? kgh + trow * rsk : zg;
                 const char *vbase = (vis && inb) ? vgh + trow * rsv : zg;
                 // (the empty asm hides each 32-bit offset from loop-invariant
@@ -840,6 +854,10 @@ void tile_kernel(Params p)
             }
             wait_vm<0>();
             __syncthreads();
+        }
+        if constexpr (!SPARSE) {
+            f_blk = div_bs(c0 * KT, bs, bsh);
+            f_slot = c0 * KT - f_blk * bs;
         }
         fetch_bids(c0);
         issue(c0, kbuf(0), vbuf(0), mbuf(0));
