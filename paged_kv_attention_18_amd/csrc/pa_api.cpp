@@ -274,7 +274,6 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
         if (tiles > max_tiles)
             max_tiles = tiles;
     }
-    (void)max_tiles;
     h->max_partitions = max_p;
     h->max_partial_floats = max_floats;
     h->max_pieces = max_pieces;
@@ -294,6 +293,8 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
     const size_t zero_bytes = 16 * (size_t)cfg->kv_head_num * (size_t)(cfg->head_size_k > cfg->head_size_v ? cfg->head_size_k : cfg->head_size_v) * 2;
     const size_t o_zero = off; off = align(off + zero_bytes);
     const size_t o_part = off; off = align(off + 2 * max_slot_floats * sizeof(float));
+    const size_t o_tq = off;
+    off = align(off + (pa::kTqHeader + 2 * (size_t)B * cfg->kv_head_num * max_tiles) * sizeof(int32_t));
     h->ws_bytes = off;
     if (hipMalloc(&h->ws_base, h->ws_bytes) != hipSuccess) {
         delete h;
@@ -316,6 +317,7 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
     h->ws.err = (uint32_t *)(base + o_err);
     h->ws.zeros = base + o_zero;
     h->ws.partials = (float *)(base + o_part);
+    h->ws.tq = (int32_t *)(base + o_tq);
     *out = h;
     return PA_OK;
 }
@@ -448,6 +450,11 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
     p.pieces = p.no_split ? 0 : p.partitions * v.pieces_per_worker;
     p.partial_stride = (int32_t)partial_floats(v.rows_per_tile, c.head_size_v);
     p.tail_min = 0;
+    // The tile kernel may run the pass as whole row tiles from per-XCD
+    // queues; the planner decides from the lengths.
+    p.tile_order = (v.path == 1 && !p.no_split && !pa::tile_streaming(c.head_size_k, c.head_size_v, v.tile_variant))
+                       ? 1
+                       : 0;
     // The streaming kernel cuts its own pieces when the lengths fit in a
     // wave's registers: one launch fewer, and no wait on plan data when a
     // worker starts or moves to the next unit.
@@ -676,6 +683,7 @@ pa_status forward_in_buffer(const pa_config *cfg, int num_cus, void *base, size_
     const size_t o_wgb = take(ent * sizeof(int32_t));
     const size_t o_spl = take(ent * 8 * sizeof(int32_t));
     const size_t o_part = take(2 * N * (size_t)p.partial_stride * sizeof(float));
+    const size_t o_tq = take((kTqHeader + 2 * B * (size_t)cfg->kv_head_num * (size_t)p.max_tiles) * sizeof(int32_t));
     if (off > capacity)
         return PA_ERR_SCRATCH;
     char *b = (char *)base;
@@ -690,6 +698,7 @@ pa_status forward_in_buffer(const pa_config *cfg, int num_cus, void *base, size_
     p.ws.wg_b = (int32_t *)(b + o_wgb);
     p.ws.splits = (int32_t *)(b + o_spl);
     p.ws.partials = (float *)(b + o_part);
+    p.ws.tq = (int32_t *)(b + o_tq);
     // earlier calls leave other contents here: clear what must start at
     // zero with a fill kernel (no memset node if the caller captures a graph)
     const hipStream_t s = (hipStream_t)stream;

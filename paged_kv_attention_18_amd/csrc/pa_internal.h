@@ -44,7 +44,18 @@ struct Workspace {
     float *partials;     // [2 * N][R * (DV + 2)]
     const void *zeros;   // 16 token rows of zeros (K or V), read in place of a bad block
     uint32_t *err;       // device error word
+    int32_t *tq;         // whole-tile task queues (Params::tile_order): kTqHeader ints, then
+                         // 2 ints per task (b, g << 16 | qt), max_batch * Hkv * max_tiles tasks
 };
+
+// Whole-tile task queues, one per XCD (see plan_kernel): the header holds the
+// length and first task of each XCD's queue, then the mode.
+constexpr int kXcds = 8;
+constexpr int kTqLength = 8, kTqStart = 16, kTqMode = 24;
+constexpr int kTqHeader = 32;
+// Largest batch the planner builds the queues for (it ranks the sequences
+// by their work with one comparison per pair).
+constexpr int kTileOrderMaxBatch = 512;
 
 struct Params {
     const void *query;
@@ -91,6 +102,9 @@ struct Params {
     // Self-planning launches: smallest piece of the claimed tail in items
     // (0: one piece per worker, no tail).
     int32_t tail_min;
+    // The planner may run the pass as whole row tiles from per-XCD task
+    // queues instead of pieces (tile kernel, ws.tq sized for the pass).
+    int32_t tile_order;
     Workspace ws;
 };
 
@@ -846,6 +860,40 @@ __host__ __device__ __forceinline__ PieceMap self_piece_map(const Params &p, int
 __device__ __forceinline__ int grab_piece(const Params &p)
 {
     return p.partitions + __hip_atomic_fetch_add(p.ws.hdr + 3, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Whole-tile mode: task k (0, 1, ...) of workgroup w.  The workgroups w with
+// w % 8 == x (those the dispatcher deals to XCD x) take the tasks of queue
+// x in rounds of Lx (their number), with no atomics: in round k the l-th of
+// them (l = w / 8) takes position k Lx + l, or k Lx + Lx - 1 - l in odd
+// rounds (a snake, so that a worker that took a group's longest tile takes a
+// short one next).  Consecutive tasks of a queue -- the row tiles of one
+// (sequence, KV head) -- thus start together on consecutive workers of one
+// XCD in every round, as those workers finish their previous tiles, which
+// were alike, together.  Returns the task's index in the task array, or -1
+// when the workgroup has no task k.
+__device__ __forceinline__ int tile_task(const Params &p, int w, int nwg, int k)
+{
+    const int x = w % kXcds, l = w / kXcds;
+    const int lx = (nwg - x + kXcds - 1) / kXcds;
+    const int j = k * lx + ((k & 1) ? lx - 1 - l : l);
+    return j < sload(p.ws.tq, kTqLength + x) ? sload(p.ws.tq, kTqStart + x) + j : -1;
+}
+
+// The cursor of whole-tile task t: all chunks of row tile (b, g, qt).
+__device__ __forceinline__ void tile_task_cursor(const Params &p, int t, Cursor &cu, int &end)
+{
+    const int32_t *e = p.ws.tq + kTqHeader + 2 * (size_t)t;
+    const int b = sload(e, 0), gq = sload(e, 1);
+    const int kv = sload(p.ws.kvlen, b), ql = sload(p.ws.qlen, b);
+    cu.b = b;
+    cu.g = gq >> 16;
+    cu.qt = gq & 0xffff;
+    cu.c = 0;
+    cu.ntile = seq_tiles(p, ql);
+    cu.nch = unit_chunks(p, kv, ql, cu.qt);
+    cu.item = 0;
+    end = cu.nch;
 }
 
 #endif  // __HIPCC__

@@ -35,6 +35,73 @@ constexpr int kPlanPieces = 64;
 // piece bisects its sequence's tiles instead of walking them
 constexpr int kPlanLdsT = 8192;
 
+// The whole-tile queues (workgroup 0 of the plan kernel, every thread).
+// Sequences are ranked by their work (chunks per KV head, most first); the
+// (sequence, KV head) groups in that order are dealt to the XCDs in snake
+// order (0..7, 7..0, ...), which balances the XCDs' work; each XCD's queue
+// lists its groups in order, every group's row tiles together (last tile,
+// the longest under the causal mask, first).  Workers of one XCD take
+// consecutive tasks (tile_task), so the tiles of a group start together and
+// read their sequence's KV from that XCD's L2.
+__device__ void build_tile_queues(const Params &p, int *s_order, int *s_xtot, const int *s_ipg, const int *s_ql)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int B = p.batch, Hkv = p.kv_head_num;
+    for (int b = tid; b < B; b += kPlanThreads) {
+        const int w = s_ipg[b];
+        int r = 0;
+        for (int b2 = 0; b2 < B; ++b2) {
+            const int w2 = s_ipg[b2];
+            r += (w2 > w || (w2 == w && b2 < b)) ? 1 : 0;
+        }
+        s_order[r] = b;
+    }
+    __syncthreads();
+    const int NG = B * Hkv;
+    // group k of the order sits on XCD x = snake(k); the r-th group of XCD x
+    // is k = 8 r + (r even ? x : 7 - x)
+    auto tiles_of = [&](int x, int r, int &b, int &g) {
+        const int k = kXcds * r + ((r & 1) ? kXcds - 1 - x : x);
+        if (k >= NG)
+            return 0;
+        b = s_order[k / Hkv];
+        g = k % Hkv;
+        return seq_tiles(p, s_ql[b]);
+    };
+    if (wv < kXcds) {
+        int tot = 0;
+        for (int r0 = 0; kXcds * r0 < NG; r0 += 64) {
+            int b = 0, g = 0;
+            const int nt = tiles_of(wv, r0 + lane, b, g);
+            tot += __shfl(wave_scan(nt, lane), 63);
+        }
+        if (lane == 0)
+            s_xtot[wv] = tot;
+    }
+    __syncthreads();
+    if (wv < kXcds) {
+        int start = 0;
+        for (int x = 0; x < wv; ++x)
+            start += s_xtot[x];
+        int run = 0;
+        for (int r0 = 0; kXcds * r0 < NG; r0 += 64) {
+            int b = 0, g = 0;
+            const int nt = tiles_of(wv, r0 + lane, b, g);
+            const int inc = wave_scan(nt, lane);
+            int32_t *e = p.ws.tq + kTqHeader + 2 * (size_t)(start + run + inc - nt);
+            for (int t = 0; t < nt; ++t) {
+                e[2 * t] = b;
+                e[2 * t + 1] = (g << 16) | (nt - 1 - t);
+            }
+            run += __shfl(inc, 63);
+        }
+        if (lane == 0) {
+            p.ws.tq[kTqLength + wv] = s_xtot[wv];
+            p.ws.tq[kTqStart + wv] = start;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
 {
     constexpr int NWV = kPlanThreads / 64;
@@ -44,8 +111,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
     // each sequence's first row tile in s_tp, and per row tile the items per
     // KV head of its sequence before it
     __shared__ int s_toff[kPlanLdsB], s_tp[kPlanLdsT];
-    __shared__ int s_carry_q, s_carry_t, s_carry_w;
+    __shared__ int s_carry_q, s_carry_t, s_carry_w, s_lmax;
     __shared__ uint32_t s_err;
+    // whole-tile mode: the sequences in order of decreasing work, and the
+    // tiles each XCD's queue holds
+    __shared__ int s_order[kTileOrderMaxBatch], s_xtot[kXcds];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const bool lead = blockIdx.x == 0;
@@ -53,6 +123,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         s_carry_q = 0;
         s_carry_t = 0;
         s_carry_w = 0;
+        s_lmax = 0;
         s_err = 0;
     }
     __syncthreads();
@@ -92,12 +163,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         __syncthreads();
         const int t0 = s_wq[wv] + iq - ql;
         const int toff = s_wt[wv] + it - nt;
-        int ipg = 0;
+        int ipg = 0, lmax = 0;
         for (int qt = 0; qt < nt; ++qt) {
             if (toff + qt < kPlanLdsT)
                 s_tp[toff + qt] = ipg;
-            ipg += unit_chunks(p, kv, ql, qt);
+            const int n = unit_chunks(p, kv, ql, qt);
+            ipg += n;
+            lmax = n > lmax ? n : lmax;
         }
+        if (lmax > 0)
+            atomicMax(&s_lmax, lmax);
         const int items = ipg * p.kv_head_num;
         if (lead && b < p.batch) {
             p.ws.qlen[b] = ql;
@@ -137,6 +212,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
     }
     const int W = s_carry_w;
     const int per = p.no_split ? 0 : (W + p.pieces - 1) / p.pieces;
+    // Whole row tiles from per-XCD queues instead of pieces, where there are
+    // enough tiles for the workers and the longest is at most half a
+    // worker's share of the chunks (every workgroup decides alike, from the
+    // lengths).
+    const long long tiles = (long long)s_carry_t * p.kv_head_num;
+    const bool ordered = p.tile_order && !p.no_split && p.batch <= kTileOrderMaxBatch && W > 0 &&
+                         tiles >= 2LL * p.partitions && 2LL * s_lmax * p.partitions <= (long long)W;
     if (lead && tid == 0) {
         p.ws.cu_q[p.batch] = s_carry_q;
         p.ws.wsb[p.batch] = W;
@@ -170,7 +252,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         // Piece k starts at item k * pe, in the last sequence b with
         // wsb[b] <= k * pe.  Its split entry (entry k - 1) records the unit
         // that boundary k cuts, if it falls strictly inside one.
-        const int nk = (W + pe - 1) / pe < p.pieces ? (W + pe - 1) / pe : p.pieces;
+        const int nk = ordered ? 0 : ((W + pe - 1) / pe < p.pieces ? (W + pe - 1) / pe : p.pieces);
         for (int k = k0 + tid; k < k1 && k < nk; k += kPlanThreads) {
             const int s = k * pe;
             int lo = 0, hi = p.batch - 1;
@@ -191,10 +273,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
             const int t0 = lds ? s_t0[b] : p.ws.cu_q[b];
             (void)piece_start(p, k, s, s - pe, b, kv, ql, ipg, wsb_of(b), t0, true, table ? s_tp + s_toff[b] : nullptr);
         }
-        // boundaries past the last item
-        for (int k = max((W + pe - 1) / pe, k0) + tid; k < k1; k += kPlanThreads)
+        // boundaries past the last item (every boundary in whole-tile mode)
+        for (int k = max(nk, k0) + tid; k < k1; k += kPlanThreads)
             if (k > 0)
                 p.ws.splits[(size_t)(k - 1) * 8] = -1;
+    }
+    if (lead && p.tile_order) {
+        if (ordered)
+            build_tile_queues(p, s_order, s_xtot, s_ipg, s_ql);
+        if (tid == 0)
+            p.ws.tq[kTqMode] = ordered ? 1 : 0;
     }
     if (lead && tid == 0 && s_err)
         set_error(p.ws.err, s_err);

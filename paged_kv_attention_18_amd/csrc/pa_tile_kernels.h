@@ -299,9 +299,20 @@ void tile_kernel(Params p)
     int piece = xcd_logical_index(blockIdx.x, gridDim.x);
     Cursor cu;
     int end;
-    if (piece >= p.partitions || !wg_range(p, piece, cu, end))
-        return;
     __shared__ int s_piece;
+    // Whole-tile mode (the planner's choice for this pass): tasks come from
+    // the queue of this workgroup's XCD (the dispatcher deals workgroups
+    // round-robin over the XCDs), one whole row tile each (tile_task).
+    const bool ordered = p.tile_order && sload(p.ws.tq, kTqMode) != 0;
+    int task_k = 0;   // whole-tile mode: tasks taken so far
+    if (ordered) {
+        piece = tile_task(p, blockIdx.x, gridDim.x, task_k++);
+        if (piece < 0)
+            return;
+        tile_task_cursor(p, piece, cu, end);
+    } else if (piece >= p.partitions || !wg_range(p, piece, cu, end)) {
+        return;
+    }
 
     const uint16_t *__restrict__ qg = (const uint16_t *)p.query;
     const char *__restrict__ kg = (const char *)p.key_cache;
@@ -944,6 +955,15 @@ void tile_kernel(Params p)
             more = cu.b < p.batch;
         }
         if (!more) {
+            if (ordered) {
+                // the next whole tile, if any
+                piece = tile_task(p, blockIdx.x, gridDim.x, task_k++);
+                if (piece < 0)
+                    break;
+                tile_task_cursor(p, piece, cu, end);
+                first_seg = true;
+                continue;
+            }
             // this piece is done: take the next one, if any
             if (p.no_split || p.pieces <= p.partitions)
                 break;

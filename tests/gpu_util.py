@@ -42,7 +42,13 @@ def run_hip(p: synth.Problem, flags=0, num_partitions=0, att=None, lse=True):
     own = att is None
     if own:
         att = binding.for_problem(p, flags=flags, num_partitions=num_partitions)
-    o, l = binding.run_problem(att, p, return_lse=True)
+    # NaN-filled outputs: a row the kernels never write cannot pass on
+    # whatever the allocator's memory held
+    w = p.workload
+    out = torch.full((p.num_q_tokens, w.head_num, w.head_size_v), float("nan"), dtype=p.query.dtype,
+                     device=p.query.device)
+    lse = torch.full((p.num_q_tokens, w.head_num), float("nan"), dtype=torch.float32, device=p.query.device)
+    o, l = binding.run_problem(att, p, out=out, lse=lse)
     torch.cuda.synchronize()
     res = (o.to(torch.float64).cpu().numpy(), l.to(torch.float64).cpu().numpy(), att)
     return res
