@@ -36,23 +36,36 @@ constexpr int kPlanPieces = 64;
 constexpr int kPlanLdsT = 8192;
 
 // The whole-tile queues (workgroup 0 of the plan kernel, every thread).
-// Sequences are ranked by their work (chunks per KV head, most first); the
+// Sequences are ranked by their longest row tile (then their work); the
 // (sequence, KV head) groups in that order are dealt to the XCDs in snake
 // order (0..7, 7..0, ...), which balances the XCDs' work; each XCD's queue
 // lists its groups in order, every group's row tiles together (last tile,
 // the longest under the causal mask, first).  Workers of one XCD take
 // consecutive tasks (tile_task), so the tiles of a group start together and
 // read their sequence's KV from that XCD's L2.
-__device__ void build_tile_queues(const Params &p, int *s_order, int *s_xtot, const int *s_ipg, const int *s_ql)
+__device__ void build_tile_queues(const Params &p, int *s_order, int *s_key, int *s_xtot, const int *s_ipg,
+                                  const int *s_ql)
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int B = p.batch, Hkv = p.kv_head_num;
+    // rank key: the sequence's longest row tile in chunks (a queue then
+    // runs roughly longest task first), then its work, then its index
     for (int b = tid; b < B; b += kPlanThreads) {
-        const int w = s_ipg[b];
+        const int kv = p.ws.kvlen[b], ql = s_ql[b];
+        int lm = 0;
+        for (int qt = seq_tiles(p, ql) - 1; qt >= 0; --qt) {
+            const int n = unit_chunks(p, kv, ql, qt);
+            lm = n > lm ? n : lm;
+        }
+        s_key[b] = lm;
+    }
+    __syncthreads();
+    for (int b = tid; b < B; b += kPlanThreads) {
+        const int m = s_key[b], w = s_ipg[b];
         int r = 0;
         for (int b2 = 0; b2 < B; ++b2) {
-            const int w2 = s_ipg[b2];
-            r += (w2 > w || (w2 == w && b2 < b)) ? 1 : 0;
+            const int m2 = s_key[b2], w2 = s_ipg[b2];
+            r += (m2 > m || (m2 == m && (w2 > w || (w2 == w && b2 < b)))) ? 1 : 0;
         }
         s_order[r] = b;
     }
@@ -115,7 +128,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
     __shared__ uint32_t s_err;
     // whole-tile mode: the sequences in order of decreasing work, and the
     // tiles each XCD's queue holds
-    __shared__ int s_order[kTileOrderMaxBatch], s_xtot[kXcds];
+    __shared__ int s_order[kTileOrderMaxBatch], s_key[kTileOrderMaxBatch], s_xtot[kXcds];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const bool lead = blockIdx.x == 0;
@@ -280,7 +293,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
     }
     if (lead && p.tile_order) {
         if (ordered)
-            build_tile_queues(p, s_order, s_xtot, s_ipg, s_ql);
+            build_tile_queues(p, s_order, s_key, s_xtot, s_ipg, s_ql);
         if (tid == 0)
             p.ws.tq[kTqMode] = ordered ? 1 : 0;
     }
