@@ -274,6 +274,10 @@ void tile_kernel(Params p)
     static_assert(!SH || DV <= DK, "V inside the K row");
     // explicit interleave of operand reads and MFMAs (128-row tiles)
     constexpr bool SCHED = MB == 2;
+    // the same for the 576/512 tiles, a few fragments ahead (one 16-row
+    // block per wave, registers for a short ring only)
+    constexpr bool PIPE = MB == 1 && DK > 256;
+    constexpr int PFK = 2, PFV = 3;
 
     // the S stages of the ring, each a K tile, a V tile (none with one K/V
     // cache) and a mask slab (tensor mask only)
@@ -615,6 +619,26 @@ void tile_kernel(Params p)
                             sacc[mb][n] = Mfma<DT>::run(ka[ks & 1][n], qb[mb][ks], sacc[mb][n]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+            } else if constexpr (PIPE) {
+                // fragment i + PFK is read while fragment i is multiplied
+                constexpr int NR = KS * NTT;
+                auto kread = [&](int i) __attribute__((always_inline)) -> u32x4 {
+                    const int ks = i / NTT, n = i % NTT;
+                    return *(const lds_u32x4 *)(kb + ((ks & 1) ? koO : koE) + 16 * n * RBK + 64 * ks);
+                };
+                u32x4 kr[PFK + 1];
+#pragma unroll
+                for (int i = 0; i < PFK && i < NR; ++i)
+                    kr[i] = kread(i);
+#pragma unroll
+                for (int i = 0; i < NR; ++i) {
+                    if (i + PFK < NR)
+                        kr[(i + PFK) % (PFK + 1)] = kread(i + PFK);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        sacc[mb][i % NTT] = Mfma<DT>::run(kr[i % (PFK + 1)], qb[mb][i / NTT], sacc[mb][i % NTT]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             } else {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -726,18 +750,43 @@ void tile_kernel(Params p)
                     vm.x = (tok_ok(tb) ? 0xffffu : 0u) | (tok_ok(tb + 1) ? 0xffff0000u : 0u);
                     vm.y = (tok_ok(tb + 2) ? 0xffffu : 0u) | (tok_ok(tb + 3) ? 0xffff0000u : 0u);
                 }
-#pragma unroll
-                for (int nd = 0; nd < ND; ++nd) {
+                auto vread = [&](int nd) __attribute__((always_inline)) -> uint2 {
                     const v4i16 b0 =
                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + vo[nd % NVO] + 32 * NVO * (nd / NVO)));
-                    uint2 bv = __builtin_bit_cast(uint2, b0);
-                    if (tail) {
-                        bv.x &= vm.x;
-                        bv.y &= vm.y;
-                    }
+                    return __builtin_bit_cast(uint2, b0);
+                };
+                if constexpr (PIPE) {
+                    // column tile nd + PFV is read while tile nd is multiplied
+                    uint2 vr[PFV + 1];
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        oacc[mb][nd] = Mfma16<DT>::run(pa[mb], bv, oacc[mb][nd]);
+                    for (int i = 0; i < PFV && i < ND; ++i)
+                        vr[i] = vread(i);
+#pragma unroll
+                    for (int nd = 0; nd < ND; ++nd) {
+                        if (nd + PFV < ND)
+                            vr[(nd + PFV) % (PFV + 1)] = vread(nd + PFV);
+                        uint2 bv = vr[nd % (PFV + 1)];
+                        if (tail) {
+                            bv.x &= vm.x;
+                            bv.y &= vm.y;
+                        }
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            oacc[mb][nd] = Mfma16<DT>::run(pa[mb], bv, oacc[mb][nd]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else {
+#pragma unroll
+                    for (int nd = 0; nd < ND; ++nd) {
+                        uint2 bv = vread(nd);
+                        if (tail) {
+                            bv.x &= vm.x;
+                            bv.y &= vm.y;
+                        }
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            oacc[mb][nd] = Mfma16<DT>::run(pa[mb], bv, oacc[mb][nd]);
+                    }
                 }
             } else {
 #pragma unroll
@@ -1737,9 +1786,10 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
 // the streaming kernel (one wave, 16-token chunks, four stages).  1: up to
 // 64 rows.  2: more rows, two 16-row blocks per wave.  Dk = 576 has variant
 // 0 only: 4 waves of 16 rows each own all 512 output columns (no duplicated
-// K . Q^T work), two workgroups per CU: 16-token chunks in two stages (69 KB
-// of LDS), or with a shared K/V cache, where only K tiles are staged,
-// 32-token chunks in two stages (74 KB).
+// K . Q^T work): 16-token chunks in three stages (104 KB of LDS, one
+// workgroup per CU; two stages with the tensor mask), or with a shared K/V
+// cache, where only K tiles are staged, 32-token chunks in two stages
+// (74 KB, two workgroups per CU).
 
 template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH, int MODE>
 const void *pick(TileShape *t)
@@ -1763,7 +1813,13 @@ const void *kernel_for(int variant, bool shared, TileShape *t)
             else
                 return pick<DT, DK, DV, 1, 32, 4, 1, 2, true, MODE>(t);
         }
-        return pick<DT, DK, DV, 1, 16, 4, 1, 2, false, MODE>(t);
+        // separate K and V tiles: three stages in one workgroup per CU (two
+        // chunks of 34 KB in flight; the mask slabs of the tensor mask leave
+        // room for two)
+        if constexpr (MODE == MODE_TENSOR)
+            return pick<DT, DK, DV, 1, 16, 4, 1, 2, false, MODE>(t);
+        else
+            return pick<DT, DK, DV, 1, 16, 4, 1, 3, false, MODE>(t);
     } else {
         constexpr int KT = DK <= 128 ? 64 : 32;
         if constexpr (MODE == MODE_SPARSE) {
