@@ -270,14 +270,27 @@ def make_block_tables(context_lens, block_size, rng, num_blocks=None, slack=0.10
     return tables, num_blocks
 
 
-def generate(w: Workload, device="cpu", seed: Optional[int] = None, values=True,
-             max_blocks=None) -> Problem:
-    """Draw one problem for workload ``w`` (see the module docstring)."""
+def layout(w: Workload, seed: Optional[int] = None, max_blocks=None):
+    """The integer part of problem ``w`` without any tensor values:
+    (context_lens int32[B], q_seq_lens int32[B] or None, block_tables
+    int32[B, max_blocks], num_blocks, sparse lists int32[T, Hkv, topk] or
+    None) -- the same draws ``generate`` makes."""
     seed = w.seed if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     kv, ql = w.lengths(rng)
     kv = np.asarray(kv, dtype=np.int32)
+    ql = None if ql is None else np.asarray(ql, dtype=np.int32)
     tables, nb = make_block_tables(kv, w.block_size, rng, w.num_blocks, w.slack, max_blocks)
+    lists = (topk_lists(kv, ql, w.kv_head_num, w.topk, np.random.Generator(np.random.PCG64(seed * 16 + 4)))
+             if w.mask == "sparse" else None)
+    return kv, ql, tables, nb, lists
+
+
+def generate(w: Workload, device="cpu", seed: Optional[int] = None, values=True,
+             max_blocks=None) -> Problem:
+    """Draw one problem for workload ``w`` (see the module docstring)."""
+    seed = w.seed if seed is None else seed
+    kv, ql, tables, nb, lists = layout(w, seed, max_blocks)
     T = int(kv.shape[0]) if ql is None else int(np.asarray(ql, dtype=np.int64).sum())
     dt = DTYPES[w.dtype]
     qshape = (T, w.head_num, w.head_size_k)
@@ -300,9 +313,7 @@ def generate(w: Workload, device="cpu", seed: Optional[int] = None, values=True,
         context_lens_np=kv, q_seq_lens_np=None if ql is None else np.asarray(ql, np.int32),
         block_tables_np=tables, num_blocks=nb, max_num_blocks_per_seq=int(tables.shape[1]),
         mask_tensor=causal_mask_tensor(w.mask_fill, device) if w.mask == "tensor" else None,
-        topk_idx=torch.from_numpy(topk_lists(kv, ql, w.kv_head_num, w.topk,
-                                             np.random.Generator(np.random.PCG64(seed * 16 + 4)))).to(device)
-        if w.mask == "sparse" else None,
+        topk_idx=torch.from_numpy(lists).to(device) if lists is not None else None,
     )
 
 
