@@ -452,7 +452,8 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
     p.tail_min = 0;
     // The tile kernel may run the pass as whole row tiles from per-XCD
     // queues; the planner decides from the lengths.
-    p.tile_order = (v.path == 1 && !p.no_split && !pa::tile_streaming(c.head_size_k, c.head_size_v, v.tile_variant))
+    p.tile_order = (v.path == 1 && !p.no_split && !pa::tile_streaming(c.head_size_k, c.head_size_v, v.tile_variant) &&
+                    pa::tile_whole_tasks(c.head_size_k, shared))
                        ? 1
                        : 0;
     // The streaming kernel cuts its own pieces when the lengths fit in a

@@ -48,11 +48,22 @@ struct Workspace {
                          // 2 ints per task (b, g << 16 | qt), max_batch * Hkv * max_tiles tasks
 };
 
+// Whether the tile kernel instance for head size dk runs whole-tile tasks
+// (Params::tile_order): all but the 576/512 instances that read V out of the
+// K tile (one K/V cache), which sit at the register limit and run pieces
+// only.
+__host__ __device__ constexpr bool tile_whole_tasks(int dk, bool shared)
+{
+    return !(shared && dk > 256);
+}
+
 // Whole-tile task queues, one per XCD (see plan_kernel): the header holds the
-// length and first task of each XCD's queue, then the mode.
+// length and first task of each XCD's queue, the mode, then each queue's
+// claim counter in a 128-byte line of its own.
 constexpr int kXcds = 8;
 constexpr int kTqLength = 8, kTqStart = 16, kTqMode = 24;
-constexpr int kTqHeader = 32;
+constexpr int kTqCounter = 32, kTqCounterStride = 32;
+constexpr int kTqHeader = kTqCounter + kXcds * kTqCounterStride;
 // Largest batch the planner builds the queues for (it ranks the sequences
 // by their work with one comparison per pair).
 constexpr int kTileOrderMaxBatch = 512;
@@ -862,22 +873,47 @@ __device__ __forceinline__ int grab_piece(const Params &p)
     return p.partitions + __hip_atomic_fetch_add(p.ws.hdr + 3, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Whole-tile mode: task k (0, 1, ...) of workgroup w.  The workgroups w with
-// w % 8 == x (those the dispatcher deals to XCD x) take the tasks of queue
-// x in rounds of Lx (their number), with no atomics: in round k the l-th of
-// them (l = w / 8) takes position k Lx + l, or k Lx + Lx - 1 - l in odd
-// rounds (a snake, so that a worker that took a group's longest tile takes a
-// short one next).  Consecutive tasks of a queue -- the row tiles of one
-// (sequence, KV head) -- thus start together on consecutive workers of one
-// XCD in every round, as those workers finish their previous tiles, which
-// were alike, together.  Returns the task's index in the task array, or -1
-// when the workgroup has no task k.
-__device__ __forceinline__ int tile_task(const Params &p, int w, int nwg, int k)
+// Whole-tile mode.  The workgroups w with w % 8 == x (those the dispatcher
+// deals to XCD x, Lx of them) take the tasks of queue x.  Each takes its first
+// task at position w / 8; every later position (Lx, Lx + 1, ...) is claimed
+// from the queue's counter by a workgroup a few chunks before its current task
+// ends, so a worker that runs slow takes fewer tasks.  Consecutive positions
+// -- the row tiles of one (sequence, KV head) -- start close together on one
+// XCD and read their sequence's KV from its L2.  A workgroup whose queue is
+// empty claims from the other queues in turn.
+__device__ __forceinline__ int tile_queue_workers(int x, int nwg)
+{
+    return (nwg - x + kXcds - 1) / kXcds;
+}
+
+// The first task of workgroup w (index in the task array), or -1.
+__device__ __forceinline__ int tile_first_task(const Params &p, int w)
 {
     const int x = w % kXcds, l = w / kXcds;
-    const int lx = (nwg - x + kXcds - 1) / kXcds;
-    const int j = k * lx + ((k & 1) ? lx - 1 - l : l);
-    return j < sload(p.ws.tq, kTqLength + x) ? sload(p.ws.tq, kTqStart + x) + j : -1;
+    return l < sload(p.ws.tq, kTqLength + x) ? sload(p.ws.tq, kTqStart + x) + l : -1;
+}
+
+// One lane: the next unclaimed position of queue x (possibly past its end).
+// System scope, as the piece counter: workgroups on every XCD see one
+// sequence of values.
+__device__ __forceinline__ int tile_claim(const Params &p, int x, int nwg)
+{
+    return tile_queue_workers(x, nwg) + __hip_atomic_fetch_add(p.ws.tq + kTqCounter + kTqCounterStride * x, 1,
+                                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// One lane: the task at position pos of queue x, claimed earlier, or else one
+// claimed from the other queues in turn; -1 when every queue is exhausted.
+__device__ __forceinline__ int tile_next_task(const Params &p, int x, int nwg, int pos)
+{
+    for (int k = 0; k < kXcds; ++k) {
+        const int y = (x + k) & (kXcds - 1);
+        if (k > 0)
+            pos = tile_claim(p, y, nwg);
+        if (pos < p.ws.tq[kTqLength + y])
+            return p.ws.tq[kTqStart + y] + pos;
+    }
+    return -1;
 }
 
 // The cursor of whole-tile task t: all chunks of row tile (b, g, qt).

@@ -41,8 +41,9 @@ constexpr int kPlanLdsT = 8192;
 // order (0..7, 7..0, ...), which balances the XCDs' work; each XCD's queue
 // lists its groups in order, every group's row tiles together (last tile,
 // the longest under the causal mask, first).  Workers of one XCD take
-// consecutive tasks (tile_task), so the tiles of a group start together and
-// read their sequence's KV from that XCD's L2.
+// consecutive tasks (tile_first_task, tile_claim), so the tiles of a group
+// start close together and read their sequence's KV from that XCD's L2.  The
+// queues' claim counters start at 0.
 __device__ void build_tile_queues(const Params &p, int *s_order, int *s_key, int *s_xtot, const int *s_ipg,
                                   const int *s_ql)
 {
@@ -111,6 +112,8 @@ __device__ void build_tile_queues(const Params &p, int *s_order, int *s_key, int
         if (lane == 0) {
             p.ws.tq[kTqLength + wv] = s_xtot[wv];
             p.ws.tq[kTqStart + wv] = start;
+            __hip_atomic_store(p.ws.tq + kTqCounter + kTqCounterStride * wv, 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
 }

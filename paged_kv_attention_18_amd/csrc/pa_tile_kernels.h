@@ -306,11 +306,16 @@ void tile_kernel(Params p)
     __shared__ int s_piece;
     // Whole-tile mode (the planner's choice for this pass): tasks come from
     // the queue of this workgroup's XCD (the dispatcher deals workgroups
-    // round-robin over the XCDs), one whole row tile each (tile_task).
-    const bool ordered = p.tile_order && sload(p.ws.tq, kTqMode) != 0;
-    int task_k = 0;   // whole-tile mode: tasks taken so far
+    // round-robin over the XCDs), one whole row tile each: the first at a
+    // fixed position, the others claimed (tile_claim) when kClaimAhead chunks
+    // of the current one are left, by thread 0, whose claim returns while
+    // those chunks are computed.
+    const bool ordered = tile_whole_tasks(DK, SH) && p.tile_order && sload(p.ws.tq, kTqMode) != 0;
+    const int xq = blockIdx.x % kXcds;   // whole-tile mode: this workgroup's queue
+    constexpr int kClaimAhead = 3;
+    int nxt = 0;   // whole-tile mode, lane 0 of wave 0: the position claimed for the next task
     if (ordered) {
-        piece = tile_task(p, blockIdx.x, gridDim.x, task_k++);
+        piece = tile_first_task(p, blockIdx.x);
         if (piece < 0)
             return;
         tile_task_cursor(p, piece, cu, end);
@@ -938,12 +943,16 @@ void tile_kernel(Params p)
         // mask, before the start of its last row's window (c KT < max_lo).
         // Those chunks are a leading and a trailing run of the segment; the
         // chunks between take the unmasked instance.  Three loops, each with
-        // one instance of compute, keep the register pressure of one.
+        // one instance of compute, keep the register pressure of one.  In
+        // whole-tile mode the trailing run is at least kClaimAhead chunks
+        // long, and the next task is claimed before it.
         int cu0 = c0, cu1 = c0;   // the unmasked run [cu0, cu1)
         if constexpr (!SPARSE) {
             cu0 = BAND ? (max_lo + KT - 1) / KT : c0;
             cu0 = cu0 < c0 ? c0 : (cu0 > c1 ? c1 : cu0);
             cu1 = min_lim > 0 ? min_lim / KT : 0;
+            if (ordered && cu1 > c1 - kClaimAhead)
+                cu1 = c1 - kClaimAhead;
             cu1 = cu1 < cu0 ? cu0 : (cu1 > c1 ? c1 : cu1);
         }
         int c = c0, st = 0;
@@ -951,6 +960,8 @@ void tile_kernel(Params p)
             step(std::true_type{}, st, c);
         for (; c < cu1; ++c, st = st + 1 == S ? 0 : st + 1)
             step(std::false_type{}, st, c);
+        if (ordered && threadIdx.x == 0)
+            nxt = tile_claim(p, xq, gridDim.x);
         for (; c < c1; ++c, st = st + 1 == S ? 0 : st + 1)
             step(std::true_type{}, st, c);
 
@@ -1006,7 +1017,10 @@ void tile_kernel(Params p)
         if (!more) {
             if (ordered) {
                 // the next whole tile, if any
-                piece = tile_task(p, blockIdx.x, gridDim.x, task_k++);
+                if (threadIdx.x == 0)
+                    s_piece = tile_next_task(p, xq, gridDim.x, nxt);
+                __syncthreads();
+                piece = s_piece;
                 if (piece < 0)
                     break;
                 tile_task_cursor(p, piece, cu, end);
