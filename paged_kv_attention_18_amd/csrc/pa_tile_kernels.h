@@ -336,6 +336,8 @@ void tile_kernel(Params p)
     const uint32_t rsk = (uint32_t)p.kv_head_num * RBK;   // bytes per token row of the cache
     const uint32_t rsv = p.v_row_bytes;
     const uint32_t nb32 = p.num_blocks < 0x7fffffff ? (uint32_t)p.num_blocks : 0x7fffffffu;
+    // every KT-token chunk lies in one cache block
+    const bool chunk_in_block = bs % KT == 0;
     // Scores are kept raw (q . k) and scaled on the way into exp2 by
     // sc = |scale| log2(e); a negative scale is folded into Q.
     const bool neg_scale = p.scale_log2 < 0.f;
@@ -491,14 +493,29 @@ void tile_kernel(Params p)
                 (void)c;
                 // (wave-uniform: read once into scalar registers)
                 int blk = __builtin_amdgcn_readfirstlane(f_blk), slot = __builtin_amdgcn_readfirstlane(f_slot);
+                if (chunk_in_block) {
+                    // the chunk lies in one block: one id for its groups
+                    const int b0 = sload(bt, blk < nblk ? blk : nblk - 1);
 #pragma unroll
-                for (int q = 0; q < NTT; ++q) {
-                    bid[q] = sload(bt, blk < nblk ? blk : nblk - 1);
-                    bslot[q] = slot;
-                    slot += 16;
+                    for (int q = 0; q < NTT; ++q) {
+                        bid[q] = b0;
+                        bslot[q] = slot + 16 * q;
+                    }
+                    slot += KT;
                     if (slot == bs) {
                         slot = 0;
                         ++blk;
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < NTT; ++q) {
+                        bid[q] = sload(bt, blk < nblk ? blk : nblk - 1);
+                        bslot[q] = slot;
+                        slot += 16;
+                        if (slot == bs) {
+                            slot = 0;
+                            ++blk;
+                        }
                     }
                 }
                 f_blk = blk;
