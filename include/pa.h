@@ -302,7 +302,9 @@ pa_status pa_read_probe(const void *src, int64_t bytes, uint32_t *sink, int32_t 
  * kernel, 1 for the MFMA tile kernel, 2 for the MFMA streaming kernel (units
  * of at most 16 rows), for a call with that max_q_seq_len (at most
  * cfg.max_q_seq_len); *rows_per_tile and *tokens_per_chunk describe its work
- * unit; *partitions is the attention grid size.
+ * unit; *partitions is the attention grid size (a sparse-list pass takes at
+ * most max(CUs, two per (sequence, KV head, row tile)) of them, and a
+ * whole-unit pass one per unit).
  */
 pa_status pa_describe(const pa_handle *h, int32_t max_q_seq_len, int32_t *path,
                       int32_t *rows_per_tile, int32_t *tokens_per_chunk, int32_t *partitions);

@@ -447,6 +447,16 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
     }
     p.partitions = p.no_split ? batch * c.kv_head_num * p.max_tiles
                               : (v.partitions < h->max_partitions ? v.partitions : h->max_partitions);
+    // Sparse lists: every unit holds the same ceil(topk / 16) chunks.  Cut
+    // into more than two pieces each, its fp32 partials (131 KB per piece at
+    // 576/512) cost more than the extra workers gain: at most two workers
+    // per unit, and at least one per CU.
+    if (!p.no_split && c.mask == PA_MASK_SPARSE) {
+        const int64_t units = (int64_t)batch * c.kv_head_num * p.max_tiles;
+        const int64_t cap = std::max<int64_t>(h->num_cus, 2 * units);
+        if (p.partitions > cap)
+            p.partitions = (int32_t)cap;
+    }
     p.pieces = p.no_split ? 0 : p.partitions * v.pieces_per_worker;
     p.partial_stride = (int32_t)partial_floats(v.rows_per_tile, c.head_size_v);
     p.tail_min = 0;
