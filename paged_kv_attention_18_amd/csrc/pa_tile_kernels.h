@@ -350,6 +350,7 @@ void tile_kernel(Params p)
     // 16-bit operand types); a moved reference rescales O and the sum.
     const float grow_raw = 8.f / sc;
     uint32_t err = 0;
+    bool bad_id = false;   // a visible group's block id was out of range (wave-uniform)
     bool first_seg = true;
 
     // Per-lane byte offset, inside a 16-token group of the cache, of the piece
@@ -573,22 +574,27 @@ void tile_kernel(Params p)
                 const int j0 = c * KT + 16 * q;
                 const bool vis = j0 < nvis && (!BAND || j0 + 16 > lo_tile);
                 const bool inb = (unsigned)bid[q] < nb32;
-                err |= (vis && !inb) ? (uint32_t)PA_DEVERR_BLOCK_ID : 0u;
+                bad_id |= vis && !inb;
                 const size_t trow = (size_t)(uint32_t)bid[q] * (uint32_t)bs + (uint32_t)bslot[q];
-                const char *kbase = (vis && inb) ? kgh + trow * rsk : zg;
-                const char *vbase = (vis && inb) ? vgh + trow * rsv : zg;
+                // (a bit select, which stays on the scalar unit)
+                const uint64_t sel = (vis && inb) ? ~0ull : 0ull;
+                const char *kbase = (const char *)((((uint64_t)kgh + trow * rsk) & sel) | ((uint64_t)zg & ~sel));
+                const char *vbase = (const char *)((((uint64_t)vgh + trow * rsv) & sel) | ((uint64_t)zg & ~sel));
                 // (the empty asm hides each 32-bit offset from loop-invariant
                 // hoisting: otherwise the 64-bit forms of all of a chunk's
                 // offsets stay live across the chunk loop, and where the
                 // registers run out one is spilled and reloaded behind the
-                // next chunk's first load, which then waits for that load)
+                // next chunk's first load, which then waits for that load;
+                // with one K and one V offset per wave the two 64-bit forms
+                // fit, and keeping them saves a copy per load)
 #pragma unroll
                 for (int m = 0; m < MK; ++m) {
                     const int i = wave + NW * m;
                     lds_u8 *dst = (!PAD || i < IPGK) ? kb + (q * IPGK + i) * 1024 : (lds_u8 *)sJunk;
                     const char *src = (!PAD || i < IPGK) ? kbase : zg;
                     uint32_t off = voK[m];
-                    asm volatile("" : "+v"(off));
+                    if constexpr (MK + MV > 2)
+                        asm volatile("" : "+v"(off));
                     lds_load16(src + off, dst);
                 }
 #pragma unroll
@@ -597,7 +603,8 @@ void tile_kernel(Params p)
                     lds_u8 *dst = (!PAD || i < IPGV) ? vb + (q * IPGV + i) * 1024 : (lds_u8 *)sJunk;
                     const char *src = (!PAD || i < IPGV) ? vbase : zg;
                     uint32_t off = voV[m];
-                    asm volatile("" : "+v"(off));
+                    if constexpr (MK + MV > 2)
+                        asm volatile("" : "+v"(off));
                     lds_load16(src + off, dst);
                 }
             }
@@ -1056,6 +1063,8 @@ void tile_kernel(Params p)
             first_seg = true;
         }
     }
+    if (bad_id)
+        err |= (uint32_t)PA_DEVERR_BLOCK_ID;
     if (err)
         set_error(p.ws.err, err);
 }
