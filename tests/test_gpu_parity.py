@@ -572,6 +572,29 @@ def test_deterministic_runs():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_whole_tile_mode_claims_are_deterministic():
+    """Prefill-sized causal units with a handful of workers: the planner runs
+    whole row tiles from per-XCD queues, workers claim tasks at run time, and
+    with 4 workers the queues of the other 4 XCDs are served only by claims
+    from other queues.  Whole tiles are computed in one piece whichever worker
+    runs them, so every worker count and every run gives the same bits, and
+    those match the oracle."""
+    log("whole-tile mode: claims")
+    p_cpu = synth.custom([600, 900, 1300, 700], 8, 2, 128, 128, 128, "f16", "causal",
+                         q_seq_lens=[256, 128, 256, 64], seed=28)
+    ref_o, ref_l = oracle_full(p_cpu)
+    p = to_device(p_cpu)
+    runs = []
+    for parts in (4, 8, 6, 4):
+        o, l, att = run_hip(p, num_partitions=parts)
+        assert att.device_error() == 0
+        runs.append((o, l))
+    assert_close(runs[0][0], ref_o, "f16", "whole-tile mode")
+    assert_lse_close(runs[0][1], ref_l, "whole-tile mode")
+    for o, l in runs[1:]:
+        assert np.array_equal(o, runs[0][0]) and np.array_equal(l, runs[0][1])
+
+
 def test_bad_block_id_is_flagged_not_read():
     log("bad block id")
     p = synth.custom([100, 50], 4, 2, 64, 64, 16, "f16", seed=27)
