@@ -64,6 +64,10 @@ CASES = {
     # splitfuse-like causal units of up to 1200 rows: the 128-row tile kernel, plan and merge
     "causal_tiles": dict(lens=([300, 37, 520, 16, 900], [40, 5, 300, 16, 64]), H=8, Hkv=2, D=(128, 128), bs=64,
                          dt="f16", mask="causal", parts=48, small=2),
+    # prefill-sized causal units on 8 workers: whole row tiles from per-XCD
+    # queues with claimed tasks (the queues and their counters in the array)
+    "causal_whole_tiles": dict(lens=([600, 900, 1300, 700], [256, 128, 256, 64]), H=8, Hkv=2, D=(128, 128),
+                               bs=128, dt="f16", mask="causal", parts=8, small=2),
     # 576/512 on one KV head
     "mla": dict(lens=[1500, 77, 640, 33, 2100], H=64, Hkv=1, D=(576, 512), bs=128, dt="bf16", mask="none",
                 parts=40, small=2),
@@ -108,7 +112,8 @@ def run_case(name, seed):
 def test_noalloc_matches_pa_forward_two_calls():
     # configurations alternate on the one array: stale words from the
     # previous configuration's layout must not leak into the next pass
-    for name, seed in (("gqa_decode", 71), ("causal_tiles", 72), ("mla", 73), ("gqa_decode", 74)):
+    for name, seed in (("gqa_decode", 71), ("causal_tiles", 72), ("causal_whole_tiles", 75), ("mla", 73),
+                       ("gqa_decode", 74)):
         run_case(name, seed)
 
 
