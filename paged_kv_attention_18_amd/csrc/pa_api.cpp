@@ -36,6 +36,9 @@ struct Variant {
     int partitions;  // balanced-mode workers (waves for the VALU kernel, workgroups for MFMA)
     int pieces_per_worker;
     bool claimed_tail;   // self-planning launches cut a claimed tail (up to pa::kTailRounds rounds)
+    bool streaming;      // MFMA: the one-wave streaming kernel (units of at most 16 rows)
+    int hp;              // KV heads per unit (2: head pairs, streaming kernel)
+    int self_variant, tail_variant;   // streaming: the self-planning variants (without, with claims)
     int max_pieces() const { return partitions * (claimed_tail ? 1 + pa::kTailRounds : pieces_per_worker); }
 };
 
@@ -72,6 +75,11 @@ constexpr int kSparseTileRows = 64;
 // static piece per worker, and the same with a claimed tail of pieces.
 constexpr int kSelfPlanVariant = 3;
 constexpr int kSelfPlanTailVariant = 4;
+// The streaming kernel on head pairs (variants 0, 3, 4 with two KV heads per
+// unit): a unit reads 512-byte runs of each token row instead of 256-byte
+// ones, which the memory system serves faster.
+constexpr bool kHeadPairs = true;
+constexpr int kPairVariant = 5, kPairSelfPlanVariant = 6, kPairSelfPlanTailVariant = 7;
 // band units of at most this many KV chunks run whole (no split, no merge)
 constexpr int kBandWholeUnitChunks = 8;
 
@@ -96,6 +104,7 @@ struct pa_handle {
     Variant choose(int max_q) const
     {
         Variant v{};
+        v.hp = 1;
         const int G = cfg.head_num / cfg.kv_head_num;
         const int rows = max_q * G;
         const bool dec_ok = pa::decode_supported(cfg.head_size_k, cfg.head_size_v);
@@ -123,21 +132,33 @@ struct pa_handle {
             if ((rows > 16 || cfg.mask == PA_MASK_SPARSE) && pa::tile_supported(dk, dv, 1))
                 var = (rows > pa::tile_rows(dk, dv, 1, sh, mode) && pa::tile_supported(dk, dv, 2) &&
                        cfg.mask != PA_MASK_TENSOR && cfg.mask != PA_MASK_SPARSE) ? 2 : 1;
+            v.streaming = pa::tile_streaming(dk, dv, var);
+            v.hp = 1;
+            v.self_variant = kSelfPlanVariant;
+            v.tail_variant = kSelfPlanTailVariant;
+            // head pairs where both heads' rows still fit one 16-row block
+            if (kHeadPairs && v.streaming && cfg.kv_head_num % 2 == 0 && 2 * rows <= 16 &&
+                pa::tile_supported(dk, dv, kPairVariant)) {
+                var = kPairVariant;
+                v.hp = 2;
+                v.self_variant = kPairSelfPlanVariant;
+                v.tail_variant = kPairSelfPlanTailVariant;
+            }
             v.tile_variant = var;
             v.rows_per_tile = pa::tile_rows(dk, dv, var, sh, mode);
             v.chunk = pa::tile_chunk(dk, dv, var, sh, mode);
             v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var, sh, mode);
-            if (var == 0 && pa::tile_supported(dk, dv, kSelfPlanVariant)) {
+            if (v.streaming && pa::tile_supported(dk, dv, v.self_variant)) {
                 // the self-planning twins of the streaming kernel run the same grid
-                for (int sv : {kSelfPlanVariant, kSelfPlanTailVariant}) {
+                for (int sv : {v.self_variant, v.tail_variant}) {
                     const int w3 = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, sv, sh, mode);
                     v.partitions = w3 < v.partitions ? w3 : v.partitions;
                 }
             }
-            v.pieces_per_worker = var == 0 ? 1 : kMaxPiecesPerWorker;
+            v.pieces_per_worker = v.streaming ? 1 : kMaxPiecesPerWorker;
             // the self-planning streaming kernel may add rounds of claimed
             // pieces (pa::PieceMap)
-            v.claimed_tail = var == 0 && pa::tile_supported(dk, dv, kSelfPlanTailVariant) &&
+            v.claimed_tail = v.streaming && pa::tile_supported(dk, dv, v.tail_variant) &&
                              !(cfg.flags & PA_FLAG_STATIC_PIECES);
         }
         if (cfg.num_partitions > 0)
@@ -270,7 +291,7 @@ pa_status pa_create(const pa_config *cfg, pa_handle **out)
             max_pieces = (size_t)v.max_pieces();
         if ((size_t)v.max_pieces() * f > max_slot_floats)
             max_slot_floats = (size_t)v.max_pieces() * f;
-        const int tiles = (int)(((int64_t)q * G + v.rows_per_tile - 1) / v.rows_per_tile);
+        const int tiles = (int)(((int64_t)q * G * v.hp + v.rows_per_tile - 1) / v.rows_per_tile);
         if (tiles > max_tiles)
             max_tiles = tiles;
     }
@@ -385,7 +406,9 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
         return PA_OK;
     *empty = false;
     v = h->choose(max_q_seq_len);
-    const int G = c.head_num / c.kv_head_num;
+    // (head pairs: a unit is two KV heads and their 2 G query heads; the
+    // row -> (token, query head) map is the same with G and Hkv so taken)
+    const int G = c.head_num / c.kv_head_num * v.hp;
 
     p = pa::Params{};
     p.query = query;
@@ -393,7 +416,7 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
     p.value_cache = shared ? key_cache : value_cache;
     p.shared_kv = shared ? 1 : 0;
     p.v_row_bytes = (uint32_t)c.kv_head_num * (uint32_t)(shared ? c.head_size_k : c.head_size_v) * 2u;
-    p.v_head_bytes = (uint32_t)(shared ? c.head_size_k : c.head_size_v) * 2u;
+    p.v_head_bytes = (uint32_t)(shared ? c.head_size_k : c.head_size_v) * 2u * (uint32_t)v.hp;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     p.q_seq_lens = q_seq_lens;
@@ -403,7 +426,7 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
     p.batch = batch;
     p.num_q_tokens = num_q_tokens;
     p.head_num = c.head_num;
-    p.kv_head_num = c.kv_head_num;
+    p.kv_head_num = c.kv_head_num / v.hp;
     p.group = G;
     p.head_size_k = c.head_size_k;
     p.head_size_v = c.head_size_v;
@@ -440,19 +463,19 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
         !pa::tile_streaming(c.head_size_k, c.head_size_v, v.tile_variant)) {
         const int64_t rows = std::min<int64_t>((int64_t)max_q_seq_len * G, v.rows_per_tile);
         const int64_t keys = (rows + G - 1) / G + 1 + (int64_t)c.window_left + c.window_right;
-        const int64_t units = (int64_t)batch * c.kv_head_num * p.max_tiles;
+        const int64_t units = (int64_t)batch * p.kv_head_num * p.max_tiles;
         if ((keys + v.chunk - 1) / v.chunk + 1 <= kBandWholeUnitChunks &&
             units <= std::min(v.partitions, h->max_partitions))
             p.no_split = 1;
     }
-    p.partitions = p.no_split ? batch * c.kv_head_num * p.max_tiles
+    p.partitions = p.no_split ? batch * p.kv_head_num * p.max_tiles
                               : (v.partitions < h->max_partitions ? v.partitions : h->max_partitions);
     // Sparse lists: every unit holds the same ceil(topk / 16) chunks.  Cut
     // into more than two pieces each, its fp32 partials (131 KB per piece at
     // 576/512) cost more than the extra workers gain: at most two workers
     // per unit, and at least one per CU.
     if (!p.no_split && c.mask == PA_MASK_SPARSE) {
-        const int64_t units = (int64_t)batch * c.kv_head_num * p.max_tiles;
+        const int64_t units = (int64_t)batch * p.kv_head_num * p.max_tiles;
         const int64_t cap = std::max<int64_t>(h->num_cus, 2 * units);
         if (p.partitions > cap)
             p.partitions = (int32_t)cap;
@@ -469,9 +492,9 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
     // The streaming kernel cuts its own pieces when the lengths fit in a
     // wave's registers: one launch fewer, and no wait on plan data when a
     // worker starts or moves to the next unit.
-    p.self_plan = (v.path == 1 && v.tile_variant == 0 && !p.no_split && batch <= pa::kSelfPlanMaxBatch &&
+    p.self_plan = (v.path == 1 && v.streaming && !p.no_split && batch <= pa::kSelfPlanMaxBatch &&
                    p.pieces == p.partitions && max_q_seq_len <= 16 &&
-                   pa::tile_supported(c.head_size_k, c.head_size_v, kSelfPlanVariant))
+                   pa::tile_supported(c.head_size_k, c.head_size_v, v.self_variant))
                       ? 1
                       : 0;
     // self-planning: claimed pieces after the static ones, in rounds that
@@ -480,7 +503,7 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
     // shorter passes take the kernel without the claiming code
     if (p.self_plan && v.claimed_tail) {
         const int64_t cap = (int64_t)c.max_num_blocks_per_seq * c.block_size;
-        const int64_t w_max = (int64_t)batch * c.kv_head_num * ((cap + v.chunk - 1) / v.chunk);
+        const int64_t w_max = (int64_t)batch * p.kv_head_num * ((cap + v.chunk - 1) / v.chunk);
         if (w_max >= (int64_t)pa::kTailMinShare * pa::kTailMinChunks * p.partitions)
             p.tail_min = pa::kTailMinChunks;
     }
@@ -509,7 +532,7 @@ static pa_status launch_pass(pa_handle *h, const pa::Params &p, const Variant &v
         return PA_ERR_HIP;
     hipError_t e = v.path == 0 ? pa::launch_decode(p, c.dtype, v.rows_pad, s)
                                : pa::launch_tile(p, c.dtype,
-                                                 p.self_plan ? (p.tail_min > 0 ? kSelfPlanTailVariant : kSelfPlanVariant)
+                                                 p.self_plan ? (p.tail_min > 0 ? v.tail_variant : v.self_variant)
                                                              : v.tile_variant,
                                                  s);
     if (e != hipSuccess)

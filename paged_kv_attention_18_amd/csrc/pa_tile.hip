@@ -67,10 +67,13 @@ hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s)
     // the plan was made for this kernel's chunk and tile sizes
     if (!k || t.kt != p.chunk || 16 * t.mb * (t.nw / t.cs) != p.rows_per_tile)
         return hipErrorInvalidValue;
-    // only the streaming kernel's variants 3 and 4 plan for themselves, for
-    // at most kSelfPlanMaxBatch sequences of at most 16 query tokens, one
-    // static piece per workgroup (variant 4 may add claimed pieces)
-    if ((p.self_plan != 0) != (variant == 3 || variant == 4) || (p.tail_min > 0) != (variant == 4) ||
+    // only the streaming kernel's variants 3 and 4 (6 and 7 on head pairs)
+    // plan for themselves, for at most kSelfPlanMaxBatch sequences of at most
+    // 16 query tokens, one static piece per workgroup (variants 4 and 7 may
+    // add claimed pieces)
+    const bool self_var = variant == 3 || variant == 4 || variant == 6 || variant == 7;
+    const bool tail_var = variant == 4 || variant == 7;
+    if ((p.self_plan != 0) != self_var || (p.tail_min > 0) != tail_var ||
         (p.self_plan && (t.nw != 1 || p.batch > kSelfPlanMaxBatch || p.pieces != p.partitions || p.max_q > 16)))
         return hipErrorInvalidValue;
     void *args[] = {(void *)&p};

@@ -1099,25 +1099,36 @@ void tile_kernel(Params p)
 // drains.  Every stage record carries the chunks left in its piece, and the
 // last chunk of a worker's stream is flagged, so the two waves agree on the
 // number of barriers.
-template <int DT, int DK, int DV, int KT, int S, int MODE, bool SELF, bool TAIL>
-__global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
+template <int DT, int DK, int DV, int KT, int S, int MODE, bool SELF, bool TAIL, int HP>
+__global__ __launch_bounds__(128, DK * HP > 128 ? (HP > 1 ? 2 : 1) : 3) void stream_kernel(Params p)
 {
     static_assert(SELF || !TAIL, "a claimed tail needs the kernel's own plan");
     constexpr bool BAND = MODE == MODE_BAND, TMASK = MODE == MODE_TENSOR;
     constexpr int SDW = slab_row_dwords<KT>();
     constexpr int SLB = TMASK ? slab_bytes<16, KT>() : 0;   // bytes of a mask slab stage
-    constexpr int RBK = 2 * DK, RBV = 2 * DV;     // LDS row bytes
-    constexpr int KS = DK / 32;
+    // HP KV heads per unit (head pairs: HP = 2): their K (V) rows sit side by
+    // side in the cache, so a unit reads HP * Dk contiguous elements of each
+    // token row and stages them as one wide row; each query row takes the
+    // products with its own head's half (Q is zero in the other) and its
+    // output from its own head's half of the wide PV product.
+    constexpr int DKE = HP * DK, DVE = HP * DV;   // staged row elements
+    constexpr int RBK = 2 * DKE, RBV = 2 * DVE;   // LDS row bytes
+    constexpr int RBQ = 2 * DK;                   // Q tile row bytes (one query head)
+    constexpr int KS = DKE / 32;
+    constexpr int KSQ = DK / 32;                  // Q slices of one head
     constexpr int NTT = KT / 16;
-    constexpr int ND = DV / 16;
-    constexpr int IPGK = RBK / 64;                // 1 KiB loads per 16 rows of K (and of the Q tile)
+    constexpr int ND = DVE / 16;
+    constexpr int NDO = DV / 16;                  // output column tiles of one head
+    constexpr int IPGK = RBK / 64;                // 1 KiB loads per 16 rows of K
     constexpr int IPGV = RBV / 64;
-    constexpr int LW = NTT * (IPGK + IPGV);       // loads per chunk (plus IPGK for a Q tile)
-    constexpr int STK = KT * RBK, STV = KT * RBV, STQ = 16 * RBK;
+    constexpr int IPGQ = RBQ / 64;                // ... of the Q tile
+    constexpr int LW = NTT * (IPGK + IPGV);       // loads per chunk (plus IPGQ for a Q tile)
+    constexpr int STK = KT * RBK, STV = KT * RBV, STQ = 16 * RBQ;
     constexpr int MW = TAIL ? 13 : 12;            // ints per stage record
     constexpr int kClaimAhead = 4;                // chunks between a claim and its deadline
-    static_assert(DK <= 256 && DV <= 256 && DK % 32 == 0 && DV % 64 == 0 && (KT == 16 || KT == 32), "shape");
-    static_assert(S >= 2 && S <= 4 && LW * (S - 2) + IPGK < 64, "ring");
+    static_assert(DKE <= 256 && DVE <= 256 && DK % 32 == 0 && DV % 64 == 0 && (KT == 16 || KT == 32), "shape");
+    static_assert(HP == 1 || (HP == 2 && DK == DV), "head pairs");
+    static_assert(S >= 2 && S <= 4 && LW * (S - 2) + IPGQ < 64, "ring");
 
     __shared__ __attribute__((aligned(1024))) uint8_t sK[S * STK];
     __shared__ __attribute__((aligned(1024))) uint8_t sV[S * STV];
@@ -1162,15 +1173,19 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
 
     // per-lane offsets of the loads (inside a 16-token group / the Q tile)
     uint32_t voK[IPGK], voV[IPGV];
-    int qrow[IPGK], qlp[IPGK];
+    int qrow[IPGQ], qlp[IPGQ];
 #pragma unroll
     for (int m = 0; m < IPGK; ++m) {
         const int x = m * 1024 + 16 * lane;
         const int row = x / RBK;
-        const int lp = ((x % RBK) >> 4) ^ (row & 7);
-        voK[m] = row * rsk + 16 * lp;
+        voK[m] = row * rsk + 16 * (((x % RBK) >> 4) ^ (row & 7));
+    }
+#pragma unroll
+    for (int m = 0; m < IPGQ; ++m) {
+        const int x = m * 1024 + 16 * lane;
+        const int row = x / RBQ;
         qrow[m] = row;
-        qlp[m] = lp;
+        qlp[m] = ((x % RBQ) >> 4) ^ (row & 7);
     }
 #pragma unroll
     for (int m = 0; m < IPGV; ++m) {
@@ -1182,6 +1197,7 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
     const int kq = 16 * (lg ^ (lr & 3));
     const int kb2 = 64 * ((lr >> 2) & 1);
     const int koE = lr * RBK + kq + kb2, koO = lr * RBK + kq - kb2;
+    const int qoE = lr * RBQ + kq + kb2, qoO = lr * RBQ + kq - kb2;
     constexpr int NVO = v_offsets<RBV>();
     int vo[NVO];
 #pragma unroll
@@ -1473,7 +1489,7 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
         if (seg_begin) {
             // Q tile of the segment (rows past the unit read the zero page)
 #pragma unroll
-            for (int m = 0; m < IPGK; ++m) {
+            for (int m = 0; m < IPGQ; ++m) {
                 const int rg = ic.qt * 16 + qrow[m];
                 const int t = it0 + rg / G;
                 const bool ok = qrow[m] < irows && t < p.num_q_tokens;
@@ -1609,11 +1625,16 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
             nvis = md[6];
             const int kv = md[7], ql = md[8], rows = md[10];
             const lds_u8 *qs = (const lds_u8 *)sQ + st * STQ;
+            // (head pairs: this lane's row belongs to head hh of the pair;
+            // its Q is zero in the other head's slices)
+            const int hh = HP > 1 ? ((qt * 16 + lr) % G) / (G / HP) : 0;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                qb[ks] = *(const lds_u32x4 *)(qs + ((ks & 1) ? koO : koE) + 64 * ks);
+                const int kq_ = ks % KSQ;
+                u32x4 q = *(const lds_u32x4 *)(qs + ((kq_ & 1) ? qoO : qoE) + 64 * kq_);
                 if (neg_scale)   // exact: softmax(c s) = softmax(|c| (-s)) with -s = (-q) . k
-                    qb[ks] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+                    q ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+                qb[ks] = (HP == 1 || ks / KSQ == hh) ? q : u32x4{0u, 0u, 0u, 0u};
             }
             lo_tile = md[11];
             const int prefix = seq_prefix(kv, ql);
@@ -1794,20 +1815,28 @@ __global__ __launch_bounds__(128, DK > 128 ? 1 : 3) void stream_kernel(Params p)
                 const int rg = qt * 16 + row_t;
                 const int t = t0 + rg / G;
                 const int h = g * G + rg % G;
+                // (head pairs: the row's own head's half of the output)
+                const int hr = HP > 1 ? (rg % G) / (G / HP) : 0;
+                auto out_col = [&](int nd) __attribute__((always_inline)) -> float {
+                    if constexpr (HP == 1)
+                        return oacc[nd][r];
+                    else
+                        return hr ? oacc[NDO + nd][r] : oacc[nd][r];
+                };
                 if (whole) {
                     if (t >= p.num_q_tokens)
                         continue;
                     const float inv = Lr > 0.f ? 1.f / Lr : 0.f;
                     uint16_t *dst = og + ((size_t)t * H + h) * DV;
 #pragma unroll
-                    for (int nd = 0; nd < ND; ++nd)
-                        dst[16 * nd + lr] = to_bits<DT>(oacc[nd][r] * inv);
+                    for (int nd = 0; nd < NDO; ++nd)
+                        dst[16 * nd + lr] = to_bits<DT>(out_col(nd) * inv);
                     if (lr == 0 && p.lse)
                         p.lse[(size_t)t * H + h] = Lr > 0.f ? (Mr + log2f(Lr)) * 0.69314718055994531f : -INFINITY;
                 } else {
 #pragma unroll
-                    for (int nd = 0; nd < ND; ++nd)
-                        part[row_t * DV + 16 * nd + lr] = oacc[nd][r];
+                    for (int nd = 0; nd < NDO; ++nd)
+                        part[row_t * DV + 16 * nd + lr] = out_col(nd);
                     if (lr == 0) {
                         part[16 * DV + row_t] = Mr;
                         part[16 * DV + 16 + row_t] = Lr;
@@ -1869,15 +1898,31 @@ const void *kernel_for(int variant, bool shared, TileShape *t)
         } else {
             if (variant == 0) {   // one wave per workgroup, streaming across units
                 *t = TileShape{1, 16, 1, 1, 4, 128};
-                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, false, false>;
+                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, false, false, 1>;
             }
             if (variant == 3) {   // the same, planning for itself
                 *t = TileShape{1, 16, 1, 1, 4, 128};
-                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, true, false>;
+                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, true, false, 1>;
             }
             if (variant == 4) {   // the same, with a claimed tail of pieces
                 *t = TileShape{1, 16, 1, 1, 4, 128};
-                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, true, true>;
+                return (const void *)&stream_kernel<DT, DK, DV, 16, 4, MODE, true, true, 1>;
+            }
+            if constexpr (DK == 128 && DV == 128) {
+                // 5, 6, 7: variants 0, 3, 4 on head pairs (three stages:
+                // two workgroups per CU)
+                if (variant == 5) {
+                    *t = TileShape{1, 16, 1, 1, 3, 128};
+                    return (const void *)&stream_kernel<DT, DK, DV, 16, 3, MODE, false, false, 2>;
+                }
+                if (variant == 6) {
+                    *t = TileShape{1, 16, 1, 1, 3, 128};
+                    return (const void *)&stream_kernel<DT, DK, DV, 16, 3, MODE, true, false, 2>;
+                }
+                if (variant == 7) {
+                    *t = TileShape{1, 16, 1, 1, 3, 128};
+                    return (const void *)&stream_kernel<DT, DK, DV, 16, 3, MODE, true, true, 2>;
+                }
             }
             if constexpr (MODE == MODE_TENSOR) {
                 if (variant == 1)

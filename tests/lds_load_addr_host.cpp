@@ -185,18 +185,21 @@ struct Shape {
     bool stream;
     int mb, kt, nw, cs, s;
     bool sh;   // V read out of the K tile in LDS
+    int hp;    // KV heads per unit (2: the streaming kernel on head pairs)
 };
 
 // Every load of one kernel shape over one case.  st[0]: K/V loads, st[1]:
 // Q tile loads (streaming kernel), st[2]: mask slab loads.
 void run(const Case &c, const Shape &sh, Stats stv[3])
 {
-    const int B = c.B, G = c.H / c.Hkv, DK = c.DK, DV = c.DV;
+    // (head pairs: the pass runs with G and Hkv taken per pair of KV heads)
+    const int HP = sh.hp, Hkv = c.Hkv / HP;
+    const int B = c.B, G = c.H / c.Hkv * HP, DK = c.DK, DV = c.DV;
     const bool BAND = c.mode == M_BAND, TMASK = c.mode == M_TENSOR, SPARSE = c.mode == M_SPARSE;
     const int R = sh.stream ? 16 : 16 * sh.mb * (sh.nw / sh.cs);
     const int KT = sh.kt, NTT = KT / 16, NW = sh.stream ? 1 : sh.nw;
-    const int RBK = 2 * DK, RBV = 2 * DV;
-    const int IPGK = RBK / 64, IPGV = sh.sh ? 0 : RBV / 64;
+    const int RBK = 2 * DK * HP, RBV = 2 * DV * HP, RBQ = 2 * DK;
+    const int IPGK = RBK / 64, IPGV = sh.sh ? 0 : RBV / 64, IPGQ = RBQ / 64;
     const int MK = sh.stream ? IPGK : (IPGK + NW - 1) / NW;
     const int MV = sh.stream ? IPGV : (IPGV + NW - 1) / NW;
     const bool PAD = !sh.stream && (MK * NW != IPGK || MV * NW != IPGV);
@@ -213,7 +216,7 @@ void run(const Case &c, const Shape &sh, Stats stv[3])
     p.batch = B;
     p.num_q_tokens = (int)T;
     p.head_num = c.H;
-    p.kv_head_num = c.Hkv;
+    p.kv_head_num = Hkv;
     p.group = G;
     p.head_size_k = DK;
     p.head_size_v = DV;
@@ -238,9 +241,9 @@ void run(const Case &c, const Shape &sh, Stats stv[3])
     p.tile_shift = l2(R);
 
     // buffers, in bytes, as the library sizes or takes them
-    const long long rsk = (long long)c.Hkv * RBK;                                   // K token row
+    const long long rsk = (long long)Hkv * RBK;                                     // K token row
     const long long rsv = (long long)c.Hkv * 2 * (c.shared ? DK : DV);              // V source token row
-    const long long vhead = 2LL * (c.shared ? DK : DV);                             // V source head stride
+    const long long vhead = 2LL * (c.shared ? DK : DV) * HP;                        // V source head stride
     long long bufsize[NBUF];
     bufsize[BQ] = T * c.H * DK * 2;
     bufsize[BK] = c.nb * c.bs * rsk;
@@ -280,7 +283,7 @@ void run(const Case &c, const Shape &sh, Stats stv[3])
             const int ntile = pa::seq_tiles(p, ql);
             const int prefix = pa::seq_prefix(kv, ql);
             const int t0 = cu[b];
-            for (int g = 0; g < c.Hkv; ++g) {
+            for (int g = 0; g < Hkv; ++g) {
                 const long long kgh = (long long)g * RBK;      // head column, K cache
                 const long long vgh = (long long)g * vhead;    // head column, V source
                 for (int qt = 0; qt < ntile; ++qt) {
@@ -329,12 +332,12 @@ void run(const Case &c, const Shape &sh, Stats stv[3])
                     // streaming kernel: the unit's Q tile, loaded with its first
                     // chunk (rows past the unit read the zero page)
                     if (sh.stream) {
-                        for (int m = 0; m < IPGK; ++m) {
+                        for (int m = 0; m < IPGQ; ++m) {
                             for (int l = 0; l < 64; ++l) {
                                 const int x = m * 1024 + 16 * l;
-                                const int qrow = x / RBK;
-                                const int qlp = ((x % RBK) >> 4) ^ (qrow & 7);
-                                if (16 * qlp + 16 > RBK)
+                                const int qrow = x / RBQ;
+                                const int qlp = ((x % RBQ) >> 4) ^ (qrow & 7);
+                                if (16 * qlp + 16 > RBQ)
                                     fail("Q piece past its row");
                                 const int rg = qt * 16 + qrow;
                                 const int t = t0 + rg / G;
@@ -345,7 +348,7 @@ void run(const Case &c, const Shape &sh, Stats stv[3])
                                 } else {
                                     ln[l] = Lane{BZ, 16LL * qlp, 0, -1};
                                 }
-                                if (m * 1024 + 16 * l + 16 > 16 * RBK)
+                                if (m * 1024 + 16 * l + 16 > 16 * RBQ)
                                     fail("Q tile LDS write past its stage");
                             }
                             instr(st[1], ln, 16, bufsize, "Q");
@@ -516,7 +519,7 @@ int main(int argc, char **argv)
         // every kernel shape the library has for this case
         const int mode = c.mode == M_BAND ? 1 : c.mode == M_TENSOR ? 2 : c.mode == M_SPARSE ? 3 : 0;
         std::vector<Shape> shapes;
-        for (int v = 0; v <= 4; ++v) {
+        for (int v = 0; v <= 7; ++v) {
             pa::TileShape t{};
             const void *k = mode == 1 ? pa::tile_kernel_band(0, c.DK, c.DV, v, c.shared != 0, &t)
                           : mode == 2 ? pa::tile_kernel_tensor(0, c.DK, c.DV, v, c.shared != 0, &t)
@@ -524,14 +527,20 @@ int main(int argc, char **argv)
                                       : pa::tile_kernel_plain(0, c.DK, c.DV, v, c.shared != 0, &t);
             if (!k)
                 continue;
+            // variants 5 to 7: the streaming kernel on head pairs (the library
+            // takes them for an even number of KV heads)
+            const int hp = v >= 5 ? 2 : 1;
+            if (hp == 2 && c.Hkv % 2 != 0)
+                continue;
             Shape s{pa::tile_streaming(c.DK, c.DV, v), t.mb, t.kt, t.nw, t.cs, t.s,
-                    c.shared != 0 && c.DK > 256};   // only the 576/512 instances read V out of the K tile
+                    c.shared != 0 && c.DK > 256,   // only the 576/512 instances read V out of the K tile
+                    hp};
             if (!s.stream && pa::tile_rows(c.DK, c.DV, v, c.shared != 0, mode) != 16 * t.mb * (t.nw / t.cs))
                 fail("tile rows disagree with the shape of variant " + std::to_string(v));
             bool dup = false;
             for (const Shape &o : shapes)
                 dup |= o.stream == s.stream && o.mb == s.mb && o.kt == s.kt && o.nw == s.nw && o.cs == s.cs &&
-                       o.sh == s.sh;
+                       o.sh == s.sh && o.hp == s.hp;
             if (!dup)
                 shapes.push_back(s);
         }
@@ -540,8 +549,8 @@ int main(int argc, char **argv)
         for (const Shape &s : shapes) {
             Stats st[3];
             run(c, s, st);
-            std::printf("case %s kernel %s_MB%d_KT%d_NW%d", c.name.c_str(), s.stream ? "stream" : "tile", s.mb, s.kt,
-                        s.nw);
+            std::printf("case %s kernel %s%s_MB%d_KT%d_NW%d", c.name.c_str(), s.stream ? "stream" : "tile",
+                        s.hp > 1 ? "_pairs" : "", s.mb, s.kt, s.nw);
             print_stats("kv", st[0]);
             print_stats("q", st[1]);
             print_stats("mask", st[2]);
