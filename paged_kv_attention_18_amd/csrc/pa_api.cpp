@@ -155,7 +155,10 @@ struct pa_handle {
                     v.partitions = w3 < v.partitions ? w3 : v.partitions;
                 }
             }
-            v.pieces_per_worker = v.streaming ? 1 : kMaxPiecesPerWorker;
+            // one piece per worker for the streaming kernel and for the one
+            // kernel above head size 256 (variant 0: 64-row tiles whose fp32
+            // partials, 131 KB per piece at 576/512, outweigh finer pieces)
+            v.pieces_per_worker = (v.streaming || var == 0) ? 1 : kMaxPiecesPerWorker;
             // the self-planning streaming kernel may add rounds of claimed
             // pieces (pa::PieceMap)
             v.claimed_tail = v.streaming && pa::tile_supported(dk, dv, v.tail_variant) &&
