@@ -210,10 +210,13 @@ def read_peak(dev, nbytes=2 << 30, reps=10):
             "method": f"pa_read_probe: {wgs} workgroups x 256 threads, contiguous shares, 8 x 16-byte loads in flight per thread"}
 
 
-def measure(w, dev, steps, warmup, flags=0, partitions=0, graph=False, copies=0, peak=None):
-    """Times `steps` forward passes of workload w (after `warmup`): the whole
-    pass without per-kernel events (throughput), each pass on its own
-    (percentiles), and each kernel with the library's HIP events (roofline)."""
+def measure(w, dev, steps, warmup, flags=0, partitions=0, graph=False, copies=0, peak=None, warmup_ms=150.0):
+    """Times `steps` forward passes of workload w (after `warmup` untimed
+    ones): the whole pass without per-kernel events (throughput), each pass
+    on its own (percentiles), and each kernel with the library's HIP events
+    (roofline).  warmup None: at least 5 passes and at least warmup_ms of GPU
+    time (the matrix-core kernels run 15-25 % slower in their first ~50 ms of
+    sustained work, while the clocks settle)."""
     import numpy as np
     import torch
 
@@ -235,8 +238,22 @@ def measure(w, dev, steps, warmup, flags=0, partitions=0, graph=False, copies=0,
         att.forward(p.query, kcs[k % copies], vcs[k % copies], p.block_tables, p.context_lens,
                     p.q_seq_lens, max_q_seq_len=ql_max, out=out, topk_indices=p.topk_idx)
 
-    for k in range(warmup):
-        step(k)
+    if warmup is None:
+        # two passes for the one-time costs, then one timed to size the rest
+        step(0)
+        step(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        step(2)
+        e1.record()
+        torch.cuda.synchronize()
+        warmup = min(20000, max(5, 3 + math.ceil(warmup_ms / max(e0.elapsed_time(e1), 1e-3))))
+        for k in range(3, warmup):
+            step(k)
+    else:
+        for k in range(warmup):
+            step(k)
     torch.cuda.synchronize()
     if att.device_error() != 0:
         raise RuntimeError("device error flag set during warm-up")
@@ -313,7 +330,7 @@ def measure(w, dev, steps, warmup, flags=0, partitions=0, graph=False, copies=0,
             roofline["measured_read_peak"] = peak
             roofline["frac_of_measured_read_peak"] = hbm_gbps / peak
     res = {
-        "p": p, "desc": desc, "copies": copies, "ms_per_step": ms_per_step, "step_ms": pct(step_ms),
+        "p": p, "desc": desc, "copies": copies, "warmup": warmup, "ms_per_step": ms_per_step, "step_ms": pct(step_ms),
         "attention_ms": pct(attn), "kv_bytes": kv_bytes, "flops": flops, "roofline": roofline,
         "kernels_ms": {"plan": kms[0] / planned if planned else None, "attention": attn_ms,
                        "merge": kms[2] / passes},
@@ -345,7 +362,11 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed passes before the timed ones (default: at least 5 and at least --warmup-ms)")
+    ap.add_argument("--warmup-ms", type=float, default=150.0,
+                    help="GPU time of the default warm-up, in ms (the compute-bound kernels speed up over the "
+                         "first ~50 ms of sustained work)")
     ap.add_argument("--workload", default="skewed_long_decode",
                     help="tiny_decode | gqa_decode | skewed_long_decode | splitfuse_causal | mla_decode | ...")
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies to rotate over (0 = auto)")
@@ -389,7 +410,7 @@ def main():
           file=sys.stderr, flush=True)
     w = synth.WORKLOADS[int(args.workload)] if args.workload.isdigit() else synth.by_name(args.workload)
     r = measure(w, dev, args.steps, args.warmup, args.flags, args.partitions, args.graph, args.copies,
-                peak["gbps_best"])
+                peak["gbps_best"], args.warmup_ms)
     print(f"# {w.name}: {r['ms_per_step'] * 1e3:.1f} us per step", file=sys.stderr, flush=True)
     p = r["p"]
     tokens = p.num_q_tokens
@@ -399,7 +420,7 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": r["warmup"],
         "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -428,7 +449,8 @@ def main():
         rows = []
         for name in TABLE:
             wt = synth.by_name(name)
-            rt = headline if name == w.name else measure(wt, dev, args.table_steps, 3, peak=peak["gbps_best"])
+            rt = headline if name == w.name else measure(wt, dev, args.table_steps, None, peak=peak["gbps_best"],
+                                                             warmup_ms=args.warmup_ms)
             rows.append(table_row(wt, rt))
             print(f"# table {name}: {rt['step_ms']['p50'] * 1e3:.1f} us p50", file=sys.stderr, flush=True)
             if rt is not headline:

@@ -269,14 +269,17 @@ const char *pa_status_string(pa_status s);
 pa_status pa_get_device_error(pa_handle *h, uint32_t *code, int32_t clear);
 
 /*
- * Per-kernel timing for measurement.  While enabled, pa_forward records HIP
- * events on its stream around each of its kernels (plan, attention, merge).
+ * Per-kernel timing for measurement.  While enabled, pa_forward launches
+ * each of its kernels (plan, attention, merge) with a pair of HIP events on
+ * its stream that take the kernel's own start and end timestamps
+ * (hipExtLaunchKernel; no marker packets are added between the kernels).
  * pa_read_timing synchronises, adds up the elapsed times of all recorded
  * passes since the last read into ms[3] (plan, attention, merge) and the
  * number of passes into *count, and resets the totals.  A pass whose
  * attention kernel planned for itself launches no plan kernel: ms[0] sums
  * the passes that launched one, and *plan_launches (if not NULL) receives
- * their number.  If per_pass_cap > 0, per_pass_ms (host, 3 * per_pass_cap
+ * their number; a pass without split entries launches no merge kernel and
+ * counts 0 for it.  If per_pass_cap > 0, per_pass_ms (host, 3 * per_pass_cap
  * doubles) receives (plan, attention, merge) of each of the first
  * per_pass_cap passes, plan = -1 for a pass without a plan kernel.  At most
  * 1024 passes are kept between reads; later ones are not timed.

@@ -16,6 +16,7 @@
 namespace {
 
 constexpr int kMaxTimedPasses = 1024;
+constexpr int kEventsPerPass = 6;   // start and stop of the plan, attention and merge kernels
 // Pieces of the item range per worker in balanced mode.  With more pieces
 // than workers, workers that finish early take the remaining pieces, which
 // evens out end times; it pays where a chunk is long (many rows on the
@@ -97,8 +98,9 @@ struct pa_handle {
     size_t max_pieces = 0;   // pieces of a pass, at most (split entries and partial slot pairs)
     // timing
     bool timing = false;
-    std::vector<hipEvent_t> events;   // 4 per pass
+    std::vector<hipEvent_t> events;   // per pass: start and stop of plan, attention, merge
     std::vector<char> planned;        // per timed pass: the plan kernel was launched
+    std::vector<char> merged;         // ... the merge kernel was launched
     int timed = 0;
 
     Variant choose(int max_q) const
@@ -525,29 +527,26 @@ static int64_t pass_pieces(const pa::Params &p)
 static pa_status launch_pass(pa_handle *h, const pa::Params &p, const Variant &v, hipStream_t s)
 {
     const pa_config &c = h->cfg;
+    // timed passes: each kernel's own start and end (events on the launch)
     const bool timed = h->timing && h->timed < kMaxTimedPasses;
-    hipEvent_t *ev = timed ? &h->events[4 * h->timed] : nullptr;
-    if (timed && hipEventRecord(ev[0], s) != hipSuccess)
+    hipEvent_t *ev = timed ? &h->events[kEventsPerPass * h->timed] : nullptr;
+    hipEvent_t none = nullptr;
+    if (!p.self_plan && pa::launch_plan(p, s, timed ? ev[0] : none, timed ? ev[1] : none) != hipSuccess)
         return PA_ERR_HIP;
-    if (!p.self_plan && pa::launch_plan(p, s) != hipSuccess)
-        return PA_ERR_HIP;
-    if (timed && hipEventRecord(ev[1], s) != hipSuccess)
-        return PA_ERR_HIP;
-    hipError_t e = v.path == 0 ? pa::launch_decode(p, c.dtype, v.rows_pad, s)
+    hipError_t e = v.path == 0 ? pa::launch_decode(p, c.dtype, v.rows_pad, s, timed ? ev[2] : none,
+                                                   timed ? ev[3] : none)
                                : pa::launch_tile(p, c.dtype,
                                                  p.self_plan ? (p.tail_min > 0 ? v.tail_variant : v.self_variant)
                                                              : v.tile_variant,
-                                                 s);
+                                                 s, timed ? ev[2] : none, timed ? ev[3] : none);
     if (e != hipSuccess)
         return PA_ERR_HIP;
-    if (timed && hipEventRecord(ev[2], s) != hipSuccess)
-        return PA_ERR_HIP;
-    if (pa::launch_merge(p, c.dtype, s) != hipSuccess)
+    bool merged = false;
+    if (pa::launch_merge(p, c.dtype, s, timed ? ev[4] : none, timed ? ev[5] : none, &merged) != hipSuccess)
         return PA_ERR_HIP;
     if (timed) {
-        if (hipEventRecord(ev[3], s) != hipSuccess)
-            return PA_ERR_HIP;
         h->planned[h->timed] = p.self_plan ? 0 : 1;
+        h->merged[h->timed] = merged ? 1 : 0;
         ++h->timed;
     }
     return PA_OK;
@@ -609,8 +608,9 @@ pa_status pa_set_timing(pa_handle *h, int32_t enable)
     if (!h)
         return PA_ERR_INVALID_ARG;
     if (enable && h->events.empty()) {
-        h->events.resize(4 * kMaxTimedPasses);
+        h->events.resize(kEventsPerPass * kMaxTimedPasses);
         h->planned.assign(kMaxTimedPasses, 0);
+        h->merged.assign(kMaxTimedPasses, 0);
         for (auto &e : h->events)
             if (hipEventCreate(&e) != hipSuccess)
                 return PA_ERR_HIP;
@@ -629,19 +629,21 @@ pa_status pa_read_timing(pa_handle *h, double ms[3], int32_t *count, int32_t *pl
     *count = h->timed;
     int planned = 0;
     if (h->timed > 0) {
-        if (hipEventSynchronize(h->events[4 * h->timed - 1]) != hipSuccess)
+        const int last = h->timed - 1;
+        if (hipEventSynchronize(h->events[kEventsPerPass * last + (h->merged[last] ? 5 : 3)]) != hipSuccess)
             return PA_ERR_HIP;
         for (int k = 0; k < h->timed; ++k) {
             for (int j = 0; j < 3; ++j) {
+                // passes whose kernel planned for itself launched no plan
+                // kernel (-1); passes without split entries, no merge (0)
+                const bool none = (j == 0 && !h->planned[k]) || (j == 2 && !h->merged[k]);
                 float t = 0.f;
-                if (hipEventElapsedTime(&t, h->events[4 * k + j], h->events[4 * k + j + 1]) != hipSuccess)
+                if (!none && hipEventElapsedTime(&t, h->events[kEventsPerPass * k + 2 * j],
+                                                 h->events[kEventsPerPass * k + 2 * j + 1]) != hipSuccess)
                     return PA_ERR_HIP;
-                // passes whose kernel planned for itself launched no plan kernel
-                const bool none = j == 0 && !h->planned[k];
-                if (!none)
-                    ms[j] += t;
+                ms[j] += t;
                 if (k < per_pass_cap)
-                    per_pass_ms[3 * k + j] = none ? -1.0 : (double)t;
+                    per_pass_ms[3 * k + j] = (j == 0 && !h->planned[k]) ? -1.0 : (double)t;
             }
             planned += h->planned[k] ? 1 : 0;
         }

@@ -525,7 +525,7 @@ int decode_workers_per_cu(int dtype, int dk, int dv, int rows_pad)
     return n * (kThreads / 64);
 }
 
-hipError_t launch_decode(const Params &p, int dtype, int rows_pad, hipStream_t s)
+hipError_t launch_decode(const Params &p, int dtype, int rows_pad, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
     const void *k = decode_kernel_ptr(dtype, p.head_size_k, p.head_size_v, rows_pad);
     if (!k)
@@ -533,7 +533,7 @@ hipError_t launch_decode(const Params &p, int dtype, int rows_pad, hipStream_t s
     const int per_wg = kThreads / 64;
     const int grid = (p.partitions + per_wg - 1) / per_wg;
     void *args[] = {(void *)&p};
-    return hipLaunchKernel(k, dim3(grid), dim3(kThreads), args, 0, s);
+    return launch_kernel(k, dim3(grid), dim3(kThreads), args, s, e0, e1);
 }
 
 }  // namespace pa

@@ -2,6 +2,7 @@
 // of the paged-attention library (gfx950).  Internal: not part of the C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -134,12 +135,29 @@ constexpr int kTailMinChunks = 16;
 // streams gains less than the merge work the extra pieces cost.
 constexpr int kTailMinShare = 20;   // in units of the tail minimum
 
-// Launchers (defined in the .hip files).
-hipError_t launch_plan(const Params &p, hipStream_t s);
-hipError_t launch_merge(const Params &p, int dtype, hipStream_t s);
+// Launches kernel k.  With events (timed passes) the start and stop events
+// take the kernel's own start and end timestamps (hipExtLaunchKernel): no
+// marker packets between the kernels of a pass, which slowed the
+// compute-bound kernels by 3-5 % when markers were recorded around them.
+inline hipError_t launch_kernel(const void *k, dim3 grid, dim3 block, void **args, hipStream_t s, hipEvent_t e0,
+                                hipEvent_t e1)
+{
+    if (e0 || e1)
+        return hipExtLaunchKernel(k, grid, block, args, 0, s, e0, e1, 0);
+    return hipLaunchKernel(k, grid, block, args, 0, s);
+}
+
+// Launchers (defined in the .hip files); e0, e1: optional timing events.
+hipError_t launch_plan(const Params &p, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+// *launched (if given): whether a kernel was enqueued (passes without split
+// entries have nothing to merge)
+hipError_t launch_merge(const Params &p, int dtype, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr,
+                        bool *launched = nullptr);
 // Returns hipErrorInvalidValue when no kernel exists for the shape.
-hipError_t launch_decode(const Params &p, int dtype, int rows_pad, hipStream_t s);
-hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s);
+hipError_t launch_decode(const Params &p, int dtype, int rows_pad, hipStream_t s, hipEvent_t e0 = nullptr,
+                         hipEvent_t e1 = nullptr);
+hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s, hipEvent_t e0 = nullptr,
+                       hipEvent_t e1 = nullptr);
 // Allocation-free passes (pa_forward_noalloc).  validate_config applies
 // pa_create's checks.  forward_in_buffer runs one pass of pa_forward for cfg
 // without a handle: it lays the pass's workspace out in `base` (device

@@ -437,16 +437,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int row_group
 
 }  // namespace
 
-hipError_t launch_plan(const Params &p, hipStream_t s)
+hipError_t launch_plan(const Params &p, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
     // one workgroup when the piece phase cannot keep the sequences in LDS
     const int wgs = (p.no_split || p.batch > kPlanLdsB) ? 1 : (p.pieces + kPlanPieces - 1) / kPlanPieces;
-    hipLaunchKernelGGL(plan_kernel, dim3(wgs > 0 ? wgs : 1), dim3(kPlanThreads), 0, s, p);
-    return hipGetLastError();
+    Params pc = p;
+    void *args[] = {(void *)&pc};
+    return launch_kernel((const void *)&plan_kernel, dim3(wgs > 0 ? wgs : 1), dim3(kPlanThreads), args, s, e0, e1);
 }
 
-hipError_t launch_merge(const Params &p, int dtype, hipStream_t s)
+hipError_t launch_merge(const Params &p, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1, bool *launched)
 {
+    if (launched)
+        *launched = false;
     // row groups of the largest unit this pass can have (a decode unit has
     // only its query heads' rows, fewer than the tile's)
     const long long max_rows = (long long)p.max_q * p.group;
@@ -464,8 +467,13 @@ hipError_t launch_merge(const Params &p, int dtype, hipStream_t s)
     const bool tail = p.self_plan && p.tail_min > 0;
     void (*k)(Params, int) = dtype == 0 ? (tail ? merge_kernel<0, true> : merge_kernel<0, false>)
                                         : (tail ? merge_kernel<1, true> : merge_kernel<1, false>);
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, p, row_groups);
-    return hipGetLastError();
+    Params pc = p;
+    int rg = row_groups;
+    void *args[] = {(void *)&pc, (void *)&rg};
+    const hipError_t e = launch_kernel((const void *)k, dim3((unsigned)grid), dim3(kThreads), args, s, e0, e1);
+    if (launched)
+        *launched = e == hipSuccess;
+    return e;
 }
 
 }  // namespace pa

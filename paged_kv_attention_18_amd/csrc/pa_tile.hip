@@ -59,7 +59,7 @@ int tile_workers_per_cu(int dtype, int dk, int dv, int variant, bool shared, int
     return n;
 }
 
-hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s)
+hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
     TileShape t;
     const int mode = p.band ? MODE_BAND : (p.tmask ? MODE_TENSOR : (p.sparse ? MODE_SPARSE : MODE_PLAIN));
@@ -77,7 +77,7 @@ hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s)
         (p.self_plan && (t.nw != 1 || p.batch > kSelfPlanMaxBatch || p.pieces != p.partitions || p.max_q > 16)))
         return hipErrorInvalidValue;
     void *args[] = {(void *)&p};
-    return hipLaunchKernel(k, dim3(p.partitions), dim3(t.threads), args, 0, s);
+    return launch_kernel(k, dim3(p.partitions), dim3(t.threads), args, s, e0, e1);
 }
 
 }  // namespace pa
