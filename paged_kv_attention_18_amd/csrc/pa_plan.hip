@@ -44,31 +44,30 @@ constexpr int kPlanLdsT = 8192;
 // consecutive tasks (tile_first_task, tile_claim), so the tiles of a group
 // start close together and read their sequence's KV from that XCD's L2.  The
 // queues' claim counters start at 0.
-__device__ void build_tile_queues(const Params &p, int *s_order, int *s_key, int *s_xtot, const int *s_ipg,
+// s_key[b]: the sequence's longest row tile in chunks (the first phase of the
+// plan kernel leaves it there).
+__device__ void build_tile_queues(const Params &p, int *s_order, const int *s_key, int *s_xtot, const int *s_ipg,
                                   const int *s_ql)
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int B = p.batch, Hkv = p.kv_head_num;
-    // rank key: the sequence's longest row tile in chunks (a queue then
-    // runs roughly longest task first), then its work, then its index
-    for (int b = tid; b < B; b += kPlanThreads) {
-        const int kv = p.ws.kvlen[b], ql = s_ql[b];
-        int lm = 0;
-        for (int qt = seq_tiles(p, ql) - 1; qt >= 0; --qt) {
-            const int n = unit_chunks(p, kv, ql, qt);
-            lm = n > lm ? n : lm;
-        }
-        s_key[b] = lm;
-    }
-    __syncthreads();
-    for (int b = tid; b < B; b += kPlanThreads) {
+    // rank: the longest row tile (a queue then runs roughly longest task
+    // first), then the work, then the index; one wave per sequence counts
+    // the sequences ahead of it, 64 at a time
+    for (int b = wv; b < B; b += kPlanThreads / 64) {
         const int m = s_key[b], w = s_ipg[b];
         int r = 0;
-        for (int b2 = 0; b2 < B; ++b2) {
-            const int m2 = s_key[b2], w2 = s_ipg[b2];
-            r += (m2 > m || (m2 == m && (w2 > w || (w2 == w && b2 < b)))) ? 1 : 0;
+        for (int b0 = 0; b0 < B; b0 += 64) {
+            const int b2 = b0 + lane;
+            bool ahead = false;
+            if (b2 < B) {
+                const int m2 = s_key[b2], w2 = s_ipg[b2];
+                ahead = m2 > m || (m2 == m && (w2 > w || (w2 == w && b2 < b)));
+            }
+            r += __popcll(__ballot(ahead));
         }
-        s_order[r] = b;
+        if (lane == 0)
+            s_order[r] = b;
     }
     __syncthreads();
     const int NG = B * Hkv;
@@ -189,6 +188,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         }
         if (lmax > 0)
             atomicMax(&s_lmax, lmax);
+        if (b < p.batch && b < kTileOrderMaxBatch)
+            s_key[b] = lmax;   // whole-tile mode: the rank key
         const int items = ipg * p.kv_head_num;
         if (lead && b < p.batch) {
             p.ws.qlen[b] = ql;
@@ -263,7 +264,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
             return;
         const int k0 = spread ? blockIdx.x * kPlanPieces : 0;
         const int k1 = spread ? min(k0 + kPlanPieces, p.pieces) : p.pieces;
-        auto wsb_of = [&](int b) { return lds ? s_wsb[b] : p.ws.wsb[b]; };
         const bool table = lds && s_carry_t <= kPlanLdsT;
         // Piece k starts at item k * pe, in the last sequence b with
         // wsb[b] <= k * pe.  Its split entry (entry k - 1) records the unit
@@ -271,23 +271,45 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p)
         const int nk = ordered ? 0 : ((W + pe - 1) / pe < p.pieces ? (W + pe - 1) / pe : p.pieces);
         for (int k = k0 + tid; k < k1 && k < nk; k += kPlanThreads) {
             const int s = k * pe;
+            // (LDS and global reads on separate paths: a pointer that may be
+            // either compiles to flat loads, each waited for)
             int lo = 0, hi = p.batch - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (wsb_of(mid) <= s)
-                    lo = mid;
-                else
-                    hi = mid - 1;
+            if (lds) {
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_wsb[mid] <= s)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+            } else {
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (p.ws.wsb[mid] <= s)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
             }
             const int b = lo;
             p.ws.wg_b[k] = b;
             if (k == 0)
                 continue;
-            const int kv = lds ? s_kv[b] : p.ws.kvlen[b];
-            const int ql = lds ? s_ql[b] : p.ws.qlen[b];
-            const int ipg = lds ? s_ipg[b] : p.ws.ipg[b];
-            const int t0 = lds ? s_t0[b] : p.ws.cu_q[b];
-            (void)piece_start(p, k, s, s - pe, b, kv, ql, ipg, wsb_of(b), t0, true, table ? s_tp + s_toff[b] : nullptr);
+            int kv, ql, ipg, t0, wb;
+            if (lds) {
+                kv = s_kv[b];
+                ql = s_ql[b];
+                ipg = s_ipg[b];
+                t0 = s_t0[b];
+                wb = s_wsb[b];
+            } else {
+                kv = p.ws.kvlen[b];
+                ql = p.ws.qlen[b];
+                ipg = p.ws.ipg[b];
+                t0 = p.ws.cu_q[b];
+                wb = p.ws.wsb[b];
+            }
+            (void)piece_start(p, k, s, s - pe, b, kv, ql, ipg, wb, t0, true, table ? s_tp + s_toff[b] : nullptr);
         }
         // boundaries past the last item (every boundary in whole-tile mode)
         for (int k = max(nk, k0) + tid; k < k1; k += kPlanThreads)
