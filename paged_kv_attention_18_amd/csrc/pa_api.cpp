@@ -129,11 +129,13 @@ struct pa_handle {
             const bool sh = (cfg.flags & PA_FLAG_SHARED_KV) != 0;
             const int mode = kernel_mode(cfg.mask);   // the kernels' shapes depend on the mode
             int var = 0;
-            // (no variant 2 with the tensor mask; sparse lists: variant 1
-            // below 576, the one 576/512 variant above)
+            // (variant 2 with the tensor mask at head sizes up to 128 only;
+            // sparse lists: variant 1 below 576, the one 576/512 variant
+            // above)
             if ((rows > 16 || cfg.mask == PA_MASK_SPARSE) && pa::tile_supported(dk, dv, 1))
                 var = (rows > pa::tile_rows(dk, dv, 1, sh, mode) && pa::tile_supported(dk, dv, 2) &&
-                       cfg.mask != PA_MASK_TENSOR && cfg.mask != PA_MASK_SPARSE) ? 2 : 1;
+                       cfg.mask != PA_MASK_SPARSE &&
+                       (cfg.mask != PA_MASK_TENSOR || pa::tile_rows(dk, dv, 2, sh, mode) > 0)) ? 2 : 1;
             v.streaming = pa::tile_streaming(dk, dv, var);
             v.hp = 1;
             v.self_variant = kSelfPlanVariant;

@@ -1867,9 +1867,8 @@ const void *pick(TileShape *t)
     return (const void *)&tile_kernel<DT, DK, DV, MB, KT, NW, CS, S, SH, MODE>;
 }
 
-// The tensor mask has variants 0 and 1 only (variant 1 with 32-token
-// chunks, which leaves LDS room for the matrix slices); the host takes
-// variant 1 for every unit of more than 16 rows.
+// The tensor mask takes 32-token chunks in variants 1 and 2 (LDS room for
+// the matrix slices); variant 2 (128-row tiles) at head sizes up to 128.
 template <int DT, int DK, int DV, int MODE>
 const void *kernel_for(int variant, bool shared, TileShape *t)
 {
@@ -1925,8 +1924,14 @@ const void *kernel_for(int variant, bool shared, TileShape *t)
                 }
             }
             if constexpr (MODE == MODE_TENSOR) {
+                // 32-token chunks: the mask slabs of two stages fit beside
+                // the K/V tiles of two workgroups per CU
                 if (variant == 1)
                     return pick<DT, DK, DV, 1, 32, 4, 1, 2, false, MODE>(t);
+                if constexpr (DK <= 128 && DV <= 128) {
+                    if (variant == 2)
+                        return pick<DT, DK, DV, 2, 32, 4, 1, 2, false, MODE>(t);
+                }
             } else {
                 if (variant == 1)
                     return pick<DT, DK, DV, 1, KT, 4, 1, 2, false, MODE>(t);
