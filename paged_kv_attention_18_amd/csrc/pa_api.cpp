@@ -83,6 +83,9 @@ constexpr bool kHeadPairs = true;
 constexpr int kPairVariant = 5, kPairSelfPlanVariant = 6, kPairSelfPlanTailVariant = 7;
 // band units of at most this many KV chunks run whole (no split, no merge)
 constexpr int kBandWholeUnitChunks = 8;
+// decode passes whose units have at most this many chunks (by the block
+// tables' capacity) run every unit whole on the streaming kernel
+constexpr int kStreamWholeUnitChunks = 8;
 
 }  // namespace
 
@@ -475,6 +478,18 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
             units <= std::min(v.partitions, h->max_partitions))
             p.no_split = 1;
     }
+    // Short decode passes (no unit longer than kStreamWholeUnitChunks
+    // chunks, no more units than workers): the self-planning streaming
+    // kernel runs every unit whole, so the pass has no partials and no merge
+    // launch (the merge's launch and round trips outweigh splitting units of
+    // a few chunks).
+    if (!p.no_split && v.path == 1 && v.streaming && batch <= pa::kSelfPlanMaxBatch && max_q_seq_len <= 16) {
+        const int64_t units = (int64_t)batch * p.kv_head_num * p.max_tiles;
+        const int64_t cap = (int64_t)c.max_num_blocks_per_seq * c.block_size;
+        if ((cap + v.chunk - 1) / v.chunk <= kStreamWholeUnitChunks &&
+            units <= std::min(v.partitions, h->max_partitions))
+            p.no_split = 1;
+    }
     p.partitions = p.no_split ? batch * p.kv_head_num * p.max_tiles
                               : (v.partitions < h->max_partitions ? v.partitions : h->max_partitions);
     // Sparse lists: every unit holds the same ceil(topk / 16) chunks.  Cut
@@ -499,8 +514,8 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
     // The streaming kernel cuts its own pieces when the lengths fit in a
     // wave's registers: one launch fewer, and no wait on plan data when a
     // worker starts or moves to the next unit.
-    p.self_plan = (v.path == 1 && v.streaming && !p.no_split && batch <= pa::kSelfPlanMaxBatch &&
-                   p.pieces == p.partitions && max_q_seq_len <= 16 &&
+    p.self_plan = (v.path == 1 && v.streaming && batch <= pa::kSelfPlanMaxBatch &&
+                   (p.no_split || p.pieces == p.partitions) && max_q_seq_len <= 16 &&
                    pa::tile_supported(c.head_size_k, c.head_size_v, v.self_variant))
                       ? 1
                       : 0;
@@ -508,7 +523,7 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
     // shrink down to kTailMinChunks chunks, where the block tables can hold
     // a pass long enough for them (the kernel decides from the lengths);
     // shorter passes take the kernel without the claiming code
-    if (p.self_plan && v.claimed_tail) {
+    if (p.self_plan && v.claimed_tail && !p.no_split) {
         const int64_t cap = (int64_t)c.max_num_blocks_per_seq * c.block_size;
         const int64_t w_max = (int64_t)batch * p.kv_head_num * ((cap + v.chunk - 1) / v.chunk);
         if (w_max >= (int64_t)pa::kTailMinShare * pa::kTailMinChunks * p.partitions)

@@ -70,11 +70,12 @@ hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s, h
     // only the streaming kernel's variants 3 and 4 (6 and 7 on head pairs)
     // plan for themselves, for at most kSelfPlanMaxBatch sequences of at most
     // 16 query tokens, one static piece per workgroup (variants 4 and 7 may
-    // add claimed pieces)
+    // add claimed pieces) or, without split, one whole unit per workgroup
     const bool self_var = variant == 3 || variant == 4 || variant == 6 || variant == 7;
     const bool tail_var = variant == 4 || variant == 7;
     if ((p.self_plan != 0) != self_var || (p.tail_min > 0) != tail_var ||
-        (p.self_plan && (t.nw != 1 || p.batch > kSelfPlanMaxBatch || p.pieces != p.partitions || p.max_q > 16)))
+        (p.self_plan && (t.nw != 1 || p.batch > kSelfPlanMaxBatch || (!p.no_split && p.pieces != p.partitions) ||
+                         p.max_q > 16)))
         return hipErrorInvalidValue;
     void *args[] = {(void *)&p};
     return launch_kernel(k, dim3(p.partitions), dim3(t.threads), args, s, e0, e1);

@@ -1290,6 +1290,40 @@ __global__ __launch_bounds__(128, DK * HP > 128 ? (HP > 1 ? 2 : 1) : 3) void str
             }
         }
         const int W = cw;
+        if (p.no_split) {
+            // Whole units (short passes): workgroup w runs unit (b, g) =
+            // (w / Hkv, w % Hkv) at once, so the pass writes no partials
+            // and launches no merge.
+            const int b = worker / p.kv_head_num, g = worker - b * p.kv_head_num;
+            have = b < p.batch;
+            if (have) {
+                const int l0 = b / spl, i0 = b - l0 * spl;   // the lane and slot holding b
+                auto pick4 = [&](const int(&r)[4]) __attribute__((always_inline)) {
+                    return __builtin_amdgcn_readlane(i0 == 0 ? r[0] : (i0 == 1 ? r[1] : (i0 == 2 ? r[2] : r[3])), l0);
+                };
+                const int ipg = pick4(ipr), kv = pick4(kvr), ql = pick4(qlr);
+                have = ipg > 0;
+                if (have) {
+                    ic.b = b;
+                    ic.g = g;
+                    ic.qt = 0;
+                    ic.c = 0;
+                    ic.ntile = seq_tiles(p, ql);
+                    ic.nch = unit_chunks(p, kv, ql, 0);
+                    ic.item = pick4(wsbr) + g * ipg;
+                    iend = ic.item + ipg;
+                }
+            }
+            if (worker == 0) {
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1)
+                    serr |= __shfl_xor(serr, d);
+                if (cq != p.num_q_tokens)
+                    serr |= PA_DEVERR_TOKENS;
+                if (lane == 0 && serr)
+                    set_error(p.ws.err, serr);
+            }
+        } else {
         const PieceMap ipm = self_piece_map(p, W);
         if (TAIL && lane == 0)
             s_pm = ipm;
@@ -1340,6 +1374,7 @@ __global__ __launch_bounds__(128, DK * HP > 128 ? (HP > 1 ? 2 : 1) : 3) void str
         ic = piece_start(p, ipiece, s0, sp0, b0, pick4(kvr), pick4(qlr), pick4(ipr), pick4(wsbr), pick4(t0r),
                          lane == 0);
         iend = s1;
+        }
         }
     } else {
         have = wg_range(p, ipiece, ic, iend);

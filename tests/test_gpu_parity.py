@@ -53,6 +53,26 @@ def test_decode_parity(case):
         check_full(p, flags=F.PA_FLAG_FORCE_VALU, what=f"decode valu {case}")
 
 
+# Short decode passes: block tables of at most 128 tokens (8 chunks of 16), so
+# the self-planning streaming kernel runs every unit whole (no partials, no
+# merge launch); with and without head pairs, an empty sequence included.
+SHORT_DECODE_CASES = [
+    # (lens, H, Hkv, D, bs, dtype)
+    ([116, 79, 105, 3], 4, 4, 64, 16, "f16"),
+    ([100, 37, 128, 0, 60, 1], 32, 8, 128, 16, "bf16"),     # head pairs (G = 4)
+    ([128, 17, 64], 16, 2, 128, 32, "f16"),                 # G = 8: head pairs of 16 rows
+    ([90, 128, 33], 8, 8, 256, 16, "bf16"),                 # Dk = 256
+]
+
+
+@pytest.mark.parametrize("case", SHORT_DECODE_CASES, ids=["G1", "G4_pairs", "G8_pairs", "D256"])
+def test_short_decode_runs_whole_units(case):
+    lens, H, Hkv, D, bs, dt = case
+    log(f"short decode {case}")
+    p_cpu = synth.custom(lens, H, Hkv, D, D, bs, dt, seed=41, max_blocks=128 // bs)
+    check_full(p_cpu, what=f"short decode {case}")
+
+
 @pytest.mark.parametrize("case", DECODE_CASES[:3], ids=["G1", "G4", "G8"])
 def test_decode_no_split_and_forced_mfma_agree(case):
     lens, H, Hkv, D, bs, dt = case

@@ -21,6 +21,8 @@ CASES = [
     ("decode_planned_valu",
      lambda: synth.custom([700, 129, 2050, 5], 32, 8, 128, 128, 128, "bf16", seed=7), F.PA_FLAG_FORCE_VALU,
      True, True),
+    ("decode_short_whole_units",   # every unit whole: neither a plan nor a merge kernel
+     lambda: synth.custom([116, 79, 105, 3], 32, 8, 128, 128, 16, "f16", seed=9, max_blocks=8), 0, False, False),
     ("causal_planned",
      lambda: synth.custom([300, 24, 900], 8, 2, 128, 128, 64, "f16", "causal", q_seq_lens=[40, 8, 200], seed=8),
      0, True, True),
