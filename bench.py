@@ -35,7 +35,7 @@ METRIC = "paged-attn decode tokens/s + achieved HBM GB/s (KV bytes read) vs peak
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # dense fp16 / bf16 matrix-core peak
 RIDGE = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)   # FLOP per byte where the bounds meet
-CPU_SHARE = 16          # host threads a one-GPU machine grants
+CPU_SHARE = 16          # host threads the CPU baseline uses at most (the host cores per GPU)
 
 
 def kernel_sources_digest():
