@@ -545,15 +545,18 @@ def test_block_permutation_bit_exact():
 def test_hip_graph_replays_match_eager():
     """pa_forward captured in a HIP graph (through torch's graph capture):
     every replay, with other GPU work and synchronisations in between,
-    gives the eager result bit for bit (decode with split units, and a
-    causal splitfuse mix on the matrix cores)."""
+    gives the eager result bit for bit (decode with split units, a causal
+    splitfuse mix on the matrix cores, the claimed tail, and a short decode
+    whose units run whole with no merge)."""
     log("graph replay")
     tail = synth.custom(np.random.default_rng(29).integers(1000, 4000, size=24).tolist(), 32, 8, 128, 128, 128,
                         "bf16", seed=29)
+    short = synth.custom([116, 79, 105, 3], 32, 8, 128, 128, 16, "f16", seed=30, max_blocks=8)
     for p_cpu, parts in ((synth.custom([3000, 100, 2049, 700], 32, 8, 128, 128, 128, "bf16", seed=27), 0),
                          (synth.custom([600, 90], 8, 2, 128, 128, 64, "f16", "causal", q_seq_lens=[130, 6],
                                        seed=28), 0),
-                         (tail, 16)):   # the streaming kernel's claimed tail (counter reset by the merge)
+                         (tail, 16),    # the streaming kernel's claimed tail (counter reset by the merge)
+                         (short, 0)):   # whole units: one kernel, no merge
         p = to_device(p_cpu)
         att = binding.for_problem(p, num_partitions=parts)
         T, H, Dv = p.num_q_tokens, p.workload.head_num, p.workload.head_size_v

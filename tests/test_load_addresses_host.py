@@ -1,6 +1,7 @@
 """Every LDS load of the matrix-core kernels, enumerated on the host
 (tests/lds_load_addr_host.cpp) for the named workloads at full size, the GPU
-parity tests' shapes and caches just under and just over 4 GiB.
+parity tests' shapes (the random sweep's included) and caches just under and
+just over 4 GiB.
 
 Asserted: every lane's address stays inside its buffer, row and LDS stage;
 the K/V and mask-slab loads split into a wave-uniform base (the kernel's own
@@ -20,6 +21,7 @@ import pytest
 from paged_kv_attention_18_amd import binding, synth
 
 import test_gpu_parity as gp
+import test_gpu_random_parity as rp
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 MODES = {"none": 0, "causal": 1, "band": 2, "tensor": 3, "sparse": 4}
@@ -71,6 +73,8 @@ def _test_shapes():
                                                        seed=13, shared_kv=shared))
     for i, case in enumerate(gp.SPARSE_CASES):
         yield _from_problem(f"sparse{i}", gp._sparse_problem(case, 21))
+    for i in range(rp.N_CASES):   # the seeded random sweep
+        yield _from_problem(f"random{i}", rp.draw(i)[1])
     for name, B, (lo, hi), qr, H, Hkv, Dk, Dv, bs, dt, mask, win, shared, P in gp.TAIL_MODE_CASES:
         rng = np.random.default_rng(B * 7 + P)
         lens = rng.integers(lo, hi, size=B).tolist()
