@@ -305,9 +305,11 @@ pa_status pa_read_probe(const void *src, int64_t bytes, uint32_t *sink, int32_t 
  * kernel, 1 for the MFMA tile kernel, 2 for the MFMA streaming kernel (units
  * of at most 16 rows), for a call with that max_q_seq_len (at most
  * cfg.max_q_seq_len); *rows_per_tile and *tokens_per_chunk describe its work
- * unit; *partitions is the attention grid size (a sparse-list pass takes at
- * most max(CUs, two per (sequence, KV head, row tile)) of them, and a
- * whole-unit pass one per unit).
+ * unit; *partitions is the number of workers a split pass launches.  A pass
+ * may launch fewer: a sparse-list pass at most max(CUs, two per (sequence,
+ * KV head, row tile)), and a pass whose units run whole (band units of a few
+ * chunks, decode passes whose block tables hold at most 8 chunks per
+ * sequence, PA_FLAG_NO_SPLIT) one workgroup per unit.
  */
 pa_status pa_describe(const pa_handle *h, int32_t max_q_seq_len, int32_t *path,
                       int32_t *rows_per_tile, int32_t *tokens_per_chunk, int32_t *partitions);
