@@ -25,7 +25,7 @@ namespace pa {
 //  (pieces P, P + 1, ...) until none is left, so the workers finish
 //  together even when they stream at different rates.  The pieces are
 //  either all alike, or (the self-planning streaming kernel, PieceMap) P
-//  static pieces holding about four fifths of the items followed by rounds
+//  static pieces holding about nine tenths of the items followed by rounds
 //  of smaller pieces that workers claim as they run out.  In no-split mode
 //  (per = 0) every workgroup is one unit.  A unit whose items lie in more
 //  than one piece is split: each of its pieces leaves an fp32 partial
@@ -866,14 +866,16 @@ __device__ __forceinline__ PieceMap header_piece_map(const int32_t *hdr)
 
 // The self-planning streaming kernel's map of W items: with a claimed tail
 // when the launch asks for one and every share holds at least
-// kTailMinShare * m items (static pieces of 4/5 of a share, so a tail holds
-// at least m), else one uniform piece per worker.
+// kTailMinShare * m items (static pieces of 9/10 of a share, so a tail holds
+// at least 2 m), else one uniform piece per worker.  (Static pieces of 4/5
+// took 5 us longer per pass on the long skewed decode with head pairs, 19/20
+// 20 us longer.)
 __host__ __device__ __forceinline__ PieceMap self_piece_map(const Params &p, int W)
 {
     const int P = p.partitions, m = p.tail_min;
     if (m > 0 && (int64_t)W >= (int64_t)kTailMinShare * m * P) {
         PieceMap pm{W, W / P, 0, m, P, 0};
-        pm.a = (int)(((int64_t)4 * pm.per) / 5);
+        pm.a = (int)(((int64_t)9 * pm.per) / 10);
         int left = pm.per - pm.a;
         while (left > 0)
             (void)tail_piece_size(pm, pm.nr++, left);

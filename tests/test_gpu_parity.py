@@ -646,7 +646,7 @@ def test_decode_batch_sizes_around_self_planning(batch):
 
 
 # The self-planning streaming kernel's claimed tail: each worker streams a
-# static piece of about four fifths of its share, then claims further, smaller
+# static piece of about nine tenths of its share, then claims further, smaller
 # pieces from a counter while it computes, so fast workers take more.  Few
 # workers make the tail appear at sizes the oracle finishes quickly (it needs
 # at least 20 * 16 chunks per worker); the map of pieces depends on the
