@@ -127,13 +127,15 @@ constexpr int kSelfPlanMaxBatch = 256;
 // has at most (1 + kTailRounds) * workers pieces.
 constexpr int kTailRounds = 8;
 // Smallest claimed piece of the streaming kernel, in chunks: a worker claims
-// its next piece while it computes the current one, at least 4 chunks
-// before its issuing side needs it (the ring is 4 stages deep); and every
-// piece beyond the first of a unit costs a partial write and its merge.
-constexpr int kTailMinChunks = 16;
+// its next piece when S + 4 chunks of the current one are left (S, the ring
+// depth, is at most 4), and the answer must be in LDS before its issuing side
+// needs it; and every piece beyond the first of a unit costs a partial write
+// and its merge.  (16 chunks took 4-6 us longer per pass on the long skewed
+// decode with head pairs: more small pieces in the merge.)
+constexpr int kTailMinChunks = 8;
 // Shares of fewer chunks per worker keep one piece each: balancing short
 // streams gains less than the merge work the extra pieces cost.
-constexpr int kTailMinShare = 20;   // in units of the tail minimum
+constexpr int kTailMinShare = 40;   // in units of the tail minimum (320 chunks)
 
 // Launches kernel k.  With events (timed passes) the start and stop events
 // take the kernel's own start and end timestamps (hipExtLaunchKernel): no

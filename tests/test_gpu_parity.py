@@ -649,7 +649,7 @@ def test_decode_batch_sizes_around_self_planning(batch):
 # static piece of about nine tenths of its share, then claims further, smaller
 # pieces from a counter while it computes, so fast workers take more.  Few
 # workers make the tail appear at sizes the oracle finishes quickly (it needs
-# at least 20 * 16 chunks per worker); the map of pieces depends on the
+# at least 320 chunks per worker); the map of pieces depends on the
 # lengths alone, so results are the same whichever worker ran which piece.
 TAIL_CASES = [
     # (batch, length range, H, Hkv, D, bs, dtype, workers)
