@@ -110,9 +110,13 @@ enum {
     PA_FLAG_SHARED_KV = 1u << 3,   /* one cache for K and V: the V row of a token is the leading
                                       head_size_v elements of its K row (requires Dv <= Dk); see
                                       pa_forward's value_cache */
-    PA_FLAG_STATIC_PIECES = 1u << 4 /* measurement: the decode streaming kernel keeps one piece per
-                                       worker (no pieces claimed at run time); results agree with
-                                       the default to the usual tolerance, not bit for bit */
+    PA_FLAG_STATIC_PIECES = 1u << 4, /* measurement: the decode streaming kernel keeps one piece per
+                                        worker (no pieces claimed at run time); results agree with
+                                        the default to the usual tolerance, not bit for bit */
+    PA_FLAG_PLAN_KERNEL = 1u << 5    /* testing: every pass runs the plan kernel (no attention kernel
+                                        cuts its own pieces).  Without a claimed tail (short passes,
+                                        or with PA_FLAG_STATIC_PIECES) the pieces are the same and so
+                                        are the results, bit for bit */
 };
 
 /* Device error word bits (pa_get_device_error). */

@@ -23,6 +23,7 @@ PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 PA_F16, PA_BF16 = 0, 1
 PA_MASK_NONE, PA_MASK_CAUSAL, PA_MASK_BAND, PA_MASK_TENSOR, PA_MASK_SPARSE = 0, 1, 2, 3, 4
 PA_FLAG_FORCE_VALU, PA_FLAG_FORCE_MFMA, PA_FLAG_NO_SPLIT, PA_FLAG_SHARED_KV, PA_FLAG_STATIC_PIECES = 1, 2, 4, 8, 16
+PA_FLAG_PLAN_KERNEL = 32
 PA_DEVERR_BLOCK_ID, PA_DEVERR_TABLE_SHORT, PA_DEVERR_QLEN, PA_DEVERR_TOKENS, PA_DEVERR_CTX = 1, 2, 4, 8, 16
 
 EXPORTS = ("pa_create", "pa_forward", "pa_forward_sparse", "pa_destroy", "pa_status_string",

@@ -40,6 +40,7 @@ struct Variant {
     bool streaming;      // MFMA: the one-wave streaming kernel (units of at most 16 rows)
     int hp;              // KV heads per unit (2: head pairs, streaming kernel)
     int self_variant, tail_variant;   // streaming: the self-planning variants (without, with claims)
+    bool tile_self;      // 576/512 tile kernel: its self-planning twin serves this mode at full occupancy
     int max_pieces() const { return partitions * (claimed_tail ? 1 + pa::kTailRounds : pieces_per_worker); }
 };
 
@@ -81,6 +82,9 @@ constexpr int kSelfPlanTailVariant = 4;
 // ones, which the memory system serves faster.
 constexpr bool kHeadPairs = true;
 constexpr int kPairVariant = 5, kPairSelfPlanVariant = 6, kPairSelfPlanTailVariant = 7;
+// The 576/512 tile kernel (variant 0) planning for itself, for passes of one
+// row tile per (sequence, KV head) and one piece per worker
+constexpr int kTileSelfPlanVariant = 8;
 // band units of at most this many KV chunks run whole (no split, no merge)
 constexpr int kBandWholeUnitChunks = 8;
 // decode passes whose units have at most this many chunks (by the block
@@ -155,6 +159,18 @@ struct pa_handle {
             v.rows_per_tile = pa::tile_rows(dk, dv, var, sh, mode);
             v.chunk = pa::tile_chunk(dk, dv, var, sh, mode);
             v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var, sh, mode);
+            // the self-planning twin of the 576/512 kernel, where it keeps
+            // the same workgroups per CU; not for the one-cache kernel
+            // without a mask, whose attention time grew by as much as the
+            // plan launch saved (272 -> 281 us on the 128-sequence MLA
+            // decode with one cache; the band and sparse-list modes of the
+            // same kernel still gain)
+            v.tile_self = !v.streaming && var == 0 && !(sh && cfg.mask == PA_MASK_NONE) &&
+                          pa::tile_chunk(dk, dv, kTileSelfPlanVariant, sh, mode) == v.chunk &&
+                          num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, kTileSelfPlanVariant, sh, mode) >=
+                              v.partitions;
+            if (v.tile_self)
+                v.self_variant = kTileSelfPlanVariant;
             if (v.streaming && pa::tile_supported(dk, dv, v.self_variant)) {
                 // the self-planning twins of the streaming kernel run the same grid
                 for (int sv : {v.self_variant, v.tail_variant}) {
@@ -211,7 +227,7 @@ static pa_status check_config(const pa_config *c)
     if ((c->flags & PA_FLAG_FORCE_VALU) && (c->flags & PA_FLAG_FORCE_MFMA))
         return PA_ERR_INVALID_ARG;
     if (c->flags & ~(uint32_t)(PA_FLAG_FORCE_VALU | PA_FLAG_FORCE_MFMA | PA_FLAG_NO_SPLIT | PA_FLAG_SHARED_KV |
-                               PA_FLAG_STATIC_PIECES))
+                               PA_FLAG_STATIC_PIECES | PA_FLAG_PLAN_KERNEL))
         return PA_ERR_INVALID_ARG;
     if ((c->flags & PA_FLAG_SHARED_KV) && c->head_size_v > c->head_size_k)
         return PA_ERR_INVALID_ARG;   // V must fit inside the K row
@@ -513,12 +529,18 @@ static pa_status setup_params(const pa_handle *h, const void *query, const void 
                        : 0;
     // The streaming kernel cuts its own pieces when the lengths fit in a
     // wave's registers: one launch fewer, and no wait on plan data when a
-    // worker starts or moves to the next unit.
-    p.self_plan = (v.path == 1 && v.streaming && batch <= pa::kSelfPlanMaxBatch &&
-                   (p.no_split || p.pieces == p.partitions) && max_q_seq_len <= 16 &&
-                   pa::tile_supported(c.head_size_k, c.head_size_v, v.self_variant))
+    // worker starts or moves to the next unit.  So does the 576/512 tile
+    // kernel for passes of one row tile per (sequence, KV head) (decode,
+    // sparse lists), whose pieces are then cut in the same way.
+    const bool stream_self = v.streaming && max_q_seq_len <= 16 &&
+                             pa::tile_supported(c.head_size_k, c.head_size_v, v.self_variant);
+    const bool tile_self = v.tile_self && p.max_tiles == 1;
+    p.self_plan = (v.path == 1 && (stream_self || tile_self) && batch <= pa::kSelfPlanMaxBatch &&
+                   (p.no_split || p.pieces == p.partitions) && !(c.flags & PA_FLAG_PLAN_KERNEL))
                       ? 1
                       : 0;
+    if (p.self_plan)
+        p.tile_order = 0;
     // self-planning: claimed pieces after the static ones, in rounds that
     // shrink down to kTailMinChunks chunks, where the block tables can hold
     // a pass long enough for them (the kernel decides from the lengths);

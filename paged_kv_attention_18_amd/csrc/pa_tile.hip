@@ -68,14 +68,17 @@ hipError_t launch_tile(const Params &p, int dtype, int variant, hipStream_t s, h
     if (!k || t.kt != p.chunk || 16 * t.mb * (t.nw / t.cs) != p.rows_per_tile)
         return hipErrorInvalidValue;
     // only the streaming kernel's variants 3 and 4 (6 and 7 on head pairs)
-    // plan for themselves, for at most kSelfPlanMaxBatch sequences of at most
-    // 16 query tokens, one static piece per workgroup (variants 4 and 7 may
-    // add claimed pieces) or, without split, one whole unit per workgroup
-    const bool self_var = variant == 3 || variant == 4 || variant == 6 || variant == 7;
+    // and the 576/512 kernel's variant 8 plan for themselves, for at most
+    // kSelfPlanMaxBatch sequences, one static piece per workgroup (variants 4
+    // and 7 may add claimed pieces) or, without split, one whole unit per
+    // workgroup: the streaming kernel for at most 16 query tokens per
+    // sequence, variant 8 for one row tile per (sequence, KV head) and no
+    // whole-tile tasks
+    const bool self_var = variant == 3 || variant == 4 || variant == 6 || variant == 7 || variant == 8;
     const bool tail_var = variant == 4 || variant == 7;
     if ((p.self_plan != 0) != self_var || (p.tail_min > 0) != tail_var ||
-        (p.self_plan && (t.nw != 1 || p.batch > kSelfPlanMaxBatch || (!p.no_split && p.pieces != p.partitions) ||
-                         p.max_q > 16)))
+        (p.self_plan && (p.batch > kSelfPlanMaxBatch || (!p.no_split && p.pieces != p.partitions) ||
+                         (t.nw == 1 ? p.max_q > 16 : (p.max_tiles != 1 || p.tile_order != 0)))))
         return hipErrorInvalidValue;
     void *args[] = {(void *)&p};
     return launch_kernel(k, dim3(p.partitions), dim3(t.threads), args, s, e0, e1);

@@ -246,7 +246,7 @@ constexpr int tile_min_wgs()
 // piece comes from the cache row of its entry's token (the rows of a chunk
 // sit one per lane and each lane takes its own with ds_bpermute), and a
 // per-chunk bit mask marks the entries that select a visible token.
-template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH, int MODE>
+template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH, int MODE, bool SELF = false>
 __global__ __launch_bounds__(64 * NW, (tile_min_wgs<DK, DV, MB, KT, S, NW, CS, SH, MODE == MODE_TENSOR>()))
 void tile_kernel(Params p)
 {
@@ -304,17 +304,160 @@ void tile_kernel(Params p)
     Cursor cu;
     int end;
     __shared__ int s_piece;
+    // SELF (the kernel plans for itself): context length, query length,
+    // first packed query row and first item of each sequence
+    __shared__ int s_skv[SELF ? kSelfPlanMaxBatch : 1], s_sql[SELF ? kSelfPlanMaxBatch : 1];
+    __shared__ int s_st0[SELF ? kSelfPlanMaxBatch : 1], s_swsb[SELF ? kSelfPlanMaxBatch + 1 : 1];
+    auto seq_kv = [&](int b) __attribute__((always_inline)) {
+        if constexpr (SELF)
+            return (int)__builtin_amdgcn_readfirstlane(s_skv[b]);
+        else
+            return sload(p.ws.kvlen, b);
+    };
+    auto seq_ql = [&](int b) __attribute__((always_inline)) {
+        if constexpr (SELF)
+            return (int)__builtin_amdgcn_readfirstlane(s_sql[b]);
+        else
+            return sload(p.ws.qlen, b);
+    };
+    auto seq_t0 = [&](int b) __attribute__((always_inline)) {
+        if constexpr (SELF)
+            return (int)__builtin_amdgcn_readfirstlane(s_st0[b]);
+        else
+            return sload(p.ws.cu_q, b);
+    };
+    auto seq_wsb = [&](int b) __attribute__((always_inline)) {
+        return (int)__builtin_amdgcn_readfirstlane(s_swsb[b]);
+    };
     // Whole-tile mode (the planner's choice for this pass): tasks come from
     // the queue of this workgroup's XCD (the dispatcher deals workgroups
     // round-robin over the XCDs), one whole row tile each: the first at a
     // fixed position, the others claimed (tile_claim) when kClaimAhead chunks
     // of the current one are left, by thread 0, whose claim returns while
     // those chunks are computed.
-    const bool ordered = tile_whole_tasks(DK, SH) && p.tile_order && sload(p.ws.tq, kTqMode) != 0;
+    const bool ordered = !SELF && tile_whole_tasks(DK, SH) && p.tile_order && sload(p.ws.tq, kTqMode) != 0;
     const int xq = blockIdx.x % kXcds;   // whole-tile mode: this workgroup's queue
     constexpr int kClaimAhead = 3;
     int nxt = 0;   // whole-tile mode, lane 0 of wave 0: the position claimed for the next task
-    if (ordered) {
+    if constexpr (SELF) {
+        // The kernel's own plan, for at most kSelfPlanMaxBatch sequences of
+        // one row tile per (sequence, KV head), one piece per workgroup or
+        // (no split) one unit: wave 0 reads the lengths, up to four
+        // consecutive sequences per lane, and keeps each sequence's lengths,
+        // first packed query row and first item in LDS; then every wave
+        // finds its piece there and cuts it as the plan kernel would.
+        // Workgroup 0 writes the header and the error bits, every
+        // workgroup the split entry its piece starts.
+        if (piece >= p.partitions)
+            return;
+        if (wave == 0) {
+            const int cap = seq_cap(p);
+            const int spl = (p.batch + 63) >> 6;
+            int kvr[4] = {0, 0, 0, 0}, qlr[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int b = spl * lane + i;
+                if (i < spl && b < p.batch) {
+                    kvr[i] = p.context_lens[b];
+                    qlr[i] = p.q_seq_lens ? p.q_seq_lens[b] : 1;
+                }
+            }
+            uint32_t serr = 0;
+            int t0r[4], wsbr[4];
+            int lq = 0, lw = 0;   // the lane's running sums
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int b = spl * lane + i;
+                int ipg = 0;
+                if (i < spl && b < p.batch) {
+                    serr |= sanitize_seq(p, cap, kvr[i], qlr[i]);
+                    ipg = seq_items_per_group(p, kvr[i], qlr[i]);
+                }
+                t0r[i] = lq;
+                wsbr[i] = lw;
+                lq += qlr[i];
+                lw += ipg * p.kv_head_num;
+            }
+            const int iq = wave_scan(lq, lane), iw = wave_scan(lw, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int b = spl * lane + i;
+                if (i < spl && b < p.batch) {
+                    s_skv[b] = kvr[i];
+                    s_sql[b] = qlr[i];
+                    s_st0[b] = t0r[i] + iq - lq;
+                    s_swsb[b] = wsbr[i] + iw - lw;
+                }
+            }
+            const int cq = __builtin_amdgcn_readlane(iq, 63), W = __builtin_amdgcn_readlane(iw, 63);
+            if (lane == 0)
+                s_swsb[p.batch] = W;
+            if (piece == 0) {
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1)
+                    serr |= __shfl_xor(serr, d);
+                if (cq != p.num_q_tokens)
+                    serr |= PA_DEVERR_TOKENS;
+                if (lane == 0) {
+                    // the header as the plan kernel writes it (the piece
+                    // counter, hdr[3], is the merge kernel's to reset)
+                    const int per = p.no_split ? 0 : (W + p.pieces - 1) / p.pieces;
+                    p.ws.hdr[0] = W;
+                    p.ws.hdr[1] = per > 0 ? per : (p.no_split ? 0 : 1);
+                    p.ws.hdr[2] = p.no_split ? 0 : p.pieces;
+                    p.ws.hdr[4] = p.no_split ? 0 : p.pieces;
+                    p.ws.hdr[5] = 0;
+                    p.ws.hdr[6] = p.partitions;
+                    p.ws.hdr[7] = 0;
+                    if (serr)
+                        set_error(p.ws.err, serr);
+                }
+            }
+        }
+        __syncthreads();
+        const int W = seq_wsb(p.batch);
+        if (p.no_split) {
+            // workgroup w: unit (w / Hkv, w % Hkv), if its sequence has rows
+            const int b = piece / p.kv_head_num;
+            if (b >= p.batch)
+                return;
+            const int ql = seq_ql(b);
+            if (ql <= 0)
+                return;
+            const int kv = seq_kv(b);
+            cu.b = b;
+            cu.g = piece - b * p.kv_head_num;
+            cu.qt = 0;
+            cu.c = 0;
+            cu.ntile = seq_tiles(p, ql);
+            cu.nch = unit_chunks(p, kv, ql, 0);
+            cu.item = seq_wsb(b) + cu.g * cu.nch;
+            end = cu.item + cu.nch;
+        } else {
+            // pieces of per items (one per workgroup: pieces == partitions)
+            const int per = (W + p.pieces - 1) / p.pieces;
+            const int s0 = piece * per;
+            if (per <= 0 || s0 >= W) {
+                // a boundary past the last item cuts nothing
+                if (piece > 0 && wave == 0 && lane == 0)
+                    p.ws.splits[(size_t)(piece - 1) * 8] = -1;
+                return;
+            }
+            end = s0 + per < W ? s0 + per : W;
+            // the sequence holding item s0: the last one whose first item is <= s0
+            int lo = 0, hi = p.batch - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (seq_wsb(mid) <= s0)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const int kv = seq_kv(lo), ql = seq_ql(lo);
+            cu = piece_start(p, piece, s0, s0 - per, lo, kv, ql, seq_items_per_group(p, kv, ql), seq_wsb(lo),
+                             seq_t0(lo), wave == 0 && lane == 0);
+        }
+    } else if (ordered) {
         piece = tile_first_task(p, blockIdx.x);
         if (piece < 0)
             return;
@@ -396,8 +539,8 @@ void tile_kernel(Params p)
 
     while (true) {
         const int b = cu.b, g = cu.g, qt = cu.qt;
-        const int kv = sload(p.ws.kvlen, b);
-        const int ql = sload(p.ws.qlen, b);
+        const int kv = seq_kv(b);
+        const int ql = seq_ql(b);
         // chunks [c0, c1) of the segment, counted from the sequence start (a
         // unit starts at the chunk holding its lowest visible token)
         const int cb = BAND ? unit_first_chunk(p, kv, ql, qt) : 0;
@@ -408,7 +551,7 @@ void tile_kernel(Params p)
         const int rows = ql * G;
         int rows_tile = rows - qt * R;
         rows_tile = rows_tile < R ? rows_tile : R;
-        const int t0 = sload(p.ws.cu_q, b);
+        const int t0 = seq_t0(b);
         const int prefix = seq_prefix(kv, ql);
         // tokens [lo_tile, nvis) are seen by some row of the tile; every row
         // sees [max_lo, min_lim) (the thresholds below which, and from which
@@ -1035,7 +1178,20 @@ void tile_kernel(Params p)
         cu.item += nseg;
         bool more = cu.item < end;
         if (more) {
-            cursor_next_unit(p, cu);
+            if constexpr (SELF) {
+                // the next unit: one row tile per (sequence, KV head)
+                cu.c = 0;
+                if (++cu.g >= p.kv_head_num) {
+                    cu.g = 0;
+                    do {
+                        ++cu.b;
+                    } while (cu.b < p.batch && seq_ql(cu.b) <= 0);
+                }
+                if (cu.b < p.batch)
+                    cu.nch = unit_chunks(p, seq_kv(cu.b), seq_ql(cu.b), 0);
+            } else {
+                cursor_next_unit(p, cu);
+            }
             more = cu.b < p.batch;
         }
         if (!more) {
@@ -1052,7 +1208,7 @@ void tile_kernel(Params p)
                 continue;
             }
             // this piece is done: take the next one, if any
-            if (p.no_split || p.pieces <= p.partitions)
+            if (SELF || p.no_split || p.pieces <= p.partitions)
                 break;
             if (threadIdx.x == 0)
                 s_piece = grab_piece(p);
@@ -1895,11 +2051,11 @@ __global__ __launch_bounds__(128, DK * HP > 128 ? (HP > 1 ? 2 : 1) : 3) void str
 // cache, where only K tiles are staged, 32-token chunks in two stages
 // (74 KB, two workgroups per CU).
 
-template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH, int MODE>
+template <int DT, int DK, int DV, int MB, int KT, int NW, int CS, int S, bool SH, int MODE, bool SELF = false>
 const void *pick(TileShape *t)
 {
     *t = TileShape{MB, KT, NW, CS, S, 64 * NW};
-    return (const void *)&tile_kernel<DT, DK, DV, MB, KT, NW, CS, S, SH, MODE>;
+    return (const void *)&tile_kernel<DT, DK, DV, MB, KT, NW, CS, S, SH, MODE, SELF>;
 }
 
 // The tensor mask takes 32-token chunks in variants 1 and 2 (LDS room for
@@ -1908,6 +2064,19 @@ template <int DT, int DK, int DV, int MODE>
 const void *kernel_for(int variant, bool shared, TileShape *t)
 {
     if constexpr (DK > 256) {
+        // variant 8: variant 0 planning for itself (not with the tensor mask)
+        if (variant == 8) {
+            if constexpr (MODE != MODE_TENSOR) {
+                if (shared) {
+                    if constexpr (MODE == MODE_SPARSE)
+                        return pick<DT, DK, DV, 1, 16, 4, 1, 2, true, MODE, true>(t);
+                    else
+                        return pick<DT, DK, DV, 1, 32, 4, 1, 2, true, MODE, true>(t);
+                }
+                return pick<DT, DK, DV, 1, 16, 4, 1, 3, false, MODE, true>(t);
+            }
+            return nullptr;
+        }
         if (variant != 0)
             return nullptr;
         if (shared) {

@@ -76,7 +76,7 @@ def test_config_struct_matches_header():
     dict(dtype=7), dict(mask=4), dict(mask=binding.PA_MASK_TENSOR),   # (no matrix given)
     dict(scale=float("inf")), dict(scale=float("nan")),
     dict(num_partitions=-1), dict(flags=binding.PA_FLAG_FORCE_VALU | binding.PA_FLAG_FORCE_MFMA),
-    dict(flags=64), dict(flags=32),
+    dict(flags=64), dict(flags=128),
     dict(flags=binding.PA_FLAG_SHARED_KV, head_size_k=64, head_size_v=128),
     dict(mask=binding.PA_MASK_BAND, window_left=-1), dict(mask=binding.PA_MASK_BAND, window_right=-5),
     dict(mask=binding.PA_MASK_BAND, window_left=(1 << 30) + 1),

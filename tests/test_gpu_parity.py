@@ -732,6 +732,88 @@ def test_claimed_tail_repeatable_and_reset_between_calls():
     assert att.device_error() == 0
 
 
+# Kernels that cut their own pieces (the streaming kernel; the 576/512 tile
+# kernel for one row tile per unit) cut them as the plan kernel does.  With
+# PA_FLAG_PLAN_KERNEL the plan kernel runs instead, on the same pieces, so the
+# two passes give the same bits; the per-kernel events show which one ran.
+SELF_PLAN_CASES = [
+    # (name, problem, flags)
+    ("mla_decode", lambda: synth.custom([700, 0, 33, 2050, 16, 1500, 290], 32, 1, 576, 512, 64, "bf16", seed=41), 0),
+    ("mla_decode_fewer_items_than_workers",
+     lambda: synth.custom([20, 3, 40], 16, 1, 576, 512, 16, "f16", seed=42), 0),
+    ("mla_decode_rows_0", lambda: synth.custom([300, 90, 5, 600], 16, 1, 576, 512, 32, "bf16",
+                                               q_seq_lens=[1, 0, 1, 0], seed=43), 0),
+    ("band_shared_whole_units", lambda: synth.custom([300, 5, 900, 129], 64, 1, 576, 512, 64, "bf16", "band",
+                                                     window=(127, 0), shared_kv=True, seed=44), 0),
+    ("sparse_lists", lambda: _sparse_problem(([1500, 77, 640, 0, 333], 64, 1, 576, 512, 128, "bf16", None, 512,
+                                              True), 45), 0),
+    ("stream_static_pieces", lambda: synth.custom([700, 129, 2050, 5], 32, 8, 128, 128, 128, "bf16", seed=7),
+     F.PA_FLAG_STATIC_PIECES),
+    ("stream_whole_units", lambda: synth.custom([116, 79, 105, 3], 32, 8, 128, 128, 16, "f16", seed=9,
+                                                max_blocks=8), 0),
+]
+
+
+@pytest.mark.parametrize("case", SELF_PLAN_CASES, ids=[c[0] for c in SELF_PLAN_CASES])
+def test_self_planned_pass_matches_plan_kernel(case):
+    name, make, flags = case
+    log(f"self plan {name}")
+    p_cpu = make()
+    p = to_device(p_cpu)
+    res = []
+    for extra, planned in ((0, 0), (F.PA_FLAG_PLAN_KERNEL, 1)):
+        att = binding.for_problem(p, flags=flags | extra)
+        binding.pa_set_timing(att.handle, 1)
+        o, l, _ = run_hip(p, att=att)
+        _, passes, n_planned, _ = binding.pa_read_timing(att.handle)
+        assert (passes, n_planned) == (1, planned), name
+        assert att.device_error() == 0, name
+        res.append((o, l))
+    assert np.array_equal(res[0][0], res[1][0], equal_nan=True), name
+    assert np.array_equal(res[0][1], res[1][1], equal_nan=True), name
+    ref_o, ref_l = oracle_full(p_cpu)
+    assert_close(res[0][0], ref_o, p_cpu.workload.dtype, name)
+    assert_lse_close(res[0][1], ref_l, name)
+
+
+def test_self_planned_576_flags_bad_lengths():
+    """The 576/512 kernel's own plan flags what the plan kernel flags: a query
+    token count that disagrees with the lengths, and a context the block table
+    cannot hold (clamped)."""
+    log("576 self plan: errors")
+    p = synth.custom([30, 40], 16, 1, 576, 512, 16, "bf16", q_seq_lens=[1, 1], seed=46)
+    g = to_device(p)
+    ref_o, _ = oracle_full(p)
+    g.query = g.query[:1].contiguous()   # the lengths ask for 2 query tokens
+    att = binding.for_problem(g)
+    binding.pa_set_timing(att.handle, 1)
+    o, _, _ = run_hip(g, att=att)
+    assert binding.pa_read_timing(att.handle)[2] == 0   # no plan kernel
+    assert att.device_error() & F.PA_DEVERR_TOKENS
+    assert_close(o, ref_o[:1], "bf16", "rows that exist")
+    g = to_device(synth.custom([100, 50], 16, 1, 576, 512, 16, "bf16", seed=47))
+    g.context_lens = torch.tensor([100, 10_000], dtype=torch.int32, device="cuda")   # table too short
+    att = binding.for_problem(g)
+    binding.run_problem(att, g)
+    torch.cuda.synchronize()
+    assert att.device_error() & F.PA_DEVERR_TABLE_SHORT
+
+
+@pytest.mark.parametrize("batch", [255, 256, 257])
+def test_576_batch_sizes_around_self_planning(batch):
+    """Up to 256 sequences the 576/512 kernel plans for itself, past that the
+    plan kernel runs: both agree with the oracle."""
+    log(f"576 batch {batch}")
+    rng = np.random.default_rng(500 + batch)
+    lens = rng.integers(1, 120, size=batch).tolist()
+    p = synth.custom(lens, 16, 1, 576, 512, 16, "bf16", seed=batch)
+    att = binding.for_problem(to_device(p))
+    binding.pa_set_timing(att.handle, 1)
+    check_full(p, what=f"576 batch {batch}")
+    o, l, _ = run_hip(to_device(p), att=att)
+    assert binding.pa_read_timing(att.handle)[2] == (0 if batch <= 256 else 1)
+
+
 def test_stream_sequences_without_rows():
     log("sequences without query rows")
     p = synth.custom([40, 70, 5, 130, 64, 1, 333], 8, 4, 128, 128, 16, "bf16",

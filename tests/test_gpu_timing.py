@@ -23,6 +23,8 @@ CASES = [
      True, True),
     ("decode_short_whole_units",   # every unit whole: neither a plan nor a merge kernel
      lambda: synth.custom([116, 79, 105, 3], 32, 8, 128, 128, 16, "f16", seed=9, max_blocks=8), 0, False, False),
+    ("mla_self_planned",   # the 576/512 kernel cuts its own pieces: no plan kernel
+     lambda: synth.custom([700, 129, 2050, 5], 16, 1, 576, 512, 64, "bf16", seed=7), 0, False, True),
     ("causal_planned",
      lambda: synth.custom([300, 24, 900], 8, 2, 128, 128, 64, "f16", "causal", q_seq_lens=[40, 8, 200], seed=8),
      0, True, True),
