@@ -160,12 +160,8 @@ struct pa_handle {
             v.chunk = pa::tile_chunk(dk, dv, var, sh, mode);
             v.partitions = num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, var, sh, mode);
             // the self-planning twin of the 576/512 kernel, where it keeps
-            // the same workgroups per CU; not for the one-cache kernel
-            // without a mask, whose attention time grew by as much as the
-            // plan launch saved (272 -> 281 us on the 128-sequence MLA
-            // decode with one cache; the band and sparse-list modes of the
-            // same kernel still gain)
-            v.tile_self = !v.streaming && var == 0 && !(sh && cfg.mask == PA_MASK_NONE) &&
+            // the same workgroups per CU
+            v.tile_self = !v.streaming && var == 0 &&
                           pa::tile_chunk(dk, dv, kTileSelfPlanVariant, sh, mode) == v.chunk &&
                           num_cus * pa::tile_workers_per_cu(cfg.dtype, dk, dv, kTileSelfPlanVariant, sh, mode) >=
                               v.partitions;

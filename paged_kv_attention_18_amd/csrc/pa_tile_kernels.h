@@ -1134,6 +1134,15 @@ void tile_kernel(Params p)
 
         // -------------------------------------------------------- finalise
         if (wave_active) {
+            // One-cache 576/512 tiles (at the register limit): the lane's
+            // row and column taken afresh, so that the store indices derived
+            // from them are computed here instead of being kept (spilled)
+            // through the chunk loop
+            constexpr bool FRESH = SH && !SPARSE && DK > 256;
+            int lane_f = lane;
+            if constexpr (FRESH)
+                asm volatile("" : "+v"(lane_f));
+            const int lr_f = FRESH ? (lane_f & 15) : lr, lg_f = FRESH ? (lane_f >> 4) : lg;
             const int slot = first_seg ? 0 : 1;
             float *part = p.ws.partials + (size_t)(2 * piece + slot) * p.partial_stride;
 #pragma unroll
@@ -1142,9 +1151,9 @@ void tile_kernel(Params p)
                 const float Ms = m_run[mb] * sc;   // log2 domain
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float Lr = __shfl(L, 4 * lg + r);
-                    const float Mr = __shfl(Ms, 4 * lg + r);
-                    const int row_t = wr0 + 16 * mb + 4 * lg + r;
+                    const float Lr = __shfl(L, 4 * lg_f + r);
+                    const float Mr = __shfl(Ms, 4 * lg_f + r);
+                    const int row_t = wr0 + 16 * mb + 4 * lg_f + r;
                     if (row_t >= rows_tile)
                         continue;
                     const int rg = qt * R + row_t;
@@ -1157,15 +1166,15 @@ void tile_kernel(Params p)
                         uint16_t *dst = og + ((size_t)t * H + h) * DV;
 #pragma unroll
                         for (int nd = 0; nd < ND; ++nd)
-                            dst[col0 + 16 * nd + lr] = to_bits<DT>(oacc[mb][nd][r] * inv);
-                        if (lr == 0 && csl == 0 && p.lse)
+                            dst[col0 + 16 * nd + lr_f] = to_bits<DT>(oacc[mb][nd][r] * inv);
+                        if (lr_f == 0 && csl == 0 && p.lse)
                             p.lse[(size_t)t * H + h] =
                                 Lr > 0.f ? (Mr + log2f(Lr)) * 0.69314718055994531f : -INFINITY;
                     } else {
 #pragma unroll
                         for (int nd = 0; nd < ND; ++nd)
-                            part[row_t * DV + col0 + 16 * nd + lr] = oacc[mb][nd][r];
-                        if (lr == 0 && csl == 0) {
+                            part[row_t * DV + col0 + 16 * nd + lr_f] = oacc[mb][nd][r];
+                        if (lr_f == 0 && csl == 0) {
                             part[R * DV + row_t] = Mr;
                             part[R * DV + R + row_t] = Lr;
                         }
