@@ -745,6 +745,13 @@ SELF_PLAN_CASES = [
                                                q_seq_lens=[1, 0, 1, 0], seed=43), 0),
     ("band_shared_whole_units", lambda: synth.custom([300, 5, 900, 129], 64, 1, 576, 512, 64, "bf16", "band",
                                                      window=(127, 0), shared_kv=True, seed=44), 0),
+    # several query tokens per sequence, still one 64-row tile (G 16, at most 4 tokens): causal rows
+    ("mla_causal_four_tokens", lambda: synth.custom(
+        np.random.default_rng(48).integers(4, 700, size=60).tolist(), 16, 1, 576, 512, 32, "f16", "causal",
+        q_seq_lens=np.random.default_rng(49).integers(0, 5, size=60).tolist(), seed=48), 0),
+    ("mla_decode_200_sequences", lambda: synth.custom(
+        np.random.default_rng(50).integers(0, 1500, size=200).tolist(), 16, 1, 576, 512, 64, "bf16",
+        shared_kv=True, seed=50), 0),
     ("sparse_lists", lambda: _sparse_problem(([1500, 77, 640, 0, 333], 64, 1, 576, 512, 128, "bf16", None, 512,
                                               True), 45), 0),
     ("stream_static_pieces", lambda: synth.custom([700, 129, 2050, 5], 32, 8, 128, 128, 128, "bf16", seed=7),
