@@ -39,7 +39,7 @@ struct Variant {
     bool claimed_tail;   // self-planning launches cut a claimed tail (up to pa::kTailRounds rounds)
     bool streaming;      // MFMA: the one-wave streaming kernel (units of at most 16 rows)
     int hp;              // KV heads per unit (2: head pairs, streaming kernel)
-    int self_variant, tail_variant;   // streaming: the self-planning variants (without, with claims)
+    int self_variant, tail_variant;   // the self-planning variants (streaming: without, with claims; 576/512: 8)
     bool tile_self;      // 576/512 tile kernel: its self-planning twin serves this mode at full occupancy
     int max_pieces() const { return partitions * (claimed_tail ? 1 + pa::kTailRounds : pieces_per_worker); }
 };
