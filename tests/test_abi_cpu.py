@@ -105,6 +105,15 @@ def test_create_without_gpu_reports_hip_error(lib):
     assert create_status(lib, good_cfg()) in (binding.PA_ERR_HIP, binding.PA_ERR_UNSUPPORTED)
 
 
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU error path")
+@pytest.mark.parametrize("flags", [binding.PA_FLAG_PLAN_KERNEL, binding.PA_FLAG_PLAN_KERNEL | binding.PA_FLAG_STATIC_PIECES,
+                                   binding.PA_FLAG_PLAN_KERNEL | binding.PA_FLAG_NO_SPLIT])
+def test_create_accepts_every_declared_flag(lib, flags):
+    """Declared flags pass the configuration check (which runs before any HIP
+    call); without a GPU the call then fails in HIP, not as an invalid argument."""
+    assert create_status(lib, good_cfg(flags=flags)) in (binding.PA_ERR_HIP, binding.PA_ERR_UNSUPPORTED)
+
+
 def test_forward_null_handle(lib):
     st = lib.pa_forward(None, 1, 1, 1, 1, 1, None, 1, 1, 1, 1, None, None)
     assert st == binding.PA_ERR_INVALID_ARG
