@@ -546,8 +546,9 @@ def test_hip_graph_replays_match_eager():
     """pa_forward captured in a HIP graph (through torch's graph capture):
     every replay, with other GPU work and synchronisations in between,
     gives the eager result bit for bit (decode with split units, a causal
-    splitfuse mix on the matrix cores, the claimed tail, and a short decode
-    whose units run whole with no merge)."""
+    splitfuse mix on the matrix cores, the claimed tail, a short decode
+    whose units run whole with no merge, and the 576/512 kernel planning for
+    itself, split and whole)."""
     log("graph replay")
     tail = synth.custom(np.random.default_rng(29).integers(1000, 4000, size=24).tolist(), 32, 8, 128, 128, 128,
                         "bf16", seed=29)
@@ -556,7 +557,12 @@ def test_hip_graph_replays_match_eager():
                          (synth.custom([600, 90], 8, 2, 128, 128, 64, "f16", "causal", q_seq_lens=[130, 6],
                                        seed=28), 0),
                          (tail, 16),    # the streaming kernel's claimed tail (counter reset by the merge)
-                         (short, 0)):   # whole units: one kernel, no merge
+                         (short, 0),    # whole units: one kernel, no merge
+                         # the 576/512 kernel planning for itself, one cache, then band whole units
+                         (synth.custom([700, 33, 2050, 5], 16, 1, 576, 512, 64, "bf16", seed=31,
+                                       shared_kv=True), 0),
+                         (synth.custom([300, 5, 900, 129], 64, 1, 576, 512, 64, "bf16", "band", window=(127, 0),
+                                       shared_kv=True, seed=32), 0)):
         p = to_device(p_cpu)
         att = binding.for_problem(p, num_partitions=parts)
         T, H, Dv = p.num_q_tokens, p.workload.head_num, p.workload.head_size_v
