@@ -21,7 +21,7 @@ from gpu_util import assert_close, assert_lse_close, log, oracle_full, run_hip, 
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 96
 MAX_WORK = 1.5e9   # row x token x (Dk + Dv) products per case (the oracle stays fast)
 
 
