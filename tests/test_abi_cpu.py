@@ -169,6 +169,26 @@ def test_piece_map_host_invariants(tmp_path):
     assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
 
 
+def test_self_plan_matches_plan_kernel_host(tmp_path):
+    """The 576/512 tile kernel's own plan, compiled for the host from the
+    library's header: for 3000 seeded passes of one row tile per unit (no
+    mask, causal, band, sparse lists; empty and malformed lengths; 1 to 256
+    sequences; split and whole units) every worker walks the same segments,
+    and every split entry is the same, as with the plan kernel's arrays
+    (tests/self_plan_host.cpp)."""
+    hipcc = "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not installed")
+    src = os.path.join(ROOT, "tests", "self_plan_host.cpp")
+    exe = str(tmp_path / "self_plan_host")
+    csrc = os.path.join(ROOT, "paged_kv_attention_18_amd", "csrc")
+    subprocess.run([hipcc, "-x", "hip", "--offload-arch=gfx950", "-O2", "-std=c++17",
+                    "-I", os.path.join(ROOT, "include"), "-I", csrc, src, "-o", exe],
+                   check=True, capture_output=True, text=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.startswith("ok 3000 "), r.stdout + r.stderr
+
+
 def test_valu_decode_addresses_in_bounds_host(tmp_path):
     """The VALU decode kernel's addressing and the planning it runs on,
     compiled for the host from the library's own header: for the causal case
